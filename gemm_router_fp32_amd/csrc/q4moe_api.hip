@@ -1,0 +1,460 @@
+// libq4moe C-ABI: host-side validation, workspace layout and launches.
+// Declarations, argument meaning, layouts and error behaviour: include/q4moe.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "q4moe.h"
+#include "q4moe_kernels.hpp"
+
+using namespace q4moe;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+q4moe_status fail(q4moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t up_to(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
+
+constexpr int kMaxDim = 4096;
+
+q4moe_status device_ready() {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(Q4MOE_EDEVICE, "no HIP device: %s", hipGetErrorString(e));
+    return Q4MOE_OK;
+}
+
+q4moe_status launched(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(Q4MOE_EDEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+    return Q4MOE_OK;
+}
+
+q4moe_status check_router(const q4moe_router* r) {
+    if (!r) return fail(Q4MOE_EINVAL, "router descriptor is NULL");
+    if (!r->w_g || !r->bias) return fail(Q4MOE_EINVAL, "router w_g / bias is NULL");
+    if (r->n_experts < 1 || r->n_experts > 256)
+        return fail(Q4MOE_EINVAL, "router n_experts %d outside [1, 256]", r->n_experts);
+    if (r->hidden < 32 || r->hidden % 32 != 0 || r->hidden > kMaxDim)
+        return fail(Q4MOE_EINVAL, "router hidden %d must be a multiple of 32 in [32, %d]", r->hidden, kMaxDim);
+    if (r->top_k < 1 || r->top_k > 8 || r->top_k > r->n_experts)
+        return fail(Q4MOE_EINVAL, "top_k %d outside [1, min(8, n_experts)]", r->top_k);
+    if (!aligned(r->w_g, 16)) return fail(Q4MOE_EALIGN, "router w_g not 16-byte aligned");
+    if (!aligned(r->bias, 4)) return fail(Q4MOE_EALIGN, "router bias not 4-byte aligned");
+    return Q4MOE_OK;
+}
+
+q4moe_status check_experts(const q4moe_experts* ex, const q4moe_router* r) {
+    if (!ex) return fail(Q4MOE_EINVAL, "experts descriptor is NULL");
+    if (ex->fmt != Q4MOE_NVFP4 && ex->fmt != Q4MOE_INT4_G64)
+        return fail(Q4MOE_EINVAL, "unknown expert format %d", ex->fmt);
+    if (ex->n_experts != r->n_experts || ex->hidden != r->hidden)
+        return fail(Q4MOE_EINVAL, "experts (%d x hidden %d) do not match the router (%d x hidden %d)",
+                    ex->n_experts, ex->hidden, r->n_experts, r->hidden);
+    const int q = ex->fmt == Q4MOE_NVFP4 ? 32 : 64;
+    if (ex->hidden % q != 0 || ex->inter < q || ex->inter % q != 0 || ex->inter > kMaxDim)
+        return fail(Q4MOE_EINVAL, "hidden %d / inter %d must be multiples of %d in [%d, %d]", ex->hidden,
+                    ex->inter, q, q, kMaxDim);
+    if (!ex->up_codes || !ex->up_scales || !ex->down_codes || !ex->down_scales)
+        return fail(Q4MOE_EINVAL, "expert code / scale pointer is NULL");
+    if (ex->fmt == Q4MOE_NVFP4 && (!ex->up_gscale || !ex->down_gscale))
+        return fail(Q4MOE_EINVAL, "NVFP4 experts need up_gscale and down_gscale");
+    if (ex->fmt == Q4MOE_INT4_G64 && (ex->up_gscale || ex->down_gscale))
+        return fail(Q4MOE_EINVAL, "INT4_G64 experts take no per-tensor scale (pass NULL)");
+    if (!aligned(ex->up_codes, 16) || !aligned(ex->down_codes, 16))
+        return fail(Q4MOE_EALIGN, "expert codes not 16-byte aligned");
+    if (!aligned(ex->up_scales, 4) || !aligned(ex->down_scales, 4))
+        return fail(Q4MOE_EALIGN, "expert scales not 4-byte aligned");
+    if ((ex->up_gscale && !aligned(ex->up_gscale, 4)) || (ex->down_gscale && !aligned(ex->down_gscale, 4)))
+        return fail(Q4MOE_EALIGN, "expert gscale not 4-byte aligned");
+    return Q4MOE_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layouts
+// ---------------------------------------------------------------------------
+
+struct RouterWs {
+    size_t ctrl, logits, ids, w, total;
+};
+
+RouterWs router_ws(int E, int K, int T) {
+    RouterWs l;
+    size_t o = 0;
+    l.ctrl = o;
+    o += up_to(CTRL_WORDS * 4);
+    l.logits = o;
+    o += up_to((size_t)T * E * 4);
+    l.ids = o;
+    o += up_to((size_t)T * K * 4);
+    l.w = o;
+    o += up_to((size_t)T * K * 4);
+    l.total = o;
+    return l;
+}
+
+struct DecodeWs {
+    RouterWs r;
+    size_t h, y32, total;
+};
+
+DecodeWs decode_ws(int E, int H, int I, int K, int T) {
+    DecodeWs l;
+    l.r = router_ws(E, K, T);
+    size_t o = l.r.total;
+    l.h = o;
+    o += up_to((size_t)T * K * I * 4);
+    l.y32 = o;
+    o += up_to((size_t)T * H * 4);
+    l.total = o;
+    return l;
+}
+
+struct GemvWs {
+    size_t ctrl, keys, total;
+};
+
+GemvWs gemv_ws(int T) {
+    GemvWs l;
+    l.ctrl = 0;
+    l.keys = up_to(CTRL_WORDS * 4);
+    l.total = l.keys + up_to((size_t)T * 8);
+    return l;
+}
+
+q4moe_status check_ws(const void* ws, size_t have, size_t need) {
+    if (!ws) return fail(Q4MOE_EINVAL, "workspace is NULL");
+    if (!aligned(ws, 16)) return fail(Q4MOE_EALIGN, "workspace not 16-byte aligned");
+    if (have < need) return fail(Q4MOE_EWORKSPACE, "workspace %zu bytes, need %zu", have, need);
+    return Q4MOE_OK;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+RouterArgs router_args(const q4moe_router* r, const uint16_t* x, int T, void* ws, const RouterWs& l,
+                       int32_t* ids_out, float* w_out, float* logits_out) {
+    RouterArgs a;
+    a.wg = r->w_g;
+    a.bias = r->bias;
+    a.x = x;
+    a.E = r->n_experts;
+    a.H = r->hidden;
+    a.T = T;
+    a.K = r->top_k;
+    a.logits = at<float>(ws, l.logits);
+    a.ids = at<int32_t>(ws, l.ids);
+    a.w = at<float>(ws, l.w);
+    a.ids_out = ids_out;
+    a.w_out = w_out;
+    a.logits_out = logits_out;
+    return a;
+}
+
+q4moe_status launch_router(const RouterArgs& a, hipStream_t s) {
+    dim3 g1((a.E + 3) / 4, (a.T + 3) / 4);
+    hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, a);
+    q4moe_status st = launched("router logits");
+    if (st != Q4MOE_OK) return st;
+    hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
+    return launched("router top-k");
+}
+
+template <int FMT>
+q4moe_status launch_up(const MoeArgs& a, hipStream_t s) {
+    dim3 grid((a.I + 7) / 8, a.T * a.K);
+    const int C = (a.H / 32 + 31) / 32;
+    switch (C) {
+        case 1: hipLaunchKernelGGL((k_up<1, FMT>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_up<2, FMT>), grid, dim3(256), 0, s, a); break;
+        case 3: hipLaunchKernelGGL((k_up<3, FMT>), grid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL((k_up<4, FMT>), grid, dim3(256), 0, s, a); break;
+        default: return fail(Q4MOE_EUNSUPPORTED, "hidden %d too wide", a.H);
+    }
+    return launched("up projection");
+}
+
+template <int FMT, int T>
+q4moe_status launch_down_t(const MoeArgs& a, hipStream_t s) {
+    dim3 grid((a.H + 15) / 16);
+    const int C = (a.I / 32 + 63) / 64;
+    switch (C) {
+        case 1: hipLaunchKernelGGL((k_down<1, FMT, T>), grid, dim3(256), 0, s, a); break;
+        case 2: hipLaunchKernelGGL((k_down<2, FMT, T>), grid, dim3(256), 0, s, a); break;
+        default: return fail(Q4MOE_EUNSUPPORTED, "inter %d too wide", a.I);
+    }
+    return launched("down projection");
+}
+
+template <int FMT>
+q4moe_status launch_down(const MoeArgs& a, hipStream_t s) {
+    switch (a.T) {
+        case 1: return launch_down_t<FMT, 1>(a, s);
+        case 2: return launch_down_t<FMT, 2>(a, s);
+        case 3: return launch_down_t<FMT, 3>(a, s);
+        default: return launch_down_t<FMT, 4>(a, s);
+    }
+}
+
+}  // namespace
+
+// ===========================================================================
+// Entry points
+// ===========================================================================
+
+extern "C" {
+
+const char* q4moe_status_str(q4moe_status s) {
+    switch (s) {
+        case Q4MOE_OK: return "ok";
+        case Q4MOE_EINVAL: return "invalid argument";
+        case Q4MOE_EALIGN: return "misaligned pointer";
+        case Q4MOE_EUNSUPPORTED: return "unsupported";
+        case Q4MOE_EWORKSPACE: return "workspace too small";
+        case Q4MOE_EDEVICE: return "device error";
+    }
+    return "unknown status";
+}
+
+const char* q4moe_last_error(void) { return g_err; }
+
+int32_t q4moe_abi_version(void) { return Q4MOE_ABI_VERSION; }
+
+q4moe_status q4moe_ws_init(void* ws, size_t ws_bytes, void* stream) {
+    if (!ws) return fail(Q4MOE_EINVAL, "workspace is NULL");
+    if (!aligned(ws, 16) || ws_bytes % 16 != 0)
+        return fail(Q4MOE_EALIGN, "workspace must be 16-byte aligned and a multiple of 16 bytes");
+    q4moe_status st = device_ready();
+    if (st != Q4MOE_OK) return st;
+    const size_t n16 = ws_bytes / 16;
+    if (n16 == 0) return Q4MOE_OK;
+    const size_t blocks = (n16 + 255) / 256 < 1024 ? (n16 + 255) / 256 : 1024;
+    hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (uint4*)ws, n16);
+    return launched("workspace init");
+}
+
+q4moe_status q4moe_ws_check(const void* ws, size_t ws_bytes, void* stream, uint32_t* flags) {
+    if (!ws || !flags) return fail(Q4MOE_EINVAL, "workspace / flags is NULL");
+    if (ws_bytes < CTRL_WORDS * 4) return fail(Q4MOE_EWORKSPACE, "workspace smaller than its control words");
+    q4moe_status st = device_ready();
+    if (st != Q4MOE_OK) return st;
+    hipError_t e = hipMemcpyAsync(flags, static_cast<const uint32_t*>(ws) + CTRL_FLAGS, 4, hipMemcpyDeviceToHost,
+                                  (hipStream_t)stream);
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(Q4MOE_EDEVICE, "reading the workspace status: %s", hipGetErrorString(e));
+    return Q4MOE_OK;
+}
+
+// --- router ----------------------------------------------------------------
+
+size_t q4moe_router_topk_ws_bytes(const q4moe_router* r, int32_t n_tok) {
+    if (!r || n_tok < 1) return 0;
+    return router_ws(r->n_experts, r->top_k, n_tok).total;
+}
+
+q4moe_status q4moe_router_topk(const q4moe_router* r, const uint16_t* x_bf16, int32_t n_tok, int32_t* ids,
+                               float* w, float* logits, void* ws, size_t ws_bytes, void* stream) {
+    q4moe_status st = check_router(r);
+    if (st != Q4MOE_OK) return st;
+    if (n_tok < 1 || n_tok > 65536) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 65536]", n_tok);
+    if (!x_bf16 || !ids || !w) return fail(Q4MOE_EINVAL, "x / ids / w is NULL");
+    if (!aligned(x_bf16, 16)) return fail(Q4MOE_EALIGN, "x not 16-byte aligned");
+    if (!aligned(ids, 4) || !aligned(w, 4) || (logits && !aligned(logits, 4)))
+        return fail(Q4MOE_EALIGN, "ids / w / logits not 4-byte aligned");
+    RouterWs l = router_ws(r->n_experts, r->top_k, n_tok);
+    if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    return launch_router(router_args(r, x_bf16, n_tok, ws, l, ids, w, logits), (hipStream_t)stream);
+}
+
+// --- reference dequantization --------------------------------------------
+
+q4moe_status q4moe_dequant_ref(const q4moe_qmat* m, float* out, void* stream) {
+    if (!m) return fail(Q4MOE_EINVAL, "matrix descriptor is NULL");
+    if (m->fmt != Q4MOE_NVFP4 && m->fmt != Q4MOE_INT4_G64) return fail(Q4MOE_EINVAL, "unknown format %d", m->fmt);
+    const int blk = m->fmt == Q4MOE_NVFP4 ? 16 : 64;
+    if (m->rows < 1 || m->cols < blk || m->cols % blk != 0)
+        return fail(Q4MOE_EINVAL, "shape %d x %d: rows >= 1 and cols a positive multiple of %d", m->rows, m->cols,
+                    blk);
+    if (!m->codes || !m->scales || !out) return fail(Q4MOE_EINVAL, "codes / scales / out is NULL");
+    if (m->fmt == Q4MOE_NVFP4 && !m->gscale) return fail(Q4MOE_EINVAL, "NVFP4 needs gscale");
+    if (m->fmt == Q4MOE_INT4_G64 && m->gscale) return fail(Q4MOE_EINVAL, "INT4_G64 takes no gscale");
+    if (!aligned(m->codes, 16) || !aligned(out, 16)) return fail(Q4MOE_EALIGN, "codes / out not 16-byte aligned");
+    if (!aligned(m->scales, 4)) return fail(Q4MOE_EALIGN, "scales not 4-byte aligned");
+    q4moe_status st = device_ready();
+    if (st != Q4MOE_OK) return st;
+    const size_t ndw = (size_t)m->rows * m->cols / 8;
+    hipLaunchKernelGGL(k_dequant, dim3((unsigned)((ndw + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       m->fmt, m->rows, m->cols, m->codes, m->scales, m->gscale, out);
+    return launched("dequant");
+}
+
+// --- W4A16 decode ---------------------------------------------------------
+
+size_t q4moe_w4a16_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
+    if (!r || !ex || n_tok < 1) return 0;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
+}
+
+q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
+                                     q4moe_decode_taps* out) {
+    if (!r || !ex || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok);
+    out->y32 = l.y32;
+    out->h = l.h;
+    return Q4MOE_OK;
+}
+
+q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                                int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
+                                size_t ws_bytes, void* stream) {
+    q4moe_status st = check_router(r);
+    if (st != Q4MOE_OK) return st;
+    if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
+    if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
+    if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
+    if ((ids && !aligned(ids, 4)) || (w && !aligned(w, 4))) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok);
+    if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+
+    RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
+    if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;
+
+    MoeArgs a;
+    a.fmt = ex->fmt;
+    a.E = ex->n_experts;
+    a.H = ex->hidden;
+    a.I = ex->inter;
+    a.K = r->top_k;
+    a.T = n_tok;
+    a.upc = ex->up_codes;
+    a.ups = ex->up_scales;
+    a.upg = ex->up_gscale;
+    a.dnc = ex->down_codes;
+    a.dns = ex->down_scales;
+    a.dng = ex->down_gscale;
+    a.x = x_bf16;
+    a.ids = ra.ids;
+    a.w = ra.w;
+    a.h = at<float>(ws, l.h);
+    a.y32 = at<float>(ws, l.y32);
+    a.y = y_bf16;
+    if (ex->fmt == Q4MOE_NVFP4) {
+        if ((st = launch_up<FMT_NVFP4>(a, s)) != Q4MOE_OK) return st;
+        return launch_down<FMT_NVFP4>(a, s);
+    }
+    if ((st = launch_up<FMT_INT4>(a, s)) != Q4MOE_OK) return st;
+    return launch_down<FMT_INT4>(a, s);
+}
+
+// --- W4A4 grouped (not built yet) -----------------------------------------
+
+size_t q4moe_w4a4_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
+    (void)r;
+    (void)ex;
+    (void)n_tok;
+    return 0;
+}
+
+q4moe_status q4moe_w4a4_grouped_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
+                                     q4moe_w4a4_taps* out) {
+    (void)r;
+    (void)ex;
+    (void)n_tok;
+    (void)out;
+    return fail(Q4MOE_EUNSUPPORTED, "W4A4 grouped path not available in this build");
+}
+
+q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                                int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
+                                size_t ws_bytes, void* stream) {
+    (void)r;
+    (void)ex;
+    (void)x_bf16;
+    (void)n_tok;
+    (void)y_bf16;
+    (void)ids;
+    (void)w;
+    (void)ws;
+    (void)ws_bytes;
+    (void)stream;
+    return fail(Q4MOE_EUNSUPPORTED, "W4A4 grouped path not available in this build");
+}
+
+// --- lm_head GEMV ---------------------------------------------------------
+
+size_t q4moe_w4a16_gemv_ws_bytes(const q4moe_qmat* m, int32_t n_tok) {
+    if (!m || n_tok < 1) return 0;
+    return gemv_ws(n_tok).total;
+}
+
+q4moe_status q4moe_w4a16_gemv(const q4moe_qmat* m, const uint16_t* x_bf16, int32_t n_tok, float* logits,
+                              int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+    if (!m) return fail(Q4MOE_EINVAL, "matrix descriptor is NULL");
+    if (m->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the lm_head GEMV takes NVFP4 only");
+    if (m->rows < 1 || m->cols < 32 || m->cols % 32 != 0 || m->cols > kMaxDim)
+        return fail(Q4MOE_EINVAL, "shape %d x %d: cols a multiple of 32 in [32, %d]", m->rows, m->cols, kMaxDim);
+    if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    if (!m->codes || !m->scales || !m->gscale || !x_bf16 || !logits)
+        return fail(Q4MOE_EINVAL, "codes / scales / gscale / x / logits is NULL");
+    if (!aligned(m->codes, 16) || !aligned(x_bf16, 16) || !aligned(logits, 16))
+        return fail(Q4MOE_EALIGN, "codes / x / logits not 16-byte aligned");
+    if (!aligned(m->scales, 4) || (argmax && !aligned(argmax, 4)))
+        return fail(Q4MOE_EALIGN, "scales / argmax not 4-byte aligned");
+    GemvWs l = gemv_ws(n_tok);
+    q4moe_status st = check_ws(ws, ws_bytes, l.total);
+    if (st != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    GemvArgs a;
+    a.rows = m->rows;
+    a.cols = m->cols;
+    a.T = n_tok;
+    a.codes = m->codes;
+    a.scales = static_cast<const uint8_t*>(m->scales);
+    a.gscale = m->gscale;
+    a.x = x_bf16;
+    a.logits = logits;
+    a.argmax = argmax;
+    a.keys = at<unsigned long long>(ws, l.keys);
+    a.ctrl = at<uint32_t>(ws, l.ctrl);
+    const int C = (m->cols / 32 + 31) / 32;
+    dim3 grid((m->rows + 63) / 64);
+    hipStream_t s = (hipStream_t)stream;
+#define Q4_GEMV(CC, TT) hipLaunchKernelGGL((k_gemv<CC, TT>), grid, dim3(256), 0, s, a)
+#define Q4_GEMV_T(CC)                \
+    switch (n_tok) {                 \
+        case 1: Q4_GEMV(CC, 1); break; \
+        case 2: Q4_GEMV(CC, 2); break; \
+        case 3: Q4_GEMV(CC, 3); break; \
+        default: Q4_GEMV(CC, 4); break; \
+    }
+    switch (C) {
+        case 1: Q4_GEMV_T(1); break;
+        case 2: Q4_GEMV_T(2); break;
+        case 3: Q4_GEMV_T(3); break;
+        default: Q4_GEMV_T(4); break;
+    }
+#undef Q4_GEMV_T
+#undef Q4_GEMV
+    return launched("lm_head gemv");
+}
+
+}  // extern "C"

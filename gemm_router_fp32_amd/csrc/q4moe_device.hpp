@@ -1,0 +1,194 @@
+// Device helpers shared by the libq4moe kernels (gfx950, wave64).
+//
+// Element formats ("Let's optimize Nemotron 3.5 Lightning - a worklog",
+// Step 1: NVFP4 with one scale per 16 weights; "NVIDIA-Nemotron-3.5-
+// Lightning-30B-A3B-W4A16" README, What was changed: int4, group 64,
+// symmetric): E2M1 codes are decoded by the gfx950 FP4 conversion
+// instructions, E4M3FN scale bytes and int4 nibbles by integer arithmetic.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4moe {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Element decoding
+// ---------------------------------------------------------------------------
+
+// E4M3FN byte -> fp32, exact.  Exponent field e (bias 7) and mantissa m:
+// e == 0 is subnormal m * 2^-9; otherwise the fp32 with exponent e - 7 and
+// the mantissa bits on top; S.1111.111 is NaN.
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+    if (e == 15u && m == 7u) mag = __builtin_nanf("");
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// Two E2M1 codes (byte `sel` of v: low nibble = first element) -> fp32 pair.
+template <int sel>
+__device__ __forceinline__ f32x2 fp4x2_f32(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, sel);
+}
+
+// Two E2M1 codes -> bf16 pair (every E2M1 value is exact in bf16).
+template <int sel>
+__device__ __forceinline__ bf16x2 fp4x2_bf16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(v, 1.0f, sel);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v) { return __builtin_bit_cast(bf16x2, v); }
+
+__device__ __forceinline__ float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums (DPP inside rows of 16 lanes, then lane permutes)
+// ---------------------------------------------------------------------------
+
+template <int ctrl>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
+}
+
+// Sum over aligned segments of SEG lanes (SEG in {16, 32, 64}); every lane of
+// a segment receives the segment's sum.
+template <int SEG>
+__device__ __forceinline__ float seg_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x124>(v);  // row_ror:4
+    v += dpp<0x128>(v);  // row_ror:8
+    if constexpr (SEG >= 32) v += __shfl_xor(v, 16, 64);
+    if constexpr (SEG >= 64) v += __shfl_xor(v, 32, 64);
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// One 16-byte chunk (32 consecutive elements of a row) times activations.
+// ---------------------------------------------------------------------------
+
+// NVFP4 chunk . bf16 activations.  q: 4 code dwords; xa: 16 bf16 pairs
+// (natural order: pair j = elements 2j, 2j+1); s0/s1: the two block scales.
+__device__ __forceinline__ float nvfp4_chunk_bf16(const uint4 q, const uint32_t* xa, float s0, float s1) {
+    float p0 = 0.f, p1 = 0.f;
+    p0 = dot2_bf16(fp4x2_bf16<0>(q.x), as_bf16x2(xa[0]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<1>(q.x), as_bf16x2(xa[1]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<2>(q.x), as_bf16x2(xa[2]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<3>(q.x), as_bf16x2(xa[3]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<0>(q.y), as_bf16x2(xa[4]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<1>(q.y), as_bf16x2(xa[5]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<2>(q.y), as_bf16x2(xa[6]), p0);
+    p0 = dot2_bf16(fp4x2_bf16<3>(q.y), as_bf16x2(xa[7]), p0);
+    p1 = dot2_bf16(fp4x2_bf16<0>(q.z), as_bf16x2(xa[8]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<1>(q.z), as_bf16x2(xa[9]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<2>(q.z), as_bf16x2(xa[10]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<3>(q.z), as_bf16x2(xa[11]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<0>(q.w), as_bf16x2(xa[12]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<1>(q.w), as_bf16x2(xa[13]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<2>(q.w), as_bf16x2(xa[14]), p1);
+    p1 = dot2_bf16(fp4x2_bf16<3>(q.w), as_bf16x2(xa[15]), p1);
+    return p0 * s0 + p1 * s1;
+}
+
+// NVFP4 chunk . fp32 activations (h of the down projection).
+template <int sel>
+__device__ __forceinline__ float fp4_pair_fma(uint32_t v, const float* h, float acc) {
+    const f32x2 w = fp4x2_f32<sel>(v);
+    acc = __builtin_fmaf(w.x, h[2 * sel], acc);
+    return __builtin_fmaf(w.y, h[2 * sel + 1], acc);
+}
+
+__device__ __forceinline__ float nvfp4_chunk_f32(const uint4 q, const float* h, float s0, float s1) {
+    float p0 = 0.f, p1 = 0.f;
+    p0 = fp4_pair_fma<0>(q.x, h + 0, p0);
+    p0 = fp4_pair_fma<1>(q.x, h + 0, p0);
+    p0 = fp4_pair_fma<2>(q.x, h + 0, p0);
+    p0 = fp4_pair_fma<3>(q.x, h + 0, p0);
+    p0 = fp4_pair_fma<0>(q.y, h + 8, p0);
+    p0 = fp4_pair_fma<1>(q.y, h + 8, p0);
+    p0 = fp4_pair_fma<2>(q.y, h + 8, p0);
+    p0 = fp4_pair_fma<3>(q.y, h + 8, p0);
+    p1 = fp4_pair_fma<0>(q.z, h + 16, p1);
+    p1 = fp4_pair_fma<1>(q.z, h + 16, p1);
+    p1 = fp4_pair_fma<2>(q.z, h + 16, p1);
+    p1 = fp4_pair_fma<3>(q.z, h + 16, p1);
+    p1 = fp4_pair_fma<0>(q.w, h + 24, p1);
+    p1 = fp4_pair_fma<1>(q.w, h + 24, p1);
+    p1 = fp4_pair_fma<2>(q.w, h + 24, p1);
+    p1 = fp4_pair_fma<3>(q.w, h + 24, p1);
+    return p0 * s0 + p1 * s1;
+}
+
+// int4 (two's complement nibbles) . bf16 activations.  Each code is turned
+// into the bf16 number 136 + code (exact: an offset-binary nibble placed
+// under the exponent of 128), so a dot2 gives sum (code + 136) * x and the
+// caller subtracts 136 * sum(x).  xq holds the activation pairs in the order
+// the unpacking produces: for dword d, (x0,x4), (x1,x5), (x2,x6), (x3,x7).
+__device__ __forceinline__ float int4_chunk_bf16(const uint4 q, const uint32_t* xq) {
+    float p = 0.f;
+    const uint32_t v[4] = {q.x ^ 0x88888888u, q.y ^ 0x88888888u, q.z ^ 0x88888888u, q.w ^ 0x88888888u};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        p = dot2_bf16(as_bf16x2((v[d] & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 0]), p);
+        p = dot2_bf16(as_bf16x2(((v[d] >> 4) & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 1]), p);
+        p = dot2_bf16(as_bf16x2(((v[d] >> 8) & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 2]), p);
+        p = dot2_bf16(as_bf16x2(((v[d] >> 12) & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 3]), p);
+    }
+    return p;
+}
+
+// Reorder the natural bf16 pairs of 8 elements (P0..P3 = (x0,x1)..(x6,x7))
+// into the int4 unpacking order (x0,x4), (x1,x5), (x2,x6), (x3,x7).
+__device__ __forceinline__ void int4_pair_order(const uint32_t* p, uint32_t* q) {
+    q[0] = __builtin_amdgcn_perm(p[2], p[0], 0x05040100u);
+    q[1] = __builtin_amdgcn_perm(p[2], p[0], 0x07060302u);
+    q[2] = __builtin_amdgcn_perm(p[3], p[1], 0x05040100u);
+    q[3] = __builtin_amdgcn_perm(p[3], p[1], 0x07060302u);
+}
+
+// Byte k of v as fp32 (the backend selects v_cvt_f32_ubyte<k>).
+template <int k>
+__device__ __forceinline__ float ubyte_f32(uint32_t v) { return (float)((v >> (8 * k)) & 0xffu); }
+
+// int4 (two's complement nibbles) . fp32 activations: offset-binary bytes
+// converted with the byte-to-float instructions; the caller subtracts
+// 8 * sum(h).
+__device__ __forceinline__ float int4_chunk_f32(const uint4 q, const float* h) {
+    float p = 0.f;
+    const uint32_t v[4] = {q.x ^ 0x88888888u, q.y ^ 0x88888888u, q.z ^ 0x88888888u, q.w ^ 0x88888888u};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const uint32_t lo = v[d] & 0x0F0F0F0Fu, hi = (v[d] >> 4) & 0x0F0F0F0Fu;
+        const float* hd = h + 8 * d;
+        p = __builtin_fmaf(ubyte_f32<0>(lo), hd[0], p);
+        p = __builtin_fmaf(ubyte_f32<0>(hi), hd[1], p);
+        p = __builtin_fmaf(ubyte_f32<1>(lo), hd[2], p);
+        p = __builtin_fmaf(ubyte_f32<1>(hi), hd[3], p);
+        p = __builtin_fmaf(ubyte_f32<2>(lo), hd[4], p);
+        p = __builtin_fmaf(ubyte_f32<2>(hi), hd[5], p);
+        p = __builtin_fmaf(ubyte_f32<3>(lo), hd[6], p);
+        p = __builtin_fmaf(ubyte_f32<3>(hi), hd[7], p);
+    }
+    return p;
+}
+
+__device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+}  // namespace q4moe

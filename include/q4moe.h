@@ -1,0 +1,196 @@
+/*
+ * libq4moe: batch-1 / few-token decode of the routed mixture-of-experts
+ * layers of a 4-bit block-quantized hybrid MoE language model, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [W] "Let's optimize Nemotron 3.5 Lightning - a worklog": Step 1 (W4A16:
+ *      NVFP4 weights, group 16, 16-bit activations, dequantized in-kernel),
+ *      Step 3 (routed experts W4A4 with a dynamic NVFP4 input quantizer;
+ *      router kept at 16/32 bits), Step 4 (NVFP4 lm_head [131072 x 2688]),
+ *      Interlude (a batch-1 GEMM is a weight read), Step 5 (k = 3 drafts:
+ *      the verifier runs 4 tokens per step).
+ *  [G] "NVIDIA-Nemotron-3.5-Lightning-30B-A3B-W4A16" README: What was
+ *      changed (int4, group 64, symmetric, weight-only; 128 routed experts
+ *      per MoE layer, 23 layers), Group size 64 (down_proj input is 1856
+ *      wide), Checkpoint layout (per-expert 2-D up_proj and down_proj, no
+ *      gate projection), Left at bfloat16 (router .gate with an fp32
+ *      e_score_correction_bias).
+ *  [Q] "Quantization (PTQ + QAD)": Precision Recipes, router compute FP32.
+ *  [S] "The Model Card's Recommended Config Was 1.9x Slower Than No
+ *      Config": The setup (128 routed experts, 6 active).
+ *
+ * Readings where the pages are silent (the library and its tests use them):
+ *  - router: logits l = W_g x in fp32; scores s = sigmoid(l); experts are
+ *    selected by the key s + bias, largest first, equal keys -> lower expert
+ *    index first; gate weights are the selected scores divided by their sum
+ *    (the bias only selects);
+ *  - expert MLP: y = sum_i w_i * down_i( relu(up_i x)^2 ), accumulated in
+ *    fp32, h kept in fp32, y rounded once to bf16 (nearest even);
+ *  - NVFP4 element: E2M1 code (OCP MX v1.0) times an E4M3FN block scale (OCP
+ *    OFP8) per 16 consecutive input elements, times an fp32 per-tensor
+ *    scale; int4-g64 element: two's complement nibble times a bf16 scale per
+ *    64 consecutive input elements;
+ *  - packing: element (r, 2j) is the low nibble (bits 3..0) of byte
+ *    r*cols/2 + j, element (r, 2j+1) the high nibble.
+ *
+ * Conventions for every entry point:
+ *  - All pointers inside descriptors and all array arguments are DEVICE
+ *    pointers, except the descriptors themselves (host structs, read during
+ *    the call only).  The caller owns every buffer and the stream; the
+ *    library never allocates, frees, copies host<->device or synchronizes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is
+ *    enqueued asynchronously on it.
+ *  - Arguments are validated on the host before anything is enqueued; on a
+ *    non-OK status nothing was enqueued and q4moe_last_error() describes the
+ *    problem.  Nothing throws, aborts or prints.
+ *  - Alignment: code arrays, x, y, logits and workspaces 16-byte aligned;
+ *    scale arrays 4-byte aligned.
+ *  - Workspaces: size from the matching *_ws_bytes() call; zero-filled before
+ *    the first use (q4moe_ws_init).  Every call leaves the workspace's
+ *    control words zero again, so one workspace serves any number of calls
+ *    issued in order on one stream; calls that overlap in time must use
+ *    different workspaces.
+ */
+#ifndef Q4MOE_H
+#define Q4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4MOE_ABI_VERSION 1
+
+typedef enum {
+    Q4MOE_OK = 0,
+    Q4MOE_EINVAL = 1,       /* null pointer, bad size or shape */
+    Q4MOE_EALIGN = 2,       /* misaligned pointer */
+    Q4MOE_EUNSUPPORTED = 3, /* valid but not implemented (format / shape) */
+    Q4MOE_EWORKSPACE = 4,   /* workspace too small */
+    Q4MOE_EDEVICE = 5       /* HIP runtime or kernel-side failure */
+} q4moe_status;
+
+typedef enum { Q4MOE_NVFP4 = 1, Q4MOE_INT4_G64 = 2 } q4moe_fmt;
+
+/* One quantized matrix, logical row-major [rows x cols]; y = W x.
+ * codes:  rows*cols/2 bytes (two elements per byte, low nibble first).
+ * scales: NVFP4 -> uint8 E4M3FN [rows][cols/16];
+ *         INT4_G64 -> bf16 bit patterns (uint16) [rows][cols/64].
+ * gscale: NVFP4 -> device pointer to one fp32 per-tensor scale;
+ *         INT4_G64 -> must be NULL. */
+typedef struct {
+    int32_t fmt, rows, cols;
+    const uint8_t* codes;
+    const void* scales;
+    const float* gscale;
+} q4moe_qmat;
+
+/* An expert bank, expert-major, every expert the same shape ([G] Checkpoint
+ * layout: per-expert up_proj [inter x hidden] and down_proj [hidden x inter]).
+ *  up_codes   [E][inter][hidden/2]    up_scales   [E][inter][hidden/blk]
+ *  down_codes [E][hidden][inter/2]    down_scales [E][hidden][inter/blk]
+ *  up_gscale, down_gscale: fp32 [E] (NVFP4) or NULL (INT4_G64).
+ * blk = 16 (NVFP4) or 64 (INT4_G64).  Supported: hidden and inter multiples
+ * of 32 (NVFP4) or 64 (INT4_G64), each at most 4096. */
+typedef struct {
+    int32_t fmt, n_experts, hidden, inter;
+    const uint8_t* up_codes;
+    const void* up_scales;
+    const float* up_gscale;
+    const uint8_t* down_codes;
+    const void* down_scales;
+    const float* down_gscale;
+} q4moe_experts;
+
+/* Router ([Q] router compute FP32; [G] fp32 e_score_correction_bias):
+ * w_g fp32 [n_experts][hidden] row-major, bias fp32 [n_experts];
+ * 1 <= top_k <= min(8, n_experts), n_experts <= 256. */
+typedef struct {
+    const float* w_g;
+    const float* bias;
+    int32_t n_experts, hidden, top_k;
+} q4moe_router;
+
+/* Router top-k for n_tok bf16 tokens x [n_tok][hidden] (1 <= n_tok <= 65536).
+ * Outputs ids int32 [n_tok][top_k] in selection order and w fp32
+ * [n_tok][top_k]; logits (nullable) fp32 [n_tok][n_experts]. */
+size_t q4moe_router_topk_ws_bytes(const q4moe_router* r, int32_t n_tok);
+q4moe_status q4moe_router_topk(const q4moe_router* r, const uint16_t* x_bf16, int32_t n_tok,
+                               int32_t* ids, float* w, float* logits, void* ws, size_t ws_bytes,
+                               void* stream);
+
+/* Reference dequantization of one matrix to fp32 [rows][cols], element for
+ * element the value the format defines: NVFP4 fl32((e2m1 * e4m3fn) * g),
+ * INT4_G64 int4 * bf16 ([W] Step 1; [G] What was changed).  No workspace. */
+q4moe_status q4moe_dequant_ref(const q4moe_qmat* m, float* out, void* stream);
+
+/* W4A16 routed-MoE decode of n_tok tokens (1 <= n_tok <= 4) through one
+ * layer ([W] Step 1 and Interlude; Step 5 for n_tok = 4): router top-k,
+ * up GEMV, relu^2, down GEMV, weighted combine.  x bf16 [n_tok][hidden],
+ * y bf16 [n_tok][hidden]; ids/w (nullable) receive the routing. */
+size_t q4moe_w4a16_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
+q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex,
+                                const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
+                                int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
+
+/* Byte offsets, inside a decode workspace, of values the decode leaves there
+ * after each call: y32 fp32 [n_tok][hidden] (y before rounding) and
+ * h fp32 [n_tok*top_k][inter] (relu(u)^2, rows ordered (token, slot)). */
+typedef struct { size_t y32, h; } q4moe_decode_taps;
+q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                     int32_t n_tok, q4moe_decode_taps* out);
+
+/* W4A4 routed-MoE chunk of n_tok tokens (1 <= n_tok <= 65536), NVFP4 only
+ * ([W] Step 3: routed experts take 4-bit weights and activations, the
+ * activations quantized on the fly per block of 16 with an E4M3FN scale
+ * amax/6).  Tokens are routed, dispatched per expert, and each expert runs
+ * as a grouped GEMM on the matrix cores.  x bf16 [n_tok][hidden] -> y bf16
+ * [n_tok][hidden]; ids int32 / w fp32 [n_tok][top_k] are required outputs. */
+size_t q4moe_w4a4_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
+q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex,
+                                const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
+                                int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace offsets of the W4A4 stage values left after each call.
+ * Rows p = 0 .. n_tok*top_k-1 are in dispatch order (expert ascending, then
+ * token ascending); perm int32 [n_tok*top_k] maps row p to t*top_k + slot;
+ * expert_offsets int32 [n_experts+1] are the row ranges per expert.
+ *  xq_codes uint8 [n_tok][hidden/2], xq_scales uint8 [n_tok][hidden/16]
+ *  h32 fp32 [rows][inter]        (relu(u)^2 before quantization)
+ *  hq_codes uint8 [rows][inter/2], hq_scales uint8 [rows][inter/16]
+ *  y32 fp32 [n_tok][hidden]      (y before rounding) */
+typedef struct {
+    size_t perm, expert_offsets, xq_codes, xq_scales, h32, hq_codes, hq_scales, y32;
+} q4moe_w4a4_taps;
+q4moe_status q4moe_w4a4_grouped_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                     int32_t n_tok, q4moe_w4a4_taps* out);
+
+/* NVFP4 W4A16 GEMV for the lm_head ([W] Step 4; [C] precision table:
+ * lm_head NVFP4 weight-only, block 16): logits fp32 [n_tok][rows] =
+ * W x_t for bf16 x [n_tok][cols], 1 <= n_tok <= 4; argmax (nullable) int32
+ * [n_tok] = lowest row index among the largest logits. */
+size_t q4moe_w4a16_gemv_ws_bytes(const q4moe_qmat* m, int32_t n_tok);
+q4moe_status q4moe_w4a16_gemv(const q4moe_qmat* m, const uint16_t* x_bf16, int32_t n_tok,
+                              float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* Zero-fill a workspace on `stream` with a kernel (no memset node, so it can
+ * be captured in a graph). */
+q4moe_status q4moe_ws_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Kernel-side status word of a workspace: 0 = fine.  Reads device memory
+ * synchronously on `stream` (for tests and diagnostics, not the hot path). */
+q4moe_status q4moe_ws_check(const void* ws, size_t ws_bytes, void* stream, uint32_t* flags);
+
+const char* q4moe_status_str(q4moe_status s);
+/* Detail of the last non-OK status on the calling thread. */
+const char* q4moe_last_error(void);
+int32_t q4moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -90,3 +90,40 @@ def brute_quant(v):
     best = np.where(s == 0.0, 0, best)
     code = best.astype(np.uint8) | (np.signbit(blocks).astype(np.uint8) << 3)
     return pack(code.reshape(rows, cols)), sb.reshape(rows, cols // 16)
+
+
+# ---------------------------------------------------------------------------
+# Output gate for bf16 results against unrounded fp64 oracle values:
+#   |y - yhat| <= ulp_bf16(yhat)/2 + 2e-3 * max(|yhat|, 1e-2 * max|yhat|)
+# (one bf16 rounding of the exact value plus 2e-3 relative error with a
+# floor at 1 % of the largest output, where relative error is meaningless)
+# ---------------------------------------------------------------------------
+
+def half_ulp_bf16(v):
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.ldexp(1.0, (e - 8).astype(np.int64)), 2.0 ** -134)
+
+
+def gate_out(y_bf16_bits, yhat, rel=2e-3):
+    """Return (ok, worst ratio of error to the allowed bound)."""
+    y = bf16_bits_to_f64(y_bf16_bits).astype(np.float64)
+    yhat = np.asarray(yhat, dtype=np.float64)
+    floor = 1e-2 * np.abs(yhat).max(axis=-1, keepdims=True)
+    bound = half_ulp_bf16(yhat) + rel * np.maximum(np.abs(yhat), floor)
+    ratio = np.abs(y - yhat) / bound
+    return bool(np.all(ratio <= 1.0)), float(ratio.max())
+
+
+def gate_f32(y32, yhat, rel=2e-3):
+    yhat = np.asarray(yhat, dtype=np.float64)
+    floor = 1e-2 * np.abs(yhat).max(axis=-1, keepdims=True)
+    ratio = np.abs(np.asarray(y32, np.float64) - yhat) / (rel * np.maximum(np.abs(yhat), floor))
+    return bool(np.all(ratio <= 1.0)), float(ratio.max())
+
+
+def bf16_rne_of_f32(a):
+    """Nearest-even bf16 bits of fp32 values (exact: integer arithmetic)."""
+    u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every entry point the header declares,
+and validates arguments on the host (no device is touched on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gemm_router_fp32_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(g.SO_PATH):
+        from gemm_router_fp32_amd import build
+        build.build()
+    return g.lib()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "q4moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(g.EXPORTS)
+
+
+def test_version_and_strings(L):
+    assert g.q4moe_abi_version() == 1
+    assert L.q4moe_status_str(0) == b"ok"
+    assert L.q4moe_status_str(4) == b"workspace too small"
+
+
+A16 = 1 << 20  # a fake 16-byte-aligned device address; never dereferenced
+
+
+def _router(E=128, H=2688, k=6, wg=A16, b=A16):
+    return g.RouterS(wg, b, E, H, k)
+
+
+def _experts(fmt=1, E=128, H=2688, I=1856, gs=A16):
+    return g.ExpertsS(fmt, E, H, I, A16, A16, gs if fmt == 1 else None, A16, A16, gs if fmt == 1 else None)
+
+
+def _decode(L, r, ex, x=A16, T=1, y=A16, ws=A16, wsb=1 << 30):
+    return L.q4moe_w4a16_decode(ctypes.byref(r), ctypes.byref(ex), x, T, y, None, None, ws, wsb, None)
+
+
+def test_decode_validation(L):
+    r, ex = _router(), _experts()
+    assert _decode(L, r, ex, x=None) == g.EINVAL
+    assert _decode(L, _router(k=0), ex) == g.EINVAL
+    assert _decode(L, _router(k=9), ex) == g.EINVAL
+    assert _decode(L, _router(wg=None), ex) == g.EINVAL
+    assert _decode(L, r, ex, T=0) == g.EINVAL
+    assert _decode(L, r, ex, T=5) == g.EINVAL
+    assert _decode(L, r, _experts(I=1850)) == g.EINVAL
+    assert _decode(L, r, _experts(fmt=7)) == g.EINVAL
+    assert _decode(L, r, _experts(gs=None)) == g.EINVAL
+    assert _decode(L, _router(H=2600), _experts(H=2600)) == g.EINVAL
+    assert b"hidden" in L.q4moe_last_error()
+    assert _decode(L, r, ex, x=A16 + 2) == g.EALIGN
+    assert _decode(L, r, ex, ws=A16 + 8) == g.EALIGN
+    need = L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+    assert need > 0
+    assert _decode(L, r, ex, wsb=need - 1) == g.EWORKSPACE
+
+
+def test_int4_needs_group_64(L):
+    # every call here fails validation, so nothing reaches a device
+    r = _router(H=2688)
+    assert _decode(L, r, _experts(fmt=2, I=1856 + 32)) == g.EINVAL  # 1888 % 64 != 0
+    ex = g.ExpertsS(2, 128, 2688, 1856, A16, A16, A16, A16, A16, None)  # int4 takes no gscale
+    assert _decode(L, r, ex) == g.EINVAL
+
+
+def test_no_device_is_a_clean_status(L):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    r, ex = _router(), _experts()
+    assert _decode(L, r, ex) == g.EDEVICE
+    assert b"device" in L.q4moe_last_error().lower()
+
+
+def test_dequant_and_gemv_validation(L):
+    m = g.QMatS(1, 128, 2688, A16, A16, A16)
+    assert L.q4moe_dequant_ref(ctypes.byref(m), None, None) == g.EINVAL
+    assert L.q4moe_dequant_ref(ctypes.byref(g.QMatS(1, 128, 40, A16, A16, A16)), A16, None) == g.EINVAL
+    assert L.q4moe_dequant_ref(ctypes.byref(g.QMatS(2, 128, 2688, A16, A16, A16)), A16, None) == g.EINVAL
+    assert L.q4moe_dequant_ref(ctypes.byref(g.QMatS(1, 128, 2688, A16, A16 + 1, A16)), A16, None) == g.EALIGN
+    need = L.q4moe_w4a16_gemv_ws_bytes(ctypes.byref(m), 4)
+    assert L.q4moe_w4a16_gemv(ctypes.byref(m), A16, 5, A16, None, A16, need, None) == g.EINVAL
+    assert L.q4moe_w4a16_gemv(ctypes.byref(m), A16, 4, A16, None, A16, need - 1, None) == g.EWORKSPACE
+    mi = g.QMatS(2, 128, 2688, A16, A16, None)
+    assert L.q4moe_w4a16_gemv(ctypes.byref(mi), A16, 1, A16, None, A16, need, None) == g.EUNSUPPORTED
+
+
+def test_router_validation(L):
+    r = _router()
+    assert L.q4moe_router_topk(ctypes.byref(r), A16, 0, A16, A16, None, A16, 1 << 20, None) == g.EINVAL
+    assert L.q4moe_router_topk(ctypes.byref(_router(E=300)), A16, 1, A16, A16, None, A16, 1 << 20, None) == g.EINVAL
+    assert L.q4moe_router_topk(ctypes.byref(r), A16, 1, A16 + 2, A16, None, A16, 1 << 20, None) == g.EALIGN
+    assert L.q4moe_router_topk(ctypes.byref(r), A16, 1, A16, A16, None, A16, 8, None) == g.EWORKSPACE
