@@ -7,7 +7,7 @@
 #include <cstring>
 
 #include "q4moe.h"
-#include "q4moe_kernels.hpp"
+#include "q4moe_fused.hpp"
 
 using namespace q4moe;
 
@@ -108,19 +108,75 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t h, y32, total;
+    size_t keys, scores, h, z, y32, total;
 };
 
 DecodeWs decode_ws(int E, int H, int I, int K, int T) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
     size_t o = l.r.total;
-    l.h = o;
-    o += up_to((size_t)T * K * I * 4);
+    l.keys = o;
+    o += up_to((size_t)kReplicas * E * 4);
+    l.scores = o;
+    o += up_to((size_t)kReplicas * E * 4);
+    l.h = o;  // copy 0 is the h tap; the single-token launch keeps kReplicas copies
+    o += up_to((size_t)(T > kReplicas ? T : kReplicas) * K * I * 4);
+    l.z = o;
+    o += up_to((size_t)K * H * 4);
     l.y32 = o;
     o += up_to((size_t)T * H * 4);
     l.total = o;
     return l;
+}
+
+// Workgroups of the fused decode that fit on the device at once (so that
+// every workgroup is resident and every wait can be satisfied), cached per
+// device and kernel variant.
+constexpr int kMaxDevices = 64;
+constexpr int kFusedVariants = 16;
+int g_fused_grid[kMaxDevices][kFusedVariants];
+
+template <int FMT, int C, int C2>
+int fused_grid(int dev, int variant) {
+    if (dev < 0 || dev >= kMaxDevices) return 0;
+    int& cached = g_fused_grid[dev][variant];
+    if (cached != 0) return cached;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<FMT, C, C2>, 64 * kWaves, 0) !=
+        hipSuccess)
+        return 0;
+    cached = cus * (per_cu < 1 ? 0 : 1);
+    return cached;
+}
+
+template <int FMT, int C, int C2>
+q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
+    const int grid = fused_grid<FMT, C, C2>(dev, variant);
+    // the router needs one workgroup per expert; a workgroup stages at most
+    // kMaxWgUp up rows (caller falls back to separate launches otherwise)
+    if (grid < a.E || ((long long)a.K * a.I + grid - 1) / grid > kMaxWgUp) return Q4MOE_EUNSUPPORTED;
+    hipLaunchKernelGGL((k_decode_fused<FMT, C, C2>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+    return launched("fused decode");
+}
+
+template <int FMT>
+q4moe_status launch_fused(const FusedArgs& a, hipStream_t s) {
+    const int C = (a.H / 32 + 31) / 32, C2 = (a.I / 32 + 63) / 64;
+    const int v = (C - 1) * 2 + (C2 - 1);
+    switch (v) {
+        case 0: return launch_fused_v<FMT, 1, 1>(a, s, v);
+        case 1: return launch_fused_v<FMT, 1, 2>(a, s, v);
+        case 2: return launch_fused_v<FMT, 2, 1>(a, s, v);
+        case 3: return launch_fused_v<FMT, 2, 2>(a, s, v);
+        case 4: return launch_fused_v<FMT, 3, 1>(a, s, v);
+        case 5: return launch_fused_v<FMT, 3, 2>(a, s, v);
+        case 6: return launch_fused_v<FMT, 4, 1>(a, s, v);
+        case 7: return launch_fused_v<FMT, 4, 2>(a, s, v);
+    }
+    return Q4MOE_EUNSUPPORTED;
 }
 
 struct GemvWs {
@@ -334,6 +390,36 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
     if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
     if ((st = device_ready()) != Q4MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+
+    if (n_tok == 1) {  // one persistent launch for the whole layer
+        FusedArgs f;
+        f.E = r->n_experts;
+        f.H = ex->hidden;
+        f.I = ex->inter;
+        f.K = r->top_k;
+        f.wg = r->w_g;
+        f.bias = r->bias;
+        f.x = x_bf16;
+        f.upc = ex->up_codes;
+        f.ups = ex->up_scales;
+        f.upg = ex->up_gscale;
+        f.dnc = ex->down_codes;
+        f.dns = ex->down_scales;
+        f.dng = ex->down_gscale;
+        f.y = y_bf16;
+        f.ids_out = ids;
+        f.w_out = w;
+        f.ctrl = at<uint32_t>(ws, l.r.ctrl);
+        f.keys = at<float>(ws, l.keys);
+        f.scores = at<float>(ws, l.scores);
+        f.ids = at<int32_t>(ws, l.r.ids);
+        f.w = at<float>(ws, l.r.w);
+        f.h = at<float>(ws, l.h);
+        f.z = at<float>(ws, l.z);
+        f.y32 = at<float>(ws, l.y32);
+        st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
+        if (st != Q4MOE_EUNSUPPORTED) return st;
+    }
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
     if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;
