@@ -108,21 +108,21 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t keys, scores, h, z, y32, total;
+    size_t sc_tag, h_tag, z_tag, h, y32, total;
 };
 
 DecodeWs decode_ws(int E, int H, int I, int K, int T) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
     size_t o = l.r.total;
-    l.keys = o;
-    o += up_to((size_t)kReplicas * E * 4);
-    l.scores = o;
-    o += up_to((size_t)kReplicas * E * 4);
-    l.h = o;  // copy 0 is the h tap; the single-token launch keeps kReplicas copies
-    o += up_to((size_t)(T > kReplicas ? T : kReplicas) * K * I * 4);
-    l.z = o;
-    o += up_to((size_t)K * H * 4);
+    l.sc_tag = o;  // single-token launch: (score, epoch) pairs, kReplicas copies
+    o += up_to((size_t)kReplicas * E * 8);
+    l.h_tag = o;   // (h, epoch) pairs, kReplicas copies
+    o += up_to((size_t)kReplicas * K * I * 8);
+    l.z_tag = o;   // (w * g * z, epoch) pairs
+    o += up_to((size_t)K * H * 8);
+    l.h = o;       // h tap
+    o += up_to((size_t)T * K * I * 4);
     l.y32 = o;
     o += up_to((size_t)T * H * 4);
     l.total = o;
@@ -155,9 +155,15 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
     const int grid = fused_grid<FMT, C, C2>(dev, variant);
-    // the router needs one workgroup per expert; a workgroup stages at most
-    // kMaxWgUp up rows (caller falls back to separate launches otherwise)
-    if (grid < a.E || ((long long)a.K * a.I + grid - 1) / grid > kMaxWgUp) return Q4MOE_EUNSUPPORTED;
+    // The router needs one workgroup per expert; every wave's up rows must fit
+    // in kMaxUp passes and its down rows in kMaxDown (all loads in flight at
+    // once), a workgroup stages at most kMaxWgUp up rows, and its down rows
+    // span at most two slots.  Otherwise the caller uses separate launches.
+    const long long RU = (long long)a.K * a.I, RD = (long long)a.K * a.H;
+    const long long nw = (long long)grid * kWaves, nwd = (long long)grid * (kWaves - 1);
+    if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RD + nwd - 1) / nwd > kMaxDown ||
+        (RU + grid - 1) / grid > kMaxWgUp || (RD + grid - 1) / grid + 1 > a.H)
+        return Q4MOE_EUNSUPPORTED;
     hipLaunchKernelGGL((k_decode_fused<FMT, C, C2>), dim3(grid), dim3(64 * kWaves), 0, s, a);
     return launched("fused decode");
 }
@@ -410,12 +416,12 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
         f.ids_out = ids;
         f.w_out = w;
         f.ctrl = at<uint32_t>(ws, l.r.ctrl);
-        f.keys = at<float>(ws, l.keys);
-        f.scores = at<float>(ws, l.scores);
+        f.sc_tag = at<unsigned long long>(ws, l.sc_tag);
+        f.h_tag = at<unsigned long long>(ws, l.h_tag);
+        f.z_tag = at<unsigned long long>(ws, l.z_tag);
         f.ids = at<int32_t>(ws, l.r.ids);
         f.w = at<float>(ws, l.r.w);
         f.h = at<float>(ws, l.h);
-        f.z = at<float>(ws, l.z);
         f.y32 = at<float>(ws, l.y32);
         st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
         if (st != Q4MOE_EUNSUPPORTED) return st;

@@ -67,6 +67,29 @@ __device__ __forceinline__ float dpp(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), ctrl, 0xF, 0xF, true));
 }
 
+// Row-broadcast DPP step: rows in row_mask receive `src` from the row
+// broadcast (row_bcast:15 = lane 15 of the row below, row_bcast:31 = lane 31),
+// the others receive 0.
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, row_mask, 0xF,
+                                                                 false));
+}
+
+// Sum over aligned segments of SEG lanes (32 or 64) using DPP only; the sum
+// lands in the LAST lane of each segment (lane 31 / 63), other lanes hold
+// partial sums.
+template <int SEG>
+__device__ __forceinline__ float seg_sum_last(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x124>(v);  // row_ror:4
+    v += dpp<0x128>(v);  // row_ror:8   (every lane: its row's sum)
+    v += dpp_bcast<0x142, 0xA>(v);  // rows 1, 3 += rows 0, 2
+    if constexpr (SEG == 64) v += dpp_bcast<0x143, 0x8>(v);  // row 3 += lane 31
+    return v;
+}
+
 // Sum over aligned segments of SEG lanes (SEG in {16, 32, 64}); every lane of
 // a segment receives the segment's sum.
 template <int SEG>
@@ -190,5 +213,13 @@ __device__ __forceinline__ float int4_chunk_f32(const uint4 q, const float* h) {
 }
 
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Streaming (read-once) 16-byte load: non-temporal, so weight streams do not
+// displace reused data (router weights, activations) from the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ldg16_stream(const uint8_t* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 }  // namespace q4moe
