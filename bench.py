@@ -2,13 +2,17 @@
 
 One step = one token through 23 independent routed-MoE layers (hidden 2688,
 expert intermediate 1856, 128 experts, top-6), each layer a router top-6,
-up GEMV, relu^2, down GEMV and weighted combine, run one after another on
-one stream.  The stack is captured once in a HIP graph and replayed.
-Inputs are seeded synthetic tensors resident in HBM before timing starts.
+up GEMV, relu^2, down GEMV and weighted combine in one launch, run one after
+another on one stream.  The stack is captured once in a HIP graph and
+replayed.  Inputs are seeded synthetic tensors resident in HBM before timing
+starts.
 
-Prints one JSON line (metric: microseconds per layer, plus achieved HBM
-bandwidth against MI355X's 8 TB/s), with the oracle's CPU time on a
-bounded sample of the same workload beside it.
+Prints one JSON line: microseconds per layer (the metric) and achieved HBM
+bandwidth against MI355X's 8 TB/s; the decode kernel's own duration (HIP
+events around single launches) for the roofline; the other workloads (the
+int4 group-64 stack, the W4A4 1024-token chunk, the four-token verify step
+with the lm_head) as extra fields; and the oracle's CPU time on a bounded
+sample of the same workload.
 """
 import argparse
 import json
@@ -20,19 +24,30 @@ import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
 
-H, I, E, K, LAYERS = 2688, 1856, 128, 6, 23
+H, I, E, K, LAYERS, V = 2688, 1856, 128, 6, 23, 131072
 SEED = 20261202
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 METRIC = "µs per routed-MoE layer at batch 1 + achieved HBM GB/s (% of MI355X peak)"
 
 
-def layer_bytes(E_=E, H_=H, I_=I, k=K, T=1):
-    """Algorithmic HBM bytes of one NVFP4 decode layer: the k selected
-    experts' codes and E4M3 scales (up and down) and fp32 per-tensor scales,
-    the fp32 router (W_g and bias), x and y (bf16)."""
-    expert = 2 * (H_ * I_ // 2 + H_ * I_ // 16 + 4)
-    return k * expert + E_ * H_ * 4 + E_ * 4 + T * H_ * 2 * 2
+def expert_bytes(fmt):
+    """Codes + block scales (+ fp32 per-tensor scales) of one expert."""
+    if fmt == "nvfp4":
+        return 2 * (H * I // 2 + H * I // 16 + 4)
+    return 2 * (H * I // 2 + H * I // 64 * 2)
+
+
+def layer_bytes(fmt="nvfp4", n_experts_read=K, T=1):
+    """Algorithmic HBM bytes of one decode layer: the selected experts'
+    weights, the fp32 router (W_g and bias), x and y (bf16)."""
+    return n_experts_read * expert_bytes(fmt) + E * H * 4 + E * 4 + T * H * 2 * 2
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def parse():
@@ -40,36 +55,155 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--no-graph", action="store_true", help="time direct launches instead of a graph replay")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle CPU sample")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--only-stack", action="store_true", help="time the NVFP4 decode stack only")
     return ap.parse_args()
 
 
-def build_stack(torch, g, synth):
-    """Generate the 23 layers on the host (one reused buffer) and upload."""
+class Timer:
+    def __init__(self, torch):
+        self.torch = torch
+
+    def __call__(self, fn, reps):
+        t = self.torch
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        t.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps  # ms
+
+
+def build_stack(torch, g, synth, fmt):
     from gpu_util import dev
-    layers = []
-    buf = None
+    fam = synth.FAM_NVFP4 if fmt == "nvfp4" else synth.FAM_INT4
+    layers, buf = [], None
     for li in range(LAYERS):
-        bank = synth.expert_bank(SEED, synth.FAM_NVFP4, li, E, H, I, "nvfp4", out=buf)
+        bank = synth.expert_bank(SEED, fam, li, E, H, I, fmt, out=buf)
         buf = bank
-        wg, b = synth.router(SEED, synth.FAM_NVFP4, li, E, H)
-        x = synth.x_rows(SEED, synth.FAM_NVFP4, li, H, [0])
+        wg, b = synth.router(SEED, fam, li, E, H)
+        x = synth.x_rows(SEED, fam, li, H, [0])
         t = {k: dev(v) for k, v in bank.items()}
-        ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
-                       t["up_gscale"], t["down_gscale"])
+        if fmt == "nvfp4":
+            ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
+                           t["up_gscale"], t["down_gscale"])
+        else:
+            ex = g.Experts(g.INT4_G64, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"])
         r = g.Router(dev(wg), dev(b), K)
-        xt = dev(x)
-        y = torch.empty((1, H), dtype=torch.int16, device="cuda")
         ws = g.workspace(g.q4moe_w4a16_decode_ws_bytes(r, ex, 1))
-        layers.append(dict(ex=ex, r=r, x=xt, y=y, ws=ws))
-        print(f"[bench] layer {li} resident", file=sys.stderr, flush=True)
+        layers.append(dict(ex=ex, r=r, x=dev(x), y=torch.empty((1, H), dtype=torch.int16, device="cuda"), ws=ws))
+    log(f"{fmt} stack resident ({LAYERS} layers)")
     return layers
 
 
+def time_stack(torch, g, layers, steps, warmup):
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for L in layers:
+            g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        step()
+    stream.wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    timer = Timer(torch)
+    ms_step = timer(graph.replay, steps)
+    # the kernel's own duration: events just around single launches
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    durs = []
+    for rep in range(4):
+        for L in layers:
+            e0.record()
+            g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
+            e1.record()
+            e1.synchronize()
+            durs.append(e0.elapsed_time(e1))
+    flags = max(g.q4moe_ws_check(L["ws"]) for L in layers)
+    return ms_step, float(np.mean(durs[LAYERS:])), flags
+
+
+def bench_w4a4(torch, g, synth, steps):
+    from gpu_util import dev
+    T = 1024
+    bank = synth.expert_bank(SEED, synth.FAM_W4A4, 0, E, H, I, "nvfp4")
+    wg, b = synth.router(SEED, synth.FAM_W4A4, 0, E, H, 0.5 / np.sqrt(H))
+    x = synth.x_rows(SEED, synth.FAM_W4A4, 0, H, [0] * T)
+    t = {k: dev(v) for k, v in bank.items()}
+    ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
+                   t["up_gscale"], t["down_gscale"])
+    r = g.Router(dev(wg), dev(b), K)
+    xt = dev(x)
+    y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ws = g.workspace(g.q4moe_w4a4_grouped_ws_bytes(r, ex, T))
+
+    def run():
+        g.q4moe_w4a4_grouped(r, ex, xt, y, ids, w, ws=ws)
+
+    for _ in range(3):
+        run()
+    ms = Timer(torch)(run, max(5, steps // 5))
+    weights = E * expert_bytes("nvfp4")
+    flops = 2.0 * 2 * T * K * H * I
+    byts = weights + E * H * 4 + 2 * T * H * 2
+    log(f"w4a4 chunk: {ms * 1e3:.1f} us")
+    return {"us": round(ms * 1e3, 2), "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "bytes": byts, "flop": flops, "tokens": T}
+
+
+def bench_verify(torch, g, synth, steps, stack_layer0):
+    """Four tokens through one NVFP4 layer, then the NVFP4 lm_head over them."""
+    from gpu_util import dev
+    L = stack_layer0
+    x4 = dev(synth.x_rows(SEED, synth.FAM_NVFP4, 0, H, [0] * 4))
+    y4 = torch.empty((4, H), dtype=torch.int16, device="cuda")
+    ws4 = g.workspace(g.q4moe_w4a16_decode_ws_bytes(L["r"], L["ex"], 4))
+    ids4 = torch.empty((4, K), dtype=torch.int32, device="cuda")
+    codes, scales, gsc = synth.lm_head(SEED, 0, 0, V, H)
+    q = g.QMat(g.NVFP4, dev(codes), dev(scales), dev(np.array([gsc], np.float32)))
+    logits = torch.empty((4, V), dtype=torch.float32, device="cuda")
+    am = torch.empty(4, dtype=torch.int32, device="cuda")
+    wsl = g.workspace(g.q4moe_w4a16_gemv_ws_bytes(q, 4))
+
+    def moe():
+        g.q4moe_w4a16_decode(L["r"], L["ex"], x4, y4, ids=ids4, ws=ws4)
+
+    def head():
+        g.q4moe_w4a16_gemv(q, y4, logits, am, ws=wsl)
+
+    for _ in range(3):
+        moe()
+        head()
+    timer = Timer(torch)
+    ms_moe, ms_head = timer(moe, steps), timer(head, steps)
+    n_union = len(np.unique(ids4.cpu().numpy()))
+    moe_bytes = layer_bytes("nvfp4", n_union, 4)
+    head_bytes = V * H // 2 + V * H // 16 + 4 + 4 * H * 2 + 4 * V * 4
+    return {"moe_us": round(ms_moe * 1e3, 2), "moe_hbm_gbps": round(moe_bytes / (ms_moe * 1e-3) / 1e9, 1),
+            "experts_read": n_union, "lm_head_us": round(ms_head * 1e3, 2),
+            "lm_head_hbm_gbps": round(head_bytes / (ms_head * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(seconds):
-    """The oracle, as it stands, on layers of the same stack until `seconds`
+    """The oracle, as it stands, on layers of the NVFP4 stack until `seconds`
     of CPU work have run; returns microseconds per layer."""
     import oracle
     import synth
@@ -100,52 +234,40 @@ def main():
 
     import gemm_router_fp32_amd as g
     import synth
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
 
     torch.cuda.set_device(0)
     g.lib()
-    layers = build_stack(torch, g, synth)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        for L in layers:
-            g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
-
-    for _ in range(3):
-        step()
+    # a plain copy of known size (256 MiB), to scale HBM traffic counters
+    src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
     torch.cuda.synchronize()
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(stream)
-        with torch.cuda.stream(s):
-            step()  # warm the capture stream
-        stream.wait_stream(s)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
 
-    run = graph.replay if graph is not None else step
-    for _ in range(args.warmup):
-        run()
-    torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t_wall = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        run()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    layers = build_stack(torch, g, synth, "nvfp4")
+    ms_step, ms_kernel, flags = time_stack(torch, g, layers, args.steps, args.warmup)
     us_layer = 1000.0 * ms_step / LAYERS
     bytes_layer = layer_bytes()
     gbs = bytes_layer / (us_layer * 1e-6) / 1e9
-    print(f"[bench] {args.steps} steps: {ms_step:.4f} ms/step, {us_layer:.3f} us/layer, {gbs:.1f} GB/s "
-          f"(wall {wall:.3f} s)", file=sys.stderr, flush=True)
+    log(f"nvfp4 stack: {ms_step:.4f} ms/step, {us_layer:.3f} us/layer, {gbs:.1f} GB/s; "
+        f"single direct launch {ms_kernel * 1e3:.2f} us; flags {flags}")
+
+    extra = {}
+    if not args.only_stack:
+        extra["verify_step"] = bench_verify(torch, g, synth, args.steps, layers[0])
+        log(f"verify step: {extra['verify_step']}")
+        del layers
+        torch.cuda.empty_cache()
+        int4 = build_stack(torch, g, synth, "int4")
+        ms4, mk4, f4 = time_stack(torch, g, int4, args.steps, args.warmup)
+        b4 = layer_bytes("int4")
+        extra["int4_stack"] = {"us_per_layer": round(1000.0 * ms4 / LAYERS, 3),
+                               "hbm_gbps": round(b4 / (ms4 / LAYERS * 1e-3) / 1e9, 1),
+                               "tokens_per_s": round(1000.0 / ms4, 1), "single_launch_us": round(mk4 * 1e3, 3),
+                               "bytes_per_layer": b4, "flags": f4}
+        log(f"int4 stack: {extra['int4_stack']}")
+        del int4
+        torch.cuda.empty_cache()
+        extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
 
     cpu = None
     if not args.skip_cpu:
@@ -168,14 +290,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": "routed-MoE decode stack: 23 NVFP4 W4A16 layers, batch 1, "
                                "hidden 2688, inter 1856, 128 experts, top-6",
-                   "format": "nvfp4-w4a16", "layers": LAYERS, "tokens": 1,
-                   "graph": graph is not None},
+                   "format": "nvfp4-w4a16", "layers": LAYERS, "tokens": 1, "graph": True},
         "hbm_gbps": round(gbs, 1),
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(1000.0 / ms_step, 1),
         "bytes_per_layer": bytes_layer,
+        "single_launch_us": round(ms_kernel * 1e3, 3),
+        # one k_decode_fused launch per layer: its average duration is the
+        # timed region over the 23 * steps launches of the graph replays
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_decode_fused", "kernel_us": round(us_layer, 3)},
+        "workspace_flags": flags,
+        "extra": extra,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -8,6 +8,7 @@
 
 #include "q4moe.h"
 #include "q4moe_fused.hpp"
+#include "q4moe_w4a4.hpp"
 
 using namespace q4moe;
 
@@ -183,6 +184,48 @@ q4moe_status launch_fused(const FusedArgs& a, hipStream_t s) {
         case 7: return launch_fused_v<FMT, 4, 2>(a, s, v);
     }
     return Q4MOE_EUNSUPPORTED;
+}
+
+struct W4a4Ws {
+    RouterWs r;
+    size_t counts, offsets, lists, perm, inv, xq_codes, xq_scales, h32, hq_codes, hq_scales, zw, y32, total;
+};
+
+W4a4Ws w4a4_ws(int E, int H, int I, int K, int T) {
+    W4a4Ws l;
+    l.r = router_ws(E, K, T);
+    const size_t rows = (size_t)T * K;
+    size_t o = l.r.total;
+    auto take = [&](size_t& off, size_t bytes) {
+        off = o;
+        o += up_to(bytes);
+    };
+    take(l.counts, (size_t)E * 4);
+    take(l.offsets, (size_t)(E + 1) * 4);
+    take(l.lists, (size_t)E * T * 4);
+    take(l.perm, rows * 4);
+    take(l.inv, rows * 4);
+    take(l.xq_codes, (size_t)T * H / 2);
+    take(l.xq_scales, (size_t)T * H / 16);
+    take(l.h32, rows * I * 4);
+    take(l.hq_codes, rows * I / 2);
+    take(l.hq_scales, rows * I / 16);
+    take(l.zw, rows * H * 4);
+    take(l.y32, (size_t)T * H * 4);
+    l.total = o;
+    return l;
+}
+
+q4moe_status check_w4a4(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
+    q4moe_status st = check_router(r);
+    if (st != Q4MOE_OK) return st;
+    if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
+    if (ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 path takes NVFP4 experts only");
+    if (ex->hidden % 64 != 0 || ex->inter % 64 != 0)
+        return fail(Q4MOE_EUNSUPPORTED, "W4A4 needs hidden and inter multiples of 64 (got %d, %d)", ex->hidden,
+                    ex->inter);
+    if (n_tok < 1 || n_tok > 65536) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 65536]", n_tok);
+    return Q4MOE_OK;
 }
 
 struct GemvWs {
@@ -457,38 +500,125 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
     return launch_down<FMT_INT4>(a, s);
 }
 
-// --- W4A4 grouped (not built yet) -----------------------------------------
+// --- W4A4 grouped -----------------------------------------------------------
 
 size_t q4moe_w4a4_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
-    (void)r;
-    (void)ex;
-    (void)n_tok;
-    return 0;
+    if (!r || !ex || n_tok < 1) return 0;
+    return w4a4_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
 }
 
 q4moe_status q4moe_w4a4_grouped_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
                                      q4moe_w4a4_taps* out) {
-    (void)r;
-    (void)ex;
-    (void)n_tok;
-    (void)out;
-    return fail(Q4MOE_EUNSUPPORTED, "W4A4 grouped path not available in this build");
+    if (!r || !ex || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
+    W4a4Ws l = w4a4_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok);
+    out->perm = l.perm;
+    out->expert_offsets = l.offsets;
+    out->xq_codes = l.xq_codes;
+    out->xq_scales = l.xq_scales;
+    out->h32 = l.h32;
+    out->hq_codes = l.hq_codes;
+    out->hq_scales = l.hq_scales;
+    out->y32 = l.y32;
+    return Q4MOE_OK;
 }
 
 q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
                                 int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
                                 size_t ws_bytes, void* stream) {
-    (void)r;
-    (void)ex;
-    (void)x_bf16;
-    (void)n_tok;
-    (void)y_bf16;
-    (void)ids;
-    (void)w;
-    (void)ws;
-    (void)ws_bytes;
-    (void)stream;
-    return fail(Q4MOE_EUNSUPPORTED, "W4A4 grouped path not available in this build");
+    q4moe_status st = check_w4a4(r, ex, n_tok);
+    if (st != Q4MOE_OK) return st;
+    if (!x_bf16 || !y_bf16 || !ids || !w) return fail(Q4MOE_EINVAL, "x / y / ids / w is NULL");
+    if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
+    if (!aligned(ids, 4) || !aligned(w, 4)) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
+    const int E = r->n_experts, H = ex->hidden, I = ex->inter, K = r->top_k, T = n_tok;
+    W4a4Ws l = w4a4_ws(E, H, I, K, T);
+    if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t rows = (size_t)T * K;
+
+    // router
+    RouterArgs ra = router_args(r, x_bf16, T, ws, l.r, ids, w, nullptr);
+    hipLaunchKernelGGL(k_router_gemm, dim3((E + 31) / 32, (T + 31) / 32), dim3(256), 0, s, ra);
+    if ((st = launched("router gemm")) != Q4MOE_OK) return st;
+    hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, ra);
+    if ((st = launched("router top-k")) != Q4MOE_OK) return st;
+
+    // dispatch
+    DispatchArgs da;
+    da.ids = ra.ids;
+    da.T = T;
+    da.K = K;
+    da.E = E;
+    da.counts = at<int32_t>(ws, l.counts);
+    da.lists = at<int32_t>(ws, l.lists);
+    da.offsets = at<int32_t>(ws, l.offsets);
+    da.perm = at<int32_t>(ws, l.perm);
+    da.inv = at<int32_t>(ws, l.inv);
+    hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(64), 0, s, da);
+    if ((st = launched("dispatch")) != Q4MOE_OK) return st;
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(256), 0, s, da);
+    if ((st = launched("dispatch scan")) != Q4MOE_OK) return st;
+
+    // x -> NVFP4
+    QuantArgs qx;
+    qx.rows = T;
+    qx.cols = H;
+    qx.v = x_bf16;
+    qx.codes = at<uint8_t>(ws, l.xq_codes);
+    qx.scales = at<uint8_t>(ws, l.xq_scales);
+    const size_t nbx = (size_t)T * H / 16;
+    hipLaunchKernelGGL((k_quant_nvfp4<true>), dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s, qx);
+    if ((st = launched("x quantization")) != Q4MOE_OK) return st;
+
+    // up: h = relu(g u)^2
+    GemmArgs gu;
+    gu.N = I;
+    gu.Kd = H;
+    gu.wc = ex->up_codes;
+    gu.wsc = static_cast<const uint8_t*>(ex->up_scales);
+    gu.wg = ex->up_gscale;
+    gu.ac = qx.codes;
+    gu.asc = qx.scales;
+    gu.offsets = da.offsets;
+    gu.perm = da.perm;
+    gu.K = K;
+    gu.a_by_token = 1;
+    gu.wgate = ra.w;
+    gu.out = at<float>(ws, l.h32);
+    hipLaunchKernelGGL((k_grouped_gemm<EPI_UP>), dim3((I + kGemmBN - 1) / kGemmBN, E), dim3(256), 0, s, gu);
+    if ((st = launched("grouped up gemm")) != Q4MOE_OK) return st;
+
+    // h -> NVFP4
+    QuantArgs qh;
+    qh.rows = (int)rows;
+    qh.cols = I;
+    qh.v = gu.out;
+    qh.codes = at<uint8_t>(ws, l.hq_codes);
+    qh.scales = at<uint8_t>(ws, l.hq_scales);
+    const size_t nbh = rows * I / 16;
+    hipLaunchKernelGGL((k_quant_nvfp4<false>), dim3((unsigned)((nbh + 255) / 256)), dim3(256), 0, s, qh);
+    if ((st = launched("h quantization")) != Q4MOE_OK) return st;
+
+    // down: w g z per (token, slot) row
+    GemmArgs gd = gu;
+    gd.N = H;
+    gd.Kd = I;
+    gd.wc = ex->down_codes;
+    gd.wsc = static_cast<const uint8_t*>(ex->down_scales);
+    gd.wg = ex->down_gscale;
+    gd.ac = qh.codes;
+    gd.asc = qh.scales;
+    gd.a_by_token = 0;
+    gd.out = at<float>(ws, l.zw);
+    hipLaunchKernelGGL((k_grouped_gemm<EPI_DOWN>), dim3((H + kGemmBN - 1) / kGemmBN, E), dim3(256), 0, s, gd);
+    if ((st = launched("grouped down gemm")) != Q4MOE_OK) return st;
+
+    // combine
+    const size_t ny = (size_t)T * H;
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((ny + 255) / 256)), dim3(256), 0, s, T, K, H, da.inv, gd.out,
+                       at<float>(ws, l.y32), y_bf16);
+    return launched("combine");
 }
 
 // --- lm_head GEMV ---------------------------------------------------------
