@@ -272,8 +272,12 @@ RouterArgs router_args(const q4moe_router* r, const uint16_t* x, int T, void* ws
 }
 
 q4moe_status launch_router(const RouterArgs& a, hipStream_t s) {
-    dim3 g1((a.E + 3) / 4, (a.T + 3) / 4);
-    hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, a);
+    if (a.T >= 16) {  // many tokens: the MFMA router GEMM
+        hipLaunchKernelGGL(k_router_gemm, dim3((a.E + 31) / 32, (a.T + 31) / 32), dim3(512), 0, s, a);
+    } else {
+        dim3 g1((a.E + 3) / 4, (a.T + 3) / 4);
+        hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, a);
+    }
     q4moe_status st = launched("router logits");
     if (st != Q4MOE_OK) return st;
     hipLaunchKernelGGL(k_topk, dim3((a.T + 3) / 4), dim3(256), 0, s, a);
@@ -539,7 +543,7 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
 
     // router
     RouterArgs ra = router_args(r, x_bf16, T, ws, l.r, ids, w, nullptr);
-    hipLaunchKernelGGL(k_router_gemm, dim3((E + 31) / 32, (T + 31) / 32), dim3(256), 0, s, ra);
+    hipLaunchKernelGGL(k_router_gemm, dim3((E + 31) / 32, (T + 31) / 32), dim3(512), 0, s, ra);
     if ((st = launched("router gemm")) != Q4MOE_OK) return st;
     hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, ra);
     if ((st = launched("router top-k")) != Q4MOE_OK) return st;
@@ -557,7 +561,7 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     da.inv = at<int32_t>(ws, l.inv);
     hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(64), 0, s, da);
     if ((st = launched("dispatch")) != Q4MOE_OK) return st;
-    hipLaunchKernelGGL(k_dispatch_scan, dim3(1), dim3(256), 0, s, da);
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(E), dim3(256), 0, s, da);
     if ((st = launched("dispatch scan")) != Q4MOE_OK) return st;
 
     // x -> NVFP4

@@ -26,45 +26,50 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
-// Router logits for many tokens: fp32 tiled GEMM, 32 tokens x 32 experts per
-// workgroup, each thread 2 x 2 outputs.
+// Router logits for many tokens on fp32 MFMA (v_mfma_f32_32x32x2_f32):
+// a workgroup computes a 32-token x 32-expert tile; its 8 waves split the
+// hidden dimension and their partial tiles are summed in LDS in wave order.
+// Lane l feeds token/expert row l % 32 and, for each group of 8 k-values,
+// k-values 4 (l / 32) .. +3 (one per MFMA; A and B use the same k order).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_router_gemm(RouterArgs a) {
-    __shared__ float xs[32][33], ws[32][33];
-    const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+typedef float f32x16r __attribute__((ext_vector_type(16)));
+
+__global__ __launch_bounds__(512) void k_router_gemm(RouterArgs a) {
+    __shared__ float part[8][32][33];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int e0 = blockIdx.x * 32, t0 = blockIdx.y * 32;
-    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    for (int k0 = 0; k0 < a.H; k0 += 32) {
+    const int row = lane & 31, kq = lane >> 5;
+    const int t = min(t0 + row, a.T - 1), e = min(e0 + row, a.E - 1);
+    const uint16_t* xr = a.x + (size_t)t * a.H + 4 * kq;
+    const float* wr = a.wg + (size_t)e * a.H + 4 * kq;
+    const int nblk = a.H / 8;
+    const int b0 = wave * nblk / 8, b1 = (wave + 1) * nblk / 8;
+    f32x16r acc;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int idx = threadIdx.x + 256 * q;  // 0..1023
-            const int r = idx >> 5, c = idx & 31;
-            const int t = t0 + r, e = e0 + r;
-            xs[r][c] = t < a.T ? bf16_bits_to_f32(a.x[(size_t)t * a.H + k0 + c]) : 0.f;
-            ws[r][c] = e < a.E ? a.wg[(size_t)e * a.H + k0 + c] : 0.f;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int c = 0; c < 32; ++c) {
-            const float x0 = xs[2 * ty][c], x1 = xs[2 * ty + 1][c];
-            const float w0 = ws[2 * tx][c], w1 = ws[2 * tx + 1][c];
-            acc[0][0] = __builtin_fmaf(x0, w0, acc[0][0]);
-            acc[0][1] = __builtin_fmaf(x0, w1, acc[0][1]);
-            acc[1][0] = __builtin_fmaf(x1, w0, acc[1][0]);
-            acc[1][1] = __builtin_fmaf(x1, w1, acc[1][1]);
-        }
-        __syncthreads();
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+    for (int b = b0; b < b1; ++b) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(xr + 8 * b);
+        const float4 wv = *reinterpret_cast<const float4*>(wr + 8 * b);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.x & 0xffffu), wv.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.x >> 16), wv.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.y & 0xffffu), wv.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.y >> 16), wv.w, acc, 0, 0, 0);
     }
+    // lane holds column j = lane % 32 (expert) and rows 8 (r/4) + 4 (lane/32) + r % 4 (tokens)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int r = 0; r < 16; ++r) part[wave][8 * (r / 4) + 4 * kq + (r % 4)][row] = acc[r];
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 32 * 32; idx += 512) {
+        const int i = idx >> 5, j = idx & 31;
+        float v = 0.f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = t0 + 2 * ty + i, e = e0 + 2 * tx + j;
-            if (t < a.T && e < a.E) {
-                a.logits[(size_t)t * a.E + e] = acc[i][j];
-                if (a.logits_out) a.logits_out[(size_t)t * a.E + e] = acc[i][j];
-            }
+        for (int w = 0; w < 8; ++w) v += part[w][i][j];
+        const int tt = t0 + i, ee = e0 + j;
+        if (tt < a.T && ee < a.E) {
+            a.logits[(size_t)tt * a.E + ee] = v;
+            if (a.logits_out) a.logits_out[(size_t)tt * a.E + ee] = v;
         }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -102,26 +107,29 @@ __global__ __launch_bounds__(64) void k_dispatch(DispatchArgs a) {
 }
 
 // Offsets (exclusive scan of the counts), the dispatch permutation and its
-// inverse.  One workgroup.
+// inverse.  Workgroup e (grid E) loads all counts, scans them in LDS and
+// writes expert e's part of the permutation.
 __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a) {
-    __shared__ int s_off[257];
+    __shared__ int s_cnt[256], s_off[257];
+    const int e = blockIdx.x;
+    for (int i = threadIdx.x; i < a.E; i += 256) s_cnt[i] = a.counts[i];
+    __syncthreads();
     if (threadIdx.x == 0) {
         int o = 0;
-        for (int e = 0; e < a.E; ++e) {
-            s_off[e] = o;
-            o += a.counts[e];
+        for (int i = 0; i < a.E; ++i) {
+            s_off[i] = o;
+            o += s_cnt[i];
         }
         s_off[a.E] = o;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e <= a.E; e += 256) a.offsets[e] = s_off[e];
-    for (int e = 0; e < a.E; ++e) {
-        const int n = s_off[e + 1] - s_off[e];
-        for (int i = threadIdx.x; i < n; i += 256) {
-            const int pair = a.lists[(size_t)e * a.T + i];
-            a.perm[s_off[e] + i] = pair;
-            a.inv[pair] = s_off[e] + i;
-        }
+    if (e == 0)
+        for (int i = threadIdx.x; i <= a.E; i += 256) a.offsets[i] = s_off[i];
+    const int n = s_cnt[e];
+    for (int i = threadIdx.x; i < n; i += 256) {
+        const int pair = a.lists[(size_t)e * a.T + i];
+        a.perm[s_off[e] + i] = pair;
+        a.inv[pair] = s_off[e] + i;
     }
 }
 
@@ -299,32 +307,48 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-        uint4 qb = ldg16_stream(wrow_c + sh * 16);
-        uint32_t sbb = *reinterpret_cast<const uint16_t*>(wrow_s + sh * 2);
-        uint4 qa = ldg16(arow_c + sh * 16);
-        uint32_t sba = *reinterpret_cast<const uint16_t*>(arow_s + sh * 2);
-        for (int ks = 0; ks < nk; ++ks) {
-            __syncthreads();  // previous step's MFMAs are done with the tiles
-            decode32_to_lds(qb, sbb, &Bs[sr][sh * 32]);
-            if (stage_a) decode32_to_lds(qa, sba, &As[sr][sh * 32]);
-            __syncthreads();
-            if (ks + 1 < nk) {  // next step's operands, in flight during the MFMAs
-                const int kb = (ks + 1) * kGemmBK;
-                qb = ldg16_stream(wrow_c + kb / 2 + sh * 16);
-                sbb = *reinterpret_cast<const uint16_t*>(wrow_s + kb / 16 + sh * 2);
-                qa = ldg16(arow_c + kb / 2 + sh * 16);
-                sba = *reinterpret_cast<const uint16_t*>(arow_s + kb / 16 + sh * 2);
+        // operands of the next kPre k-steps are in flight in a register ring
+        constexpr int kPre = 4;
+        uint4 qb[kPre], qa[kPre];
+        uint32_t sbb[kPre], sba[kPre];
+#pragma unroll
+        for (int j = 0; j < kPre; ++j) {
+            if (j < nk) {
+                const int kb = j * kGemmBK;
+                qb[j] = ldg16_stream(wrow_c + kb / 2 + sh * 16);
+                sbb[j] = *reinterpret_cast<const uint16_t*>(wrow_s + kb / 16 + sh * 2);
+                qa[j] = ldg16(arow_c + kb / 2 + sh * 16);
+                sba[j] = *reinterpret_cast<const uint16_t*>(arow_s + kb / 16 + sh * 2);
             }
+        }
+        for (int ks0 = 0; ks0 < nk; ks0 += kPre) {
 #pragma unroll
-            for (int kk = 0; kk < kGemmBK; kk += 16) {
-                const bf16x8 bfrag =
-                    *reinterpret_cast<const bf16x8*>(&Bs[32 * wave + (lane & 31)][kk + 8 * (lane >> 5)]);
+            for (int j = 0; j < kPre; ++j) {
+                const int ks = ks0 + j;
+                if (ks < nk) {  // uniform
+                    __syncthreads();  // previous step's MFMAs are done with the tiles
+                    decode32_to_lds(qb[j], sbb[j], &Bs[sr][sh * 32]);
+                    if (stage_a) decode32_to_lds(qa[j], sba[j], &As[sr][sh * 32]);
+                    __syncthreads();
+                    if (ks + kPre < nk) {
+                        const int kb = (ks + kPre) * kGemmBK;
+                        qb[j] = ldg16_stream(wrow_c + kb / 2 + sh * 16);
+                        sbb[j] = *reinterpret_cast<const uint16_t*>(wrow_s + kb / 16 + sh * 2);
+                        qa[j] = ldg16(arow_c + kb / 2 + sh * 16);
+                        sba[j] = *reinterpret_cast<const uint16_t*>(arow_s + kb / 16 + sh * 2);
+                    }
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (i < ms) {
-                        const bf16x8 afrag =
-                            *reinterpret_cast<const bf16x8*>(&As[32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
-                        acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[i], 0, 0, 0);
+                    for (int kk = 0; kk < kGemmBK; kk += 16) {
+                        const bf16x8 bfrag =
+                            *reinterpret_cast<const bf16x8*>(&Bs[32 * wave + (lane & 31)][kk + 8 * (lane >> 5)]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if (i < ms) {
+                                const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(
+                                    &As[32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
+                                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[i], 0, 0, 0);
+                            }
+                        }
                     }
                 }
             }
