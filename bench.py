@@ -30,6 +30,7 @@ H, I, E, K, LAYERS, V = 2688, 1856, 128, 6, 23, 131072
 SEED = 20261202
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+TRAFFIC_PROFILE = "profiles/traffic_all_kernels_bench.md"
 METRIC = "µs per routed-MoE layer at batch 1 + achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -76,6 +77,39 @@ class Timer:
         t.cuda.synchronize()
         return e0.elapsed_time(e1) / reps  # ms
 
+    def each(self, fn, reps, before=None):
+        """Per-rep times (ms) from events around each call; `before` runs
+        untimed ahead of every rep (e.g. an eviction of the MALL)."""
+        t = self.torch
+        evs = [(t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        t.cuda.synchronize()
+        for a, b in evs:
+            if before is not None:
+                before()
+            a.record()
+            fn()
+            b.record()
+        t.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def spread(ms, scale=1e3, nd=3):
+    """median / p10 / p90 of per-rep times, scaled (default ms -> us)."""
+    q = np.percentile(np.asarray(ms) * scale, [50, 10, 90])
+    return {"median": round(float(q[0]), nd), "p10": round(float(q[1]), nd), "p90": round(float(q[2]), nd)}
+
+
+class Evictor:
+    """Reads and writes 2 x 512 MiB so that nothing a timed rep reads is
+    still held in the 256 MB MALL or the L2s."""
+
+    def __init__(self, torch):
+        self.src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.dst = torch.empty_like(self.src)
+
+    def __call__(self):
+        self.dst.copy_(self.src)
+
 
 def build_stack(torch, g, synth, fmt):
     from gpu_util import dev
@@ -121,8 +155,16 @@ def time_stack(torch, g, layers, steps, warmup):
     torch.cuda.synchronize()
     for _ in range(warmup):
         graph.replay()
-    timer = Timer(torch)
-    ms_step = timer(graph.replay, steps)
+    # events between consecutive replays: the K steps form one contiguous region
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    ms_step = evs[0].elapsed_time(evs[-1]) / steps
     # the kernel's own duration: events just around single launches
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     durs = []
@@ -134,7 +176,7 @@ def time_stack(torch, g, layers, steps, warmup):
             e1.synchronize()
             durs.append(e0.elapsed_time(e1))
     flags = max(g.q4moe_ws_check(L["ws"]) for L in layers)
-    return ms_step, float(np.mean(durs[LAYERS:])), flags
+    return ms_step, float(np.mean(durs[LAYERS:])), flags, per
 
 
 def bench_w4a4(torch, g, synth, steps):
@@ -158,7 +200,9 @@ def bench_w4a4(torch, g, synth, steps):
 
     for _ in range(3):
         run()
-    ms = Timer(torch)(run, max(5, steps // 5))
+    # 718 MB of weights per chunk exceed the 256 MB MALL: every rep streams from HBM
+    per = Timer(torch).each(run, max(5, steps // 5))
+    ms = float(np.median(per))
     weights = E * expert_bytes("nvfp4")
     flops = 2.0 * 2 * T * K * H * I
     byts = weights + E * H * 4 + 2 * T * H * 2
@@ -166,7 +210,7 @@ def bench_w4a4(torch, g, synth, steps):
     return {"us": round(ms * 1e3, 2), "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "mfma_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-            "bytes": byts, "flop": flops, "tokens": T}
+            "us_spread": spread(per), "bytes": byts, "flop": flops, "tokens": T}
 
 
 def bench_verify(torch, g, synth, steps, stack_layer0):
@@ -192,14 +236,20 @@ def bench_verify(torch, g, synth, steps, stack_layer0):
     for _ in range(3):
         moe()
         head()
-    timer = Timer(torch)
-    ms_moe, ms_head = timer(moe, steps), timer(head, steps)
+    # cold reps: the lm_head (198 MB) and the 4 tokens' experts fit in the MALL
+    timer, evict = Timer(torch), Evictor(torch)
+    reps = max(10, steps // 2)
+    t_moe = timer.each(moe, reps, evict)
+    t_head = timer.each(head, reps, evict)
+    ms_moe, ms_head = float(np.median(t_moe)), float(np.median(t_head))
     n_union = len(np.unique(ids4.cpu().numpy()))
     moe_bytes = layer_bytes("nvfp4", n_union, 4)
     head_bytes = V * H // 2 + V * H // 16 + 4 + 4 * H * 2 + 4 * V * 4
     return {"moe_us": round(ms_moe * 1e3, 2), "moe_hbm_gbps": round(moe_bytes / (ms_moe * 1e-3) / 1e9, 1),
-            "experts_read": n_union, "lm_head_us": round(ms_head * 1e3, 2),
-            "lm_head_hbm_gbps": round(head_bytes / (ms_head * 1e-3) / 1e9, 1)}
+            "moe_us_spread": spread(t_moe), "experts_read": n_union,
+            "lm_head_us": round(ms_head * 1e3, 2),
+            "lm_head_hbm_gbps": round(head_bytes / (ms_head * 1e-3) / 1e9, 1),
+            "lm_head_us_spread": spread(t_head), "cold": True, "reps": reps}
 
 
 def cpu_baseline(seconds):
@@ -244,7 +294,7 @@ def main():
     torch.cuda.synchronize()
 
     layers = build_stack(torch, g, synth, "nvfp4")
-    ms_step, ms_kernel, flags = time_stack(torch, g, layers, args.steps, args.warmup)
+    ms_step, ms_kernel, flags, per_step = time_stack(torch, g, layers, args.steps, args.warmup)
     us_layer = 1000.0 * ms_step / LAYERS
     bytes_layer = layer_bytes()
     gbs = bytes_layer / (us_layer * 1e-6) / 1e9
@@ -258,11 +308,12 @@ def main():
         del layers
         torch.cuda.empty_cache()
         int4 = build_stack(torch, g, synth, "int4")
-        ms4, mk4, f4 = time_stack(torch, g, int4, args.steps, args.warmup)
+        ms4, mk4, f4, per4 = time_stack(torch, g, int4, args.steps, args.warmup)
         b4 = layer_bytes("int4")
         extra["int4_stack"] = {"us_per_layer": round(1000.0 * ms4 / LAYERS, 3),
                                "hbm_gbps": round(b4 / (ms4 / LAYERS * 1e-3) / 1e9, 1),
                                "tokens_per_s": round(1000.0 / ms4, 1), "single_launch_us": round(mk4 * 1e3, 3),
+                               "us_per_layer_spread": spread(per4 / LAYERS),
                                "bytes_per_layer": b4, "flags": f4}
         log(f"int4 stack: {extra['int4_stack']}")
         del int4
@@ -275,6 +326,10 @@ def main():
         cpu = {"value": round(us_cpu, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
                "sample": f"{n} of the 23 layers, 1 token each (router + 6 experts), fp64 oracle"}
 
+    from gemm_router_fp32_amd.pmc_traffic import read_traffic
+    # HBM bytes per launch from the committed counter passes (None once the
+    # kernel's sources differ from the ones the counters were taken on)
+    traffic = read_traffic(os.path.join(ROOT, TRAFFIC_PROFILE), "k_decode_fused<1,3,1>")
     out = {
         "metric": METRIC,
         "value": round(us_layer, 4),
@@ -295,11 +350,14 @@ def main():
         "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
         "tokens_per_s": round(1000.0 / ms_step, 1),
         "bytes_per_layer": bytes_layer,
+        "us_per_layer_spread": spread(per_step / LAYERS),
+        # the stack reads 806 MB per step, > the 256 MB MALL: every layer is cold
         "single_launch_us": round(ms_kernel * 1e3, 3),
         # one k_decode_fused launch per layer: its average duration is the
         # timed region over the 23 * steps launches of the graph replays
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "traffic_unit": "bytes/launch", "traffic_source": TRAFFIC_PROFILE,
                      "kernel": "k_decode_fused", "kernel_us": round(us_layer, 3)},
         "workspace_flags": flags,
         "extra": extra,
