@@ -235,7 +235,10 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
 // while the current step's MFMAs run.
 // ---------------------------------------------------------------------------
 enum : int { EPI_UP = 0, EPI_DOWN = 1 };
-constexpr int kGemmBN = 128, kGemmBM = 128, kGemmBK = 64, kLdsPitch = kGemmBK + 8;  // bf16 elements
+// Output columns (rows of W_e) per workgroup (4 waves x 32), A rows per
+// M-tile (an expert's rows beyond it take further M-tiles), k per chunk (128
+// bytes of every weight row), LDS pitch of A (fp16).
+constexpr int kGemmBN = 128, kGemmBM = 96, kGemmBK = 256, kApitch = kGemmBK + 8;
 
 struct GemmArgs {
     int N, Kd;                 // output columns (rows of W_e), reduction length
@@ -252,130 +255,258 @@ struct GemmArgs {
     float* out;                // [rows][N] fp32, dispatch order
 };
 
-// Decode 32 NVFP4 elements (16 code bytes, two E4M3 scale bytes) to bf16 in LDS.
-__device__ __forceinline__ void decode32_to_lds(uint4 q, uint32_t sb, uint16_t* dst) {
-    const float s0 = e4m3fn_to_f32(sb & 0xffu), s1 = e4m3fn_to_f32((sb >> 8) & 0xffu);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    uint32_t o[16];
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float s = d < 2 ? s0 : s1;
-        const f32x2 p0 = fp4x2_f32<0>(w[d]), p1 = fp4x2_f32<1>(w[d]), p2 = fp4x2_f32<2>(w[d]),
-                    p3 = fp4x2_f32<3>(w[d]);
-        // products are exact and representable in bf16: truncation is exact
-        o[4 * d + 0] = (__float_as_uint(p0.x * s) >> 16) | (__float_as_uint(p0.y * s) & 0xffff0000u);
-        o[4 * d + 1] = (__float_as_uint(p1.x * s) >> 16) | (__float_as_uint(p1.y * s) & 0xffff0000u);
-        o[4 * d + 2] = (__float_as_uint(p2.x * s) >> 16) | (__float_as_uint(p2.y * s) & 0xffff0000u);
-        o[4 * d + 3] = (__float_as_uint(p3.x * s) >> 16) | (__float_as_uint(p3.y * s) & 0xffff0000u);
-    }
-    uint4* d4 = reinterpret_cast<uint4*>(dst);
-    d4[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    d4[1] = make_uint4(o[4], o[5], o[6], o[7]);
-    d4[2] = make_uint4(o[8], o[9], o[10], o[11]);
-    d4[3] = make_uint4(o[12], o[13], o[14], o[15]);
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Two E4M3FN bytes (bytes 0,1 of v, or 2,3 when HI) -> fp16 pair.  gfx950's
+// fp8 converts use the OCP E4M3FN encoding; every E4M3FN value (NaN and -0
+// included) is exact in fp16, and with scale 1 the conversion is exact.
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_f16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, HI);
 }
 
+// Eight E2M1 codes (one dword) times their block scale, as fp16.  e2m1 *
+// e4m3 has at most six significant bits and lies in [2^-10, 2688]: exact.
+__device__ __forceinline__ f16x8 fp4x8_f16(uint32_t w, f16x2 s) {
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// Grouped GEMM over the experts' dispatch rows: out[row][n] = epi(sum_k
+// A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_32x32x16_f16) with both
+// operands decoded exactly from NVFP4.  A workgroup takes 128 columns of one
+// expert and all its rows in M-tiles of 96; wave w owns columns 32w..32w+31.
+//
+// The reduction runs in chunks of 256: every weight row contributes one whole
+// 128-byte line per chunk, loaded straight into registers (lane l: row l % 32,
+// bytes 64 (l / 32) .. +63, i.e. k 128 (l / 32) .. +127 of the chunk) two
+// chunks ahead in a three-slot ring (plain loads: the four load instructions
+// of a wave take 32 bytes of each line in turn, so the line must stay in L2
+// until the last one); the A tile of the chunk is decoded into
+// LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
+// (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
+// operands.  All loads are unconditional: pieces past the end of a row (the
+// last chunk, and the chunks that pad the count to a multiple of three) read
+// the row's last bytes and get scale 0, so that every wait covers exactly the
+// loads it needs.  Offsets are 32-bit from the uniform bases: the argument
+// limits (E <= 256, rows and columns <= 4096, T * K <= 2^19) keep every
+// matrix under 2^31 bytes.
+struct BChunk {
+    uint4 q[4];
+    uint32_t s0, s1;
+};
+
+// Per-workgroup constants of the grouped GEMM.
+struct GemmCtx {
+    int e, row0, n, hk, nch, nch3, ap, ar;
+    uint32_t wc_off, ws_off;
+    float g;
+};
+
+// Valid 16-byte pieces (0..4) of this lane's half of chunk c.
+__device__ __forceinline__ int gemm_valid_pieces(const GemmArgs& a, const GemmCtx& x, int c) {
+    return min(4, max(0, (a.Kd - c * kGemmBK - 128 * x.hk) / 32));
+}
+
+// Pieces past the end of the row read the row's last 16 code bytes and last
+// scale dword instead: those lines were fetched by the last full chunk and
+// are still in L2.
+__device__ __forceinline__ void gemm_load_b(const GemmArgs& a, const GemmCtx& x, int c, BChunk& b) {
+    const int kb = c * kGemmBK, valid = gemm_valid_pieces(a, x, c);
+    const uint32_t c_last = x.wc_off + a.Kd / 2 - 16, s_last = x.ws_off + a.Kd / 16 - 4;
+    const uint32_t base = x.wc_off + kb / 2 + 64 * x.hk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b.q[i] = ldg16(a.wc + (i < valid ? base + 16 * i : c_last));
+    const uint32_t sb = x.ws_off + kb / 16 + 8 * x.hk;
+    b.s0 = *reinterpret_cast<const uint32_t*>(a.wsc + (valid > 0 ? sb : s_last));
+    b.s1 = *reinterpret_cast<const uint32_t*>(a.wsc + (valid > 2 ? sb + 4 : s_last));
+}
+
+// One M-tile (rows m0 .. m0 + mv - 1 of expert e, MS = ceil(mv / 32)
+// subtiles) against the workgroup's 128 columns.
+template <int EPI, int MS>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, int m0, int mv,
+                                          _Float16 (*As)[kApitch]) {
+    const int lane = threadIdx.x & 63;
+    uint32_t ac_off[MS], as_off[MS];
+#pragma unroll
+    for (int q = 0; q < MS; ++q) {
+        const int drow = x.row0 + m0 + min(x.ar + 32 * q, mv - 1);
+        const uint32_t arow = a.a_by_token ? (uint32_t)(a.perm[drow] / a.K) : (uint32_t)drow;
+        ac_off[q] = arow * (uint32_t)(a.Kd / 2);
+        as_off[q] = arow * (uint32_t)(a.Kd / 16);
+    }
+    uint4 qa[MS];
+    uint32_t sa[MS];
+    auto load_a = [&](int c) {
+        const int kb = c * kGemmBK;
+        const bool ok = 32 * x.ap < a.Kd - kb;
+#pragma unroll
+        for (int q = 0; q < MS; ++q) {
+            // past the end: the row's last piece (just read), with scale 0
+            qa[q] = ldg16(a.ac + (ok ? ac_off[q] + kb / 2 + 16 * x.ap : ac_off[q] + a.Kd / 2 - 16));
+            const uint32_t s2 = *reinterpret_cast<const uint16_t*>(
+                a.asc + (ok ? as_off[q] + kb / 16 + 2 * x.ap : as_off[q] + a.Kd / 16 - 2));
+            sa[q] = ok ? s2 : 0u;
+        }
+    };
+
+    f32x16 acc[MS];
+#pragma unroll
+    for (int i = 0; i < MS; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+    // issue order = wait order: B0, A0, B1 (the scheduler may not mix them)
+    BChunk bb[3];
+    gemm_load_b(a, x, 0, bb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_a(0);
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_load_b(a, x, 1, bb[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int c0 = 0; c0 < x.nch3; c0 += 3) {
+#pragma unroll
+        for (int u = 0; u < 3; ++u) {
+            const int c = c0 + u;
+            BChunk& bc = bb[u];
+            // this chunk's A into LDS (after every wave is done with the last one)
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < MS; ++q) {
+                const f16x2 sp = e4m3x2_f16<false>(sa[q]);
+                const f16x2 s_lo = {sp.x, sp.x}, s_hi = {sp.y, sp.y};
+                f16x8* dst = reinterpret_cast<f16x8*>(&As[x.ar + 32 * q][32 * x.ap]);
+                dst[0] = fp4x8_f16(qa[q].x, s_lo);
+                dst[1] = fp4x8_f16(qa[q].y, s_lo);
+                dst[2] = fp4x8_f16(qa[q].z, s_hi);
+                dst[3] = fp4x8_f16(qa[q].w, s_hi);
+            }
+            __syncthreads();
+            // next loads: A of chunk c+1, B of chunk c+2 into the free slot
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(c + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            gemm_load_b(a, x, c + 2, bb[(u + 2) % 3]);
+            __builtin_amdgcn_sched_barrier(0);
+            // 16 MFMA steps on chunk c; block scales of the lane's 8 blocks,
+            // pieces past the end get 0
+            const int valid = gemm_valid_pieces(a, x, c);
+            f16x2 sc[4] = {e4m3x2_f16<false>(bc.s0), e4m3x2_f16<true>(bc.s0), e4m3x2_f16<false>(bc.s1),
+                           e4m3x2_f16<true>(bc.s1)};
+#pragma unroll
+            for (int pc = 0; pc < 4; ++pc)
+                if (pc >= valid) sc[pc] = f16x2{0, 0};
+            const uint32_t w[16] = {bc.q[0].x, bc.q[0].y, bc.q[0].z, bc.q[0].w, bc.q[1].x, bc.q[1].y,
+                                    bc.q[1].z, bc.q[1].w, bc.q[2].x, bc.q[2].y, bc.q[2].z, bc.q[2].w,
+                                    bc.q[3].x, bc.q[3].y, bc.q[3].z, bc.q[3].w};
+            // A fragments are read one step ahead of their MFMAs
+            const _Float16* arow = &As[lane & 31][128 * x.hk];
+            f16x8 af[2][MS];
+#pragma unroll
+            for (int i = 0; i < MS; ++i) af[0][i] = *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (j + 1 < 16) {
+#pragma unroll
+                    for (int i = 0; i < MS; ++i)
+                        af[(j + 1) & 1][i] = *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch + 8 * (j + 1));
+                }
+                // dword j holds k 8j..8j+7 of the lane's half: block j / 2, piece j / 4
+                const f16x2 sp = sc[j / 4];
+                const f16x8 bfrag = fp4x8_f16(w[j], (j & 2) ? f16x2{sp.y, sp.y} : f16x2{sp.x, sp.x});
+#pragma unroll
+                for (int i = 0; i < MS; ++i)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][i], bfrag, acc[i], 0, 0, 0);
+            }
+        }
+    }
+    // epilogue: lane holds column n and rows 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4
+#pragma unroll
+    for (int i = 0; i < MS; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (m < mv && x.n < a.N) {
+                const int p = x.row0 + m0 + m;
+                float v = acc[i][r] * x.g;
+                if constexpr (EPI == EPI_UP) {
+                    v = fmaxf(v, 0.f);
+                    v = v * v;
+                } else {
+                    v = a.wgate[a.perm[p]] * v;
+                }
+                a.out[(size_t)p * a.N + x.n] = v;
+            }
+        }
+    }
+}
+
+// Grouped GEMM over the experts' dispatch rows: out[row][n] = epi(sum_k
+// A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_32x32x16_f16) with both
+// operands decoded exactly from NVFP4.  A workgroup takes 128 columns of one
+// expert and all its rows in M-tiles of 96; wave w owns columns 32w..32w+31.
+//
+// The reduction runs in chunks of 256: every weight row contributes one whole
+// 128-byte line per chunk, loaded straight into registers (lane l: row l % 32,
+// bytes 64 (l / 32) .. +63, i.e. k 128 (l / 32) .. +127 of the chunk) two
+// chunks ahead in a three-slot ring (plain loads: the four load instructions
+// of a wave take 32 bytes of each line in turn, so the line must stay in L2
+// until the last one); the A tile of the chunk is decoded into
+// LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
+// (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
+// operands.  All loads are unconditional: pieces past the end of a row (the
+// last chunk, and the chunks that pad the count to a multiple of three) read
+// the row's last bytes and get scale 0, so that every wait covers exactly the
+// loads it needs.  Offsets are 32-bit from the uniform bases: the argument
+// limits (E <= 256, rows and columns <= 4096, T * K <= 2^19) keep every
+// matrix under 2^31 bytes.
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t As[kGemmBM][kLdsPitch];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[kGemmBN][kLdsPitch];
-    const int e = blockIdx.y;
-    const int row0 = a.offsets[e], n_e = a.offsets[e + 1] - row0;
-    const int n0 = blockIdx.x * kGemmBN;
+    __shared__ __attribute__((aligned(16))) _Float16 As[kGemmBM][kApitch];
+    GemmCtx x;
+    // Expert-major placement on the XCDs: workgroup b runs on XCD b % 8, and
+    // when E % 8 == 0 all column tiles of expert e go to XCD e % 8, so that
+    // each XCD's L2 fetches an expert's A rows once.  With gridDim = (tiles,
+    // E) the flat id b covers every (tile, expert) pair exactly once.
+    const int ntiles = gridDim.x;
+    int tile = blockIdx.x;
+    x.e = blockIdx.y;
+    if (gridDim.y % 8 == 0) {
+        const int b = blockIdx.y * ntiles + blockIdx.x;
+        const int j = b / 8;
+        x.e = b % 8 + 8 * (j / ntiles);
+        tile = j % ntiles;
+    }
+    x.row0 = a.offsets[x.e];
+    const int n_e = a.offsets[x.e + 1] - x.row0;
+    if (n_e == 0) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int nk = a.Kd / kGemmBK;
-    // staging role: row tid/2 of the A and B tiles, k half (tid & 1) * 32
-    const int sr = threadIdx.x >> 1, sh = threadIdx.x & 1;
-    const uint8_t* wrow_c = a.wc + ((size_t)e * a.N + min(n0 + sr, a.N - 1)) * (a.Kd / 2);
-    const uint8_t* wrow_s = a.wsc + ((size_t)e * a.N + min(n0 + sr, a.N - 1)) * (a.Kd / 16);
-    const float g = a.wg[e];
-
+    x.hk = lane >> 5;
+    x.nch = (a.Kd + kGemmBK - 1) / kGemmBK;
+    x.nch3 = (x.nch + 2) / 3 * 3;
+    x.n = tile * kGemmBN + 32 * wave + (lane & 31);
+    const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n, a.N - 1);
+    x.wc_off = wrow * (uint32_t)(a.Kd / 2);
+    x.ws_off = wrow * (uint32_t)(a.Kd / 16);
+    x.g = a.wg[x.e];
+    // A staging role: piece ap (k 32ap..32ap+31 of the chunk) of rows ar + 32q
+    x.ap = threadIdx.x & 7;
+    x.ar = threadIdx.x >> 3;
     for (int m0 = 0; m0 < n_e; m0 += kGemmBM) {
-        const int mv = min(kGemmBM, n_e - m0);  // valid rows in this chunk
-        const int ms = (mv + 31) / 32;          // 32-row subtiles in use
-        // A row of this thread's staging row (clamped to a valid row)
-        const int am = min(sr, mv - 1);
-        const int drow = row0 + m0 + am;
-        const size_t arow = a.a_by_token ? (size_t)(a.perm[drow] / a.K) : (size_t)drow;
-        const uint8_t* arow_c = a.ac + arow * (a.Kd / 2);
-        const uint8_t* arow_s = a.asc + arow * (a.Kd / 16);
-        const bool stage_a = sr < mv;
-
-        f32x16 acc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-        // operands of the next kPre k-steps are in flight in a register ring
-        constexpr int kPre = 4;
-        uint4 qb[kPre], qa[kPre];
-        uint32_t sbb[kPre], sba[kPre];
-#pragma unroll
-        for (int j = 0; j < kPre; ++j) {
-            if (j < nk) {
-                const int kb = j * kGemmBK;
-                qb[j] = ldg16_stream(wrow_c + kb / 2 + sh * 16);
-                sbb[j] = *reinterpret_cast<const uint16_t*>(wrow_s + kb / 16 + sh * 2);
-                qa[j] = ldg16(arow_c + kb / 2 + sh * 16);
-                sba[j] = *reinterpret_cast<const uint16_t*>(arow_s + kb / 16 + sh * 2);
-            }
-        }
-        for (int ks0 = 0; ks0 < nk; ks0 += kPre) {
-#pragma unroll
-            for (int j = 0; j < kPre; ++j) {
-                const int ks = ks0 + j;
-                if (ks < nk) {  // uniform
-                    __syncthreads();  // previous step's MFMAs are done with the tiles
-                    decode32_to_lds(qb[j], sbb[j], &Bs[sr][sh * 32]);
-                    if (stage_a) decode32_to_lds(qa[j], sba[j], &As[sr][sh * 32]);
-                    __syncthreads();
-                    if (ks + kPre < nk) {
-                        const int kb = (ks + kPre) * kGemmBK;
-                        qb[j] = ldg16_stream(wrow_c + kb / 2 + sh * 16);
-                        sbb[j] = *reinterpret_cast<const uint16_t*>(wrow_s + kb / 16 + sh * 2);
-                        qa[j] = ldg16(arow_c + kb / 2 + sh * 16);
-                        sba[j] = *reinterpret_cast<const uint16_t*>(arow_s + kb / 16 + sh * 2);
-                    }
-#pragma unroll
-                    for (int kk = 0; kk < kGemmBK; kk += 16) {
-                        const bf16x8 bfrag =
-                            *reinterpret_cast<const bf16x8*>(&Bs[32 * wave + (lane & 31)][kk + 8 * (lane >> 5)]);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            if (i < ms) {
-                                const bf16x8 afrag = *reinterpret_cast<const bf16x8*>(
-                                    &As[32 * i + (lane & 31)][kk + 8 * (lane >> 5)]);
-                                acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(afrag, bfrag, acc[i], 0, 0, 0);
-                            }
-                        }
-                    }
-                }
-            }
-        }
-        // epilogue: lane holds column n = n0 + 32 wave + (lane & 31) and rows
-        // 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4
-        const int n = n0 + 32 * wave + (lane & 31);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (i < ms) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int m = 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-                    if (m < mv && n < a.N) {
-                        const int p = row0 + m0 + m;
-                        float v = acc[i][r] * g;
-                        if constexpr (EPI == EPI_UP) {
-                            v = fmaxf(v, 0.f);
-                            v = v * v;
-                        } else {
-                            v = a.wgate[a.perm[p]] * v;
-                        }
-                        a.out[(size_t)p * a.N + n] = v;
-                    }
-                }
-            }
-        }
+        const int mv = min(kGemmBM, n_e - m0);
+        const int ms = (mv + 31) / 32;
+        static_assert(kGemmBM == 96, "subtile dispatch below covers 1..3");
+        if (ms == 1)
+            gemm_tile<EPI, 1>(a, x, m0, mv, As);
+        else if (ms == 2)
+            gemm_tile<EPI, 2>(a, x, m0, mv, As);
+        else
+            gemm_tile<EPI, 3>(a, x, m0, mv, As);
     }
 }
 
