@@ -349,9 +349,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
         for (int q = 0; q < MS; ++q) {
             // past the end: the row's last piece (just read), with scale 0
             qa[q] = ldg16(a.ac + (ok ? ac_off[q] + kb / 2 + 16 * x.ap : ac_off[q] + a.Kd / 2 - 16));
-            const uint32_t s2 = *reinterpret_cast<const uint16_t*>(
+            // (the scale of a piece past the end is zeroed where it is used:
+            // touching a loaded value here would wait for every load before it)
+            sa[q] = *reinterpret_cast<const uint16_t*>(
                 a.asc + (ok ? as_off[q] + kb / 16 + 2 * x.ap : as_off[q] + a.Kd / 16 - 2));
-            sa[q] = ok ? s2 : 0u;
         }
     };
 
@@ -376,9 +377,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             BChunk& bc = bb[u];
             // this chunk's A into LDS (after every wave is done with the last one)
             __syncthreads();
+            const bool a_ok = 32 * x.ap < a.Kd - c * kGemmBK;
 #pragma unroll
             for (int q = 0; q < MS; ++q) {
-                const f16x2 sp = e4m3x2_f16<false>(sa[q]);
+                const f16x2 sp = e4m3x2_f16<false>(a_ok ? sa[q] : 0u);
                 const f16x2 s_lo = {sp.x, sp.x}, s_hi = {sp.y, sp.y};
                 f16x8* dst = reinterpret_cast<f16x8*>(&As[x.ar + 32 * q][32 * x.ap]);
                 dst[0] = fp4x8_f16(qa[q].x, s_lo);
