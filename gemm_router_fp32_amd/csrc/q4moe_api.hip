@@ -2,6 +2,7 @@
 // Declarations, argument meaning, layouts and error behaviour: include/q4moe.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -130,6 +131,18 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T) {
     return l;
 }
 
+// Workgroups of a persistent kernel: as many as fit on the device at once,
+// at most `want`; 0 if the occupancy query fails.
+template <typename K>
+int persistent_grid(K kernel, int block, int want) {
+    int dev = 0, per_cu = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess || per_cu < 1)
+        return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) return 0;
+    return std::max(1, std::min(want, per_cu * cus));
+}
+
 // Workgroups of the fused decode that fit on the device at once (so that
 // every workgroup is resident and every wait can be satisfied), cached per
 // device and kernel variant.
@@ -228,6 +241,9 @@ q4moe_status check_w4a4(const q4moe_router* r, const q4moe_experts* ex, int32_t 
     return Q4MOE_OK;
 }
 
+// Workgroups of the lm_head GEMV at most (its persistent grid is capped here).
+constexpr int kMaxGemvBlocks = 4096;
+
 struct GemvWs {
     size_t ctrl, keys, total;
 };
@@ -236,7 +252,7 @@ GemvWs gemv_ws(int T) {
     GemvWs l;
     l.ctrl = 0;
     l.keys = up_to(CTRL_WORDS * 4);
-    l.total = l.keys + up_to((size_t)T * 8);
+    l.total = l.keys + up_to((size_t)kMaxGemvBlocks * T * 8);
     return l;
 }
 
@@ -639,6 +655,8 @@ q4moe_status q4moe_w4a16_gemv(const q4moe_qmat* m, const uint16_t* x_bf16, int32
     if (m->rows < 1 || m->cols < 32 || m->cols % 32 != 0 || m->cols > kMaxDim)
         return fail(Q4MOE_EINVAL, "shape %d x %d: cols a multiple of 32 in [32, %d]", m->rows, m->cols, kMaxDim);
     if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    if ((uint64_t)m->rows * (uint64_t)(m->cols / 2) > 0xFFFFFFFFull)
+        return fail(Q4MOE_EUNSUPPORTED, "lm_head codes of %d x %d exceed 4 GiB", m->rows, m->cols);
     if (!m->codes || !m->scales || !m->gscale || !x_bf16 || !logits)
         return fail(Q4MOE_EINVAL, "codes / scales / gscale / x / logits is NULL");
     if (!aligned(m->codes, 16) || !aligned(x_bf16, 16) || !aligned(logits, 16))
@@ -660,27 +678,44 @@ q4moe_status q4moe_w4a16_gemv(const q4moe_qmat* m, const uint16_t* x_bf16, int32
     a.logits = logits;
     a.argmax = argmax;
     a.keys = at<unsigned long long>(ws, l.keys);
-    a.ctrl = at<uint32_t>(ws, l.ctrl);
-    const int C = (m->cols / 32 + 31) / 32;
-    dim3 grid((m->rows + 63) / 64);
     hipStream_t s = (hipStream_t)stream;
-#define Q4_GEMV(CC, TT) hipLaunchKernelGGL((k_gemv<CC, TT>), grid, dim3(256), 0, s, a)
-#define Q4_GEMV_T(CC)                \
-    switch (n_tok) {                 \
-        case 1: Q4_GEMV(CC, 1); break; \
-        case 2: Q4_GEMV(CC, 2); break; \
-        case 3: Q4_GEMV(CC, 3); break; \
-        default: Q4_GEMV(CC, 4); break; \
+    const int nj = (m->cols + 127) / 128;  // 128-column pieces per row: 1..32
+    const int groups = (m->rows + 15) / 16;
+    // NJ: exact for the 2688-wide lm_head, else the next multiple of 4
+    const int NJ = nj == 21 ? 21 : (nj + 3) / 4 * 4;
+    int grid = 0;
+#define Q4_GEMV(JJ, TT)                                                                              \
+    do {                                                                                             \
+        grid = persistent_grid(k_gemv_mfma<JJ, TT>, 256, std::min((groups + 3) / 4, kMaxGemvBlocks)); \
+        if (grid < 1) return fail(Q4MOE_EDEVICE, "occupancy query failed");                          \
+        hipLaunchKernelGGL((k_gemv_mfma<JJ, TT>), dim3(grid), dim3(256), 0, s, a);                   \
+    } while (0)
+#define Q4_GEMV_T(JJ)                  \
+    switch (n_tok) {                   \
+        case 1: Q4_GEMV(JJ, 1); break; \
+        case 2: Q4_GEMV(JJ, 2); break; \
+        case 3: Q4_GEMV(JJ, 3); break; \
+        default: Q4_GEMV(JJ, 4); break; \
     }
-    switch (C) {
-        case 1: Q4_GEMV_T(1); break;
-        case 2: Q4_GEMV_T(2); break;
-        case 3: Q4_GEMV_T(3); break;
-        default: Q4_GEMV_T(4); break;
+    switch (NJ) {
+        case 4: Q4_GEMV_T(4); break;
+        case 8: Q4_GEMV_T(8); break;
+        case 12: Q4_GEMV_T(12); break;
+        case 16: Q4_GEMV_T(16); break;
+        case 20: Q4_GEMV_T(20); break;
+        case 21: Q4_GEMV_T(21); break;
+        case 24: Q4_GEMV_T(24); break;
+        case 28: Q4_GEMV_T(28); break;
+        default: Q4_GEMV_T(32); break;
     }
 #undef Q4_GEMV_T
 #undef Q4_GEMV
-    return launched("lm_head gemv");
+    if ((st = launched("lm_head gemv")) != Q4MOE_OK) return st;
+    if (argmax) {
+        hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(256), 0, s, a.keys, grid, n_tok, argmax);
+        return launched("lm_head argmax");
+    }
+    return Q4MOE_OK;
 }
 
 }  // extern "C"

@@ -386,8 +386,7 @@ struct GemvArgs {
     const uint16_t* x;
     float* logits;           // [T][rows]
     int32_t* argmax;         // nullable
-    unsigned long long* keys;  // [T] workspace, zero between calls
-    uint32_t* ctrl;          // workspace control words
+    unsigned long long* keys;  // [gridDim][T] workspace: each workgroup's best key per token
 };
 
 // Order-preserving map of fp32 onto uint32 (larger float -> larger integer).
@@ -396,90 +395,211 @@ __device__ __forceinline__ uint32_t f32_order(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// 32-lane segments, two rows per wave per pass, 8 passes: 64 rows per block.
-template <int C, int T>
-__global__ __launch_bounds__(256) void k_gemv(GemvArgs a) {
-    constexpr int kPasses = 8;
+// NVFP4 GEMV on MFMA for up to four tokens: logits[t][v] = g * sum_k W[v][k] x[t][k].
+// v_mfma_f32_16x16x32_f16 with the weight rows as the 16-row operand and the
+// tokens as the 16-column operand (columns past T are zero).  A wave owns a
+// group of 16 rows at a time and issues every load of the group (NJ 16-byte
+// code pieces and NJ scale pairs per lane) before it computes; lane (m, kq)
+// takes bytes 64 j + 16 kq .. +15 of row m (k 128 j + 32 kq .. +31), and MFMA
+// step (j, d) sums k 128 j + 32 kq + 8 d .. +7 on both operands.  Weights
+// decode exactly to fp16 (e2m1 * e4m3 has at most six significant bits).
+// x sits in LDS as fp16 after scaling token t by a power of two that puts
+// its largest magnitude in [2^14, 2^15): no fp16 overflow, every bf16 value
+// at least 2^-28 of that maximum is exact, and the result is scaled back
+// exactly.  Persistent grid: wave w of workgroup b takes groups b*4+w,
+// stepping by 4*gridDim.  Each workgroup leaves its best (logit, row) key
+// per token in the workspace for k_argmax_reduce.
+constexpr int kGemvMaxCols = 4096;
+template <int NJ, int T>
+__global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    __shared__ __attribute__((aligned(16))) _Float16 xs[T][kGemvMaxCols + 8];
+    static_assert(128 * (NJ - 1) + 32 * 3 + 8 * 3 + 8 <= kGemvMaxCols + 8, "LDS reads stay in the row");
+    __shared__ float s_amax[4][T];
+    __shared__ int s_exp[T];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int seg = lane >> 5, li = lane & 31;
-    const int nch = a.cols / 32;
-    uint32_t xa[T][C][16];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const int ch = li * C + c;
-            if (ch < nch)
-                load_x_chunk(a.x + (size_t)t * a.cols, ch, xa[t][c]);
-            else
-#pragma unroll
-                for (int j = 0; j < 16; ++j) xa[t][c][j] = 0u;
-        }
-    const float g = *a.gscale;
-    unsigned long long best[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) best[t] = 0ull;
+    const int cols = a.cols;
 
-    for (int ps = 0; ps < kPasses; ++ps) {
-        const int r = (blockIdx.x * kPasses + ps) * 8 + wave * 2 + seg;
-        const bool rowok = r < a.rows;
-        float acc[T];
+    // x -> registers in 16-byte pieces (one pass, every load in flight at
+    // once), per-token largest magnitude, power-of-two scale, fp16 into LDS
+    {
+        constexpr int kXP = (T * kGemvMaxCols / 8 + 255) / 256;
+        const int per_t = cols / 8, total = T * per_t;
+        uint4 xv[kXP];
 #pragma unroll
-        for (int t = 0; t < T; ++t) acc[t] = 0.f;
-        if (rowok) {
-            const uint8_t* rc = a.codes + (size_t)r * (a.cols / 2);
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            xv[i] = p < total ? *reinterpret_cast<const uint4*>(a.x + (size_t)p * 8) : make_uint4(0u, 0u, 0u, 0u);
+        }
+        float m[T];
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const int ch = li * C + c;
-                if (ch < nch) {
-                    const uint4 q = ldg16(rc + ch * 16);
-                    const uint32_t sb =
-                        *reinterpret_cast<const uint16_t*>(a.scales + (size_t)r * (a.cols / 16) + ch * 2);
-                    const float s0 = e4m3fn_to_f32(sb & 0xffu), s1 = e4m3fn_to_f32(sb >> 8);
+        for (int t = 0; t < T; ++t) m[t] = 0.f;
 #pragma unroll
-                    for (int t = 0; t < T; ++t) acc[t] += nvfp4_chunk_bf16(q, xa[t][c], s0, s1);
-                }
-            }
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            const int tp = p / per_t;
+            const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+            float mx = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                mx = fmaxf(mx, fmaxf(fabsf(bf16_bits_to_f32(w[d] & 0xffffu)), fabsf(bf16_bits_to_f32(w[d] >> 16))));
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                if (tp == t) m[t] = fmaxf(m[t], mx);
         }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            const float l = seg_sum<32>(acc[t]) * g;
-            if (li == 0 && rowok) {
-                a.logits[(size_t)t * a.rows + r] = l;
-                const unsigned long long key =
-                    ((unsigned long long)f32_order(l) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)r);
-                best[t] = key > best[t] ? key : best[t];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) m[t] = fmaxf(m[t], __shfl_xor(m[t], o, 64));
+            if (lane == 0) s_amax[wave][t] = m[t];
+        }
+        __syncthreads();
+        if (threadIdx.x < T) {
+            const float mx = fmaxf(fmaxf(s_amax[0][threadIdx.x], s_amax[1][threadIdx.x]),
+                                   fmaxf(s_amax[2][threadIdx.x], s_amax[3][threadIdx.x]));
+            // scale 2^(14 - ilogb(max)); no scaling for 0, inf or NaN
+            s_exp[threadIdx.x] = (mx > 0.f && mx <= 3.4e38f) ? 14 - ilogbf(mx) : 0;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            if (p < total) {
+                const int tp = p / per_t, k0 = (p - tp * per_t) * 8;
+                const float sc = ldexpf(1.0f, s_exp[tp]);
+                const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w};
+                h8 hv;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    hv[2 * d] = (_Float16)(bf16_bits_to_f32(w[d] & 0xffffu) * sc);
+                    hv[2 * d + 1] = (_Float16)(bf16_bits_to_f32(w[d] >> 16) * sc);
+                }
+                *reinterpret_cast<h8*>(&xs[tp][k0]) = hv;
+            }
+        }
+        // zeros past the row: reads of pieces past the end stay finite
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+#pragma unroll 1
+            for (int k = cols + threadIdx.x; k < kGemvMaxCols + 8; k += 256) xs[t][k] = (_Float16)0.f;
+        __syncthreads();
+    }
+    const float g = *a.gscale;
+    const int m16 = lane & 15, kq = lane >> 4;
+    const int n = m16;  // token column of this lane in the 16-column operand
+    float unscale = 0.f;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        if (n == t) unscale = ldexpf(g, -s_exp[t]);
+    unsigned long long best = 0ull;
+
+    const int groups = (a.rows + 15) / 16;
+    for (int grp = blockIdx.x * 4 + wave; grp < groups; grp += gridDim.x * 4) {
+        // 32-bit offsets from the uniform bases (the host checks the matrix
+        // is under 4 GiB), so each load takes one offset register
+        const uint32_t r = (uint32_t)min(grp * 16 + m16, a.rows - 1);
+        const uint32_t rc = r * (uint32_t)(cols / 2), rs = r * (uint32_t)(cols / 16);
+        // pieces in batches of kB: batch b+1 is issued before batch b is
+        // computed (straight-line code: every wait covers exactly its batch)
+        constexpr int kB = 7;
+        uint4 q[NJ];
+        uint32_t sc[NJ];
+        auto issue = [&](int j0) {
+#pragma unroll
+            for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
+                const bool ok = 128 * j + 32 * kq < cols;
+                q[j] = ldg16(a.codes + (rc + (ok ? 64 * j + 16 * kq : cols / 2 - 16)));
+                sc[j] = *reinterpret_cast<const uint16_t*>(a.scales + (rs + (ok ? 8 * j + 2 * kq : cols / 16 - 2)));
+            }
+        };
+        f4 acc = {0.f, 0.f, 0.f, 0.f};
+        issue(0);
+#pragma unroll
+        for (int j0 = 0; j0 < NJ; j0 += kB) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (j0 + kB < NJ) issue(j0 + kB);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
+                const bool ok = 128 * j + 32 * kq < cols;
+                const h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? sc[j] : 0u, 1.0f, false);
+                const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const h2 s = (d < 2) ? h2{sp.x, sp.x} : h2{sp.y, sp.y};
+                    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 0) * s;
+                    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 1) * s;
+                    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 2) * s;
+                    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 3) * s;
+                    const h8 wf = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+                    h8 xf = {0, 0, 0, 0, 0, 0, 0, 0};
+                    // (in bounds for every piece: 128 j + 32 kq + 8 d + 8 <= 4096 + 8)
+                    if (n < T) xf = *reinterpret_cast<const h8*>(&xs[n][128 * j + 32 * kq + 8 * d]);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf, acc, 0, 0, 0);
+                }
+            }
+        }
+        // lane holds rows grp*16 + 4 kq + r of token n
+        if (n < T) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                const int row = grp * 16 + 4 * kq + rr;
+                if (row < a.rows) {
+                    const float l = acc[rr] * unscale;
+                    a.logits[(size_t)n * a.rows + row] = l;
+                    const unsigned long long key =
+                        ((unsigned long long)f32_order(l) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)row);
+                    best = key > best ? key : best;
+                }
             }
         }
     }
-    // block-level maximum of the keys, then one atomic per token per block
-    __shared__ unsigned long long sbest[8][T];
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        unsigned long long v = best[t];
-        const unsigned long long o = __shfl_xor(v, 32, 64);
-        v = o > v ? o : v;
-        if (lane == 0) sbest[wave][t] = v;
+    // per token: the lanes n, n+16, n+32, n+48 of every wave, then the block
+    {
+        unsigned long long o = __shfl_xor(best, 16, 64);
+        best = o > best ? o : best;
+        o = __shfl_xor(best, 32, 64);
+        best = o > best ? o : best;
     }
+    __shared__ unsigned long long sbest[4][T];
+    if (lane < T) sbest[wave][lane] = best;
     __syncthreads();
+    // this workgroup's best key per token; k_argmax_reduce merges them after
+    // the launch (a kernel boundary orders the stores: no fences, no atomics)
     if (threadIdx.x < T) {
         unsigned long long v = 0ull;
         for (int wv = 0; wv < 4; ++wv) v = sbest[wv][threadIdx.x] > v ? sbest[wv][threadIdx.x] : v;
-        atomicMax(a.keys + threadIdx.x, v);
+        a.keys[(size_t)blockIdx.x * T + threadIdx.x] = v;
     }
-    // the last block to finish publishes the argmax and clears the keys
-    __shared__ bool last;
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) last = atomicAdd(a.ctrl + CTRL_TICKET, 1u) == gridDim.x - 1;
-    __syncthreads();
-    if (last) {
-        __threadfence();
-        if (threadIdx.x < T) {
-            const unsigned long long k = atomicExch(a.keys + threadIdx.x, 0ull);
-            if (a.argmax) a.argmax[threadIdx.x] = (int32_t)(0xffffffffu - (uint32_t)(k & 0xffffffffull));
+}
+
+// argmax[t] = the row of the largest key over the nblocks per-workgroup keys
+// (key = order(logit) << 32 | ~row: the largest logit, then the lowest row).
+__global__ __launch_bounds__(256) void k_argmax_reduce(const unsigned long long* keys, int nblocks, int T,
+                                                       int32_t* argmax) {
+    __shared__ unsigned long long sm[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = 0; t < T; ++t) {
+        unsigned long long v = 0ull;
+        for (int b = threadIdx.x; b < nblocks; b += 256) {
+            const unsigned long long k = keys[(size_t)b * T + t];
+            v = k > v ? k : v;
         }
-        if (threadIdx.x == 0) atomicExch(a.ctrl + CTRL_TICKET, 0u);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const unsigned long long w = __shfl_xor(v, o, 64);
+            v = w > v ? w : v;
+        }
+        if (lane == 0) sm[wave] = v;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            unsigned long long m = sm[0];
+            for (int i = 1; i < 4; ++i) m = sm[i] > m ? sm[i] : m;
+            argmax[t] = (int32_t)(0xffffffffu - (uint32_t)(m & 0xffffffffull));
+        }
+        __syncthreads();
     }
 }
 

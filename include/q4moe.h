@@ -170,8 +170,14 @@ q4moe_status q4moe_w4a4_grouped_taps(const q4moe_router* r, const q4moe_experts*
 
 /* NVFP4 W4A16 GEMV for the lm_head ([W] Step 4; [C] precision table:
  * lm_head NVFP4 weight-only, block 16): logits fp32 [n_tok][rows] =
- * W x_t for bf16 x [n_tok][cols], 1 <= n_tok <= 4; argmax (nullable) int32
- * [n_tok] = lowest row index among the largest logits. */
+ * g * W x_t for bf16 x [n_tok][cols], 1 <= n_tok <= 4, cols a multiple of 32
+ * up to 4096, codes under 4 GiB; argmax (nullable) int32 [n_tok] = lowest row
+ * index among the largest logits.  Products and sums are fp32 on fp16 MFMA:
+ * weights decode exactly; token t of x is scaled by the power of two that
+ * puts its largest magnitude in [2^14, 2^15) and rounded to fp16, which is
+ * exact for every element at least 2^-28 of that maximum.  Two launches (the
+ * GEMV, then the argmax merge when argmax is given); no atomics, so the
+ * workspace needs no clearing between calls. */
 size_t q4moe_w4a16_gemv_ws_bytes(const q4moe_qmat* m, int32_t n_tok);
 q4moe_status q4moe_w4a16_gemv(const q4moe_qmat* m, const uint16_t* x_bf16, int32_t n_tok,
                               float* logits, int32_t* argmax, void* ws, size_t ws_bytes,
