@@ -110,7 +110,7 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, h, y32, total;
+    size_t sc_tag, h_tag, z_tag, h, y32, zw, total;
 };
 
 DecodeWs decode_ws(int E, int H, int I, int K, int T) {
@@ -127,6 +127,8 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T) {
     o += up_to((size_t)T * K * I * 4);
     l.y32 = o;
     o += up_to((size_t)T * H * 4);
+    l.zw = o;      // multi-token path: w * g * z per (token, slot) pair
+    o += up_to((size_t)T * K * H * 4);
     l.total = o;
     return l;
 }
@@ -291,7 +293,7 @@ q4moe_status launch_router(const RouterArgs& a, hipStream_t s) {
     if (a.T >= 16) {  // many tokens: the MFMA router GEMM
         hipLaunchKernelGGL(k_router_gemm, dim3((a.E + 31) / 32, (a.T + 31) / 32), dim3(512), 0, s, a);
     } else {
-        dim3 g1((a.E + 3) / 4, (a.T + 3) / 4);
+        dim3 g1(a.E, (a.T + 3) / 4);
         hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, a);
     }
     q4moe_status st = launched("router logits");
@@ -334,6 +336,37 @@ q4moe_status launch_down(const MoeArgs& a, hipStream_t s) {
         case 3: return launch_down_t<FMT, 3>(a, s);
         default: return launch_down_t<FMT, 4>(a, s);
     }
+}
+
+// NJ instance of the small-batch kernels for a reduction of `cols` (128
+// columns per piece; pieces past cols are masked).
+inline int small_nj(int cols) {
+    const int nj = (cols + 127) / 128;
+    return nj <= 8 ? 8 : nj <= 15 ? 15 : nj <= 16 ? 16 : nj <= 21 ? 21 : nj <= 24 ? 24 : 32;
+}
+
+q4moe_status launch_small(const SmallMoeArgs& a, hipStream_t s) {
+    const int pairs = a.T * a.K;
+    const dim3 gu((a.I + 63) / 64, pairs), gd((a.H + 63) / 64, pairs);
+#define Q4_SMALL(KERN, NJ, G) hipLaunchKernelGGL((KERN<NJ>), G, dim3(256), 0, s, a)
+#define Q4_SMALL_NJ(KERN, NJV, G)              \
+    switch (NJV) {                             \
+        case 8: Q4_SMALL(KERN, 8, G); break;   \
+        case 15: Q4_SMALL(KERN, 15, G); break; \
+        case 16: Q4_SMALL(KERN, 16, G); break; \
+        case 21: Q4_SMALL(KERN, 21, G); break; \
+        case 24: Q4_SMALL(KERN, 24, G); break; \
+        default: Q4_SMALL(KERN, 32, G); break; \
+    }
+    Q4_SMALL_NJ(k_small_up, small_nj(a.H), gu);
+    q4moe_status st = launched("small-batch up projection");
+    if (st != Q4MOE_OK) return st;
+    Q4_SMALL_NJ(k_small_down, small_nj(a.I), gd);
+    if ((st = launched("small-batch down projection")) != Q4MOE_OK) return st;
+#undef Q4_SMALL_NJ
+#undef Q4_SMALL
+    hipLaunchKernelGGL(k_small_combine, dim3((a.T * a.H + 255) / 256), dim3(256), 0, s, a);
+    return launched("small-batch combine");
 }
 
 }  // namespace
@@ -492,6 +525,29 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
     if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;
+
+    if (ex->fmt == Q4MOE_NVFP4) {  // each distinct expert streamed once, on MFMA
+        SmallMoeArgs b;
+        b.E = ex->n_experts;
+        b.H = ex->hidden;
+        b.I = ex->inter;
+        b.K = r->top_k;
+        b.T = n_tok;
+        b.upc = ex->up_codes;
+        b.ups = static_cast<const uint8_t*>(ex->up_scales);
+        b.upg = ex->up_gscale;
+        b.dnc = ex->down_codes;
+        b.dns = static_cast<const uint8_t*>(ex->down_scales);
+        b.dng = ex->down_gscale;
+        b.x = x_bf16;
+        b.ids = ra.ids;
+        b.w = ra.w;
+        b.h = at<float>(ws, l.h);
+        b.zw = at<float>(ws, l.zw);
+        b.y32 = at<float>(ws, l.y32);
+        b.y = y_bf16;
+        return launch_small(b, s);
+    }
 
     MoeArgs a;
     a.fmt = ex->fmt;

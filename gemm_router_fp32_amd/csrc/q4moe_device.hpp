@@ -222,4 +222,20 @@ __device__ __forceinline__ uint4 ldg16_stream(const uint8_t* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// Wave maximum of v, returned as a uniform value (DPP inside rows, row
+// broadcasts across rows, then lane 63 read into a scalar).
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp<0xB1>(v));
+    v = fmaxf(v, dpp<0x4E>(v));
+    v = fmaxf(v, dpp<0x124>(v));
+    v = fmaxf(v, dpp<0x128>(v));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                      __builtin_bit_cast(int, v), 0x142, 0xA, 0xF,
+                                                                      false)));
+    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                      __builtin_bit_cast(int, v), 0x143, 0xC, 0xF,
+                                                                      false)));
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
 }  // namespace q4moe

@@ -100,22 +100,6 @@ __device__ __forceinline__ float tag_value(unsigned long long t) { return __uint
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Wave maximum of v, returned as a uniform value (DPP inside rows, row
-// broadcasts across rows, then lane 63 read into a scalar).
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp<0xB1>(v));
-    v = fmaxf(v, dpp<0x4E>(v));
-    v = fmaxf(v, dpp<0x124>(v));
-    v = fmaxf(v, dpp<0x128>(v));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
-                                                                      __builtin_bit_cast(int, v), 0x142, 0xA, 0xF,
-                                                                      false)));
-    v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
-                                                                      __builtin_bit_cast(int, v), 0x143, 0xC, 0xF,
-                                                                      false)));
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
-}
-
 // Exact fp32 top-k of E <= 256 keys by one wave: expert e sits in lane
 // e % 64, register e / 64.  Each round takes the wave maximum and then the
 // lowest expert index holding it (ballot + find-first-set), so equal keys

@@ -37,36 +37,52 @@ struct RouterArgs {
     float* logits_out;  // nullable
 };
 
-// logits[t][e] = sum_c W_g[e][c] * x[t][c]: one wave per expert and up to
-// four tokens; grid (ceil(E/4), ceil(T/4)), 256 threads.
+// logits[t][e] = sum_c W_g[e][c] * x[t][c]: one workgroup per expert and up
+// to four tokens, grid (E, ceil(T/4)), 256 threads.  Thread i takes the
+// 4-column pieces i, i + 256, ... (H <= 4096: at most four), all loads issued
+// before any use; the partial sums meet in LDS in a fixed order.
 __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a) {
+    constexpr int kPieces = 4;  // 4096 / 4 / 256
+    __shared__ float part[4][4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e = blockIdx.x * 4 + wave;
-    const int t0 = blockIdx.y * 4;
-    if (e >= a.E) return;  // wave-uniform
+    const int e = blockIdx.x, t0 = blockIdx.y * 4;
     const int nt = min(4, a.T - t0);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    const int np = a.H / 4;
     const float4* wr = reinterpret_cast<const float4*>(a.wg + (size_t)e * a.H);
-    for (int j = lane; j < a.H / 4; j += kWave) {
-        const float4 wv = wr[j];
+    float4 wv[kPieces];
+    uint2 xb[kPieces][4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            if (t < nt) {
-                const uint2 xb = *reinterpret_cast<const uint2*>(a.x + (size_t)(t0 + t) * a.H + 4 * j);
-                acc[t] = __builtin_fmaf(wv.x, bf16_bits_to_f32(xb.x & 0xffffu), acc[t]);
-                acc[t] = __builtin_fmaf(wv.y, bf16_bits_to_f32(xb.x >> 16), acc[t]);
-                acc[t] = __builtin_fmaf(wv.z, bf16_bits_to_f32(xb.y & 0xffffu), acc[t]);
-                acc[t] = __builtin_fmaf(wv.w, bf16_bits_to_f32(xb.y >> 16), acc[t]);
+    for (int i = 0; i < kPieces; ++i) {
+        const int j = min((int)threadIdx.x + 256 * i, np - 1);  // clamped: unused pieces are masked below
+        wv[i] = wr[j];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            xb[i][t] = *reinterpret_cast<const uint2*>(a.x + (size_t)(t0 + min(t, nt - 1)) * a.H + 4 * j);
+    }
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+        if ((int)threadIdx.x + 256 * i < np) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                acc[t] = __builtin_fmaf(wv[i].x, bf16_bits_to_f32(xb[i][t].x & 0xffffu), acc[t]);
+                acc[t] = __builtin_fmaf(wv[i].y, bf16_bits_to_f32(xb[i][t].x >> 16), acc[t]);
+                acc[t] = __builtin_fmaf(wv[i].z, bf16_bits_to_f32(xb[i][t].y & 0xffffu), acc[t]);
+                acc[t] = __builtin_fmaf(wv[i].w, bf16_bits_to_f32(xb[i][t].y >> 16), acc[t]);
             }
         }
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const float l = seg_sum<64>(acc[t]);
-        if (lane == 0 && t < nt) {
-            a.logits[(size_t)(t0 + t) * a.E + e] = l;
-            if (a.logits_out) a.logits_out[(size_t)(t0 + t) * a.E + e] = l;
-        }
+        if (lane == 0) part[wave][t] = l;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+        const int t = threadIdx.x;
+        const float l = (part[0][t] + part[1][t]) + (part[2][t] + part[3][t]);
+        a.logits[(size_t)(t0 + t) * a.E + e] = l;
+        if (a.logits_out) a.logits_out[(size_t)(t0 + t) * a.E + e] = l;
     }
 }
 
@@ -87,46 +103,48 @@ __global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
         s[q] = 1.0f / (1.0f + expf(-l));
         key[q] = s[q] + (live[q] ? a.bias[e] : 0.f);
     }
+    // Each round: the wave maximum (DPP), then the lowest expert index holding
+    // it (ballot + find-first-set), so equal keys go to the lower index.  The
+    // loop is unrolled (K <= 8) so the selections stay in registers.
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+        if (!live[q]) key[q] = -__builtin_inff();
     float sel_s[8];
     int sel_i[8];
     float ssum = 0.f;
-    for (int i = 0; i < a.K; ++i) {
-        float bk = -__builtin_inff();
-        int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        sel_s[i] = 0.f;
+        sel_i[i] = 0;
+        if (i >= a.K) continue;
+        const float m = wave_max(fmaxf(fmaxf(key[0], key[1]), fmaxf(key[2], key[3])));
+        int best = 0x7fffffff;
+        float bs = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int e = lane + kWave * q;
-            if (live[q] && (key[q] > bk || (key[q] == bk && e < bi))) {
-                bk = key[q];
-                bi = e;
+            const unsigned long long hit = __ballot(key[q] == m);
+            if (hit && best == 0x7fffffff) {
+                const int l = (int)__builtin_ctzll(hit);
+                best = l + kWave * q;
+                bs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s[q]), l));
             }
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-            const float ok = __shfl_xor(bk, off, 64);
-            const int oi = __shfl_xor(bi, off, 64);
-            if (ok > bk || (ok == bk && oi < bi)) {
-                bk = ok;
-                bi = oi;
-            }
-        }
-        const int owner = bi & 63, slot = bi >> 6;
-        float mine = 0.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (lane == owner && slot == q) {
-                mine = s[q];
-                live[q] = false;
-            }
-        const float sb = __shfl(mine, owner, 64);
-        sel_s[i] = sb;
-        sel_i[i] = bi;
-        ssum += sb;
+            if (lane + kWave * q == best) key[q] = -__builtin_inff();
+        if (best >= a.E) {  // no finite key left (NaN logits): keep ids inside the bank
+            best = 0;
+            bs = 0.f;
+        }
+        sel_s[i] = bs;
+        sel_i[i] = best;
+        ssum += bs;
     }
     if (lane < a.K) {
         float ws = 0.f;
         int wi = 0;
-        for (int i = 0; i < a.K; ++i)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
             if (i == lane) {
                 ws = sel_s[i];
                 wi = sel_i[i];
@@ -395,6 +413,70 @@ __device__ __forceinline__ uint32_t f32_order(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+typedef float f32x4g __attribute__((ext_vector_type(4)));
+
+// One group of 16 NVFP4 rows against up to 16 LDS columns on fp16 MFMA
+// (v_mfma_f32_16x16x32_f16): returns D[4 kq + r][n] for n = lane % 16, where
+// the 16-row operand is rows (row of lane (m16, kq)) and column n of the other
+// operand is LDS row n of xs (pitch P fp16; columns n >= NT are zero).  Lane
+// (m16, kq) reads bytes 64 j + 16 kq .. +15 of its row for j < NJ (k 128 j +
+// 32 kq .. +31) and MFMA step (j, d) sums k 128 j + 32 kq + 8 d .. +7 on both
+// operands.  Weights decode exactly to fp16 (e2m1 * e4m3 has at most six
+// significant bits).  Loads go in batches of seven pieces, batch b+1 issued
+// before batch b is computed; `after_first_issue` runs (in every thread)
+// once the first batch is in flight.  Pieces past `cols` reread the row's
+// last bytes with scale 0 and read LDS columns that must hold zeros up to
+// 128 NJ.
+// Offsets are 32-bit from the uniform bases (codes under 4 GiB).
+template <int NJ, int NT, int P, typename F>
+__device__ __forceinline__ f32x4g mfma_gemv_group(const uint8_t* codes, const uint8_t* scales, uint32_t r, int cols,
+                                                  const _Float16* xs, int m16, int kq, F&& after_first_issue) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const uint32_t rc = r * (uint32_t)(cols / 2), rs = r * (uint32_t)(cols / 16);
+    constexpr int kB = 7;
+    uint4 q[NJ];
+    uint32_t sc[NJ];
+    auto issue = [&](int j0) {
+#pragma unroll
+        for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
+            const bool ok = 128 * j + 32 * kq < cols;
+            q[j] = ldg16(codes + (rc + (ok ? 64 * j + 16 * kq : cols / 2 - 16)));
+            sc[j] = *reinterpret_cast<const uint16_t*>(scales + (rs + (ok ? 8 * j + 2 * kq : cols / 16 - 2)));
+        }
+    };
+    f32x4g acc = {0.f, 0.f, 0.f, 0.f};
+    issue(0);
+    // (the caller may fill xs here, while the first batch is in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    after_first_issue();
+#pragma unroll
+    for (int j0 = 0; j0 < NJ; j0 += kB) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (j0 + kB < NJ) issue(j0 + kB);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
+            const bool ok = 128 * j + 32 * kq < cols;
+            const h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? sc[j] : 0u, 1.0f, false);
+            const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                const h2 s = (d < 2) ? h2{sp.x, sp.x} : h2{sp.y, sp.y};
+                const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 0) * s;
+                const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 1) * s;
+                const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 2) * s;
+                const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 3) * s;
+                const h8 wf = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+                h8 xf = {0, 0, 0, 0, 0, 0, 0, 0};
+                if (m16 < NT) xf = *reinterpret_cast<const h8*>(xs + m16 * P + 128 * j + 32 * kq + 8 * d);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf, acc, 0, 0, 0);
+            }
+        }
+    }
+    return acc;
+}
+
 // NVFP4 GEMV on MFMA for up to four tokens: logits[t][v] = g * sum_k W[v][k] x[t][k].
 // v_mfma_f32_16x16x32_f16 with the weight rows as the 16-row operand and the
 // tokens as the 16-column operand (columns past T are zero).  A wave owns a
@@ -497,50 +579,8 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
 
     const int groups = (a.rows + 15) / 16;
     for (int grp = blockIdx.x * 4 + wave; grp < groups; grp += gridDim.x * 4) {
-        // 32-bit offsets from the uniform bases (the host checks the matrix
-        // is under 4 GiB), so each load takes one offset register
         const uint32_t r = (uint32_t)min(grp * 16 + m16, a.rows - 1);
-        const uint32_t rc = r * (uint32_t)(cols / 2), rs = r * (uint32_t)(cols / 16);
-        // pieces in batches of kB: batch b+1 is issued before batch b is
-        // computed (straight-line code: every wait covers exactly its batch)
-        constexpr int kB = 7;
-        uint4 q[NJ];
-        uint32_t sc[NJ];
-        auto issue = [&](int j0) {
-#pragma unroll
-            for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
-                const bool ok = 128 * j + 32 * kq < cols;
-                q[j] = ldg16(a.codes + (rc + (ok ? 64 * j + 16 * kq : cols / 2 - 16)));
-                sc[j] = *reinterpret_cast<const uint16_t*>(a.scales + (rs + (ok ? 8 * j + 2 * kq : cols / 16 - 2)));
-            }
-        };
-        f4 acc = {0.f, 0.f, 0.f, 0.f};
-        issue(0);
-#pragma unroll
-        for (int j0 = 0; j0 < NJ; j0 += kB) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (j0 + kB < NJ) issue(j0 + kB);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
-                const bool ok = 128 * j + 32 * kq < cols;
-                const h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? sc[j] : 0u, 1.0f, false);
-                const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const h2 s = (d < 2) ? h2{sp.x, sp.x} : h2{sp.y, sp.y};
-                    const h2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 0) * s;
-                    const h2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 1) * s;
-                    const h2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 2) * s;
-                    const h2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w4[d], 1.0f, 3) * s;
-                    const h8 wf = {p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-                    h8 xf = {0, 0, 0, 0, 0, 0, 0, 0};
-                    // (in bounds for every piece: 128 j + 32 kq + 8 d + 8 <= 4096 + 8)
-                    if (n < T) xf = *reinterpret_cast<const h8*>(&xs[n][128 * j + 32 * kq + 8 * d]);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf, xf, acc, 0, 0, 0);
-                }
-            }
-        }
+        const f4 acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales, r, cols, &xs[0][0], m16, kq, [] {});
         // lane holds rows grp*16 + 4 kq + r of token n
         if (n < T) {
 #pragma unroll
@@ -601,6 +641,284 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const unsigned long long*
         }
         __syncthreads();
     }
+}
+
+// ---------------------------------------------------------------------------
+// Routed MoE for 2..4 tokens on MFMA (the four-token verify step of "Let's
+// optimize Nemotron 3.5 Lightning - a worklog", Step 5), NVFP4 weights.  Each
+// distinct selected expert is streamed once: the block set of the first
+// (token, slot) pair that selected it computes the expert for every token
+// (MFMA columns are free up to 16) and writes the results of every pair that
+// selected it.
+// ---------------------------------------------------------------------------
+constexpr int kSmallT = 4;  // tokens at most
+
+struct SmallMoeArgs {
+    int E, H, I, K, T;
+    const uint8_t* upc;
+    const uint8_t* ups;
+    const float* upg;
+    const uint8_t* dnc;
+    const uint8_t* dns;
+    const float* dng;
+    const uint16_t* x;   // [T][H] bf16
+    const int32_t* ids;  // [T][K]
+    const float* w;      // [T][K]
+    float* h;            // [T*K][I] fp32
+    float* zw;           // [T*K][H] fp32: w * g * z per pair
+    float* y32;          // [T][H]
+    uint16_t* y;         // [T][H] bf16
+};
+
+// The expert of pair p, and whether p is the first pair that selected it.
+__device__ __forceinline__ int small_expert(const SmallMoeArgs& a, int p, bool& leader) {
+    const int e = min(max(a.ids[p], 0), a.E - 1);  // routing ids are always in range; never read outside the bank
+    leader = true;
+    for (int q = 0; q < p; ++q)
+        if (min(max(a.ids[q], 0), a.E - 1) == e) leader = false;
+    return e;
+}
+
+// Largest magnitude of each of the 4 rows' values (per-thread partials -> block).
+__device__ __forceinline__ void block_amax4(float m[4], float (*s_amax)[4], int* s_exp) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) m[t] = fmaxf(m[t], __shfl_xor(m[t], o, 64));
+        if (lane == 0) s_amax[wave][t] = m[t];
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const float mx = fmaxf(fmaxf(s_amax[0][threadIdx.x], s_amax[1][threadIdx.x]),
+                               fmaxf(s_amax[2][threadIdx.x], s_amax[3][threadIdx.x]));
+        // scale 2^(14 - ilogb(max)) puts the largest magnitude in [2^14, 2^15)
+        s_exp[threadIdx.x] = (mx > 0.f && mx <= 3.4e38f) ? 14 - ilogbf(mx) : 0;
+    }
+    __syncthreads();
+}
+
+// Rows 0..3 of an LDS operand (pitch P fp16) from up to four bf16 rows of
+// `cols` values (row t at src + t * cols): row t is scaled by 2^s_exp[t],
+// the power of two that puts its largest magnitude in [2^14, 2^15), and
+// rounded to fp16 (exact for every bf16 value at least 2^-28 of that
+// maximum); rows past `rows` and columns past `cols` are zero.  One pass of
+// 16-byte loads, all in flight at once.
+template <int P>
+__device__ __forceinline__ void stage_bf16_rows(const uint16_t* src, int rows, int cols, _Float16* xs,
+                                                float (*s_amax)[4], int* s_exp) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    constexpr int kXP = (4 * (P / 8) + 255) / 256;
+    const int per = cols / 8, total = rows * per;
+    uint4 v[kXP];
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        v[i] = p < total ? *reinterpret_cast<const uint4*>(src + (size_t)p * 8) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int t = (threadIdx.x + 256 * i) / per;
+        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+        float mx = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+            mx = fmaxf(mx, fmaxf(fabsf(bf16_bits_to_f32(w[d] & 0xffffu)), fabsf(bf16_bits_to_f32(w[d] >> 16))));
+#pragma unroll
+        for (int tt = 0; tt < 4; ++tt)
+            if (t == tt) m[tt] = fmaxf(m[tt], mx);
+    }
+    block_amax4(m, s_amax, s_exp);
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        if (p < total) {
+            const int t = p / per, k0 = (p - t * per) * 8;
+            const float sc = ldexpf(1.0f, s_exp[t]);
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            h8 hv;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                hv[2 * d] = (_Float16)(bf16_bits_to_f32(w[d] & 0xffffu) * sc);
+                hv[2 * d + 1] = (_Float16)(bf16_bits_to_f32(w[d] >> 16) * sc);
+            }
+            *reinterpret_cast<h8*>(xs + t * P + k0) = hv;
+        }
+    }
+    // zeros: rows past `rows`, and columns past `cols` (8-aligned pieces)
+    const h8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = threadIdx.x; i < 4 * (P / 8); i += 256) {
+        const int t = i / (P / 8), k0 = (i - t * (P / 8)) * 8;
+        if (t >= rows || k0 >= cols) *reinterpret_cast<h8*>(xs + t * P + k0) = z;
+    }
+    __syncthreads();
+}
+
+// Columns c < nc of an LDS operand as fp16 hi (row c) and lo (row 4 + c)
+// parts of the fp32 rows src + col_off[c] (`cols` values): row c is scaled
+// by 2^s_exp[c] (largest magnitude into [2^14, 2^15)); hi = fp16(v), lo =
+// fp16(v - hi), so hi + lo carries v to about 2^-22.  Other rows and columns
+// past `cols` are zero.
+template <int P>
+__device__ __forceinline__ void stage_f32_hilo(const float* src, const size_t col_off[4], int nc, int cols,
+                                               _Float16* hs, float (*s_amax)[4], int* s_exp) {
+    typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+    constexpr int kXP = (4 * (P / 4) + 255) / 256;
+    const int per = cols / 4, total = nc * per;
+    float4 v[kXP];
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        const int c = p / per;
+        size_t off = col_off[0];
+#pragma unroll
+        for (int cc = 1; cc < 4; ++cc)
+            if (c == cc) off = col_off[cc];
+        v[i] = p < total ? *reinterpret_cast<const float4*>(src + off + (size_t)(p - c * per) * 4)
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float m[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int c = (threadIdx.x + 256 * i) / per;
+        const float mx = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+            if (c == cc) m[cc] = fmaxf(m[cc], mx);
+    }
+    block_amax4(m, s_amax, s_exp);
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int p = threadIdx.x + 256 * i;
+        if (p < total) {
+            const int c = p / per, k0 = (p - c * per) * 4;
+            const float sc = ldexpf(1.0f, s_exp[c]);
+            const float f[4] = {v[i].x * sc, v[i].y * sc, v[i].z * sc, v[i].w * sc};
+            h4 hi, lo;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                hi[d] = (_Float16)f[d];
+                lo[d] = (_Float16)(f[d] - (float)hi[d]);
+            }
+            *reinterpret_cast<h4*>(hs + c * P + k0) = hi;
+            *reinterpret_cast<h4*>(hs + (4 + c) * P + k0) = lo;
+        }
+    }
+    const h4 z = {0, 0, 0, 0};
+    for (int i = threadIdx.x; i < 8 * (P / 4); i += 256) {
+        const int rr = i / (P / 4), k0 = (i - rr * (P / 4)) * 4;
+        if ((rr & 3) >= nc || k0 >= cols) *reinterpret_cast<h4*>(hs + rr * P + k0) = z;
+    }
+    __syncthreads();
+}
+
+// up: u = W_up[e] x_t for all tokens t, h[pair] = relu(g u)^2 for every pair
+// (t, slot) that selected e.  Grid (ceil(I/64), T*K): 64 rows per block, one
+// 16-row group per wave.  x goes to LDS as fp16 after a per-token power-of-two
+// scaling (as in the lm_head GEMV).
+template <int NJ>
+__global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
+    constexpr int P = 128 * NJ + 8;
+    __shared__ __attribute__((aligned(16))) _Float16 xs[kSmallT][P];
+    __shared__ float s_amax[4][4];
+    __shared__ int s_exp[4];
+    bool leader;
+    const int e = small_expert(a, blockIdx.y, leader);
+    if (!leader) return;  // uniform
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m16 = lane & 15, kq = lane >> 4;
+    const int row = blockIdx.x * 64 + wave * 16 + m16;
+    const uint32_t wrow = (uint32_t)e * a.I + min(row, a.I - 1);
+    // x goes to LDS while the first weight batch is in flight
+    const f32x4g acc = mfma_gemv_group<NJ, kSmallT, P>(a.upc, a.ups, wrow, a.H, &xs[0][0], m16, kq, [&] {
+        stage_bf16_rows<P>(a.x, a.T, a.H, &xs[0][0], s_amax, s_exp);
+    });
+    // lane (n = m16, kq) holds rows 4 kq + r of token n
+    const int n = m16;
+    if (n < a.T) {
+        int pp = -1;
+        for (int sl = 0; sl < a.K; ++sl)
+            if (min(max(a.ids[n * a.K + sl], 0), a.E - 1) == e) pp = n * a.K + sl;
+        if (pp >= 0) {
+            const float sc = ldexpf(a.upg[e], -s_exp[n]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rr = blockIdx.x * 64 + wave * 16 + 4 * kq + r;
+                if (rr < a.I) {
+                    const float u = fmaxf(acc[r] * sc, 0.f);
+                    a.h[(size_t)pp * a.I + rr] = u * u;
+                }
+            }
+        }
+    }
+}
+
+// down: z = W_down[e] h_pair for every pair that selected e, zw[pair] =
+// w * g * z.  Grid (ceil(H/64), T*K).  Each pair's fp32 h is scaled by a power
+// of two and split into fp16 hi + lo (h' = hi + lo to about 2^-22), columns c
+// and 4 + c of the same MFMA, so h keeps nearly fp32 precision at no extra
+// MFMA cost.
+template <int NJ>
+__global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
+    constexpr int P = 128 * NJ + (NJ < 32 ? 8 : 0);  // (the widest instance drops the pad to fit 64 KiB)
+    __shared__ __attribute__((aligned(16))) _Float16 hs[2 * kSmallT][P];
+    __shared__ float s_amax[4][4];
+    __shared__ int s_exp[4];
+    bool leader;
+    const int e = small_expert(a, blockIdx.y, leader);
+    if (!leader) return;  // uniform
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m16 = lane & 15, kq = lane >> 4;
+    const int row = blockIdx.x * 64 + wave * 16 + m16;
+    const uint32_t wrow = (uint32_t)e * a.H + min(row, a.H - 1);
+    // columns: the pairs that selected e, in pair order (one per token at most)
+    // (static indices only, so the list stays in registers)
+    int cols[kSmallT] = {0, 0, 0, 0};
+    int nc = 0;
+    for (int pp = 0; pp < a.T * a.K; ++pp) {
+        if (min(max(a.ids[pp], 0), a.E - 1) == e) {
+#pragma unroll
+            for (int c = 0; c < kSmallT; ++c)
+                if (c == nc) cols[c] = pp;
+            nc = min(nc + 1, kSmallT);
+        }
+    }
+    size_t col_off[kSmallT];
+#pragma unroll
+    for (int c = 0; c < kSmallT; ++c) col_off[c] = (size_t)cols[c] * a.I;
+    // h goes to LDS while the first weight batch is in flight
+    const f32x4g acc = mfma_gemv_group<NJ, 2 * kSmallT, P>(a.dnc, a.dns, wrow, a.I, &hs[0][0], m16, kq, [&] {
+        stage_f32_hilo<P>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp);
+    });
+    // lane (n, kq) holds column n: hi for n < 4, lo for n >= 4; add lane n + 4's lo
+    const int n = m16;
+    float z[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) z[r] = acc[r] + __shfl(acc[r], (n < kSmallT) ? lane + kSmallT : lane, 64);
+    if (n < nc) {
+        int pp = cols[0];
+#pragma unroll
+        for (int c = 1; c < kSmallT; ++c)
+            if (c == n) pp = cols[c];
+        const float sc = ldexpf(a.w[pp] * a.dng[e], -s_exp[n]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rr = blockIdx.x * 64 + wave * 16 + 4 * kq + r;
+            if (rr < a.H) a.zw[(size_t)pp * a.H + rr] = z[r] * sc;
+        }
+    }
+}
+
+// y32[t][r] = sum over slots s (in order) of zw[t*K + s][r]; y = bf16 (RNE).
+__global__ __launch_bounds__(256) void k_small_combine(SmallMoeArgs a) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= a.T * a.H) return;
+    const int t = i / a.H, r = i - t * a.H;
+    float acc = 0.f;
+    for (int sl = 0; sl < a.K; ++sl) acc += a.zw[(size_t)(t * a.K + sl) * a.H + r];
+    a.y32[i] = acc;
+    a.y[i] = (uint16_t)f32_to_bf16_rne(acc);
 }
 
 // Zero fill (used instead of a memset so a caller may capture it in a graph).
