@@ -149,7 +149,11 @@ __device__ __forceinline__ void wave_topk(const FusedArgs& a, const float* s_key
 }
 
 // Units of [0, total) owned by wave index `w` of `n` waves: [lo, hi).
-__device__ __forceinline__ int share_lo(int total, int w, int n) { return (int)((long long)w * total / n); }
+// 32-bit: total <= 8 * 4096 and w <= 8 * (workgroups on the device), so
+// w * total stays far below 2^32.
+__device__ __forceinline__ int share_lo(int total, int w, int n) {
+    return (int)(((uint32_t)w * (uint32_t)total) / (uint32_t)n);
+}
 
 template <int FMT, int C, int C2>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
@@ -196,6 +200,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             xs[c] = pair_sum_bf16(nat);
         }
     }
+    // unit bookkeeping (routing-independent: done while the x loads fly)
+    const int RU = a.K * a.I, RD = a.K * a.H;
+    const int u0 = share_lo(RU, gw, NW), u1 = share_lo(RU, gw + 1, NW);
+    const int d0 = ctl ? 0 : share_lo(RD, gwd, NWD), d1 = ctl ? 0 : share_lo(RD, gwd + 1, NWD);
+    const int wu0 = share_lo(RU, blockIdx.x * kWaves, NW), wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
+    const int wd0 = share_lo(RD, blockIdx.x * kDownWaves, NWD),
+              wd1 = share_lo(RD, (blockIdx.x + 1) * kDownWaves, NWD);
+    // A wave's units span at most two slots: slot(u) = us0 + (u >= ubnd).
+    const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
+    const int ds0 = (d1 > d0 ? d0 : 0) / a.H, dbnd = (ds0 + 1) * a.H;
+    const int n_up_pass = (u1 - u0 + 1) / 2, n_down = d1 - d0;  // <= kMaxUp, <= kMaxDown (checked on the host)
     __syncthreads();
     const uint32_t ep = s_ep;
 
@@ -205,14 +220,25 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         const int nf4 = a.H / 4;
         const int lo = wave * nf4 / kWaves, hi = (wave + 1) * nf4 / kWaves;
         const float4* wr = reinterpret_cast<const float4*>(a.wg + (size_t)e * a.H);
+        // a wave's share is at most 128 pieces (H <= 4096): two per lane, both
+        // loads issued before either is used (clamped; the extra one is masked)
+        float4 wv[2];
+        uint2 xb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int j = min(lo + lane + 64 * i, hi - 1);
+            wv[i] = wr[j];
+            xb[i] = *reinterpret_cast<const uint2*>(a.x + 4 * j);
+        }
         float acc = 0.f;
-        for (int j = lo + lane; j < hi; j += 64) {
-            const float4 wv = wr[j];
-            const uint2 xb = *reinterpret_cast<const uint2*>(a.x + 4 * j);
-            acc = __builtin_fmaf(wv.x, bf16_bits_to_f32(xb.x & 0xffffu), acc);
-            acc = __builtin_fmaf(wv.y, bf16_bits_to_f32(xb.x >> 16), acc);
-            acc = __builtin_fmaf(wv.z, bf16_bits_to_f32(xb.y & 0xffffu), acc);
-            acc = __builtin_fmaf(wv.w, bf16_bits_to_f32(xb.y >> 16), acc);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            if (lo + lane + 64 * i < hi) {
+                acc = __builtin_fmaf(wv[i].x, bf16_bits_to_f32(xb[i].x & 0xffffu), acc);
+                acc = __builtin_fmaf(wv[i].y, bf16_bits_to_f32(xb[i].x >> 16), acc);
+                acc = __builtin_fmaf(wv[i].z, bf16_bits_to_f32(xb[i].y & 0xffffu), acc);
+                acc = __builtin_fmaf(wv[i].w, bf16_bits_to_f32(xb[i].y >> 16), acc);
+            }
         }
         acc = seg_sum_last<64>(acc);
         if (lane == 63) s_part[wave] = acc;
@@ -265,17 +291,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     Q4MOE_PHASE(3);
 
     // ---- U: issue the loads of this wave's up rows, then its down rows
-    const int RU = a.K * a.I, RD = a.K * a.H;
-    const int u0 = share_lo(RU, gw, NW), u1 = share_lo(RU, gw + 1, NW);
-    const int d0 = ctl ? 0 : share_lo(RD, gwd, NWD), d1 = ctl ? 0 : share_lo(RD, gwd + 1, NWD);
-    const int wu0 = share_lo(RU, blockIdx.x * kWaves, NW), wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
-    const int wd0 = share_lo(RD, blockIdx.x * kDownWaves, NWD),
-              wd1 = share_lo(RD, (blockIdx.x + 1) * kDownWaves, NWD);
-    // A wave's units span at most two slots: slot(u) = us0 + (u >= ubnd).
-    const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
-    const int ds0 = (d1 > d0 ? d0 : 0) / a.H, dbnd = (ds0 + 1) * a.H;
-    const int n_up_pass = (u1 - u0 + 1) / 2, n_down = d1 - d0;  // <= kMaxUp, <= kMaxDown (checked on the host)
-
     // per-tensor scales of the selected experts (lane i holds slot i's)
     float gu_l = 1.0f, gd_l = 1.0f;
     if constexpr (FMT == FMT_NVFP4) {
@@ -287,45 +302,60 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 
     // Every lane issues every load (an invalid row or chunk reads a valid
     // address and is zeroed through its scale at compute time), so the loads
-    // stay in issue order and each use waits only for its own data.
+    // stay in issue order and each use waits only for its own data.  Offsets
+    // are 32-bit from the uniform bases (the argument limits keep a bank
+    // under 2^31 bytes), and each row index (< 2^20) times its row bytes
+    // (<= 2048) is a full-rate 24-bit multiply: the row of unit u of slot s
+    // is u + ids[s] * rows - s * rows, a select between the wave's two slots.
+    const uint8_t* ups8 = reinterpret_cast<const uint8_t*>(a.ups);
+    const uint8_t* dns8 = reinterpret_cast<const uint8_t*>(a.dns);
+    const int us1 = min(us0 + 1, a.K - 1), ds1 = min(ds0 + 1, a.K - 1);
+    const int uoff0 = ids[us0] * a.I - us0 * a.I, uoff1 = ids[us1] * a.I - (us0 + 1) * a.I;
+    const int doff0 = ids[ds0] * a.H - ds0 * a.H, doff1 = ids[ds1] * a.H - (ds0 + 1) * a.H;
+    const uint32_t urb = a.H / 2, usb = (FMT == FMT_NVFP4) ? a.H / 16 : a.H / 32;  // bytes per up row
+    const uint32_t drb = a.I / 2, dsb = (FMT == FMT_NVFP4) ? a.I / 16 : a.I / 32;  // bytes per down row
+    uint32_t uco[C], uso[C];  // this lane's chunk offsets within an up row
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int ch = min(c * lpr + li, nchH - 1);
+        uco[c] = ch * 16;
+        uso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
+    }
     uint4 qu[kMaxUp][C];
     uint32_t su[kMaxUp][C];
 #pragma unroll
     for (int p = 0; p < kMaxUp; ++p) {
         int u = u0 + 2 * p + seg;
         if (u >= u1) u = u1 > u0 ? u0 : 0;
-        const int slot = us0 + (u >= ubnd ? 1 : 0), r = u - slot * a.I;
-        const size_t row = (size_t)ids[slot] * a.I + r;
+        const uint32_t row = (uint32_t)(u + (u >= ubnd ? uoff1 : uoff0));
+        const uint32_t rc = __umul24(row, urb), rs = __umul24(row, usb);
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-            const int ch = min(c * lpr + li, nchH - 1);
-            qu[p][c] = ldg16_stream(a.upc + row * (a.H / 2) + ch * 16);
-            if constexpr (FMT == FMT_NVFP4)
-                su[p][c] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.ups) +
-                                                             row * (a.H / 16) + ch * 2);
-            else
-                su[p][c] = reinterpret_cast<const uint16_t*>(a.ups)[row * (a.H / 64) + (ch >> 1)];
+            qu[p][c] = ldg16_stream(a.upc + (rc + uco[c]));
+            su[p][c] = *reinterpret_cast<const uint16_t*>(ups8 + (rs + uso[c]));
         }
     }
     compiler_fence();
     uint4 qd[kMaxDown][C2];
     uint32_t sd[kMaxDown][C2];
     if (!ctl) {
+        uint32_t dco[C2], dso[C2];
+#pragma unroll
+        for (int c = 0; c < C2; ++c) {
+            const int ch = min(lane * C2 + c, nchI - 1);
+            dco[c] = ch * 16;
+            dso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
+        }
 #pragma unroll
         for (int p = 0; p < kMaxDown; ++p) {
             int d = d0 + p;
             if (d >= d1) d = d1 > d0 ? d0 : 0;
-            const int slot = ds0 + (d >= dbnd ? 1 : 0), r = d - slot * a.H;
-            const size_t row = (size_t)ids[slot] * a.H + r;
+            const uint32_t row = (uint32_t)(d + (d >= dbnd ? doff1 : doff0));
+            const uint32_t rc = __umul24(row, drb), rs = __umul24(row, dsb);
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
-                const int ch = min(lane * C2 + c, nchI - 1);
-                qd[p][c] = ldg16_stream(a.dnc + row * (a.I / 2) + ch * 16);
-                if constexpr (FMT == FMT_NVFP4)
-                    sd[p][c] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.dns) +
-                                                                 row * (a.I / 16) + ch * 2);
-                else
-                    sd[p][c] = reinterpret_cast<const uint16_t*>(a.dns)[row * (a.I / 64) + (ch >> 1)];
+                qd[p][c] = ldg16_stream(a.dnc + (rc + dco[c]));
+                sd[p][c] = *reinterpret_cast<const uint16_t*>(dns8 + (rs + dso[c]));
             }
         }
     }
@@ -343,8 +373,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             for (int c = 0; c < C; ++c) {
                 const bool chok = li < lpr && c * lpr + li < nchH;
                 if constexpr (FMT == FMT_NVFP4) {
-                    const float s0 = chok ? e4m3fn_to_f32(su[p][c] & 0xffu) : 0.f;
-                    const float s1 = chok ? e4m3fn_to_f32(su[p][c] >> 8) : 0.f;
+                    const f32x2 sp = e4m3fn_x2_f32(su[p][c]);
+                    const float s0 = chok ? sp[0] : 0.f, s1 = chok ? sp[1] : 0.f;
                     acc += nvfp4_chunk_bf16(qu[p][c], xa[c], s0, s1);
                 } else {
                     const float sg = chok ? bf16_bits_to_f32(su[p][c]) : 0.f;
@@ -408,6 +438,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     Q4MOE_PHASE(5);
 
     // ---- D: z = w * g * (W_down h) for this wave's down rows, published
+    // (lane i holds w * g of slot i, read per row with readlane)
+    const float wgd_l = wsel[lane < a.K ? lane : 0] * gd_l;
     if (!ctl) {
         float hv[C2][32];
         float hs[C2];
@@ -443,8 +475,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 for (int c = 0; c < C2; ++c) {
                     const bool chok = lane * C2 + c < nchI;
                     if constexpr (FMT == FMT_NVFP4) {
-                        const float s0 = chok ? e4m3fn_to_f32(sd[p][c] & 0xffu) : 0.f;
-                        const float s1 = chok ? e4m3fn_to_f32(sd[p][c] >> 8) : 0.f;
+                        const f32x2 sp = e4m3fn_x2_f32(sd[p][c]);
+                        const float s0 = chok ? sp[0] : 0.f, s1 = chok ? sp[1] : 0.f;
                         zz += nvfp4_chunk_f32(qd[p][c], hv[c], s0, s1);
                     } else {
                         const float sg = chok ? bf16_bits_to_f32(sd[p][c]) : 0.f;
@@ -452,8 +484,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                     }
                 }
                 zz = seg_sum_last<64>(zz);
-                const float g = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, gd_l), slot));
-                if (lane == 63) put_tag(a.z_tag + (size_t)slot * a.H + r, (wsel[slot] * g) * zz, ep);
+                const float wg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgd_l), slot));
+                if (lane == 63) put_tag(a.z_tag + (uint32_t)(slot * a.H + r), wg * zz, ep);
             }
         }
     }

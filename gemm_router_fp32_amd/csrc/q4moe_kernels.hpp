@@ -288,7 +288,8 @@ __global__ __launch_bounds__(256) void k_up(MoeArgs a) {
                 if constexpr (FMT == FMT_NVFP4) {
                     const uint8_t* sc = reinterpret_cast<const uint8_t*>(a.ups) + row * (a.H / 16) + ch * 2;
                     const uint32_t sb = *reinterpret_cast<const uint16_t*>(sc);
-                    acc += nvfp4_chunk_bf16(q, xa[c], e4m3fn_to_f32(sb & 0xffu), e4m3fn_to_f32(sb >> 8));
+                    const f32x2 sp = e4m3fn_x2_f32(sb);
+                    acc += nvfp4_chunk_bf16(q, xa[c], sp[0], sp[1]);
                 } else {
                     const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.ups) + row * (a.H / 64);
                     const float sg = bf16_bits_to_f32(sc[ch >> 1]);
@@ -363,7 +364,8 @@ __global__ __launch_bounds__(256) void k_down(MoeArgs a) {
                     if constexpr (FMT == FMT_NVFP4) {
                         const uint8_t* sc = reinterpret_cast<const uint8_t*>(a.dns) + row * (a.I / 16) + ch * 2;
                         const uint32_t sb = *reinterpret_cast<const uint16_t*>(sc);
-                        z += nvfp4_chunk_f32(q, hv[c], e4m3fn_to_f32(sb & 0xffu), e4m3fn_to_f32(sb >> 8));
+                        const f32x2 sp = e4m3fn_x2_f32(sb);
+                        z += nvfp4_chunk_f32(q, hv[c], sp[0], sp[1]);
                     } else {
                         const uint16_t* sc = reinterpret_cast<const uint16_t*>(a.dns) + row * (a.I / 64);
                         const float sg = bf16_bits_to_f32(sc[ch >> 1]);
