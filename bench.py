@@ -29,7 +29,7 @@ sys.path.insert(0, os.path.join(ROOT, "tests"))
 H, I, E, K, LAYERS, V = 2688, 1856, 128, 6, 23, 131072
 SEED = 20261202
 PEAK_HBM_GBS = 8000.0
-PEAK_BF16_TFLOPS = 2500.0
+PEAK_F16_TFLOPS = 2500.0   # dense fp16/bf16 MFMA
 TRAFFIC_PROFILE = "profiles/traffic_all_kernels_bench.md"
 METRIC = "µs per routed-MoE layer at batch 1 + achieved HBM GB/s (% of MI355X peak)"
 
@@ -209,7 +209,7 @@ def bench_w4a4(torch, g, synth, steps):
     log(f"w4a4 chunk: {ms * 1e3:.1f} us")
     return {"us": round(ms * 1e3, 2), "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
-            "mfma_frac_of_bf16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "mfma_frac_of_fp16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
             "us_spread": spread(per), "bytes": byts, "flop": flops, "tokens": T}
 
 

@@ -228,11 +228,12 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
 // ---------------------------------------------------------------------------
 // Grouped GEMM on MFMA: for expert e and a 128-column output tile,
 // out[m][n] = sum_k A[m][k] * W_e[n][k] over the expert's rows m, with both
-// operands NVFP4 (codes + E4M3 scale per 16 along k) decoded into LDS as bf16.
-// Workgroup: 4 waves; wave w owns output columns 32w..32w+31 and up to four
-// 32-row subtiles (128 rows) of M, one v_mfma_f32_32x32x16_bf16 accumulator
-// each.  K advances 64 per step; the next step's global loads are in flight
-// while the current step's MFMAs run.
+// operands NVFP4 (codes + E4M3 scale per 16 along k), decoded exactly to fp16:
+// A into LDS, W in registers.  Workgroup: 4 waves; wave w owns output columns
+// 32w..32w+31 and up to three 32-row subtiles (96 rows) of M, one
+// v_mfma_f32_32x32x16_f16 accumulator each.  K advances 256 per chunk (128
+// bytes of every weight row); a 3-slot register ring keeps two chunks of
+// weight loads in flight while the current one computes.
 // ---------------------------------------------------------------------------
 enum : int { EPI_UP = 0, EPI_DOWN = 1 };
 // Output columns (rows of W_e) per workgroup (4 waves x 32), A rows per
