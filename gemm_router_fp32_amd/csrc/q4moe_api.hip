@@ -176,8 +176,8 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     // once), a workgroup stages at most kMaxWgUp up rows, and its down rows
     // span at most two slots.  Otherwise the caller uses separate launches.
     const long long RU = (long long)a.K * a.I, RD = (long long)a.K * a.H;
-    const long long nw = (long long)grid * kWaves, nwd = (long long)grid * (kWaves - 1);
-    if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RD + nwd - 1) / nwd > kMaxDown ||
+    const long long nw = (long long)grid * kWaves;
+    if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RD + nw - 1) / nw > kMaxDown ||
         (RU + grid - 1) / grid > kMaxWgUp || (RD + grid - 1) / grid + 1 > a.H)
         return Q4MOE_EUNSUPPORTED;
     hipLaunchKernelGGL((k_decode_fused<FMT, C, C2>), dim3(grid), dim3(64 * kWaves), 0, s, a);

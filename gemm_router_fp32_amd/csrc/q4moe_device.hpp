@@ -8,6 +8,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace q4moe {
@@ -238,6 +239,48 @@ __device__ __forceinline__ float wave_max(float v) {
                                                                       __builtin_bit_cast(int, v), 0x143, 0xC, 0xF,
                                                                       false)));
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Two E4M3FN bytes (bytes 0,1 of v, or 2,3 when HI) -> fp16 pair.  gfx950's
+// fp8 converts use the OCP E4M3FN encoding; every E4M3FN value (NaN and -0
+// included) is exact in fp16, and with scale 1 the conversion is exact.
+template <bool HI>
+__device__ __forceinline__ f16x2 e4m3x2_f16(uint32_t v) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, HI);
+}
+
+// Eight E2M1 codes (one dword) times their block scale, as fp16.  e2m1 *
+// e4m3 has at most six significant bits and lies in [2^-10, 2688]: exact.
+__device__ __forceinline__ f16x8 fp4x8_f16(uint32_t w, f16x2 s) {
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
+    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// Order-preserving int32 image of an fp32 key: for keys that are not NaN,
+// a < b exactly when key_order(a) < key_order(b), and -0 and +0 map alike to
+// 0.  NaN maps to INT_MIN, below every key.
+__device__ __forceinline__ int key_order(float f) {
+    int b = __builtin_bit_cast(int, f);
+    if ((b << 1) == 0) b = 0;
+    return f != f ? INT_MIN : (b >= 0 ? b : b ^ 0x7fffffff);
+}
+
+// Maximum over the 64 lanes of a wave (DPP only), returned to every lane.
+__device__ __forceinline__ int wave_max_i32(int v) {
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x124, 0xF, 0xF, true));  // row_ror:4
+    v = max(v, __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true));  // row_ror:8 (every lane: its row's max)
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x142, 0xA, 0xF, false));  // rows 1, 3 take rows 0, 2 in
+    v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x143, 0xC, 0xF, false));  // row 3 takes lane 31 in
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
 }  // namespace q4moe

@@ -10,17 +10,18 @@
 //   S  select:  every workgroup polls the E scores, forms the keys
 //               score + bias, and each wave runs the exact fp32 top-k itself
 //               (wave max, then the lowest index holding it).
-//   U  up:      the K x I (slot, row) units are split evenly over all waves;
-//               each wave first issues the loads of its up rows AND (waves
-//               0..6) of its down rows, which do not depend on h, then
-//               computes h = relu(W_up x)^2 for its rows into LDS.
-//   P  publish: wave 7 of each workgroup, which holds no down rows and so has
-//               no loads in flight, publishes the workgroup's h rows, then
-//               polls the h of the slots the workgroup's down rows use into
-//               LDS.  (A wave cannot wait for a polled value without also
-//               waiting for every load it has in flight.)
-//   D  down:    waves 0..6 finish z = w * g * (W_down h) from the weights
-//               already in registers and publish z.
+//   U  up:      the K x I (slot, row) up units and the K x H down units are
+//               each split evenly over all waves; each wave first issues the
+//               loads of its up rows AND of its down rows, which do not
+//               depend on h, then computes h = relu(W_up x)^2 for its rows
+//               into LDS.
+//   P  publish: the workgroup publishes its h rows (one per thread), then
+//               all its threads poll the h of the slots its down rows use
+//               into LDS.  A poll result counts only after every load the
+//               wave issued before it, so the first poll also waits for the
+//               down weights; those arrive well before the last h does.
+//   D  down:    every wave finishes z = w * g * (W_down h) from the weights
+//               already in registers and publishes z.
 //   C  combine: one workgroup per 64-row block polls that block's z of every
 //               slot and sums them in slot order (deterministic) into y.
 //
@@ -50,8 +51,8 @@ namespace q4moe {
 
 constexpr int kReplicas = 8;
 constexpr int kWaves = 8;    // waves per workgroup (one workgroup per CU)
-constexpr int kMaxUp = 4;    // up passes (two rows each) per wave, loads in flight together
-constexpr int kMaxDown = 10; // down rows per down wave, loads in flight together
+constexpr int kMaxUp = 3;    // up passes (two rows each) per wave, loads in flight together
+constexpr int kMaxDown = 8;  // down rows per wave, loads in flight together
 constexpr int kMaxWgUp = 512;        // up rows per workgroup (K * I / grid)
 constexpr int kRowBlock = 64;
 constexpr uint32_t kPollLimit = 200000;  // polls (each at least one memory round trip) before giving up
@@ -101,50 +102,59 @@ __device__ __forceinline__ float tag_value(unsigned long long t) { return __uint
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
 // Exact fp32 top-k of E <= 256 keys by one wave: expert e sits in lane
-// e % 64, register e / 64.  Each round takes the wave maximum and then the
-// lowest expert index holding it (ballot + find-first-set), so equal keys
-// go to the lower index exactly as the definition says.  The ids and the
-// renormalised gates go to this wave's LDS slots (read back per lane).
+// e % 64, register e / 64, as the order-preserving integer image of its key
+// (NaN keys and padding at INT_MIN, never chosen).  Each round takes the wave
+// maximum and then the lowest expert index holding it (first non-empty
+// ballot, find-first-set), so equal keys go to the lower index exactly as the
+// definition says; the rounds keep no branches and read no scores.  Lane i
+// then takes pick i, reads its score and divides it by the sum of the K picked
+// scores (summed in pick order), into this wave's LDS slots.
 __device__ __forceinline__ void wave_topk(const FusedArgs& a, const float* s_keys, const float* s_scores,
                                           int* s_ids, float* s_w) {
     const int lane = threadIdx.x & 63;
-    float key[4], sc[4];
+    int key[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int e = lane + 64 * q;
-        const bool live = e < a.E;
-        key[q] = live ? s_keys[e] : -__builtin_inff();
-        sc[q] = live ? s_scores[e] : 0.f;
+        const float kv = s_keys[e];  // e < 256: inside the array; past E masked
+        key[q] = e < a.E ? key_order(kv) : INT_MIN;
     }
-    float ssum = 0.f;
-    for (int i = 0; i < a.K; ++i) {
-        const float m = wave_max(fmaxf(fmaxf(key[0], key[1]), fmaxf(key[2], key[3])));
-        int best = 0x7fffffff;
-        float bs = 0.f;
+    int sel[8];
+    bool lost = false;  // fewer than K keys that are not NaN
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const unsigned long long hit = __ballot(key[q] == m);
-            if (hit && best == 0x7fffffff) {
-                const int l = (int)__builtin_ctzll(hit);
-                best = l + 64 * q;
-                bs = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sc[q]), l));
+    for (int i = 0; i < 8; ++i) {
+        sel[i] = 0;
+        if (i < a.K) {
+            const int m = wave_max_i32(max(max(key[0], key[1]), max(key[2], key[3])));
+            const unsigned long long h0 = __ballot(key[0] == m), h1 = __ballot(key[1] == m),
+                                     h2 = __ballot(key[2] == m), h3 = __ballot(key[3] == m);
+            int best = h0 ? (int)__builtin_ctzll(h0)
+                          : h1 ? 64 + (int)__builtin_ctzll(h1)
+                               : h2 ? 128 + (int)__builtin_ctzll(h2) : 192 + (int)__builtin_ctzll(h3);
+            if (m == INT_MIN) {  // only NaN keys left: keep every read inside the bank
+                lost = true;
+                best = 0;
             }
-        }
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (lane + 64 * q == best) key[q] = -__builtin_inff();
-        if (best >= a.E) {  // no finite key left (NaN keys): keep every read inside the bank
-            best = 0;
-            if (lane == 0) atomicOr(a.ctrl + CTRL_FLAGS, 2u);
+            for (int q = 0; q < 4; ++q)
+                if (lane + 64 * q == best) key[q] = INT_MIN;
+            sel[i] = best;
         }
-        if (lane == 0) {
-            s_ids[i] = best;
-            s_w[i] = bs;
-        }
-        ssum += bs;
     }
-    __builtin_amdgcn_wave_barrier();
-    if (lane < a.K) s_w[lane] = s_w[lane] / ssum;
+    if (lost && lane == 0) atomicOr(a.ctrl + CTRL_FLAGS, 2u);
+    int my = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) my = lane == i ? sel[i] : my;
+    const float sc_my = s_scores[my];
+    const float msc = lane < a.K ? sc_my : 0.f;
+    float ssum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        if (i < a.K) ssum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, msc), i));
+    if (lane < a.K) {
+        s_ids[lane] = my;
+        s_w[lane] = msc / ssum;
+    }
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -161,16 +171,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __shared__ float s_keys[256], s_scores[256];
     __shared__ int s_ids_all[kWaves][8];
     __shared__ float s_w_all[kWaves][8];
-    __shared__ float s_h[2][4096];      // h of the (at most two) slots this workgroup's down rows use
+    __shared__ float s_h[2 * 4096];     // h of the (at most two, adjacent) slots this workgroup's down rows use
     __shared__ float s_hrow[kMaxWgUp];  // this workgroup's up results, before they are published
-    __shared__ uint32_t s_ep;
+    __shared__ uint4 s_x[512];          // x (bf16, H <= 4096), read once per workgroup
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int seg = lane >> 5, li = lane & 31;
     const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
-    // down rows go to waves 0..kWaves-2; wave kWaves-1 is the control wave
-    constexpr int kDownWaves = kWaves - 1;
-    const bool ctl = wave == kWaves - 1;
-    const int NWD = gridDim.x * kDownWaves, gwd = blockIdx.x * kDownWaves + (ctl ? 0 : wave);
     const int nchH = a.H / 32, nchI = a.I / 32;
     // Up rows: lane li of a 32-lane segment takes chunks c * lpr + li
     // (c < C), so each load instruction reads one contiguous run of the row.
@@ -179,61 +185,44 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     const int rep = blockIdx.x % kReplicas;
 
     Q4MOE_PHASE(0);
-    if (threadIdx.x == 0)
-        s_ep = __hip_atomic_load(a.ctrl + FW_EPOCH + rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-
-    // activations of this lane's up chunks (independent of the routing)
-    uint32_t xa[C][16];
-    float xs[C];
+    // This call's epoch (the last completed call's + 1).  Every wave loads it
+    // and first uses it after the router, so nothing waits for it here.
+    const uint32_t ep =
+        __hip_atomic_load(a.ctrl + FW_EPOCH + rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    // Thread 128 + e polls the score of expert e: waves 2 and up store
+    // nothing in the router phase, so their poll results do not wait for
+    // the score stores to complete.
+    const int pe = (int)threadIdx.x - 128;
+    const bool poller = pe >= 0 && pe < a.E;
+    const float bias = a.bias[poller ? pe : 0];
+    // Router row of workgroup e < E (its waves split it); every workgroup
+    // issues these loads (past E it reads row 0 and ignores it), so that all
+    // of the kernel's first loads leave together, before anything waits.
+    const int nf4 = a.H / 4;
+    const int rlo = wave * nf4 / kWaves, rhi = (wave + 1) * nf4 / kWaves;
+    const float4* wr = reinterpret_cast<const float4*>(a.wg + (size_t)((int)blockIdx.x < a.E ? blockIdx.x : 0) * a.H);
+    // a wave's share is at most 128 pieces (H <= 4096): two per lane
+    // (clamped; the extra one is masked)
+    float4 wv[2];
+    uint2 xb[2];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int ch = min(c * lpr + li, nchH - 1);
-        uint32_t nat[16];
-        load_x_chunk(a.x, ch, nat);
-        if constexpr (FMT == FMT_NVFP4) {
-#pragma unroll
-            for (int j = 0; j < 16; ++j) xa[c][j] = nat[j];
-            xs[c] = 0.f;
-        } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) int4_pair_order(nat + 4 * d, xa[c] + 4 * d);
-            xs[c] = pair_sum_bf16(nat);
-        }
+    for (int i = 0; i < 2; ++i) {
+        const int j = min(rlo + lane + 64 * i, rhi - 1);
+        wv[i] = wr[j];
+        xb[i] = *reinterpret_cast<const uint2*>(a.x + 4 * j);
     }
-    // unit bookkeeping (routing-independent: done while the x loads fly)
-    const int RU = a.K * a.I, RD = a.K * a.H;
-    const int u0 = share_lo(RU, gw, NW), u1 = share_lo(RU, gw + 1, NW);
-    const int d0 = ctl ? 0 : share_lo(RD, gwd, NWD), d1 = ctl ? 0 : share_lo(RD, gwd + 1, NWD);
-    const int wu0 = share_lo(RU, blockIdx.x * kWaves, NW), wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
-    const int wd0 = share_lo(RD, blockIdx.x * kDownWaves, NWD),
-              wd1 = share_lo(RD, (blockIdx.x + 1) * kDownWaves, NWD);
-    // A wave's units span at most two slots: slot(u) = us0 + (u >= ubnd).
-    const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
-    const int ds0 = (d1 > d0 ? d0 : 0) / a.H, dbnd = (ds0 + 1) * a.H;
-    const int n_up_pass = (u1 - u0 + 1) / 2, n_down = d1 - d0;  // <= kMaxUp, <= kMaxDown (checked on the host)
-    __syncthreads();
-    const uint32_t ep = s_ep;
+
+    // x into LDS once per workgroup (the up GEMV reads it from there)
+    if ((int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+    compiler_fence();  // keep every load above in the entry block
 
     // ---- R: workgroup e computes router logit e; its waves split the row
     if ((int)blockIdx.x < a.E) {
         const int e = blockIdx.x;
-        const int nf4 = a.H / 4;
-        const int lo = wave * nf4 / kWaves, hi = (wave + 1) * nf4 / kWaves;
-        const float4* wr = reinterpret_cast<const float4*>(a.wg + (size_t)e * a.H);
-        // a wave's share is at most 128 pieces (H <= 4096): two per lane, both
-        // loads issued before either is used (clamped; the extra one is masked)
-        float4 wv[2];
-        uint2 xb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int j = min(lo + lane + 64 * i, hi - 1);
-            wv[i] = wr[j];
-            xb[i] = *reinterpret_cast<const uint2*>(a.x + 4 * j);
-        }
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            if (lo + lane + 64 * i < hi) {
+            if (rlo + lane + 64 * i < rhi) {
                 acc = __builtin_fmaf(wv[i].x, bf16_bits_to_f32(xb[i].x & 0xffffu), acc);
                 acc = __builtin_fmaf(wv[i].y, bf16_bits_to_f32(xb[i].x >> 16), acc);
                 acc = __builtin_fmaf(wv[i].z, bf16_bits_to_f32(xb[i].y & 0xffffu), acc);
@@ -253,24 +242,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
     Q4MOE_PHASE(1);
 
+    // unit bookkeeping (routing-independent: done while the scores travel)
+    const int RU = a.K * a.I, RD = a.K * a.H;
+    const int u0 = share_lo(RU, gw, NW), u1 = share_lo(RU, gw + 1, NW);
+    const int d0 = share_lo(RD, gw, NW), d1 = share_lo(RD, gw + 1, NW);
+    const int wu0 = share_lo(RU, blockIdx.x * kWaves, NW), wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
+    const int wd0 = share_lo(RD, blockIdx.x * kWaves, NW), wd1 = share_lo(RD, (blockIdx.x + 1) * kWaves, NW);
+    // A wave's units span at most two slots: slot(u) = us0 + (u >= ubnd).
+    const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
+    const int ds0 = (d1 > d0 ? d0 : 0) / a.H, dbnd = (ds0 + 1) * a.H;
+    const int n_up_pass = (u1 - u0 + 1) / 2, n_down = d1 - d0;  // <= kMaxUp, <= kMaxDown (checked on the host)
+
     // ---- S: poll the scores (one copy per workgroup), form the keys
     {
-        const int t = threadIdx.x;
-        const float b = t < a.E ? a.bias[t] : 0.f;
-        bool have = t >= a.E;
+        bool have = !poller;
         for (uint32_t polls = 0;; ++polls) {
             if (!have) {
-                const unsigned long long v = get_tag(a.sc_tag + rep * a.E + t);
+                const unsigned long long v = get_tag(a.sc_tag + rep * a.E + pe);
                 if (tag_is(v, ep)) {
                     const float sc = tag_value(v);
-                    s_scores[t] = sc;
-                    s_keys[t] = sc + b;
+                    s_scores[pe] = sc;
+                    s_keys[pe] = sc + bias;
                     have = true;
                 }
             }
             if (__syncthreads_and(have)) break;
             if (polls > kPollLimit) {
-                if (t == 0) atomicOr(flags, 1u);
+                if (threadIdx.x == 0) atomicOr(flags, 1u);
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
@@ -338,7 +336,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     compiler_fence();
     uint4 qd[kMaxDown][C2];
     uint32_t sd[kMaxDown][C2];
-    if (!ctl) {
+    {
         uint32_t dco[C2], dso[C2];
 #pragma unroll
         for (int c = 0; c < C2; ++c) {
@@ -360,6 +358,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     compiler_fence();
+
+    // activations of this lane's up chunks, from LDS
+    uint32_t xa[C][16];
+    float xs[C];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int ch = min(c * lpr + li, nchH - 1);
+        uint32_t nat[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint4 v = s_x[4 * ch + k];
+            nat[4 * k + 0] = v.x;
+            nat[4 * k + 1] = v.y;
+            nat[4 * k + 2] = v.z;
+            nat[4 * k + 3] = v.w;
+        }
+        if constexpr (FMT == FMT_NVFP4) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) xa[c][j] = nat[j];
+            xs[c] = 0.f;
+        } else {
+#pragma unroll
+            for (int d = 0; d < 4; ++d) int4_pair_order(nat + 4 * d, xa[c] + 4 * d);
+            xs[c] = pair_sum_bf16(nat);
+        }
+    }
 
     // ---- U: h = relu(W_up x)^2 for this wave's rows, into LDS
 #pragma unroll
@@ -392,11 +416,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __syncthreads();
     Q4MOE_PHASE(4);
 
-    // ---- P: the control wave publishes the workgroup's h rows, then polls
-    // the h of the slots the workgroup's down rows use into LDS
-    const int sl0 = wd1 > wd0 ? wd0 / a.H : 0, sl1 = wd1 > wd0 ? (wd1 - 1) / a.H : -1;  // at most two slots
-    if (ctl) {
-        for (int j = lane; j < wu1 - wu0; j += 64) {
+    // ---- P: publish this workgroup's h rows (thread j takes row wu0 + j),
+    // then poll the h of the slots the workgroup's down rows use into LDS
+    {
+        const int j = threadIdx.x;
+        if (j < wu1 - wu0) {
             const int u = wu0 + j;
             const int slot = u / a.I, r = u - slot * a.I;
             const float v = s_hrow[j];
@@ -404,34 +428,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.h_tag + ((size_t)rp * a.K + slot) * a.I + r, v, ep);
             a.h[(size_t)slot * a.I + r] = v;
         }
-        const int nm = (a.I + 63) / 64;  // elements per lane and slot (<= 64)
-        for (int s2 = sl0; s2 <= sl1; ++s2) {
-            const unsigned long long* src = a.h_tag + ((size_t)rep * a.K + s2) * a.I;
-            float* dst = s_h[s2 - sl0];
-            for (int m0 = 0; m0 < nm; m0 += 32) {
-                unsigned pend = 0;
+    }
+    // the workgroup's down rows span slots sl0 .. sl1 (at most two, adjacent
+    // in the [K][I] layout, so their h is one run of nh values)
+    const int sl0 = wd1 > wd0 ? wd0 / a.H : 0, sl1 = wd1 > wd0 ? (wd1 - 1) / a.H : -1;
+    {
+        const int nh = (sl1 - sl0 + 1) * a.I;  // <= 2 * 4096 = 16 per thread
+        const unsigned long long* src = a.h_tag + ((size_t)rep * a.K + sl0) * a.I;
+        uint32_t pend = 0;
 #pragma unroll
-                for (int k = 0; k < 32; ++k)
-                    if (m0 + k < nm && lane + 64 * (m0 + k) < a.I) pend |= 1u << k;
-                for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
-                    unsigned long long v[32];
+        for (int m = 0; m < 16; ++m)
+            if ((int)threadIdx.x + 512 * m < nh) pend |= 1u << m;
+        for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
+            unsigned long long v[16];
 #pragma unroll
-                    for (int k = 0; k < 32; ++k)
-                        v[k] = (pend >> k) & 1u ? get_tag(src + lane + 64 * (m0 + k)) : 0ull;
+            for (int m = 0; m < 16; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + threadIdx.x + 512 * m) : 0ull;
 #pragma unroll
-                    for (int k = 0; k < 32; ++k) {
-                        if (((pend >> k) & 1u) && tag_is(v[k], ep)) {
-                            dst[lane + 64 * (m0 + k)] = tag_value(v[k]);
-                            pend &= ~(1u << k);
-                        }
-                    }
-                    if (polls > kPollLimit) {
-                        if (lane == 0) atomicOr(flags, 1u);
-                        break;
-                    }
-                    if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
+            for (int m = 0; m < 16; ++m) {
+                if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
+                    s_h[threadIdx.x + 512 * m] = tag_value(v[m]);
+                    pend &= ~(1u << m);
                 }
             }
+            if (polls > kPollLimit) {
+                if (lane == 0) atomicOr(flags, 1u);
+                break;
+            }
+            if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
         }
     }
     __syncthreads();
@@ -440,7 +463,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // ---- D: z = w * g * (W_down h) for this wave's down rows, published
     // (lane i holds w * g of slot i, read per row with readlane)
     const float wgd_l = wsel[lane < a.K ? lane : 0] * gd_l;
-    if (!ctl) {
+    {
         float hv[C2][32];
         float hs[C2];
         int h_slot = -1;
@@ -453,7 +476,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
                     for (int c = 0; c < C2; ++c) {
                         const int ch = min(lane * C2 + c, nchI - 1);
-                        const float4* hp = reinterpret_cast<const float4*>(&s_h[slot - sl0][ch * 32]);
+                        const float4* hp = reinterpret_cast<const float4*>(&s_h[(slot - sl0) * a.I + ch * 32]);
                         hs[c] = 0.f;
 #pragma unroll
                         for (int k = 0; k < 8; ++k) {
@@ -502,14 +525,14 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         for (int s2 = 0; s2 < a.K; ++s2) pend |= 1u << s2;
         if (ok) pend = 0;
         for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
+            unsigned long long v[8];  // every load of a poll leaves before any is waited for
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) v[s2] = (pend >> s2) & 1u ? get_tag(a.z_tag + (size_t)s2 * a.H + r) : 0ull;
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
-                if ((pend >> s2) & 1u) {
-                    const unsigned long long v = get_tag(a.z_tag + (size_t)s2 * a.H + r);
-                    if (tag_is(v, ep)) {
-                        part[s2] = tag_value(v);
-                        pend &= ~(1u << s2);
-                    }
+                if (((pend >> s2) & 1u) && tag_is(v[s2], ep)) {
+                    part[s2] = tag_value(v[s2]);
+                    pend &= ~(1u << s2);
                 }
             }
             if (polls > kPollLimit) {

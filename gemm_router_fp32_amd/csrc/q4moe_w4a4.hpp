@@ -256,27 +256,6 @@ struct GemmArgs {
     float* out;                // [rows][N] fp32, dispatch order
 };
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-// Two E4M3FN bytes (bytes 0,1 of v, or 2,3 when HI) -> fp16 pair.  gfx950's
-// fp8 converts use the OCP E4M3FN encoding; every E4M3FN value (NaN and -0
-// included) is exact in fp16, and with scale 1 the conversion is exact.
-template <bool HI>
-__device__ __forceinline__ f16x2 e4m3x2_f16(uint32_t v) {
-    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v, 1.0f, HI);
-}
-
-// Eight E2M1 codes (one dword) times their block scale, as fp16.  e2m1 *
-// e4m3 has at most six significant bits and lies in [2^-10, 2688]: exact.
-__device__ __forceinline__ f16x8 fp4x8_f16(uint32_t w, f16x2 s) {
-    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s;
-    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s;
-    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s;
-    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s;
-    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
-}
-
 // Grouped GEMM over the experts' dispatch rows: out[row][n] = epi(sum_k
 // A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_32x32x16_f16) with both
 // operands decoded exactly from NVFP4.  A workgroup takes 128 columns of one
