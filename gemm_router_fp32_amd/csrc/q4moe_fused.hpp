@@ -11,17 +11,19 @@
 //               score + bias, and each wave runs the exact fp32 top-k itself
 //               (wave max, then the lowest index holding it).
 //   U  up:      the K x I (slot, row) up units and the K x H down units are
-//               each split evenly over all waves; each wave first issues the
-//               loads of its up rows AND of its down rows, which do not
-//               depend on h, then computes h = relu(W_up x)^2 for its rows
-//               into LDS.
+//               each split evenly over all waves; each wave issues the loads
+//               of its up rows, computes h = relu(W_up x)^2 for them into
+//               LDS, and then issues the loads of its down rows (which do
+//               not depend on h), so that the up rows every workgroup waits
+//               for come first and the down weights stream during the h
+//               hand-off.
 //   P  publish: the workgroup publishes its h rows (one per thread), then
 //               all its threads poll the h of the slots its down rows use
-//               into LDS.  A poll result counts only after every load the
+//               into LDS.  (A poll result counts only after every load the
 //               wave issued before it, so the first poll also waits for the
-//               down weights; those arrive well before the last h does.
-//   D  down:    every wave finishes z = w * g * (W_down h) from the weights
-//               already in registers and publishes z.
+//               down weights.)
+//   D  down:    every wave computes z = w * g * (W_down h) from the weights
+//               in registers and publishes z.
 //   C  combine: one workgroup per 64-row block polls that block's z of every
 //               slot and sums them in slot order (deterministic) into y.
 //
@@ -253,30 +255,42 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     const int ds0 = (d1 > d0 ? d0 : 0) / a.H, dbnd = (ds0 + 1) * a.H;
     const int n_up_pass = (u1 - u0 + 1) / 2, n_down = d1 - d0;  // <= kMaxUp, <= kMaxDown (checked on the host)
 
-    // ---- S: poll the scores (one copy per workgroup), form the keys
-    {
+    // ---- S: poll the scores (one copy per workgroup), form the keys.  The
+    // polling waves keep two polls in flight (every lane loads every time, so
+    // each check waits for the older poll only) and so see a score about
+    // half a memory round trip sooner than with one poll at a time.
+    if (wave >= 2 && wave < 2 + (a.E + 63) / 64) {
+        const unsigned long long* src = a.sc_tag + rep * a.E + (poller ? pe : 0);
         bool have = !poller;
-        for (uint32_t polls = 0;; ++polls) {
-            if (!have) {
-                const unsigned long long v = get_tag(a.sc_tag + rep * a.E + pe);
-                if (tag_is(v, ep)) {
-                    const float sc = tag_value(v);
-                    s_scores[pe] = sc;
-                    s_keys[pe] = sc + bias;
-                    have = true;
-                }
+        auto take = [&](unsigned long long v) {
+            if (!have && tag_is(v, ep)) {
+                const float sc = tag_value(v);
+                s_scores[pe] = sc;
+                s_keys[pe] = sc + bias;
+                have = true;
             }
-            if (__syncthreads_and(have)) break;
+        };
+        // (one exit per round: a second exit makes the compiler copy the
+        // poll registers, which waits for the newer poll as well)
+        unsigned long long va = get_tag(src);
+        unsigned long long vb = get_tag(src);
+        for (uint32_t polls = 0;; ++polls) {
+            take(va);
+            va = get_tag(src);
+            take(vb);
+            if (!__any(!have)) break;
             if (polls > kPollLimit) {
-                if (threadIdx.x == 0) atomicOr(flags, 1u);
+                if (lane == 0) atomicOr(flags, 1u);
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
+            vb = get_tag(src);
         }
     }
+    __syncthreads();
     Q4MOE_PHASE(2);
     int* ids = s_ids_all[wave];
     float* wsel = s_w_all[wave];
+
     wave_topk(a, s_keys, s_scores, ids, wsel);
     if (gw == 0 && lane < a.K) {
         const int id = ids[lane];
@@ -288,28 +302,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
     Q4MOE_PHASE(3);
 
-    // ---- U: issue the loads of this wave's up rows, then its down rows
-    // per-tensor scales of the selected experts (lane i holds slot i's)
-    float gu_l = 1.0f, gd_l = 1.0f;
-    if constexpr (FMT == FMT_NVFP4) {
-        const int sl = lane < a.K ? lane : 0;
-        gu_l = a.upg[ids[sl]];
-        gd_l = a.dng[ids[sl]];
-    }
-    compiler_fence();
-
-    // Every lane issues every load (an invalid row or chunk reads a valid
-    // address and is zeroed through its scale at compute time), so the loads
-    // stay in issue order and each use waits only for its own data.  Offsets
-    // are 32-bit from the uniform bases (the argument limits keep a bank
-    // under 2^31 bytes), and each row index (< 2^20) times its row bytes
-    // (<= 2048) is a full-rate 24-bit multiply: the row of unit u of slot s
-    // is u + ids[s] * rows - s * rows, a select between the wave's two slots.
+    // ---- U: issue the loads of this wave's up rows.  Every lane issues every
+    // load (an invalid row or chunk reads a valid address and is zeroed
+    // through its scale at compute time), so the loads stay in issue order
+    // and each use waits only for its own data.  Offsets are 32-bit from the
+    // uniform bases (the argument limits keep a bank under 2^31 bytes), and
+    // each row index (< 2^20) times its row bytes (<= 2048) is a full-rate
+    // 24-bit multiply: the row of unit u of slot s is u + ids[s] * rows -
+    // s * rows, a select between the wave's two slots.
     const uint8_t* ups8 = reinterpret_cast<const uint8_t*>(a.ups);
     const uint8_t* dns8 = reinterpret_cast<const uint8_t*>(a.dns);
     const int us1 = min(us0 + 1, a.K - 1), ds1 = min(ds0 + 1, a.K - 1);
-    const int uoff0 = ids[us0] * a.I - us0 * a.I, uoff1 = ids[us1] * a.I - (us0 + 1) * a.I;
-    const int doff0 = ids[ds0] * a.H - ds0 * a.H, doff1 = ids[ds1] * a.H - (ds0 + 1) * a.H;
     const uint32_t urb = a.H / 2, usb = (FMT == FMT_NVFP4) ? a.H / 16 : a.H / 32;  // bytes per up row
     const uint32_t drb = a.I / 2, dsb = (FMT == FMT_NVFP4) ? a.I / 16 : a.I / 32;  // bytes per down row
     uint32_t uco[C], uso[C];  // this lane's chunk offsets within an up row
@@ -321,6 +324,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
     uint4 qu[kMaxUp][C];
     uint32_t su[kMaxUp][C];
+    // per-tensor scales of the wave's two up slots
+    const int idu0 = ids[us0], idu1 = ids[us1];
+    float gu0 = 1.0f, gu1 = 1.0f;
+    if constexpr (FMT == FMT_NVFP4) {
+        gu0 = a.upg[idu0];
+        gu1 = a.upg[idu1];
+    }
+    const int uoff0 = idu0 * a.I - us0 * a.I, uoff1 = idu1 * a.I - (us0 + 1) * a.I;
+    compiler_fence();
 #pragma unroll
     for (int p = 0; p < kMaxUp; ++p) {
         int u = u0 + 2 * p + seg;
@@ -331,30 +343,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         for (int c = 0; c < C; ++c) {
             qu[p][c] = ldg16_stream(a.upc + (rc + uco[c]));
             su[p][c] = *reinterpret_cast<const uint16_t*>(ups8 + (rs + uso[c]));
-        }
-    }
-    compiler_fence();
-    uint4 qd[kMaxDown][C2];
-    uint32_t sd[kMaxDown][C2];
-    {
-        uint32_t dco[C2], dso[C2];
-#pragma unroll
-        for (int c = 0; c < C2; ++c) {
-            const int ch = min(lane * C2 + c, nchI - 1);
-            dco[c] = ch * 16;
-            dso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
-        }
-#pragma unroll
-        for (int p = 0; p < kMaxDown; ++p) {
-            int d = d0 + p;
-            if (d >= d1) d = d1 > d0 ? d0 : 0;
-            const uint32_t row = (uint32_t)(d + (d >= dbnd ? doff1 : doff0));
-            const uint32_t rc = __umul24(row, drb), rs = __umul24(row, dsb);
-#pragma unroll
-            for (int c = 0; c < C2; ++c) {
-                qd[p][c] = ldg16_stream(a.dnc + (rc + dco[c]));
-                sd[p][c] = *reinterpret_cast<const uint16_t*>(dns8 + (rs + dso[c]));
-            }
         }
     }
     compiler_fence();
@@ -406,13 +394,45 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 }
             }
             acc = seg_sum_last<32>(acc);
-            const float g = __shfl(gu_l, slot, 64);
+            const float g = slot == us0 ? gu0 : gu1;
             if (li == 31 && ok) {
                 const float rl = fmaxf(acc * g, 0.f);
                 s_hrow[u - wu0] = rl * rl;
             }
         }
     }
+    // Then the loads of this wave's down rows: issued only now, so that the
+    // up rows (which every workgroup needs first, for h) have the memory
+    // system to themselves, and the down weights stream during the h
+    // hand-off instead.  (Lane i takes the per-tensor down scale of slot i.)
+    compiler_fence();
+    float gd_l = 1.0f;
+    if constexpr (FMT == FMT_NVFP4) gd_l = a.dng[ids[lane < a.K ? lane : 0]];
+    const int doff0 = ids[ds0] * a.H - ds0 * a.H, doff1 = ids[ds1] * a.H - (ds0 + 1) * a.H;
+    uint4 qd[kMaxDown][C2];
+    uint32_t sd[kMaxDown][C2];
+    {
+        uint32_t dco[C2], dso[C2];
+#pragma unroll
+        for (int c = 0; c < C2; ++c) {
+            const int ch = min(lane * C2 + c, nchI - 1);
+            dco[c] = ch * 16;
+            dso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
+        }
+#pragma unroll
+        for (int p = 0; p < kMaxDown; ++p) {
+            int d = d0 + p;
+            if (d >= d1) d = d1 > d0 ? d0 : 0;
+            const uint32_t row = (uint32_t)(d + (d >= dbnd ? doff1 : doff0));
+            const uint32_t rc = __umul24(row, drb), rs = __umul24(row, dsb);
+#pragma unroll
+            for (int c = 0; c < C2; ++c) {
+                qd[p][c] = ldg16_stream(a.dnc + (rc + dco[c]));
+                sd[p][c] = *reinterpret_cast<const uint16_t*>(dns8 + (rs + dso[c]));
+            }
+        }
+    }
+    compiler_fence();
     __syncthreads();
     Q4MOE_PHASE(4);
 
@@ -519,15 +539,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     for (int b = wave; b < nb; b += kWaves) {
         if ((int)((long long)b * gridDim.x / nb) != (int)blockIdx.x) continue;
         const int r = b * kRowBlock + lane;
-        bool ok = r >= a.H;
         float part[8];
         uint32_t pend = 0;
         for (int s2 = 0; s2 < a.K; ++s2) pend |= 1u << s2;
-        if (ok) pend = 0;
-        for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
-            unsigned long long v[8];  // every load of a poll leaves before any is waited for
+        if (r >= a.H) pend = 0;
+        // every load of a poll leaves before any is waited for (rows and
+        // slots clamped into the array, so the load count is fixed)
+        const unsigned long long* zr = a.z_tag + min(r, a.H - 1);
+        for (uint32_t polls = 0;; ++polls) {
+            unsigned long long v[8];
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) v[s2] = (pend >> s2) & 1u ? get_tag(a.z_tag + (size_t)s2 * a.H + r) : 0ull;
+            for (int s2 = 0; s2 < 8; ++s2) v[s2] = get_tag(zr + (size_t)min(s2, a.K - 1) * a.H);
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
                 if (((pend >> s2) & 1u) && tag_is(v[s2], ep)) {
@@ -535,11 +557,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                     pend &= ~(1u << s2);
                 }
             }
+            if (!__any(pend != 0u)) break;
             if (polls > kPollLimit) {
                 if (lane == 0) atomicOr(flags, 1u);
                 break;
             }
-            if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
+            __builtin_amdgcn_s_sleep(1);
         }
         if (r < a.H) {
             float yv = 0.f;
