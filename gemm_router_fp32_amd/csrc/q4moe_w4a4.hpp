@@ -306,6 +306,12 @@ __device__ __forceinline__ void gemm_load_b(const GemmArgs& a, const GemmCtx& x,
     b.s1 = *reinterpret_cast<const uint32_t*>(a.wsc + (valid > 2 ? sb + 4 : s_last));
 }
 
+// A tile LDS column (fp16 elements) of 16-byte group g of a row: groups are
+// XOR-swizzled so that the 8 threads staging one row (group 4 ap + i for
+// piece ap, store i) write 8 different bank groups; the MFMA fragment reads
+// (one group per lane, 32 rows apart by the row pitch) stay conflict-free.
+__device__ __forceinline__ int a_col(int g) { return 8 * (g ^ ((g >> 3) & 3)); }
+
 // One M-tile (rows m0 .. m0 + mv - 1 of expert e, MS = ceil(mv / 32)
 // subtiles) against the workgroup's 128 columns.
 template <int EPI, int MS>
@@ -362,11 +368,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             for (int q = 0; q < MS; ++q) {
                 const f16x2 sp = e4m3x2_f16<false>(a_ok ? sa[q] : 0u);
                 const f16x2 s_lo = {sp.x, sp.x}, s_hi = {sp.y, sp.y};
-                f16x8* dst = reinterpret_cast<f16x8*>(&As[x.ar + 32 * q][32 * x.ap]);
-                dst[0] = fp4x8_f16(qa[q].x, s_lo);
-                dst[1] = fp4x8_f16(qa[q].y, s_lo);
-                dst[2] = fp4x8_f16(qa[q].z, s_hi);
-                dst[3] = fp4x8_f16(qa[q].w, s_hi);
+                _Float16* dst = &As[x.ar + 32 * q][0];
+                *reinterpret_cast<f16x8*>(dst + a_col(4 * x.ap + 0)) = fp4x8_f16(qa[q].x, s_lo);
+                *reinterpret_cast<f16x8*>(dst + a_col(4 * x.ap + 1)) = fp4x8_f16(qa[q].y, s_lo);
+                *reinterpret_cast<f16x8*>(dst + a_col(4 * x.ap + 2)) = fp4x8_f16(qa[q].z, s_hi);
+                *reinterpret_cast<f16x8*>(dst + a_col(4 * x.ap + 3)) = fp4x8_f16(qa[q].w, s_hi);
             }
             __syncthreads();
             // next loads: A of chunk c+1, B of chunk c+2 into the free slot
@@ -386,17 +392,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             const uint32_t w[16] = {bc.q[0].x, bc.q[0].y, bc.q[0].z, bc.q[0].w, bc.q[1].x, bc.q[1].y,
                                     bc.q[1].z, bc.q[1].w, bc.q[2].x, bc.q[2].y, bc.q[2].z, bc.q[2].w,
                                     bc.q[3].x, bc.q[3].y, bc.q[3].z, bc.q[3].w};
-            // A fragments are read one step ahead of their MFMAs
-            const _Float16* arow = &As[lane & 31][128 * x.hk];
+            // A fragments are read one step ahead of their MFMAs (step j reads
+            // group 16 hk + j of the lane's row)
+            const _Float16* arow = &As[lane & 31][0];
             f16x8 af[2][MS];
 #pragma unroll
-            for (int i = 0; i < MS; ++i) af[0][i] = *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch);
+            for (int i = 0; i < MS; ++i)
+                af[0][i] = *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch + a_col(16 * x.hk));
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 if (j + 1 < 16) {
 #pragma unroll
                     for (int i = 0; i < MS; ++i)
-                        af[(j + 1) & 1][i] = *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch + 8 * (j + 1));
+                        af[(j + 1) & 1][i] =
+                            *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch + a_col(16 * x.hk + j + 1));
                 }
                 // dword j holds k 8j..8j+7 of the lane's half: block j / 2, piece j / 4
                 const f16x2 sp = sc[j / 4];
