@@ -291,7 +291,8 @@ RouterArgs router_args(const q4moe_router* r, const uint16_t* x, int T, void* ws
 
 q4moe_status launch_router(const RouterArgs& a, hipStream_t s) {
     if (a.T >= 16) {  // many tokens: the MFMA router GEMM
-        hipLaunchKernelGGL(k_router_gemm, dim3((a.E + 31) / 32, (a.T + 31) / 32), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(k_router_gemm, dim3((a.E + kRouterTile - 1) / kRouterTile, (a.T + kRouterTile - 1) / kRouterTile),
+                           dim3(512), 0, s, a);
     } else {
         dim3 g1(a.E, (a.T + 3) / 4);
         hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, a);
@@ -615,7 +616,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
 
     // router
     RouterArgs ra = router_args(r, x_bf16, T, ws, l.r, ids, w, nullptr);
-    hipLaunchKernelGGL(k_router_gemm, dim3((E + 31) / 32, (T + 31) / 32), dim3(512), 0, s, ra);
+    hipLaunchKernelGGL(k_router_gemm, dim3((E + kRouterTile - 1) / kRouterTile, (T + kRouterTile - 1) / kRouterTile),
+                       dim3(512), 0, s, ra);
     if ((st = launched("router gemm")) != Q4MOE_OK) return st;
     hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, ra);
     if ((st = launched("router top-k")) != Q4MOE_OK) return st;
@@ -691,8 +693,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     if ((st = launched("grouped down gemm")) != Q4MOE_OK) return st;
 
     // combine
-    const size_t ny = (size_t)T * H;
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((ny + 255) / 256)), dim3(256), 0, s, T, K, H, da.inv, gd.out,
+    const size_t nq = (size_t)T * H / 4;  // 4 columns per thread (H % 64 == 0)
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, T, K, H, da.inv, gd.out,
                        at<float>(ws, l.y32), y_bf16);
     return launched("combine");
 }

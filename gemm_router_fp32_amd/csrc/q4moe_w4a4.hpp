@@ -13,9 +13,10 @@
 //
 // gfx950's 4-bit MFMA takes power-of-two (E8M0) scales per 32 elements and
 // cannot express NVFP4's E4M3 scale per 16, so both operands are decoded to
-// bf16 while they are staged in LDS: e2m1 * e4m3 has at most six significant
-// bits, so every decoded operand is exact in bf16 and every MFMA product is
-// exact in fp32; only the fp32 accumulation rounds.
+// fp16 (the activations while they are staged in LDS, the weights in
+// registers): e2m1 * e4m3 has at most six significant bits and lies in
+// [2^-10, 2688], so every decoded operand is exact in fp16 and every MFMA
+// product is exact in fp32; only the fp32 accumulation rounds.
 #pragma once
 
 #include "q4moe_kernels.hpp"
@@ -26,41 +27,54 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
-// Router logits for many tokens on fp32 MFMA (v_mfma_f32_32x32x2_f32):
-// a workgroup computes a 32-token x 32-expert tile; its 8 waves split the
-// hidden dimension and their partial tiles are summed in LDS in wave order.
-// Lane l feeds token/expert row l % 32 and, for each group of 8 k-values,
-// k-values 4 (l / 32) .. +3 (one per MFMA; A and B use the same k order).
+// Router logits for many tokens on fp32 MFMA (v_mfma_f32_16x16x4_f32): a
+// workgroup computes a 16-token x 16-expert tile (512 tiles for 1024 tokens
+// and 128 experts, so every CU gets work); its 8 waves split the hidden
+// dimension and their partial tiles are summed in LDS in wave order.  Lane l
+// feeds token/expert row l % 16 and, for each block of 16 k-values, k-values
+// 4 (l / 16) .. +3 (one per MFMA; A and B use the same k order).
 // ---------------------------------------------------------------------------
-typedef float f32x16r __attribute__((ext_vector_type(16)));
+constexpr int kRouterTile = 16;
 
 __global__ __launch_bounds__(512) void k_router_gemm(RouterArgs a) {
-    __shared__ float part[8][32][33];
+    __shared__ float part[8][16][17];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e0 = blockIdx.x * 32, t0 = blockIdx.y * 32;
-    const int row = lane & 31, kq = lane >> 5;
+    const int e0 = blockIdx.x * kRouterTile, t0 = blockIdx.y * kRouterTile;
+    const int row = lane & 15, kq = lane >> 4;
     const int t = min(t0 + row, a.T - 1), e = min(e0 + row, a.E - 1);
     const uint16_t* xr = a.x + (size_t)t * a.H + 4 * kq;
     const float* wr = a.wg + (size_t)e * a.H + 4 * kq;
-    const int nblk = a.H / 8;
+    const int nblk = a.H / 16;
     const int b0 = wave * nblk / 8, b1 = (wave + 1) * nblk / 8;
-    f32x16r acc;
+    f32x4g acc = {0.f, 0.f, 0.f, 0.f};
+    // kRouterBatch blocks' loads leave before their MFMAs (blocks past b1 are
+    // clamped to b1 - 1 and skipped)
+    constexpr int kRouterBatch = 7;
+    for (int bb = b0; bb < b1; bb += kRouterBatch) {
+        uint2 xv[kRouterBatch];
+        float4 wv[kRouterBatch];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-    for (int b = b0; b < b1; ++b) {
-        const uint2 xv = *reinterpret_cast<const uint2*>(xr + 8 * b);
-        const float4 wv = *reinterpret_cast<const float4*>(wr + 8 * b);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.x & 0xffffu), wv.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.x >> 16), wv.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.y & 0xffffu), wv.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(bf16_bits_to_f32(xv.y >> 16), wv.w, acc, 0, 0, 0);
+        for (int i = 0; i < kRouterBatch; ++i) {
+            const int b = min(bb + i, b1 - 1);
+            xv[i] = *reinterpret_cast<const uint2*>(xr + 16 * b);
+            wv[i] = *reinterpret_cast<const float4*>(wr + 16 * b);
+        }
+#pragma unroll
+        for (int i = 0; i < kRouterBatch; ++i) {
+            if (bb + i < b1) {
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].x & 0xffffu), wv[i].x, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].x >> 16), wv[i].y, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].y & 0xffffu), wv[i].z, acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].y >> 16), wv[i].w, acc, 0, 0, 0);
+            }
+        }
     }
-    // lane holds column j = lane % 32 (expert) and rows 8 (r/4) + 4 (lane/32) + r % 4 (tokens)
+    // lane holds column j = lane % 16 (expert) and rows 4 (lane / 16) + i (tokens)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) part[wave][8 * (r / 4) + 4 * kq + (r % 4)][row] = acc[r];
+    for (int i = 0; i < 4; ++i) part[wave][4 * kq + i][row] = acc[i];
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 32 * 32; idx += 512) {
-        const int i = idx >> 5, j = idx & 31;
+    if (threadIdx.x < kRouterTile * kRouterTile) {
+        const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < 8; ++w) v += part[w][i][j];
@@ -90,18 +104,30 @@ struct DispatchArgs {
 __global__ __launch_bounds__(64) void k_dispatch(DispatchArgs a) {
     const int e = blockIdx.x, lane = threadIdx.x;
     int base = 0;
-    for (int t0 = 0; t0 < a.T; t0 += 64) {
-        const int t = t0 + lane;
-        int pair = -1;
-        if (t < a.T)
-            for (int s = 0; s < a.K; ++s)
-                if (a.ids[(size_t)t * a.K + s] == e) pair = t * a.K + s;
-        const unsigned long long m = __ballot(pair >= 0);
-        if (pair >= 0) {
-            const int before = __popcll(m & ((1ull << lane) - 1ull));
-            a.lists[(size_t)e * a.T + base + before] = pair;
+    // four chunks of 64 tokens per round: all their id loads (token index
+    // clamped, K <= 8) leave before any is compared
+    for (int t0 = 0; t0 < a.T; t0 += 256) {
+        int idv[4][8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int tc = min(t0 + 64 * c + lane, a.T - 1);
+#pragma unroll
+            for (int s = 0; s < 8; ++s) idv[c][s] = s < a.K ? a.ids[(size_t)tc * a.K + s] : -1;
         }
-        base += __popcll(m);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int t = t0 + 64 * c + lane;
+            int pair = -1;
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s < a.K && idv[c][s] == e && t < a.T) pair = t * a.K + s;
+            const unsigned long long m = __ballot(pair >= 0);
+            if (pair >= 0) {
+                const int before = __popcll(m & ((1ull << lane) - 1ull));
+                a.lists[(size_t)e * a.T + base + before] = pair;
+            }
+            base += __popcll(m);
+        }
     }
     if (lane == 0) a.counts[e] = base;
 }
@@ -502,15 +528,32 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
 }
 
 // y32[t][n] = sum over slots s (in order) of zw[inv[t*K + s]][n]; y = bf16.
+// A thread takes 4 columns (H % 4 == 0) and issues its K row loads before
+// summing them.
 __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const int32_t* inv, const float* zw,
                                                  float* y32, uint16_t* y) {
-    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= (size_t)T * H) return;
     const size_t t = i / H, n = i % H;
-    float acc = 0.f;
-    for (int s = 0; s < K; ++s) acc += zw[(size_t)inv[t * K + s] * H + n];
-    y32[i] = acc;
-    y[i] = (uint16_t)f32_to_bf16_rne(acc);
+    float4 v[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+        if (s < K) v[s] = *reinterpret_cast<const float4*>(zw + (size_t)inv[t * K + s] * H + n);
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        if (s < K) {
+            acc.x += v[s].x;
+            acc.y += v[s].y;
+            acc.z += v[s].z;
+            acc.w += v[s].w;
+        }
+    }
+    *reinterpret_cast<float4*>(y32 + i) = acc;
+    uint2 b;
+    b.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
+    b.y = f32_to_bf16_rne(acc.z) | (f32_to_bf16_rne(acc.w) << 16);
+    *reinterpret_cast<uint2*>(y + i) = b;
 }
 
 }  // namespace q4moe
