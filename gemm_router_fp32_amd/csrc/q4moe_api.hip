@@ -203,7 +203,7 @@ q4moe_status launch_fused(const FusedArgs& a, hipStream_t s) {
 
 struct W4a4Ws {
     RouterWs r;
-    size_t counts, offsets, lists, perm, inv, xq_codes, xq_scales, h32, hq_codes, hq_scales, zw, y32, total;
+    size_t counts, offsets, lists, perm, inv, xq_codes, xq_scales, h32, hq_codes, hq_scales, z, y32, total;
 };
 
 W4a4Ws w4a4_ws(int E, int H, int I, int K, int T) {
@@ -225,7 +225,7 @@ W4a4Ws w4a4_ws(int E, int H, int I, int K, int T) {
     take(l.h32, rows * I * 4);
     take(l.hq_codes, rows * I / 2);
     take(l.hq_scales, rows * I / 16);
-    take(l.zw, rows * H * 4);
+    take(l.z, rows * H * 4);
     take(l.y32, (size_t)T * H * 4);
     l.total = o;
     return l;
@@ -662,7 +662,6 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     gu.perm = da.perm;
     gu.K = K;
     gu.a_by_token = 1;
-    gu.wgate = ra.w;
     gu.out = at<float>(ws, l.h32);
     hipLaunchKernelGGL((k_grouped_gemm<EPI_UP>), dim3((I + kGemmBN - 1) / kGemmBN, E), dim3(256), 0, s, gu);
     if ((st = launched("grouped up gemm")) != Q4MOE_OK) return st;
@@ -678,7 +677,7 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     hipLaunchKernelGGL((k_quant_nvfp4<false>), dim3((unsigned)((nbh + 255) / 256)), dim3(256), 0, s, qh);
     if ((st = launched("h quantization")) != Q4MOE_OK) return st;
 
-    // down: w g z per (token, slot) row
+    // down: g z per (token, slot) row (the gate is applied in the combine)
     GemmArgs gd = gu;
     gd.N = H;
     gd.Kd = I;
@@ -688,14 +687,14 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     gd.ac = qh.codes;
     gd.asc = qh.scales;
     gd.a_by_token = 0;
-    gd.out = at<float>(ws, l.zw);
+    gd.out = at<float>(ws, l.z);
     hipLaunchKernelGGL((k_grouped_gemm<EPI_DOWN>), dim3((H + kGemmBN - 1) / kGemmBN, E), dim3(256), 0, s, gd);
     if ((st = launched("grouped down gemm")) != Q4MOE_OK) return st;
 
     // combine
     const size_t nq = (size_t)T * H / 4;  // 4 columns per thread (H % 64 == 0)
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, T, K, H, da.inv, gd.out,
-                       at<float>(ws, l.y32), y_bf16);
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, T, K, H, da.inv, ra.w,
+                       gd.out, at<float>(ws, l.y32), y_bf16);
     return launched("combine");
 }
 

@@ -278,29 +278,10 @@ struct GemmArgs {
     const int32_t* perm;       // dispatch row -> pair t*K + slot
     int K;                     // top-k (pair -> token = pair / K)
     int a_by_token;            // 1: A row = token of the pair (up), 0: A row = dispatch row (down)
-    const float* wgate;        // [T*K] gates by pair (down epilogue)
     float* out;                // [rows][N] fp32, dispatch order
 };
 
-// Grouped GEMM over the experts' dispatch rows: out[row][n] = epi(sum_k
-// A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_32x32x16_f16) with both
-// operands decoded exactly from NVFP4.  A workgroup takes 128 columns of one
-// expert and all its rows in M-tiles of 96; wave w owns columns 32w..32w+31.
-//
-// The reduction runs in chunks of 256: every weight row contributes one whole
-// 128-byte line per chunk, loaded straight into registers (lane l: row l % 32,
-// bytes 64 (l / 32) .. +63, i.e. k 128 (l / 32) .. +127 of the chunk) two
-// chunks ahead in a three-slot ring (plain loads: the four load instructions
-// of a wave take 32 bytes of each line in turn, so the line must stay in L2
-// until the last one); the A tile of the chunk is decoded into
-// LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
-// (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
-// operands.  All loads are unconditional: pieces past the end of a row (the
-// last chunk, and the chunks that pad the count to a multiple of three) read
-// the row's last bytes and get scale 0, so that every wait covers exactly the
-// loads it needs.  Offsets are 32-bit from the uniform bases: the argument
-// limits (E <= 256, rows and columns <= 4096, T * K <= 2^19) keep every
-// matrix under 2^31 bytes.
+// Pieces of the grouped GEMM below (k_grouped_gemm describes the whole).
 struct BChunk {
     uint4 q[4];
     uint32_t s0, s1;
@@ -308,7 +289,7 @@ struct BChunk {
 
 // Per-workgroup constants of the grouped GEMM.
 struct GemmCtx {
-    int e, row0, n, hk, nch, nch3, ap, ar;
+    int e, row0, n, hk, nch, ap, ar;
     uint32_t wc_off, ws_off;
     float g;
 };
@@ -382,11 +363,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
     __builtin_amdgcn_sched_barrier(0);
     gemm_load_b(a, x, 1, bb[1]);
     __builtin_amdgcn_sched_barrier(0);
-    for (int c0 = 0; c0 < x.nch3; c0 += 3) {
-#pragma unroll
-        for (int u = 0; u < 3; ++u) {
-            const int c = c0 + u;
-            BChunk& bc = bb[u];
+    // chunk c computes on bc and loads chunk c + 2 into bn, the slot chunk
+    // c - 1 used
+    auto step = [&](const int c, const BChunk& bc, BChunk& bn) {
             // this chunk's A into LDS (after every wave is done with the last one)
             __syncthreads();
             const bool a_ok = 32 * x.ap < a.Kd - c * kGemmBK;
@@ -405,7 +384,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             __builtin_amdgcn_sched_barrier(0);
             load_a(c + 1);
             __builtin_amdgcn_sched_barrier(0);
-            gemm_load_b(a, x, c + 2, bb[(u + 2) % 3]);
+            gemm_load_b(a, x, c + 2, bn);
             __builtin_amdgcn_sched_barrier(0);
             // 16 MFMA steps on chunk c; block scales of the lane's 8 blocks,
             // pieces past the end get 0
@@ -440,8 +419,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
                 for (int i = 0; i < MS; ++i)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][i], bfrag, acc[i], 0, 0, 0);
             }
-        }
+    };
+    // whole turns of the ring, then the one or two chunks left (no padding
+    // chunks, and no exit from inside a turn)
+    int c = 0;
+    for (; c + 3 <= x.nch; c += 3) {
+        step(c, bb[0], bb[2]);
+        step(c + 1, bb[1], bb[0]);
+        step(c + 2, bb[2], bb[1]);
     }
+    if (c < x.nch) step(c, bb[0], bb[2]);
+    if (c + 1 < x.nch) step(c + 1, bb[1], bb[0]);
     // epilogue: lane holds column n and rows 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
@@ -454,8 +442,6 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
                 if constexpr (EPI == EPI_UP) {
                     v = fmaxf(v, 0.f);
                     v = v * v;
-                } else {
-                    v = a.wgate[a.perm[p]] * v;
                 }
                 a.out[(size_t)p * a.N + x.n] = v;
             }
@@ -476,10 +462,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 // until the last one); the A tile of the chunk is decoded into
 // LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
 // (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
-// operands.  All loads are unconditional: pieces past the end of a row (the
-// last chunk, and the chunks that pad the count to a multiple of three) read
-// the row's last bytes and get scale 0, so that every wait covers exactly the
-// loads it needs.  Offsets are 32-bit from the uniform bases: the argument
+// operands.  All loads are unconditional: pieces past the end of a row (in
+// the last chunk, and the prefetches issued by the last two chunks) read the
+// row's last bytes and get scale 0, so that every wait covers exactly the
+// loads it needs.  The chunk loop runs whole turns of the ring and then the
+// one or two chunks left, with no exit from inside a turn (an exit there makes
+// the compiler wait for every outstanding load).  Offsets are 32-bit from the uniform bases: the argument
 // limits (E <= 256, rows and columns <= 4096, T * K <= 2^19) keep every
 // matrix under 2^31 bytes.
 template <int EPI>
@@ -505,7 +493,6 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     x.hk = lane >> 5;
     x.nch = (a.Kd + kGemmBK - 1) / kGemmBK;
-    x.nch3 = (x.nch + 2) / 3 * 3;
     x.n = tile * kGemmBN + 32 * wave + (lane & 31);
     const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n, a.N - 1);
     x.wc_off = wrow * (uint32_t)(a.Kd / 2);
@@ -527,26 +514,31 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     }
 }
 
-// y32[t][n] = sum over slots s (in order) of zw[inv[t*K + s]][n]; y = bf16.
-// A thread takes 4 columns (H % 4 == 0) and issues its K row loads before
-// summing them.
-__global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const int32_t* inv, const float* zw,
-                                                 float* y32, uint16_t* y) {
+// y32[t][n] = sum over slots s (in order) of w[t*K + s] * z[inv[t*K + s]][n]
+// (the product rounded to fp32, then added); y = bf16.  A thread takes 4
+// columns (H % 4 == 0) and issues its K row loads before summing them.
+__global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const int32_t* inv, const float* w,
+                                                 const float* z, float* y32, uint16_t* y) {
     const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (i >= (size_t)T * H) return;
     const size_t t = i / H, n = i % H;
     float4 v[8];
+    float g[8];
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-        if (s < K) v[s] = *reinterpret_cast<const float4*>(zw + (size_t)inv[t * K + s] * H + n);
+    for (int s = 0; s < 8; ++s) {
+        if (s < K) {
+            v[s] = *reinterpret_cast<const float4*>(z + (size_t)inv[t * K + s] * H + n);
+            g[s] = w[t * K + s];
+        }
+    }
     float4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         if (s < K) {
-            acc.x += v[s].x;
-            acc.y += v[s].y;
-            acc.z += v[s].z;
-            acc.w += v[s].w;
+            acc.x += __fmul_rn(g[s], v[s].x);
+            acc.y += __fmul_rn(g[s], v[s].y);
+            acc.z += __fmul_rn(g[s], v[s].z);
+            acc.w += __fmul_rn(g[s], v[s].w);
         }
     }
     *reinterpret_cast<float4*>(y32 + i) = acc;
