@@ -172,13 +172,15 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
     const int grid = fused_grid<FMT, C, C2>(dev, variant);
     // The router needs one workgroup per expert; every wave's up rows must fit
-    // in kMaxUp passes and its down rows in kMaxDown (all loads in flight at
-    // once), a workgroup stages at most kMaxWgUp up rows, and its down rows
-    // span at most two slots.  Otherwise the caller uses separate launches.
-    const long long RU = (long long)a.K * a.I, RD = (long long)a.K * a.H;
+    // in kMaxUp passes (all loads in flight at once), a workgroup stages at
+    // most kMaxWgUp up rows, every down unit (kDownRows rows of one slot)
+    // needs a wave, and a workgroup's kWaves units span at most two slots.
+    // Otherwise the caller uses separate launches.
+    const long long RU = (long long)a.K * a.I;
     const long long nw = (long long)grid * kWaves;
-    if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RD + nw - 1) / nw > kMaxDown ||
-        (RU + grid - 1) / grid > kMaxWgUp || (RD + grid - 1) / grid + 1 > a.H)
+    const long long dpu = (a.H + kDownRows - 1) / kDownRows;
+    if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw ||
+        dpu < kWaves - 1)
         return Q4MOE_EUNSUPPORTED;
     hipLaunchKernelGGL((k_decode_fused<FMT, C, C2>), dim3(grid), dim3(64 * kWaves), 0, s, a);
     return launched("fused decode");

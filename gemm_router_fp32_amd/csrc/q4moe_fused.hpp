@@ -53,8 +53,8 @@ namespace q4moe {
 
 constexpr int kReplicas = 8;
 constexpr int kWaves = 8;    // waves per workgroup (one workgroup per CU)
-constexpr int kMaxUp = 3;    // up passes (two rows each) per wave, loads in flight together
-constexpr int kMaxDown = 8;  // down rows per wave, loads in flight together
+constexpr int kMaxUp = 3;      // up passes (two rows each) per wave, loads in flight together
+constexpr int kDownRows = 8;  // down rows per wave (one slot), loads in flight together
 constexpr int kMaxWgUp = 512;        // up rows per workgroup (K * I / grid)
 constexpr int kRowBlock = 64;
 constexpr uint32_t kPollLimit = 200000;  // polls (each at least one memory round trip) before giving up
@@ -103,50 +103,46 @@ __device__ __forceinline__ float tag_value(unsigned long long t) { return __uint
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Exact fp32 top-k of E <= 256 keys by one wave: expert e sits in lane
+// Exact fp32 top-k of E <= 64 * NQ keys by one wave: expert e sits in lane
 // e % 64, register e / 64, as the order-preserving integer image of its key
 // (NaN keys and padding at INT_MIN, never chosen).  Each round takes the wave
-// maximum and then the lowest expert index holding it (first non-empty
-// ballot, find-first-set), so equal keys go to the lower index exactly as the
-// definition says; the rounds keep no branches and read no scores.  Lane i
-// then takes pick i, reads its score and divides it by the sum of the K picked
-// scores (summed in pick order), into this wave's LDS slots.
+// maximum and then the lowest expert index holding it (the lowest set bit of
+// the first non-empty ballot, found without branches), so equal keys go to
+// the lower index exactly as the definition says.  The rounds form a rolled
+// loop over K that leaves pick i in lane i; lane i then reads its score and
+// divides it by the sum of the K picked scores (summed in pick order), into
+// this wave's LDS slots.
+template <int NQ>
 __device__ __forceinline__ void wave_topk(const FusedArgs& a, const float* s_keys, const float* s_scores,
                                           int* s_ids, float* s_w) {
     const int lane = threadIdx.x & 63;
-    int key[4];
+    int key[NQ];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < NQ; ++q) {
         const int e = lane + 64 * q;
         const float kv = s_keys[e];  // e < 256: inside the array; past E masked
         key[q] = e < a.E ? key_order(kv) : INT_MIN;
     }
-    int sel[8];
+    int my = 0;         // lane i: pick i
     bool lost = false;  // fewer than K keys that are not NaN
+#pragma nounroll
+    for (int i = 0; i < a.K; ++i) {
+        int m = key[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        sel[i] = 0;
-        if (i < a.K) {
-            const int m = wave_max_i32(max(max(key[0], key[1]), max(key[2], key[3])));
-            const unsigned long long h0 = __ballot(key[0] == m), h1 = __ballot(key[1] == m),
-                                     h2 = __ballot(key[2] == m), h3 = __ballot(key[3] == m);
-            int best = h0 ? (int)__builtin_ctzll(h0)
-                          : h1 ? 64 + (int)__builtin_ctzll(h1)
-                               : h2 ? 128 + (int)__builtin_ctzll(h2) : 192 + (int)__builtin_ctzll(h3);
-            if (m == INT_MIN) {  // only NaN keys left: keep every read inside the bank
-                lost = true;
-                best = 0;
-            }
+        for (int q = 1; q < NQ; ++q) m = max(m, key[q]);
+        m = wave_max_i32(m);
+        // lowest index holding m: an empty ballot counts as 1024
+        int best = 1024;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                if (lane + 64 * q == best) key[q] = INT_MIN;
-            sel[i] = best;
-        }
+        for (int q = 0; q < NQ; ++q)
+            best = min(best, 64 * q + (int)__builtin_ctzg((unsigned long long)__ballot(key[q] == m), 1024));
+        lost = lost || m == INT_MIN;
+        best = m == INT_MIN ? 0 : best;  // only NaN keys left: keep every read inside the bank
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) key[q] = lane + 64 * q == best ? INT_MIN : key[q];
+        my = lane == i ? best : my;
     }
     if (lost && lane == 0) atomicOr(a.ctrl + CTRL_FLAGS, 2u);
-    int my = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) my = lane == i ? sel[i] : my;
     const float sc_my = s_scores[my];
     const float msc = lane < a.K ? sc_my : 0.f;
     float ssum = 0.f;
@@ -158,6 +154,49 @@ __device__ __forceinline__ void wave_topk(const FusedArgs& a, const float* s_key
         s_w[lane] = msc / ssum;
     }
     __builtin_amdgcn_wave_barrier();
+}
+
+// Sums over the 64 lanes of eight values v[0..7] at once: after it, lane l
+// holds the sum of v[rows8_label(l)] over all lanes.  Each level halves the
+// lanes a value spans and pairs two values into one register: across the
+// wave halves (lanes 0-31 keep v[2i], 32-63 v[2i+1]), across 16-lane rows,
+// across 8-lane halves of a row; the last three steps sum inside each group
+// of eight lanes, so every lane of the group holds the total.
+__device__ __forceinline__ float add_swap32(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_swap16(float a, float b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float rows8_sum(const float (&v)[8]) {
+    const int lane = threadIdx.x & 63;
+    // level 1: [v0 | v1], [v2 | v3], [v4 | v5], [v6 | v7] (by wave half)
+    const float p0 = add_swap32(v[0], v[1]), p1 = add_swap32(v[2], v[3]);
+    const float p2 = add_swap32(v[4], v[5]), p3 = add_swap32(v[6], v[7]);
+    // level 2: by 16-lane row, q0 = [v0, v2, v1, v3], q1 = [v4, v6, v5, v7]
+    const float q0 = add_swap16(p0, p1), q1 = add_swap16(p2, p3);
+    // level 3: lanes 0-7 of a row take q0, lanes 8-15 q1 (row_ror:8 pairs
+    // lane i with lane i ^ 8)
+    const bool hi8 = (lane & 8) != 0;
+    const float x = hi8 ? q1 : q0, y = hi8 ? q0 : q1;
+    float r = x + dpp_mov<0x128>(y);
+    // inside each group of eight lanes: quad_perm [1,0,3,2], [2,3,0,1], then
+    // row_half_mirror (lane i with lane 7 - i of its half row)
+    r += dpp_mov<0xB1>(r);
+    r += dpp_mov<0x4E>(r);
+    r += dpp_mov<0x141>(r);
+    return r;
+}
+// Row of the eight whose sum lane l holds after rows8_sum: 4 for lanes 8-15
+// of a 16-lane row, plus [0, 2, 1, 3] by the row's index.
+__device__ __forceinline__ int rows8_label(int lane) {
+    return ((lane >> 3) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 5) & 1);
 }
 
 // Units of [0, total) owned by wave index `w` of `n` waves: [lo, hi).
@@ -245,15 +284,22 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     Q4MOE_PHASE(1);
 
     // unit bookkeeping (routing-independent: done while the scores travel)
-    const int RU = a.K * a.I, RD = a.K * a.H;
+    const int RU = a.K * a.I;
     const int u0 = share_lo(RU, gw, NW), u1 = share_lo(RU, gw + 1, NW);
-    const int d0 = share_lo(RD, gw, NW), d1 = share_lo(RD, gw + 1, NW);
     const int wu0 = share_lo(RU, blockIdx.x * kWaves, NW), wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
-    const int wd0 = share_lo(RD, blockIdx.x * kWaves, NW), wd1 = share_lo(RD, (blockIdx.x + 1) * kWaves, NW);
-    // A wave's units span at most two slots: slot(u) = us0 + (u >= ubnd).
+    // A wave's up units span at most two slots: slot(u) = us0 + (u >= ubnd).
     const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
-    const int ds0 = (d1 > d0 ? d0 : 0) / a.H, dbnd = (ds0 + 1) * a.H;
-    const int n_up_pass = (u1 - u0 + 1) / 2, n_down = d1 - d0;  // <= kMaxUp, <= kMaxDown (checked on the host)
+    const int n_up_pass = (u1 - u0 + 1) / 2;  // <= kMaxUp (checked on the host)
+    // Down units are runs of kDownRows rows inside one slot: unit q covers
+    // rows 8 (q % dpu) .. 8 (q % dpu) + 7 of slot q / dpu, and wave gw takes
+    // unit gw (the waves past the last unit hold no down rows).
+    const int dpu = (a.H + kDownRows - 1) / kDownRows, n_du = a.K * dpu;
+    const bool dwave = gw < n_du;
+    const int dslot = dwave ? gw / dpu : 0, drow0 = dwave ? (gw - dslot * dpu) * kDownRows : 0;
+    // the workgroup's down units span slots sl0 .. sl1 (at most two: dpu >=
+    // kWaves - 1 is checked on the host)
+    const int wdu0 = blockIdx.x * kWaves, wdu1 = min(wdu0 + kWaves, n_du);
+    const int sl0 = wdu1 > wdu0 ? wdu0 / dpu : 0, sl1 = wdu1 > wdu0 ? (wdu1 - 1) / dpu : -1;
 
     // ---- S: poll the scores (one copy per workgroup), form the keys.  The
     // polling waves keep two polls in flight (every lane loads every time, so
@@ -291,7 +337,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     int* ids = s_ids_all[wave];
     float* wsel = s_w_all[wave];
 
-    wave_topk(a, s_keys, s_scores, ids, wsel);
+    if (a.E <= 64 * 2)
+        wave_topk<2>(a, s_keys, s_scores, ids, wsel);
+    else
+        wave_topk<4>(a, s_keys, s_scores, ids, wsel);
     if (gw == 0 && lane < a.K) {
         const int id = ids[lane];
         const float wv = wsel[lane];
@@ -312,7 +361,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // s * rows, a select between the wave's two slots.
     const uint8_t* ups8 = reinterpret_cast<const uint8_t*>(a.ups);
     const uint8_t* dns8 = reinterpret_cast<const uint8_t*>(a.dns);
-    const int us1 = min(us0 + 1, a.K - 1), ds1 = min(ds0 + 1, a.K - 1);
+    const int us1 = min(us0 + 1, a.K - 1);
     const uint32_t urb = a.H / 2, usb = (FMT == FMT_NVFP4) ? a.H / 16 : a.H / 32;  // bytes per up row
     const uint32_t drb = a.I / 2, dsb = (FMT == FMT_NVFP4) ? a.I / 16 : a.I / 32;  // bytes per down row
     uint32_t uco[C], uso[C];  // this lane's chunk offsets within an up row
@@ -401,17 +450,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
         }
     }
-    // Then the loads of this wave's down rows: issued only now, so that the
-    // up rows (which every workgroup needs first, for h) have the memory
-    // system to themselves, and the down weights stream during the h
-    // hand-off instead.  (Lane i takes the per-tensor down scale of slot i.)
+    // Then the loads of a down wave's rows: issued only now, so that the up
+    // rows (which every workgroup needs first, for h) have the memory system
+    // to themselves, and the down weights stream during the h hand-off.  The
+    // rows past the slot's end (H % kDownRows != 0) read its last row and are
+    // dropped at the publish.  First every up load is retired (the ones of
+    // unused passes were issued before the used ones, so this costs nothing):
+    // otherwise the compiler counts them as pending past the branch and, where
+    // their registers are reused, waits for the down weights as well.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     compiler_fence();
-    float gd_l = 1.0f;
-    if constexpr (FMT == FMT_NVFP4) gd_l = a.dng[ids[lane < a.K ? lane : 0]];
-    const int doff0 = ids[ds0] * a.H - ds0 * a.H, doff1 = ids[ds1] * a.H - (ds0 + 1) * a.H;
-    uint4 qd[kMaxDown][C2];
-    uint32_t sd[kMaxDown][C2];
-    {
+    uint4 qd[kDownRows][C2];
+    uint32_t sd[kDownRows][C2];
+    float gdn = 1.0f;  // per-tensor scale of the down matrix (NVFP4)
+    if (dwave) {
+        const int drow = ids[dslot] * a.H;
         uint32_t dco[C2], dso[C2];
 #pragma unroll
         for (int c = 0; c < C2; ++c) {
@@ -420,10 +473,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             dso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
         }
 #pragma unroll
-        for (int p = 0; p < kMaxDown; ++p) {
-            int d = d0 + p;
-            if (d >= d1) d = d1 > d0 ? d0 : 0;
-            const uint32_t row = (uint32_t)(d + (d >= dbnd ? doff1 : doff0));
+        for (int p = 0; p < kDownRows; ++p) {
+            const uint32_t row = (uint32_t)(drow + min(drow0 + p, a.H - 1));
             const uint32_t rc = __umul24(row, drb), rs = __umul24(row, dsb);
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
@@ -431,13 +482,16 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 sd[p][c] = *reinterpret_cast<const uint16_t*>(dns8 + (rs + dso[c]));
             }
         }
+        if constexpr (FMT == FMT_NVFP4) gdn = a.dng[ids[dslot]];
     }
     compiler_fence();
     __syncthreads();
     Q4MOE_PHASE(4);
 
     // ---- P: publish this workgroup's h rows (thread j takes row wu0 + j),
-    // then poll the h of the slots the workgroup's down rows use into LDS
+    // then poll the h of the slots the workgroup's down rows use into LDS.
+    // (A poll result counts only after every load the wave issued before it,
+    // so the first poll also waits for the down weights.)
     {
         const int j = threadIdx.x;
         if (j < wu1 - wu0) {
@@ -449,11 +503,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             a.h[(size_t)slot * a.I + r] = v;
         }
     }
-    // the workgroup's down rows span slots sl0 .. sl1 (at most two, adjacent
-    // in the [K][I] layout, so their h is one run of nh values)
-    const int sl0 = wd1 > wd0 ? wd0 / a.H : 0, sl1 = wd1 > wd0 ? (wd1 - 1) / a.H : -1;
     {
-        const int nh = (sl1 - sl0 + 1) * a.I;  // <= 2 * 4096 = 16 per thread
+        // the slots sl0 .. sl1 are adjacent in the [K][I] layout, so their h
+        // is one run of nh <= 2 * 4096 = 16 * 512 values
+        const int nh = (sl1 - sl0 + 1) * a.I;
         const unsigned long long* src = a.h_tag + ((size_t)rep * a.K + sl0) * a.I;
         uint32_t pend = 0;
 #pragma unroll
@@ -480,57 +533,55 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __syncthreads();
     Q4MOE_PHASE(5);
 
-    // ---- D: z = w * g * (W_down h) for this wave's down rows, published
-    // (lane i holds w * g of slot i, read per row with readlane)
-    const float wgd_l = wsel[lane < a.K ? lane : 0] * gd_l;
-    {
+    // ---- D: a wave computes z = w * g * (W_down h) for its 8 rows of slot
+    // dslot (one block of code: each row waits only for its own weights),
+    // sums the rows over the lanes together and publishes them with one
+    // store.
+    if (dwave) {
         float hv[C2][32];
         float hs[C2];
-        int h_slot = -1;
 #pragma unroll
-        for (int p = 0; p < kMaxDown; ++p) {
-            if (p < n_down) {
-                const int d = d0 + p;
-                const int slot = ds0 + (d >= dbnd ? 1 : 0), r = d - slot * a.H;
-                if (slot != h_slot) {  // wave-uniform
+        for (int c = 0; c < C2; ++c) {
+            const int ch = min(lane * C2 + c, nchI - 1);
+            const float4* hp = reinterpret_cast<const float4*>(&s_h[(dslot - sl0) * a.I + ch * 32]);
+            hs[c] = 0.f;
 #pragma unroll
-                    for (int c = 0; c < C2; ++c) {
-                        const int ch = min(lane * C2 + c, nchI - 1);
-                        const float4* hp = reinterpret_cast<const float4*>(&s_h[(slot - sl0) * a.I + ch * 32]);
-                        hs[c] = 0.f;
+            for (int k = 0; k < 8; ++k) {
+                const float4 v = hp[k];
+                hv[c][4 * k + 0] = v.x;
+                hv[c][4 * k + 1] = v.y;
+                hv[c][4 * k + 2] = v.z;
+                hv[c][4 * k + 3] = v.w;
+            }
+            if constexpr (FMT == FMT_INT4) {
 #pragma unroll
-                        for (int k = 0; k < 8; ++k) {
-                            const float4 v = hp[k];
-                            hv[c][4 * k + 0] = v.x;
-                            hv[c][4 * k + 1] = v.y;
-                            hv[c][4 * k + 2] = v.z;
-                            hv[c][4 * k + 3] = v.w;
-                        }
-                        if constexpr (FMT == FMT_INT4) {
-#pragma unroll
-                            for (int j = 0; j < 32; ++j) hs[c] += hv[c][j];
-                        }
-                    }
-                    h_slot = slot;
-                }
-                float zz = 0.f;
-#pragma unroll
-                for (int c = 0; c < C2; ++c) {
-                    const bool chok = lane * C2 + c < nchI;
-                    if constexpr (FMT == FMT_NVFP4) {
-                        const f32x2 sp = e4m3fn_x2_f32(sd[p][c]);
-                        const float s0 = chok ? sp[0] : 0.f, s1 = chok ? sp[1] : 0.f;
-                        zz += nvfp4_chunk_f32(qd[p][c], hv[c], s0, s1);
-                    } else {
-                        const float sg = chok ? bf16_bits_to_f32(sd[p][c]) : 0.f;
-                        zz = __builtin_fmaf(sg, int4_chunk_f32(qd[p][c], hv[c]) - 8.0f * hs[c], zz);
-                    }
-                }
-                zz = seg_sum_last<64>(zz);
-                const float wg = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wgd_l), slot));
-                if (lane == 63) put_tag(a.z_tag + (uint32_t)(slot * a.H + r), wg * zz, ep);
+                for (int j = 0; j < 32; ++j) hs[c] += hv[c][j];
             }
         }
+        float zp[kDownRows];  // this lane's part of each row
+#pragma unroll
+        for (int p = 0; p < kDownRows; ++p) {
+            float zz = 0.f;
+#pragma unroll
+            for (int c = 0; c < C2; ++c) {
+                const bool chok = lane * C2 + c < nchI;
+                if constexpr (FMT == FMT_NVFP4) {
+                    const f32x2 sp = e4m3fn_x2_f32(sd[p][c]);
+                    const float s0 = chok ? sp[0] : 0.f, s1 = chok ? sp[1] : 0.f;
+                    zz += nvfp4_chunk_f32(qd[p][c], hv[c], s0, s1);
+                } else {
+                    const float sg = chok ? bf16_bits_to_f32(sd[p][c]) : 0.f;
+                    zz = __builtin_fmaf(sg, int4_chunk_f32(qd[p][c], hv[c]) - 8.0f * hs[c], zz);
+                }
+            }
+            zp[p] = zz;
+        }
+        // the eight row sums over the 64 lanes at once: lane l ends with the
+        // sum of row rows8_label(l)
+        const float zs = rows8_sum(zp);
+        const int rl = rows8_label(lane);
+        const float wg = wsel[dslot] * gdn;
+        if ((lane & 7) == 7 && drow0 + rl < a.H) put_tag(a.z_tag + (uint32_t)(dslot * a.H + drow0 + rl), wg * zs, ep);
     }
     Q4MOE_PHASE(6);
 
