@@ -333,9 +333,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
         ac_off[q] = arow * (uint32_t)(a.Kd / 2);
         as_off[q] = arow * (uint32_t)(a.Kd / 16);
     }
-    uint4 qa[MS];
-    uint32_t sa[MS];
-    auto load_a = [&](int c) {
+    // A pieces in a three-slot register ring alongside B's: chunk c's A is
+    // loaded two chunks ahead, into the slot chunk c - 1 staged from
+    uint4 qa3[3][MS];
+    uint32_t sa3[3][MS];
+    auto load_a = [&](int c, uint4 (&qa)[MS], uint32_t (&sa)[MS]) {
         const int kb = c * kGemmBK;
         const bool ok = 32 * x.ap < a.Kd - kb;
 #pragma unroll
@@ -355,17 +357,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
-    // issue order = wait order: B0, A0, B1 (the scheduler may not mix them)
+    // issue order = wait order: B0, A0, B1, A1 (the scheduler may not mix them)
     BChunk bb[3];
     gemm_load_b(a, x, 0, bb[0]);
     __builtin_amdgcn_sched_barrier(0);
-    load_a(0);
+    load_a(0, qa3[0], sa3[0]);
     __builtin_amdgcn_sched_barrier(0);
     gemm_load_b(a, x, 1, bb[1]);
     __builtin_amdgcn_sched_barrier(0);
-    // chunk c computes on bc and loads chunk c + 2 into bn, the slot chunk
-    // c - 1 used
-    auto step = [&](const int c, const BChunk& bc, BChunk& bn) {
+    load_a(1, qa3[1], sa3[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    // chunk c stages its A from (qa, sa), computes on bc, and loads chunk
+    // c + 2 into (qn, sn) and bn, the slots chunk c - 1 used
+    auto step = [&](const int c, const BChunk& bc, BChunk& bn, const uint4 (&qa)[MS], const uint32_t (&sa)[MS],
+                    uint4 (&qn)[MS], uint32_t (&sn)[MS]) {
             // this chunk's A into LDS (after every wave is done with the last one)
             __syncthreads();
             const bool a_ok = 32 * x.ap < a.Kd - c * kGemmBK;
@@ -380,9 +385,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
                 *reinterpret_cast<f16x8*>(dst + a_col(4 * x.ap + 3)) = fp4x8_f16(qa[q].w, s_hi);
             }
             __syncthreads();
-            // next loads: A of chunk c+1, B of chunk c+2 into the free slot
+            // next loads: A and B of chunk c+2 into the free slots
             __builtin_amdgcn_sched_barrier(0);
-            load_a(c + 1);
+            load_a(c + 2, qn, sn);
             __builtin_amdgcn_sched_barrier(0);
             gemm_load_b(a, x, c + 2, bn);
             __builtin_amdgcn_sched_barrier(0);
@@ -424,12 +429,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
     // chunks, and no exit from inside a turn)
     int c = 0;
     for (; c + 3 <= x.nch; c += 3) {
-        step(c, bb[0], bb[2]);
-        step(c + 1, bb[1], bb[0]);
-        step(c + 2, bb[2], bb[1]);
+        step(c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
+        step(c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
+        step(c + 2, bb[2], bb[1], qa3[2], sa3[2], qa3[1], sa3[1]);
     }
-    if (c < x.nch) step(c, bb[0], bb[2]);
-    if (c + 1 < x.nch) step(c + 1, bb[1], bb[0]);
+    if (c < x.nch) step(c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
+    if (c + 1 < x.nch) step(c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
     // epilogue: lane holds column n and rows 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4
 #pragma unroll
     for (int i = 0; i < MS; ++i) {
@@ -459,17 +464,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 // bytes 64 (l / 32) .. +63, i.e. k 128 (l / 32) .. +127 of the chunk) two
 // chunks ahead in a three-slot ring (plain loads: the four load instructions
 // of a wave take 32 bytes of each line in turn, so the line must stay in L2
-// until the last one); the A tile of the chunk is decoded into
-// LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
+// until the last one); the A pieces of the chunk, loaded two chunks ahead
+// in a ring of their own, are decoded into LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
 // (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
 // operands.  All loads are unconditional: pieces past the end of a row (in
 // the last chunk, and the prefetches issued by the last two chunks) read the
 // row's last bytes and get scale 0, so that every wait covers exactly the
 // loads it needs.  The chunk loop runs whole turns of the ring and then the
 // one or two chunks left, with no exit from inside a turn (an exit there makes
-// the compiler wait for every outstanding load).  Offsets are 32-bit from the uniform bases: the argument
-// limits (E <= 256, rows and columns <= 4096, T * K <= 2^19) keep every
-// matrix under 2^31 bytes.
+// the compiler wait for every outstanding load).  Offsets are 32-bit from the
+// uniform bases: the argument limits (E <= 256, rows and columns <= 4096,
+// T * K <= 2^19) keep every matrix under 2^31 bytes.
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 As[kGemmBM][kApitch];
