@@ -665,7 +665,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     gu.K = K;
     gu.a_by_token = 1;
     gu.out = at<float>(ws, l.h32);
-    hipLaunchKernelGGL((k_grouped_gemm<EPI_UP>), dim3((I + kGemmBN - 1) / kGemmBN, E), dim3(256), 0, s, gu);
+    hipLaunchKernelGGL((k_grouped_gemm<EPI_UP>), dim3((I + kGemmBN - 1) / kGemmBN, E), dim3(256),
+                       (size_t)kGemmBN * (H / 16) + 16, s, gu);
     if ((st = launched("grouped up gemm")) != Q4MOE_OK) return st;
 
     // h -> NVFP4
@@ -690,7 +691,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     gd.asc = qh.scales;
     gd.a_by_token = 0;
     gd.out = at<float>(ws, l.z);
-    hipLaunchKernelGGL((k_grouped_gemm<EPI_DOWN>), dim3((H + kGemmBN - 1) / kGemmBN, E), dim3(256), 0, s, gd);
+    hipLaunchKernelGGL((k_grouped_gemm<EPI_DOWN>), dim3((H + kGemmBN - 1) / kGemmBN, E), dim3(256),
+                       (size_t)kGemmBN * (I / 16) + 16, s, gd);
     if ((st = launched("grouped down gemm")) != Q4MOE_OK) return st;
 
     // combine

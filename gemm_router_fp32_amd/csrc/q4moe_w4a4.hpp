@@ -284,13 +284,17 @@ struct GemmArgs {
 // Pieces of the grouped GEMM below (k_grouped_gemm describes the whole).
 struct BChunk {
     uint4 q[4];
-    uint32_t s0, s1;
 };
+
+// Block scales of the workgroup's 128 weight rows (row-major, Kd / 16 bytes a
+// row), staged once per workgroup: per chunk a lane then reads its 8 bytes
+// from LDS instead of two scattered 4-byte loads from 32 rows.
+extern __shared__ __attribute__((aligned(16))) uint8_t g_gemm_sct[];
 
 // Per-workgroup constants of the grouped GEMM.
 struct GemmCtx {
-    int e, row0, n, hk, nch, ap, ar;
-    uint32_t wc_off, ws_off;
+    int e, row0, n, hk, nch, ap, ar, rb;
+    uint32_t wc_off, sc_row;
     float g;
 };
 
@@ -304,13 +308,10 @@ __device__ __forceinline__ int gemm_valid_pieces(const GemmArgs& a, const GemmCt
 // are still in L2.
 __device__ __forceinline__ void gemm_load_b(const GemmArgs& a, const GemmCtx& x, int c, BChunk& b) {
     const int kb = c * kGemmBK, valid = gemm_valid_pieces(a, x, c);
-    const uint32_t c_last = x.wc_off + a.Kd / 2 - 16, s_last = x.ws_off + a.Kd / 16 - 4;
+    const uint32_t c_last = x.wc_off + a.Kd / 2 - 16;
     const uint32_t base = x.wc_off + kb / 2 + 64 * x.hk;
 #pragma unroll
     for (int i = 0; i < 4; ++i) b.q[i] = ldg16(a.wc + (i < valid ? base + 16 * i : c_last));
-    const uint32_t sb = x.ws_off + kb / 16 + 8 * x.hk;
-    b.s0 = *reinterpret_cast<const uint32_t*>(a.wsc + (valid > 0 ? sb : s_last));
-    b.s1 = *reinterpret_cast<const uint32_t*>(a.wsc + (valid > 2 ? sb + 4 : s_last));
 }
 
 // A tile LDS column (fp16 elements) of 16-byte group g of a row: groups are
@@ -394,8 +395,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             // 16 MFMA steps on chunk c; block scales of the lane's 8 blocks,
             // pieces past the end get 0
             const int valid = gemm_valid_pieces(a, x, c);
-            f16x2 sc[4] = {e4m3x2_f16<false>(bc.s0), e4m3x2_f16<true>(bc.s0), e4m3x2_f16<false>(bc.s1),
-                           e4m3x2_f16<true>(bc.s1)};
+            // (a dword past the valid pieces reads the row's first bytes; its
+            // scales are zeroed below)
+            const int so = c * 16 + 8 * x.hk;
+            const uint32_t s0 = *reinterpret_cast<const uint32_t*>(g_gemm_sct + x.sc_row + (valid > 0 ? so : 0));
+            const uint32_t s1 = *reinterpret_cast<const uint32_t*>(g_gemm_sct + x.sc_row + (valid > 2 ? so + 4 : 0));
+            f16x2 sc[4] = {e4m3x2_f16<false>(s0), e4m3x2_f16<true>(s0), e4m3x2_f16<false>(s1), e4m3x2_f16<true>(s1)};
 #pragma unroll
             for (int pc = 0; pc < 4; ++pc)
                 if (pc >= valid) sc[pc] = f16x2{0, 0};
@@ -467,7 +472,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 // until the last one); the A pieces of the chunk, loaded two chunks ahead
 // in a ring of their own, are decoded into LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
 // (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
-// operands.  All loads are unconditional: pieces past the end of a row (in
+// operands.  The block scales of the workgroup's 128 weight rows are copied
+// into LDS once, with coalesced loads issued beside the expert's offsets
+// (per chunk a wave would otherwise gather 4 bytes from each of 32 rows,
+// twice).  All loads are unconditional: pieces past the end of a row (in
 // the last chunk, and the prefetches issued by the last two chunks) read the
 // row's last bytes and get scale 0, so that every wait covers exactly the
 // loads it needs.  The chunk loop runs whole turns of the ring and then the
@@ -492,6 +500,21 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
         x.e = b % 8 + 8 * (j / ntiles);
         tile = j % ntiles;
     }
+    // The scale rows of this tile (contiguous: rows e N + 128 tile ..), one
+    // dword per thread and pass, loaded together with the expert's offsets
+    // and stored to LDS once they are in.
+    const int sc_rb = a.Kd / 16;
+    const int sc_ndw = min(kGemmBN, a.N - tile * kGemmBN) * sc_rb / 4;
+    uint32_t scv[32];
+    {
+        const uint32_t* src =
+            reinterpret_cast<const uint32_t*>(a.wsc + ((uint32_t)x.e * a.N + tile * kGemmBN) * (uint32_t)sc_rb);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const int i = (int)threadIdx.x + 256 * j;
+            scv[j] = i < sc_ndw ? src[i] : 0u;
+        }
+    }
     x.row0 = a.offsets[x.e];
     const int n_e = a.offsets[x.e + 1] - x.row0;
     if (n_e == 0) return;
@@ -501,7 +524,13 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     x.n = tile * kGemmBN + 32 * wave + (lane & 31);
     const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n, a.N - 1);
     x.wc_off = wrow * (uint32_t)(a.Kd / 2);
-    x.ws_off = wrow * (uint32_t)(a.Kd / 16);
+    x.rb = sc_rb;
+    x.sc_row = (uint32_t)((32 * wave + (lane & 31)) * x.rb);
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const int i = (int)threadIdx.x + 256 * j;
+        if (i < sc_ndw) reinterpret_cast<uint32_t*>(g_gemm_sct)[i] = scv[j];
+    }
     x.g = a.wg[x.e];
     // A staging role: piece ap (k 32ap..32ap+31 of the chunk) of rows ar + 32q
     x.ap = threadIdx.x & 7;
