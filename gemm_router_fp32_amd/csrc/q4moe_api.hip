@@ -293,7 +293,7 @@ RouterArgs router_args(const q4moe_router* r, const uint16_t* x, int T, void* ws
 
 q4moe_status launch_router(const RouterArgs& a, hipStream_t s) {
     if (a.T >= 16) {  // many tokens: the MFMA router GEMM
-        hipLaunchKernelGGL(k_router_gemm, dim3((a.E + kRouterTile - 1) / kRouterTile, (a.T + kRouterTile - 1) / kRouterTile),
+        hipLaunchKernelGGL(k_router_gemm, dim3((a.T + kRouterTile - 1) / kRouterTile, (a.E + kRouterTile - 1) / kRouterTile),
                            dim3(512), 0, s, a);
     } else {
         dim3 g1(a.E, (a.T + 3) / 4);
@@ -618,7 +618,7 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
 
     // router
     RouterArgs ra = router_args(r, x_bf16, T, ws, l.r, ids, w, nullptr);
-    hipLaunchKernelGGL(k_router_gemm, dim3((E + kRouterTile - 1) / kRouterTile, (T + kRouterTile - 1) / kRouterTile),
+    hipLaunchKernelGGL(k_router_gemm, dim3((T + kRouterTile - 1) / kRouterTile, (E + kRouterTile - 1) / kRouterTile),
                        dim3(512), 0, s, ra);
     if ((st = launched("router gemm")) != Q4MOE_OK) return st;
     hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, ra);

@@ -32,14 +32,16 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // and 128 experts, so every CU gets work); its 8 waves split the hidden
 // dimension and their partial tiles are summed in LDS in wave order.  Lane l
 // feeds token/expert row l % 16 and, for each block of 16 k-values, k-values
-// 4 (l / 16) .. +3 (one per MFMA; A and B use the same k order).
+// 4 (l / 16) .. +3 (one per MFMA; A and B use the same k order).  The grid is
+// (token tiles, expert tiles): workgroup b runs on XCD b % 8, so all expert
+// tiles of a token tile share one XCD and read its x rows from HBM once.
 // ---------------------------------------------------------------------------
 constexpr int kRouterTile = 16;
 
 __global__ __launch_bounds__(512) void k_router_gemm(RouterArgs a) {
     __shared__ float part[8][16][17];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int e0 = blockIdx.x * kRouterTile, t0 = blockIdx.y * kRouterTile;
+    const int t0 = blockIdx.x * kRouterTile, e0 = blockIdx.y * kRouterTile;
     const int row = lane & 15, kq = lane >> 4;
     const int t = min(t0 + row, a.T - 1), e = min(e0 + row, a.E - 1);
     const uint16_t* xr = a.x + (size_t)t * a.H + 4 * kq;
