@@ -100,15 +100,19 @@ def spread(ms, scale=1e3, nd=3):
 
 
 class Evictor:
-    """Reads and writes 2 x 512 MiB so that nothing a timed rep reads is
-    still held in the 256 MB MALL or the L2s."""
+    """Reads 1 GiB so that nothing a timed rep reads is still held in the
+    256 MB MALL or the L2s.  The eviction only reads: it leaves clean lines
+    behind, as the small activation writes before a decode step would, so
+    the timed rep does not pay for writing back the evictor's own data (a
+    512 MiB copy as the eviction left the caches dirty and cost the
+    lm_head ~10 us of write-backs)."""
 
     def __init__(self, torch):
-        self.src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
-        self.dst = torch.empty_like(self.src)
+        self.buf = torch.ones(1 << 27, dtype=torch.int64, device="cuda")
+        torch.cuda.synchronize()
 
     def __call__(self):
-        self.dst.copy_(self.src)
+        self.buf.sum()
 
 
 def build_stack(torch, g, synth, fmt):

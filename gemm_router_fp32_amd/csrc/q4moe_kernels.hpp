@@ -507,7 +507,10 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
     const int cols = a.cols;
 
     // x -> registers in 16-byte pieces (one pass, every load in flight at
-    // once), per-token largest magnitude, power-of-two scale, fp16 into LDS
+    // once), per-token largest magnitude, power-of-two scale, fp16 into LDS;
+    // it runs once the first weight batch of the wave's first group is in
+    // flight, so the weight stream starts at the first instruction
+    auto x_setup = [&]()
     {
         constexpr int kXP = (T * kGemvMaxCols / 8 + 255) / 256;
         const int per_t = cols / 8, total = T * per_t;
@@ -569,20 +572,28 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
 #pragma unroll 1
             for (int k = cols + threadIdx.x; k < kGemvMaxCols + 8; k += 256) xs[t][k] = (_Float16)0.f;
         __syncthreads();
-    }
-    const float g = *a.gscale;
+    };
     const int m16 = lane & 15, kq = lane >> 4;
     const int n = m16;  // token column of this lane in the 16-column operand
+    unsigned long long best = 0ull;
+    const int groups = (a.rows + 15) / 16;
+    // every wave takes part in x_setup's barriers: a wave without a group of
+    // its own computes the last group and stores nothing
+    int grp = blockIdx.x * 4 + wave;
+    const bool first_own = grp < groups;
+    f4 acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales,
+                                                      (uint32_t)min((first_own ? grp : groups - 1) * 16 + m16, a.rows - 1),
+                                                      cols, &xs[0][0], m16, kq, x_setup);
+    const float g = *a.gscale;
     float unscale = 0.f;
 #pragma unroll
     for (int t = 0; t < T; ++t)
         if (n == t) unscale = ldexpf(g, -s_exp[t]);
-    unsigned long long best = 0ull;
-
-    const int groups = (a.rows + 15) / 16;
-    for (int grp = blockIdx.x * 4 + wave; grp < groups; grp += gridDim.x * 4) {
-        const uint32_t r = (uint32_t)min(grp * 16 + m16, a.rows - 1);
-        const f4 acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales, r, cols, &xs[0][0], m16, kq, [] {});
+    for (; grp < groups; grp += gridDim.x * 4) {
+        if (grp != blockIdx.x * 4 + wave) {
+            const uint32_t r = (uint32_t)min(grp * 16 + m16, a.rows - 1);
+            acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales, r, cols, &xs[0][0], m16, kq, [] {});
+        }
         // lane holds rows grp*16 + 4 kq + r of token n
         if (n < T) {
 #pragma unroll
