@@ -429,22 +429,39 @@ typedef float f32x4g __attribute__((ext_vector_type(4)));
 // once the first batch is in flight.  Pieces past `cols` reread the row's
 // last bytes with scale 0 and read LDS columns that must hold zeros up to
 // 128 NJ.
+// A full group (all 16 rows r0 .. r0 + 15 inside the matrix, `full`) has its
+// block scales, one contiguous run of 16 * cols / 16 bytes, copied with
+// 16-byte loads into the wave's LDS slice sblk (at least cols bytes) and read
+// from there: per piece a lane would otherwise gather 2 bytes from each of 16
+// rows.  Other groups load each scale pair from memory.
 // Offsets are 32-bit from the uniform bases (codes under 4 GiB).
 template <int NJ, int NT, int P, typename F>
 __device__ __forceinline__ f32x4g mfma_gemv_group(const uint8_t* codes, const uint8_t* scales, uint32_t r, int cols,
-                                                  const _Float16* xs, int m16, int kq, F&& after_first_issue) {
+                                                  const _Float16* xs, int m16, int kq, F&& after_first_issue,
+                                                  uint8_t* sblk, uint32_t r0, bool full) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
     typedef _Float16 h2 __attribute__((ext_vector_type(2)));
     const uint32_t rc = r * (uint32_t)(cols / 2), rs = r * (uint32_t)(cols / 16);
+    const int rb = cols / 16;  // scale bytes per row; 16 rows are rb 16-byte pieces
+    const int lane = threadIdx.x & 63;
     constexpr int kB = 7;
     uint4 q[NJ];
     uint32_t sc[NJ];
+    uint4 sv[4];  // cols <= 4096: at most 256 pieces, 4 per lane
+    if (full) {
+        const uint4* src = reinterpret_cast<const uint4*>(scales + r0 * (uint32_t)rb);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pc = lane + 64 * i;
+            sv[i] = pc < rb ? src[pc] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
     auto issue = [&](int j0) {
 #pragma unroll
         for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
             const bool ok = 128 * j + 32 * kq < cols;
             q[j] = ldg16(codes + (rc + (ok ? 64 * j + 16 * kq : cols / 2 - 16)));
-            sc[j] = *reinterpret_cast<const uint16_t*>(scales + (rs + (ok ? 8 * j + 2 * kq : cols / 16 - 2)));
+            if (!full) sc[j] = *reinterpret_cast<const uint16_t*>(scales + (rs + (ok ? 8 * j + 2 * kq : cols / 16 - 2)));
         }
     };
     f32x4g acc = {0.f, 0.f, 0.f, 0.f};
@@ -452,6 +469,14 @@ __device__ __forceinline__ f32x4g mfma_gemv_group(const uint8_t* codes, const ui
     // (the caller may fill xs here, while the first batch is in flight)
     __builtin_amdgcn_sched_barrier(0);
     after_first_issue();
+    if (full) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int pc = lane + 64 * i;
+            if (pc < rb) reinterpret_cast<uint4*>(sblk)[pc] = sv[i];
+        }
+    }
+    const uint8_t* srow = sblk + (r - r0) * (uint32_t)rb;  // (full groups only)
 #pragma unroll
     for (int j0 = 0; j0 < NJ; j0 += kB) {
         __builtin_amdgcn_sched_barrier(0);
@@ -460,7 +485,8 @@ __device__ __forceinline__ f32x4g mfma_gemv_group(const uint8_t* codes, const ui
 #pragma unroll
         for (int j = j0; j < (j0 + kB < NJ ? j0 + kB : NJ); ++j) {
             const bool ok = 128 * j + 32 * kq < cols;
-            const h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? sc[j] : 0u, 1.0f, false);
+            const uint32_t scj = full ? (uint32_t)*reinterpret_cast<const uint16_t*>(srow + (ok ? 8 * j + 2 * kq : 0)) : sc[j];
+            const h2 sp = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ok ? scj : 0u, 1.0f, false);
             const uint32_t w4[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
@@ -503,8 +529,10 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
     static_assert(128 * (NJ - 1) + 32 * 3 + 8 * 3 + 8 <= kGemvMaxCols + 8, "LDS reads stay in the row");
     __shared__ float s_amax[4][T];
     __shared__ int s_exp[T];
+    __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][kGemvMaxCols / 16];  // each wave's group scales
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int cols = a.cols;
+    uint8_t* sblk = reinterpret_cast<uint8_t*>(&s_sblk[wave][0]);
 
     // x -> registers in 16-byte pieces (one pass, every load in flight at
     // once), per-token largest magnitude, power-of-two scale, fp16 into LDS;
@@ -581,9 +609,10 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
     // its own computes the last group and stores nothing
     int grp = blockIdx.x * 4 + wave;
     const bool first_own = grp < groups;
-    f4 acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales,
-                                                      (uint32_t)min((first_own ? grp : groups - 1) * 16 + m16, a.rows - 1),
-                                                      cols, &xs[0][0], m16, kq, x_setup);
+    const int grp0 = first_own ? grp : groups - 1;
+    f4 acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales, (uint32_t)min(grp0 * 16 + m16, a.rows - 1),
+                                                      cols, &xs[0][0], m16, kq, x_setup, sblk, (uint32_t)(grp0 * 16),
+                                                      grp0 * 16 + 16 <= a.rows);
     const float g = *a.gscale;
     float unscale = 0.f;
 #pragma unroll
@@ -592,7 +621,8 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
     for (; grp < groups; grp += gridDim.x * 4) {
         if (grp != blockIdx.x * 4 + wave) {
             const uint32_t r = (uint32_t)min(grp * 16 + m16, a.rows - 1);
-            acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales, r, cols, &xs[0][0], m16, kq, [] {});
+            acc = mfma_gemv_group<NJ, T, kGemvMaxCols + 8>(a.codes, a.scales, r, cols, &xs[0][0], m16, kq, [] {}, sblk,
+                                                           (uint32_t)(grp * 16), grp * 16 + 16 <= a.rows);
         }
         // lane holds rows grp*16 + 4 kq + r of token n
         if (n < T) {
@@ -836,6 +866,7 @@ __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 xs[kSmallT][P];
     __shared__ float s_amax[4][4];
     __shared__ int s_exp[4];
+    __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][NJ * 8];  // each wave's group scales (16 rows)
     bool leader;
     const int e = small_expert(a, blockIdx.y, leader);
     if (!leader) return;  // uniform
@@ -843,10 +874,12 @@ __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
     const int m16 = lane & 15, kq = lane >> 4;
     const int row = blockIdx.x * 64 + wave * 16 + m16;
     const uint32_t wrow = (uint32_t)e * a.I + min(row, a.I - 1);
+    const int row0 = blockIdx.x * 64 + wave * 16;
     // x goes to LDS while the first weight batch is in flight
-    const f32x4g acc = mfma_gemv_group<NJ, kSmallT, P>(a.upc, a.ups, wrow, a.H, &xs[0][0], m16, kq, [&] {
-        stage_bf16_rows<P>(a.x, a.T, a.H, &xs[0][0], s_amax, s_exp);
-    });
+    const f32x4g acc = mfma_gemv_group<NJ, kSmallT, P>(
+        a.upc, a.ups, wrow, a.H, &xs[0][0], m16, kq,
+        [&] { stage_bf16_rows<P>(a.x, a.T, a.H, &xs[0][0], s_amax, s_exp); },
+        reinterpret_cast<uint8_t*>(&s_sblk[wave][0]), (uint32_t)e * a.I + (uint32_t)row0, row0 + 16 <= a.I);
     // lane (n = m16, kq) holds rows 4 kq + r of token n
     const int n = m16;
     if (n < a.T) {
@@ -901,9 +934,10 @@ __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
 #pragma unroll
     for (int c = 0; c < kSmallT; ++c) col_off[c] = (size_t)cols[c] * a.I;
     // h goes to LDS while the first weight batch is in flight
-    const f32x4g acc = mfma_gemv_group<NJ, 2 * kSmallT, P>(a.dnc, a.dns, wrow, a.I, &hs[0][0], m16, kq, [&] {
-        stage_f32_hilo<P>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp);
-    });
+    // (no LDS left for a scale slice in the widest instance: scales load per piece)
+    const f32x4g acc = mfma_gemv_group<NJ, 2 * kSmallT, P>(
+        a.dnc, a.dns, wrow, a.I, &hs[0][0], m16, kq,
+        [&] { stage_f32_hilo<P>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp); }, nullptr, 0u, false);
     // lane (n, kq) holds column n: hi for n < 4, lo for n >= 4; add lane n + 4's lo
     const int n = m16;
     float z[4];
