@@ -911,6 +911,9 @@ __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 hs[2 * kSmallT][P];
     __shared__ float s_amax[4][4];
     __shared__ int s_exp[4];
+    // each wave's group scales (16 rows), where the instance has room for them
+    constexpr bool kScaleLds = NJ <= 24;
+    __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][kScaleLds ? NJ * 8 : 1];
     bool leader;
     const int e = small_expert(a, blockIdx.y, leader);
     if (!leader) return;  // uniform
@@ -934,10 +937,14 @@ __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
 #pragma unroll
     for (int c = 0; c < kSmallT; ++c) col_off[c] = (size_t)cols[c] * a.I;
     // h goes to LDS while the first weight batch is in flight
-    // (no LDS left for a scale slice in the widest instance: scales load per piece)
+    // (the widest instances have no LDS left for the scale slice: their
+    // scales load per piece)
+    const int row0 = blockIdx.x * 64 + wave * 16;
     const f32x4g acc = mfma_gemv_group<NJ, 2 * kSmallT, P>(
         a.dnc, a.dns, wrow, a.I, &hs[0][0], m16, kq,
-        [&] { stage_f32_hilo<P>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp); }, nullptr, 0u, false);
+        [&] { stage_f32_hilo<P>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp); },
+        reinterpret_cast<uint8_t*>(&s_sblk[wave][0]), (uint32_t)e * a.H + (uint32_t)row0,
+        kScaleLds && row0 + 16 <= a.H);
     // lane (n, kq) holds column n: hi for n < 4, lo for n >= 4; add lane n + 4's lo
     const int n = m16;
     float z[4];
