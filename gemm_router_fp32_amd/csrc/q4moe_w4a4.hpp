@@ -187,18 +187,26 @@ __device__ __forceinline__ uint32_t e4m3fn_rne_sat(float d) {
     return b > 0x7Eu ? 0x7Eu : b;
 }
 
-// E2M1 magnitude code of |v| on the grid scaled by s (ties to even codes).
-__device__ __forceinline__ uint32_t e2m1_code(float mag, float s) {
-    if (s == 0.f) return 0u;
-    const float mids[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-    uint32_t idx = 0;
-#pragma unroll
-    for (int j = 0; j < 7; ++j) {
-        const float t = mids[j] * s;  // exact
-        const bool up = mag > t || (mag == t && ((j + 1) & 1) == 0);
-        idx += (up && idx == (uint32_t)j) ? 1u : 0u;
-    }
-    return idx;
+// The E2M1 code of |v| on the grid scaled by s is the number of midpoints
+// t_j = mids_j * s (exact: mids have at most 3 significant bits) that |v|
+// passes, a tie going to the even code: up at an odd j, down at an even j.
+// The thresholds increase, so three comparisons find the count (a binary
+// search: j = 3, then 1 or 5, then 0, 2, 4 or 6).  Scale 0 gives code 0 for
+// every value: the thresholds are then NaN and every comparison is false
+// (as for a NaN value).
+struct E2m1Thresholds {
+    float t[7];
+};
+__device__ __forceinline__ E2m1Thresholds e2m1_thresholds(float s) {
+    const float sc = s == 0.f ? __builtin_nanf("") : s;
+    return {{0.25f * sc, 0.75f * sc, 1.25f * sc, 1.75f * sc, 2.5f * sc, 3.5f * sc, 5.0f * sc}};
+}
+__device__ __forceinline__ uint32_t e2m1_code(float mag, const E2m1Thresholds& th) {
+    const uint32_t b2 = mag >= th.t[3] ? 1u : 0u;
+    const uint32_t b1 = mag >= (b2 ? th.t[5] : th.t[1]) ? 1u : 0u;
+    const float tl = b2 ? (b1 ? th.t[6] : th.t[4]) : (b1 ? th.t[2] : th.t[0]);
+    const uint32_t b0 = mag > tl ? 1u : 0u;
+    return (b2 << 2) | (b1 << 1) | b0;
 }
 
 struct QuantArgs {
@@ -208,49 +216,55 @@ struct QuantArgs {
     uint8_t* scales;    // [rows][cols/16]
 };
 
+// One lane per 16 input bytes (4 fp32 or 8 bf16 values: a quarter or a half
+// of a block), so every load instruction reads 1 KB in one run; the block
+// maximum is taken across the block's 2 or 4 neighbouring lanes (quad
+// permutes), each lane stores its own code bytes and the block's first lane
+// the scale byte.  Lanes past the end work on the last piece and store
+// nothing (a block's lanes are always all live or all past the end).
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
-    const size_t blk = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t nb_row = (size_t)a.cols / 16;
-    if (blk >= (size_t)a.rows * nb_row) return;
-    const size_t r = blk / nb_row, b = blk % nb_row;
-    float v[16];
+    constexpr int VPL = BF16_IN ? 8 : 4;  // values per lane
+    constexpr int LPB = 16 / VPL;         // lanes per block
+    const size_t n_pieces = (size_t)a.rows * (size_t)a.cols / VPL;
+    const size_t gp = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = gp < n_pieces;
+    const size_t pc = live ? gp : n_pieces - 1;
+    float v[VPL];
     if constexpr (BF16_IN) {
-        const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + r * a.cols + b * 16);
-        const uint4 q0 = p[0], q1 = p[1];
-        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            v[2 * j] = bf16_bits_to_f32(w[j] & 0xffffu);
-            v[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
-        }
-    } else {
-        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + r * a.cols + b * 16);
+        const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + pc * VPL);
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 q = p[k];
-            v[4 * k] = q.x;
-            v[4 * k + 1] = q.y;
-            v[4 * k + 2] = q.z;
-            v[4 * k + 3] = q.w;
+            v[2 * k] = bf16_bits_to_f32(w[k] & 0xffffu);
+            v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
         }
+    } else {
+        const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + pc * VPL);
+        v[0] = q.x;
+        v[1] = q.y;
+        v[2] = q.z;
+        v[3] = q.w;
     }
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    for (int k = 0; k < VPL; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    // across the block's lanes: quad_perm [1,0,3,2], then [2,3,0,1]
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, true)));
+    if constexpr (LPB == 4)
+        amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x4E, 0xF, 0xF, true)));
     const uint32_t sb = e4m3fn_rne_sat(__fdiv_rn(amax, 6.0f));
-    const float s = e4m3fn_to_f32(sb);
-    uint32_t lo = 0, hi = 0;
+    const E2m1Thresholds th = e2m1_thresholds(e4m3fn_to_f32(sb));
+    uint32_t word = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const uint32_t c = e2m1_code(fabsf(v[j]), s) | ((__float_as_uint(v[j]) >> 31) << 3);
-        if (j < 8)
-            lo |= c << (4 * j);
+    for (int k = 0; k < VPL; ++k) word |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * k);
+    if (live) {
+        if constexpr (BF16_IN)
+            *reinterpret_cast<uint32_t*>(a.codes + pc * (VPL / 2)) = word;
         else
-            hi |= c << (4 * (j - 8));
+            *reinterpret_cast<uint16_t*>(a.codes + pc * (VPL / 2)) = (uint16_t)word;
+        if (pc % LPB == 0) a.scales[pc / LPB] = (uint8_t)sb;
     }
-    *reinterpret_cast<uint2*>(a.codes + r * (a.cols / 2) + b * 8) = make_uint2(lo, hi);
-    a.scales[r * nb_row + b] = (uint8_t)sb;
 }
 
 // ---------------------------------------------------------------------------
