@@ -162,6 +162,13 @@ __device__ __forceinline__ float nvfp4_chunk_f32(const uint4 q, const float* h, 
     return p0 * s0 + p1 * s1;
 }
 
+// The nibbles in bits 3..0 and 19..16 of v (two's complement codes c) as
+// the bf16 pair 136 + c: the code's sign bit flipped gives the offset-binary
+// c + 8 under the exponent of 128, in one and-xor.
+__device__ __forceinline__ bf16x2 int4x2_bf16(uint32_t v) {
+    return as_bf16x2((v & 0x000F000Fu) ^ 0x43084308u);
+}
+
 // int4 (two's complement nibbles) . bf16 activations.  Each code is turned
 // into the bf16 number 136 + code (exact: an offset-binary nibble placed
 // under the exponent of 128), so a dot2 gives sum (code + 136) * x and the
@@ -169,13 +176,29 @@ __device__ __forceinline__ float nvfp4_chunk_f32(const uint4 q, const float* h, 
 // the unpacking produces: for dword d, (x0,x4), (x1,x5), (x2,x6), (x3,x7).
 __device__ __forceinline__ float int4_chunk_bf16(const uint4 q, const uint32_t* xq) {
     float p = 0.f;
-    const uint32_t v[4] = {q.x ^ 0x88888888u, q.y ^ 0x88888888u, q.z ^ 0x88888888u, q.w ^ 0x88888888u};
+    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-        p = dot2_bf16(as_bf16x2((v[d] & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 0]), p);
-        p = dot2_bf16(as_bf16x2(((v[d] >> 4) & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 1]), p);
-        p = dot2_bf16(as_bf16x2(((v[d] >> 8) & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 2]), p);
-        p = dot2_bf16(as_bf16x2(((v[d] >> 12) & 0x000F000Fu) | 0x43004300u), as_bf16x2(xq[4 * d + 3]), p);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) p = dot2_bf16(int4x2_bf16(v[d] >> (4 * s)), as_bf16x2(xq[4 * d + s]), p);
+    }
+    return p;
+}
+
+// The same weights against fp32 activations held as bf16 hi + lo halves
+// (hq, lq, in the unpacking order): each weight pair is unpacked once and
+// meets both halves, so the sum carries about 17 bits of each activation.
+__device__ __forceinline__ float int4_chunk_bf16_hl(const uint4 q, const uint32_t* hq, const uint32_t* lq) {
+    float p = 0.f;
+    const uint32_t v[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const bf16x2 w = int4x2_bf16(v[d] >> (4 * s));
+            p = dot2_bf16(w, as_bf16x2(hq[4 * d + s]), p);
+            p = dot2_bf16(w, as_bf16x2(lq[4 * d + s]), p);
+        }
     }
     return p;
 }

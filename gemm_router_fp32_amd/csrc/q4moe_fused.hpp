@@ -213,6 +213,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __shared__ int s_ids_all[kWaves][8];
     __shared__ float s_w_all[kWaves][8];
     __shared__ float s_h[2 * 4096];     // h of the (at most two, adjacent) slots this workgroup's down rows use
+    uint16_t* const s_h16 = reinterpret_cast<uint16_t*>(s_h);  // int4: bf16 hi halves, then lo halves
     __shared__ float s_hrow[kMaxWgUp];  // this workgroup's up results, before they are published
     __shared__ uint4 s_x[512];          // x (bf16, H <= 4096), read once per workgroup
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -519,7 +520,19 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
-                    s_h[threadIdx.x + 512 * m] = tag_value(v[m]);
+                    const int i = threadIdx.x + 512 * m;
+                    if constexpr (FMT == FMT_NVFP4) {
+                        s_h[i] = tag_value(v[m]);
+                    } else {
+                        // int4: h as bf16 hi + lo halves (about 17 bits),
+                        // each in the pair order of the nibble unpacking
+                        const float hv = tag_value(v[m]);
+                        const uint32_t hi = f32_to_bf16_rne(hv);
+                        const uint32_t lo = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
+                        const int pi = (i & ~7) | ((i & 3) << 1) | ((i >> 2) & 1);
+                        s_h16[pi] = (uint16_t)hi;
+                        s_h16[2 * 4096 + pi] = (uint16_t)lo;
+                    }
                     pend &= ~(1u << m);
                 }
             }
@@ -538,43 +551,75 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // sums the rows over the lanes together and publishes them with one
     // store.
     if (dwave) {
-        float hv[C2][32];
-        float hs[C2];
-#pragma unroll
-        for (int c = 0; c < C2; ++c) {
-            const int ch = min(lane * C2 + c, nchI - 1);
-            const float4* hp = reinterpret_cast<const float4*>(&s_h[(dslot - sl0) * a.I + ch * 32]);
-            hs[c] = 0.f;
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float4 v = hp[k];
-                hv[c][4 * k + 0] = v.x;
-                hv[c][4 * k + 1] = v.y;
-                hv[c][4 * k + 2] = v.z;
-                hv[c][4 * k + 3] = v.w;
-            }
-            if constexpr (FMT == FMT_INT4) {
-#pragma unroll
-                for (int j = 0; j < 32; ++j) hs[c] += hv[c][j];
-            }
-        }
         float zp[kDownRows];  // this lane's part of each row
-#pragma unroll
-        for (int p = 0; p < kDownRows; ++p) {
-            float zz = 0.f;
+        if constexpr (FMT == FMT_NVFP4) {
+            float hv[C2][32];
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
-                const bool chok = lane * C2 + c < nchI;
-                if constexpr (FMT == FMT_NVFP4) {
+                const int ch = min(lane * C2 + c, nchI - 1);
+                const float4* hp = reinterpret_cast<const float4*>(&s_h[(dslot - sl0) * a.I + ch * 32]);
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const float4 v = hp[k];
+                    hv[c][4 * k + 0] = v.x;
+                    hv[c][4 * k + 1] = v.y;
+                    hv[c][4 * k + 2] = v.z;
+                    hv[c][4 * k + 3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < kDownRows; ++p) {
+                float zz = 0.f;
+#pragma unroll
+                for (int c = 0; c < C2; ++c) {
+                    const bool chok = lane * C2 + c < nchI;
                     const f32x2 sp = e4m3fn_x2_f32(sd[p][c]);
                     const float s0 = chok ? sp[0] : 0.f, s1 = chok ? sp[1] : 0.f;
                     zz += nvfp4_chunk_f32(qd[p][c], hv[c], s0, s1);
-                } else {
-                    const float sg = chok ? bf16_bits_to_f32(sd[p][c]) : 0.f;
-                    zz = __builtin_fmaf(sg, int4_chunk_f32(qd[p][c], hv[c]) - 8.0f * hs[c], zz);
                 }
+                zp[p] = zz;
             }
-            zp[p] = zz;
+        } else {
+            // int4: a dot2 of the bf16 weights 136 + code with h's hi and
+            // lo halves; 136 * sum(h) is taken off once per chunk
+            uint32_t hq[C2][16], lq[C2][16];
+            float hs[C2];
+#pragma unroll
+            for (int c = 0; c < C2; ++c) {
+                const int ch = min(lane * C2 + c, nchI - 1);
+                const uint4* hp = reinterpret_cast<const uint4*>(&s_h16[(dslot - sl0) * a.I + ch * 32]);
+                const uint4* lp = reinterpret_cast<const uint4*>(&s_h16[2 * 4096 + (dslot - sl0) * a.I + ch * 32]);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint4 v = hp[k], w = lp[k];
+                    hq[c][4 * k + 0] = v.x;
+                    hq[c][4 * k + 1] = v.y;
+                    hq[c][4 * k + 2] = v.z;
+                    hq[c][4 * k + 3] = v.w;
+                    lq[c][4 * k + 0] = w.x;
+                    lq[c][4 * k + 1] = w.y;
+                    lq[c][4 * k + 2] = w.z;
+                    lq[c][4 * k + 3] = w.w;
+                }
+                float t = 0.f;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    t = dot2_bf16(as_bf16x2(hq[c][j]), as_bf16x2(0x3F803F80u), t);
+                    t = dot2_bf16(as_bf16x2(lq[c][j]), as_bf16x2(0x3F803F80u), t);
+                }
+                hs[c] = 136.0f * t;
+            }
+#pragma unroll
+            for (int p = 0; p < kDownRows; ++p) {
+                float zz = 0.f;
+#pragma unroll
+                for (int c = 0; c < C2; ++c) {
+                    const bool chok = lane * C2 + c < nchI;
+                    const float sg = chok ? bf16_bits_to_f32(sd[p][c]) : 0.f;
+                    zz = __builtin_fmaf(sg, int4_chunk_bf16_hl(qd[p][c], hq[c], lq[c]) - hs[c], zz);
+                }
+                zp[p] = zz;
+            }
         }
         // the eight row sums over the 64 lanes at once: lane l ends with the
         // sum of row rows8_label(l)
