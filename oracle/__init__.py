@@ -35,6 +35,13 @@ class _Bank(ctypes.Structure):
                 ("down_g", ctypes.c_void_p)]
 
 
+class _Shared(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("S", ctypes.c_int32),
+                ("up_codes", ctypes.c_void_p), ("down_codes", ctypes.c_void_p),
+                ("up_wscale", ctypes.c_float), ("up_iscale", ctypes.c_float),
+                ("down_wscale", ctypes.c_float), ("down_iscale", ctypes.c_float)]
+
+
 def lib():
     global _LIB
     if _LIB is None:
@@ -59,6 +66,11 @@ def lib():
         L.q4o_w4a4_down_combine.argtypes = [ctypes.POINTER(_Bank), i32, i32, p, p, p, p, p]
         L.q4o_w4a4_up.argtypes = [ctypes.POINTER(_Bank), i32, i32, p, p, p, p]
         L.q4o_gemv_nvfp4.argtypes = [i32, i32, p, p, f, i32, p, p, p, p]
+        L.q4o_fp8_code.restype = u32
+        L.q4o_fp8_code.argtypes = [f, f]
+        L.q4o_fp8_quant.argtypes = [i32, p, f, p]
+        L.q4o_fp8_gemv.argtypes = [i32, i32, p, p, f, f, p]
+        L.q4o_shared_fp8.argtypes = [ctypes.POINTER(_Shared), p, p, p, p, p, p]
         _LIB = L
     return _LIB
 
@@ -229,3 +241,49 @@ def gemv_nvfp4(codes, scales, g, x):
     lib().q4o_gemv_nvfp4(rows, cols, _p(codes), _p(scales), float(g), T, _p(x), _p(logits),
                          _p(am), _p(gap))
     return logits, am, gap
+
+
+# --- shared expert, FP8 per-tensor W8A8 ------------------------------------
+
+def fp8_code(v, s):
+    """E4M3FN code of fl32(v / s): nearest-even, saturating at 448."""
+    return lib().q4o_fp8_code(float(v), float(s))
+
+
+def fp8_quant(v, s):
+    v = _c(v, np.float32).reshape(-1)
+    out = np.zeros(v.size, np.uint8)
+    lib().q4o_fp8_quant(v.size, _p(v), float(s), _p(out))
+    return out
+
+
+def fp8_gemv(w, a, s_w, s_in):
+    """(sum_c e4m3(w[r, c]) e4m3(a[c])) * s_w * s_in for codes w [rows, cols], a [cols]."""
+    w = _c(w, np.uint8)
+    a = _c(a, np.uint8).reshape(-1)
+    rows, cols = w.shape
+    assert a.size == cols
+    out = np.zeros(rows, np.float64)
+    lib().q4o_fp8_gemv(rows, cols, _p(w), _p(a), float(s_w), float(s_in), _p(out))
+    return out
+
+
+def shared_fp8(sh, x):
+    """One token through the shared expert.  sh: dict with up_codes [S, H],
+    down_codes [H, S] (uint8 E4M3FN) and the four fp32 scales; x: bf16 bits
+    [H].  Returns dict xq, u, h32, hq, z."""
+    up = _c(sh["up_codes"], np.uint8)
+    dn = _c(sh["down_codes"], np.uint8)
+    S, H = up.shape
+    assert dn.shape == (H, S)
+    x = _c(x, np.uint16).reshape(-1)
+    assert x.size == H
+    d = _Shared(H, S, _p(up).value, _p(dn).value, float(sh["up_wscale"]), float(sh["up_iscale"]),
+                float(sh["down_wscale"]), float(sh["down_iscale"]))
+    xq = np.zeros(H, np.uint8)
+    u = np.zeros(S, np.float64)
+    h32 = np.zeros(S, np.float32)
+    hq = np.zeros(S, np.uint8)
+    z = np.zeros(H, np.float64)
+    lib().q4o_shared_fp8(ctypes.byref(d), _p(x), _p(xq), _p(u), _p(h32), _p(hq), _p(z))
+    return {"xq": xq, "u": u, "h32": h32, "hq": hq, "z": z}

@@ -429,3 +429,56 @@ int32_t q4o_threads(void) {
     return 1;
 #endif
 }
+
+/* ---- Shared expert, FP8 per-tensor W8A8 -------------------------------
+ * [W] Step 3 (shared experts go to FP8) and the precision table of [C]
+ * (shared experts: FP8 per-tensor W8A8).  Readings: weights are E4M3FN
+ * codes with one fp32 scale per tensor; each activation (x into up, h into
+ * down) is quantized with one static fp32 input scale per tensor, the
+ * calibrated value the recipe stores; code = E4M3FN nearest-even of
+ * fl32(v / s), saturating at 448, sign of v kept (finite v).  The expert MLP
+ * is the routed one, relu(up x)^2 then down, and its output joins y
+ * unweighted before the one bf16 rounding. */
+
+uint32_t q4o_fp8_code(float v, float s) {
+    float q = v / s; /* one fp32 division, rounded to nearest */
+    uint32_t sign = signbit(q) ? 0x80u : 0u;
+    return sign | q4o_e4m3fn_from(fabsf(q));
+}
+
+void q4o_fp8_quant(int32_t n, const float* v, float s, uint8_t* codes) {
+    for (int32_t i = 0; i < n; ++i) codes[i] = (uint8_t)q4o_fp8_code(v[i], s);
+}
+
+/* out[r] = (sum_c e4m3(w[r][c]) * e4m3(a[c])) * s_w * s_in in fp64.  Each
+ * product has at most 8 significant bits and is a multiple of 2^-18 below
+ * 2^18, so for up to 2^15 columns every partial sum is exact in fp64. */
+void q4o_fp8_gemv(int32_t rows, int32_t cols, const uint8_t* w, const uint8_t* a, float s_w,
+                  float s_in, double* out) {
+    double* av = (double*)malloc(sizeof(double) * (size_t)cols);
+    for (int32_t c = 0; c < cols; ++c) av[c] = q4o_e4m3fn(a[c]);
+#pragma omp parallel for schedule(static)
+    for (int32_t r = 0; r < rows; ++r) {
+        const uint8_t* wr = w + (size_t)r * cols;
+        double acc = 0.0;
+        for (int32_t c = 0; c < cols; ++c) acc += q4o_e4m3fn(wr[c]) * av[c];
+        out[r] = acc * (double)s_w * (double)s_in;
+    }
+    free(av);
+}
+
+void q4o_shared_fp8(const q4o_shared* sh, const uint16_t* x, uint8_t* xq, double* u, float* h32,
+                    uint8_t* hq, double* z) {
+    const int32_t H = sh->H, S = sh->S;
+    float* xf = (float*)malloc(sizeof(float) * (size_t)H);
+    for (int32_t k = 0; k < H; ++k) xf[k] = (float)q4o_bf16(x[k]);
+    q4o_fp8_quant(H, xf, sh->up_iscale, xq);
+    q4o_fp8_gemv(S, H, sh->up_codes, xq, sh->up_wscale, sh->up_iscale, u);
+    for (int32_t j = 0; j < S; ++j) {
+        double r = u[j] > 0.0 ? u[j] : 0.0;
+        h32[j] = (float)(r * r);
+    }
+    q4o_fp8_quant(S, h32, sh->down_iscale, hq);
+    q4o_fp8_gemv(H, S, sh->down_codes, hq, sh->down_wscale, sh->down_iscale, z);
+    free(xf);
+}

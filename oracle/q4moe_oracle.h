@@ -35,7 +35,11 @@
  *  - NVFP4 activation quantizer (W4A4): per 16-block, scale byte =
  *    E4M3FN round-to-nearest-even (saturating at 448) of fl32(amax / 6);
  *    code = nearest E2M1 magnitude of |v| / scale, ties to the even code,
- *    saturating at 6, sign bit = sign bit of v; scale 0 -> magnitude 0.
+ *    saturating at 6, sign bit = sign bit of v; scale 0 -> magnitude 0;
+ *  - shared expert (FP8 per-tensor W8A8): E4M3FN weights with an fp32 scale
+ *    per tensor, static fp32 input scales per tensor, activation code =
+ *    E4M3FN nearest-even of fl32(v / s) saturating at 448; relu^2 like the
+ *    routed experts; its output joins y with weight 1, before the rounding.
  */
 #ifndef Q4MOE_ORACLE_H
 #define Q4MOE_ORACLE_H
@@ -114,6 +118,30 @@ void q4o_w4a4_up(const q4o_bank* bank, int32_t T, int32_t k, const int32_t* ids,
 void q4o_gemv_nvfp4(int32_t rows, int32_t cols, const uint8_t* codes, const uint8_t* scales,
                     float g, int32_t T, const uint16_t* x, double* logits, int32_t* argmax,
                     double* gap);
+
+/* Shared expert, FP8 per-tensor W8A8 ([W] Step 3; [C] precision table).
+ * up_codes E4M3FN [S][H], down_codes E4M3FN [H][S]; per-tensor fp32 weight
+ * scales and static fp32 input scales (x into up, h into down). */
+typedef struct {
+    int32_t H, S;
+    const uint8_t* up_codes;
+    const uint8_t* down_codes;
+    float up_wscale, up_iscale, down_wscale, down_iscale;
+} q4o_shared;
+
+/* E4M3FN code of fl32(v / s): nearest-even, saturating at 448, sign kept. */
+uint32_t q4o_fp8_code(float v, float s);
+void q4o_fp8_quant(int32_t n, const float* v, float s, uint8_t* codes);
+
+/* out[r] = (sum_c e4m3(w[r][c]) e4m3(a[c])) * s_w * s_in, fp64 (exact sums). */
+void q4o_fp8_gemv(int32_t rows, int32_t cols, const uint8_t* w, const uint8_t* a, float s_w,
+                  float s_in, double* out);
+
+/* The whole shared expert for one token: xq [H] codes; u [S] fp64;
+ * h32 [S] = fl32(relu(u)^2), the h quantizer's input; hq [S] codes;
+ * z [H] fp64, the expert's output (joins y with weight 1). */
+void q4o_shared_fp8(const q4o_shared* sh, const uint16_t* x, uint8_t* xq, double* u, float* h32,
+                    uint8_t* hq, double* z);
 
 /* bf16 bit pattern nearest to v (RNE), for chaining an oracle output. */
 uint32_t q4o_bf16_from(double v);

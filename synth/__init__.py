@@ -11,7 +11,9 @@ with the shapes and value distributions of the workloads:
 * NVFP4 matrices: uniform random nibble codes (all 16, including -0) and
   E4M3FN block scales uniform over the seven powers of two 2^-4 .. 2^2;
 * int4 group-64 matrices: uniform nibble codes (two's complement -8..7) and
-  bf16 group scales |N(0, 0.01^2)| + 1e-3.
+  bf16 group scales |N(0, 0.01^2)| + 1e-3;
+* FP8 shared expert: E4M3FN weight bytes uniform over FP8_WEIGHT_BYTES and
+  fixed power-of-two per-tensor scales (FP8_SHARED_SCALES).
 
 Expert weights are the logical row-major layout: element (r, 2j) is the low
 nibble of byte r*cols/2 + j, scale (r, b) is entry r*(cols/block) + b.
@@ -29,6 +31,7 @@ _LIB = None
 
 # Stream identifiers (the third element of a key tuple).
 S_X, S_WG, S_BIAS, S_UP_CODES, S_UP_SCALES, S_DN_CODES, S_DN_SCALES, S_LM_CODES, S_LM_SCALES = range(1, 10)
+S_SH_UP, S_SH_DN = 10, 11
 # Workload families (the first element of a key tuple).  One-token and
 # four-token NVFP4 decode and the 23-layer NVFP4 stack share a family, so
 # layer 0 of the stack is the one-layer workload.
@@ -36,6 +39,15 @@ FAM_NVFP4, FAM_INT4, FAM_W4A4 = 0, 1, 2
 
 # E4M3FN bytes of 2^k for k = -4..2 (exponent field k+7, mantissa 0).
 NVFP4_SCALE_BYTES = np.array([(k + 7) << 3 for k in range(-4, 3)], dtype=np.uint8)
+
+# FP8 shared-expert weight bytes: both signs, exponent fields 1..10, every
+# mantissa (magnitudes 2^-6 .. 15), so no NaN and no subnormal.
+FP8_WEIGHT_BYTES = np.array([(sg << 7) | (e << 3) | m for sg in (0, 1) for e in range(1, 11) for m in range(8)],
+                            dtype=np.uint8)
+# Per-tensor scales of the synthetic shared expert (the static input scales
+# keep x / s and h / s inside the E4M3FN range for these distributions).
+FP8_SHARED_SCALES = {"up_wscale": 2.0 ** -8, "up_iscale": 2.0 ** -6,
+                     "down_wscale": 2.0 ** -8, "down_iscale": 2.0 ** -5}
 
 NTHREADS = max(1, min(16, os.cpu_count() or 1))
 _CHUNK = 1 << 20
@@ -213,3 +225,14 @@ def lm_head(seed, fam, layer, V, H, gscale=1.0 / 64):
     with ThreadPoolExecutor(NTHREADS) as pool:
         codes, scales = nvfp4_matrix(seed, fam, layer, S_LM_CODES, S_LM_SCALES, 0, V, H, pool)
     return codes, scales, np.float32(gscale)
+
+
+def shared_fp8(seed, fam, layer, H, S):
+    """FP8 shared expert: up_codes [S, H], down_codes [H, S] (E4M3FN bytes)
+    and its four per-tensor scales, as a dict."""
+    with ThreadPoolExecutor(NTHREADS) as pool:
+        up = choice_bytes(key(seed, fam, layer, S_SH_UP), S * H, FP8_WEIGHT_BYTES, pool)
+        dn = choice_bytes(key(seed, fam, layer, S_SH_DN), H * S, FP8_WEIGHT_BYTES, pool)
+    sh = {"up_codes": up.reshape(S, H), "down_codes": dn.reshape(H, S)}
+    sh.update({k: np.float32(v) for k, v in FP8_SHARED_SCALES.items()})
+    return sh
