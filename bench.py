@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 sys.path.insert(0, os.path.join(ROOT, "tests"))
 
 H, I, E, K, LAYERS, V = 2688, 1856, 128, 6, 23, 131072
+S_SHARED = 3712  # shared expert intermediate size (2 x 1856; derived from the checkpoint table's shared-expert bytes)
 SEED = 20261202
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0   # dense fp16/bf16 MFMA
@@ -115,7 +116,9 @@ class Evictor:
         self.buf.sum()
 
 
-def build_stack(torch, g, synth, fmt):
+def build_stack(torch, g, synth, fmt, shared=False):
+    """The 23 layers, resident; with `shared`, each layer also carries the
+    FP8 shared expert [S_SHARED x H] and runs the shared decode entry."""
     from gpu_util import dev
     fam = synth.FAM_NVFP4 if fmt == "nvfp4" else synth.FAM_INT4
     layers, buf = [], None
@@ -131,10 +134,24 @@ def build_stack(torch, g, synth, fmt):
         else:
             ex = g.Experts(g.INT4_G64, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"])
         r = g.Router(dev(wg), dev(b), K)
-        ws = g.workspace(g.q4moe_w4a16_decode_ws_bytes(r, ex, 1))
-        layers.append(dict(ex=ex, r=r, x=dev(x), y=torch.empty((1, H), dtype=torch.int16, device="cuda"), ws=ws))
-    log(f"{fmt} stack resident ({LAYERS} layers)")
+        L = dict(ex=ex, r=r, x=dev(x), y=torch.empty((1, H), dtype=torch.int16, device="cuda"))
+        if shared:
+            sh = synth.shared_fp8(SEED, fam, li, H, S_SHARED)
+            L["sh"] = g.SharedFp8(dev(sh["up_codes"]), dev(sh["down_codes"]), sh["up_wscale"], sh["up_iscale"],
+                                  sh["down_wscale"], sh["down_iscale"])
+            L["ws"] = g.workspace(g.q4moe_w4a16_decode_shared_ws_bytes(r, ex, L["sh"], 1))
+        else:
+            L["ws"] = g.workspace(g.q4moe_w4a16_decode_ws_bytes(r, ex, 1))
+        layers.append(L)
+    log(f"{fmt} stack{' + shared expert' if shared else ''} resident ({LAYERS} layers)")
     return layers
+
+
+def decode_call(g, L):
+    if "sh" in L:
+        g.q4moe_w4a16_decode_shared(L["r"], L["ex"], L["sh"], L["x"], L["y"], ws=L["ws"])
+    else:
+        g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
 
 
 def time_stack(torch, g, layers, steps, warmup):
@@ -142,7 +159,7 @@ def time_stack(torch, g, layers, steps, warmup):
 
     def step():
         for L in layers:
-            g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
+            decode_call(g, L)
 
     for _ in range(3):
         step()
@@ -175,7 +192,7 @@ def time_stack(torch, g, layers, steps, warmup):
     for rep in range(4):
         for L in layers:
             e0.record()
-            g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
+            decode_call(g, L)
             e1.record()
             e1.synchronize()
             durs.append(e0.elapsed_time(e1))
@@ -321,6 +338,17 @@ def main():
                                "bytes_per_layer": b4, "flags": f4}
         log(f"int4 stack: {extra['int4_stack']}")
         del int4
+        torch.cuda.empty_cache()
+        shl = build_stack(torch, g, synth, "nvfp4", shared=True)
+        mss, mks, fs, pers = time_stack(torch, g, shl, args.steps, args.warmup)
+        bs = layer_bytes() + 2 * H * S_SHARED
+        extra["shared_stack"] = {"us_per_layer": round(1000.0 * mss / LAYERS, 3),
+                                 "hbm_gbps": round(bs / (mss / LAYERS * 1e-3) / 1e9, 1),
+                                 "tokens_per_s": round(1000.0 / mss, 1), "single_launch_us": round(mks * 1e3, 3),
+                                 "us_per_layer_spread": spread(pers / LAYERS),
+                                 "bytes_per_layer": bs, "shared_inter": S_SHARED, "flags": fs}
+        log(f"nvfp4 + fp8 shared expert stack: {extra['shared_stack']}")
+        del shl
         torch.cuda.empty_cache()
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
 

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -110,10 +111,11 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, h, y32, zw, total;
+    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, total;
 };
 
-DecodeWs decode_ws(int E, int H, int I, int K, int T) {
+// S: the shared expert's intermediate size (0: no shared expert).
+DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
     size_t o = l.r.total;
@@ -121,8 +123,16 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T) {
     o += up_to((size_t)kReplicas * E * 8);
     l.h_tag = o;   // (h, epoch) pairs, kReplicas copies
     o += up_to((size_t)kReplicas * K * I * 8);
-    l.z_tag = o;   // (w * g * z, epoch) pairs
-    o += up_to((size_t)K * H * 8);
+    l.z_tag = o;   // (w * g * z, epoch) pairs; slot K: the shared expert
+    o += up_to((size_t)(K + (S > 0 ? 1 : 0)) * H * 8);
+    l.hq_tag = o;  // shared expert: (four h codes, epoch), kReplicas copies
+    o += up_to((size_t)kReplicas * (S / 4) * 8);
+    l.sh_xq = o;   // shared expert taps
+    o += up_to(S > 0 ? (size_t)H : 0);
+    l.sh_h = o;
+    o += up_to((size_t)S * 4);
+    l.sh_hq = o;
+    o += up_to((size_t)S);
     l.h = o;       // h tap
     o += up_to((size_t)T * K * I * 4);
     l.y32 = o;
@@ -149,28 +159,28 @@ int persistent_grid(K kernel, int block, int want) {
 // every workgroup is resident and every wait can be satisfied), cached per
 // device and kernel variant.
 constexpr int kMaxDevices = 64;
-constexpr int kFusedVariants = 16;
+constexpr int kFusedVariants = 32;
 int g_fused_grid[kMaxDevices][kFusedVariants];
 
-template <int FMT, int C, int C2>
+template <int FMT, int C, int C2, bool SH>
 int fused_grid(int dev, int variant) {
     if (dev < 0 || dev >= kMaxDevices) return 0;
     int& cached = g_fused_grid[dev][variant];
     if (cached != 0) return cached;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<FMT, C, C2>, 64 * kWaves, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<FMT, C, C2, SH>, 64 * kWaves, 0) !=
         hipSuccess)
         return 0;
     cached = cus * (per_cu < 1 ? 0 : 1);
     return cached;
 }
 
-template <int FMT, int C, int C2>
+template <int FMT, int C, int C2, bool SH>
 q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
-    const int grid = fused_grid<FMT, C, C2>(dev, variant);
+    const int grid = fused_grid<FMT, C, C2, SH>(dev, variant);
     // The router needs one workgroup per expert; every wave's up rows must fit
     // in kMaxUp passes (all loads in flight at once), a workgroup stages at
     // most kMaxWgUp up rows, every down unit (kDownRows rows of one slot)
@@ -182,23 +192,27 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw ||
         dpu < kWaves - 1)
         return Q4MOE_EUNSUPPORTED;
-    hipLaunchKernelGGL((k_decode_fused<FMT, C, C2>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+    // shared expert: at most 4 h-code quads (16 up rows) per workgroup and
+    // two down rows per wave
+    if (SH && (a.S / 4 > 4LL * grid || a.H > 2 * nw)) return Q4MOE_EUNSUPPORTED;
+    hipLaunchKernelGGL((k_decode_fused<FMT, C, C2, SH>), dim3(grid), dim3(64 * kWaves), 0, s, a);
     return launched("fused decode");
 }
 
-template <int FMT>
+template <int FMT, bool SH = false>
 q4moe_status launch_fused(const FusedArgs& a, hipStream_t s) {
     const int C = (a.H / 32 + 31) / 32, C2 = (a.I / 32 + 63) / 64;
     const int v = (C - 1) * 2 + (C2 - 1);
+    const int slot = v + (SH ? 8 : 0);  // grid cache entry
     switch (v) {
-        case 0: return launch_fused_v<FMT, 1, 1>(a, s, v);
-        case 1: return launch_fused_v<FMT, 1, 2>(a, s, v);
-        case 2: return launch_fused_v<FMT, 2, 1>(a, s, v);
-        case 3: return launch_fused_v<FMT, 2, 2>(a, s, v);
-        case 4: return launch_fused_v<FMT, 3, 1>(a, s, v);
-        case 5: return launch_fused_v<FMT, 3, 2>(a, s, v);
-        case 6: return launch_fused_v<FMT, 4, 1>(a, s, v);
-        case 7: return launch_fused_v<FMT, 4, 2>(a, s, v);
+        case 0: return launch_fused_v<FMT, 1, 1, SH>(a, s, slot);
+        case 1: return launch_fused_v<FMT, 1, 2, SH>(a, s, slot);
+        case 2: return launch_fused_v<FMT, 2, 1, SH>(a, s, slot);
+        case 3: return launch_fused_v<FMT, 2, 2, SH>(a, s, slot);
+        case 4: return launch_fused_v<FMT, 3, 1, SH>(a, s, slot);
+        case 5: return launch_fused_v<FMT, 3, 2, SH>(a, s, slot);
+        case 6: return launch_fused_v<FMT, 4, 1, SH>(a, s, slot);
+        case 7: return launch_fused_v<FMT, 4, 2, SH>(a, s, slot);
     }
     return Q4MOE_EUNSUPPORTED;
 }
@@ -481,17 +495,37 @@ q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts*
     return Q4MOE_OK;
 }
 
-q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
-                                int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
-                                size_t ws_bytes, void* stream) {
+namespace {
+
+q4moe_status check_shared(const q4moe_shared_fp8* sh, const q4moe_experts* ex, int32_t n_tok) {
+    if (!sh) return fail(Q4MOE_EINVAL, "shared expert descriptor is NULL");
+    if (sh->hidden != ex->hidden)
+        return fail(Q4MOE_EINVAL, "shared expert hidden %d differs from the experts' %d", sh->hidden, ex->hidden);
+    if (sh->inter < 64 || sh->inter % 64 != 0 || sh->inter > kMaxDim)
+        return fail(Q4MOE_EINVAL, "shared expert inter %d must be a multiple of 64 in [64, %d]", sh->inter, kMaxDim);
+    if (!sh->up_codes || !sh->down_codes) return fail(Q4MOE_EINVAL, "shared expert codes are NULL");
+    if (!aligned(sh->up_codes, 16) || !aligned(sh->down_codes, 16))
+        return fail(Q4MOE_EALIGN, "shared expert codes not 16-byte aligned");
+    const float sc[4] = {sh->up_wscale, sh->up_iscale, sh->down_wscale, sh->down_iscale};
+    for (float v : sc)
+        if (!std::isfinite(v) || v == 0.0f) return fail(Q4MOE_EINVAL, "shared expert scales must be finite and non-zero");
+    if (ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs with NVFP4 routed experts");
+    if (n_tok != 1) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs for one token (n_tok = %d)", n_tok);
+    return Q4MOE_OK;
+}
+
+q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
+                         const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w,
+                         void* ws, size_t ws_bytes, void* stream) {
     q4moe_status st = check_router(r);
     if (st != Q4MOE_OK) return st;
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    if (sh && (st = check_shared(sh, ex, n_tok)) != Q4MOE_OK) return st;
     if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
     if ((ids && !aligned(ids, 4)) || (w && !aligned(w, 4))) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok);
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh ? sh->inter : 0);
     if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
     if ((st = device_ready()) != Q4MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
@@ -522,6 +556,29 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
         f.w = at<float>(ws, l.r.w);
         f.h = at<float>(ws, l.h);
         f.y32 = at<float>(ws, l.y32);
+        f.S = 0;
+        f.shu = f.shd = nullptr;
+        f.su_w = f.su_in = f.sd_w = f.sd_in = 1.0f;
+        f.hq_tag = nullptr;
+        f.sh_xq = f.sh_hq = nullptr;
+        f.sh_h = nullptr;
+        if (sh) {
+            f.S = sh->inter;
+            f.shu = sh->up_codes;
+            f.shd = sh->down_codes;
+            f.su_w = sh->up_wscale;
+            f.su_in = sh->up_iscale;
+            f.sd_w = sh->down_wscale;
+            f.sd_in = sh->down_iscale;
+            f.hq_tag = at<unsigned long long>(ws, l.hq_tag);
+            f.sh_xq = at<uint8_t>(ws, l.sh_xq);
+            f.sh_h = at<float>(ws, l.sh_h);
+            f.sh_hq = at<uint8_t>(ws, l.sh_hq);
+            st = launch_fused<FMT_NVFP4, true>(f, s);
+            if (st == Q4MOE_EUNSUPPORTED)
+                return fail(st, "the shared expert's single launch does not fit this device and shape");
+            return st;
+        }
         st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
         if (st != Q4MOE_EUNSUPPORTED) return st;
     }
@@ -577,6 +634,40 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
     }
     if ((st = launch_up<FMT_INT4>(a, s)) != Q4MOE_OK) return st;
     return launch_down<FMT_INT4>(a, s);
+}
+
+}  // namespace
+
+q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                                int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
+                                size_t ws_bytes, void* stream) {
+    return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
+size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
+                                          const q4moe_shared_fp8* sh, int32_t n_tok) {
+    if (!r || !ex || !sh || n_tok < 1) return 0;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter).total;
+}
+
+q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_experts* ex,
+                                       const q4moe_shared_fp8* sh, const uint16_t* x_bf16, int32_t n_tok,
+                                       uint16_t* y_bf16, int32_t* ids, float* w, void* ws, size_t ws_bytes,
+                                       void* stream) {
+    if (!sh) return fail(Q4MOE_EINVAL, "shared expert descriptor is NULL");
+    return decode_impl(r, ex, sh, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
+q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                            const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_shared_taps* out) {
+    if (!r || !ex || !sh || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter);
+    out->y32 = l.y32;
+    out->h = l.h;
+    out->xq = l.sh_xq;
+    out->sh_h32 = l.sh_h;
+    out->sh_hq = l.sh_hq;
+    return Q4MOE_OK;
 }
 
 // --- W4A4 grouped -----------------------------------------------------------

@@ -29,6 +29,25 @@ __device__ __forceinline__ float e4m3fn_to_f32(uint32_t b) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b & 0xffu, 1.0f, false)[0];
 }
 
+// E4M3FN byte nearest (ties to even) to a finite d >= 0, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3fn_rne_sat(float d) {
+    if (!(d < 448.0f)) return 0x7Eu;  // [448, inf) and NaN
+    if (d < 0.015625f) {              // below 2^-6: subnormal steps of 2^-9
+        return (uint32_t)__builtin_rintf(d * 512.0f);  // exact scaling; 8 -> 0x08 = 2^-6
+    }
+    const uint32_t u = __float_as_uint(d);
+    int e = (int)(u >> 23) - 127;  // -6 .. 8
+    uint32_t m = (u >> 20) & 7u;
+    const uint32_t rem = u & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    if (m == 8u) {
+        m = 0u;
+        ++e;
+    }
+    const uint32_t b = ((uint32_t)(e + 7) << 3) | m;
+    return b > 0x7Eu ? 0x7Eu : b;
+}
+
 // Bytes 0 and 1 of v (two E4M3FN scales) -> fp32 pair, exact.
 __device__ __forceinline__ f32x2 e4m3fn_x2_f32(uint32_t v) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, false);

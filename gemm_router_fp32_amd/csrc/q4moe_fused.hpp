@@ -87,6 +87,17 @@ struct FusedArgs {
     float* w;                     // [K]    tap
     float* h;                     // [K][I] tap
     float* y32;                   // [H]
+    // FP8 per-tensor W8A8 shared expert (the SH variants): up [S][H] and
+    // down [H][S] E4M3FN codes, per-tensor weight scales and static input
+    // scales; its output z is slot K of z_tag.
+    int S;
+    const uint8_t* shu;
+    const uint8_t* shd;
+    float su_w, su_in, sd_w, sd_in;
+    unsigned long long* hq_tag;   // [kReplicas][S/4] (four h codes, epoch)
+    uint8_t* sh_xq;               // [H] tap: x codes
+    float* sh_h;                  // [S] tap: relu(u)^2 before quantization
+    uint8_t* sh_hq;               // [S] tap: h codes
 };
 
 __device__ __forceinline__ unsigned long long tagged(float v, uint32_t ep) {
@@ -206,7 +217,35 @@ __device__ __forceinline__ int share_lo(int total, int w, int n) {
     return (int)(((uint32_t)w * (uint32_t)total) / (uint32_t)n);
 }
 
-template <int FMT, int C, int C2>
+// E4M3FN code of fl32(v / s) with v's sign (finite v): the FP8 activation
+// quantizer of the shared expert.
+__device__ __forceinline__ uint32_t fp8_act_code(float v, float s) {
+    const float q = __fdiv_rn(v, s);
+    return ((__float_as_uint(q) >> 24) & 0x80u) | e4m3fn_rne_sat(fabsf(q));
+}
+
+// Sixteen E4M3FN weights . sixteen bf16 activations (pairs in natural
+// order): every fp8 value is exact in bf16, so each product is exact.
+__device__ __forceinline__ float fp8_chunk_bf16(const uint4 q, const uint4 x0, const uint4 x1) {
+    float p = 0.f;
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false), as_bf16x2(x0.x), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true), as_bf16x2(x0.y), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false), as_bf16x2(x0.z), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true), as_bf16x2(x0.w), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.z, 1.0f, false), as_bf16x2(x1.x), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.z, 1.0f, true), as_bf16x2(x1.y), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.w, 1.0f, false), as_bf16x2(x1.z), p);
+    p = dot2_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.w, 1.0f, true), as_bf16x2(x1.w), p);
+    return p;
+}
+
+// Four E4M3FN codes (one dword) -> four bf16 (exact), as two dwords.
+__device__ __forceinline__ uint2 fp8x4_bf16(uint32_t v) {
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true)));
+}
+
+template <int FMT, int C, int C2, bool SH>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __shared__ float s_part[kWaves];
     __shared__ float s_keys[256], s_scores[256];
@@ -216,6 +255,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     uint16_t* const s_h16 = reinterpret_cast<uint16_t*>(s_h);  // int4: bf16 hi halves, then lo halves
     __shared__ float s_hrow[kMaxWgUp];  // this workgroup's up results, before they are published
     __shared__ uint4 s_x[512];          // x (bf16, H <= 4096), read once per workgroup
+    // shared expert: x and h codes decoded to bf16 (natural order), and this
+    // workgroup's (at most 16) h codes before they are published
+    __shared__ uint32_t s_xb[SH ? 2048 : 1], s_shb[SH ? 2048 : 1], s_shq[SH ? 4 : 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int seg = lane >> 5, li = lane & 31;
     const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
@@ -256,6 +298,40 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 
     // x into LDS once per workgroup (the up GEMV reads it from there)
     if ((int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+
+    // Shared expert: its weights do not depend on the routing, so their
+    // loads leave now and stream while the router runs.  Workgroup b takes
+    // the up rows of h-code quads [sq0, sq1) (at most 16 rows: one per
+    // 32-lane segment, lane li reading chunks li + 32 c), and wave gw the
+    // (at most two) down rows [sd0, sd1), lane l reading chunks l + 64 c.
+    // Reads past a row's end are clamped into it and masked at use.
+    constexpr int CS = SH ? 2 * C : 1;  // H / 16 <= 32 * CS
+    constexpr int CD = SH ? 4 : 1;      // S / 16 <= 64 * CD
+    uint4 qsu[CS], qsd[2][CD];
+    int sq0 = 0, sq1 = 0, shr = 0, sd0 = 0, sd1 = 0;
+    if constexpr (SH) {
+        const int nq = a.S / 4;
+        sq0 = share_lo(nq, blockIdx.x, gridDim.x);
+        sq1 = share_lo(nq, blockIdx.x + 1, gridDim.x);
+        shr = 4 * sq0 + 2 * wave + seg;
+        const uint32_t rb = (uint32_t)(shr < 4 * sq1 ? shr : 0) * (uint32_t)a.H;
+#pragma unroll
+        for (int c = 0; c < CS; ++c) {
+            const int ch = min(li + 32 * c, a.H / 16 - 1);
+            qsu[c] = ldg16_stream(a.shu + (rb + (uint32_t)ch * 16u));
+        }
+        sd0 = share_lo(a.H, gw, NW);
+        sd1 = share_lo(a.H, gw + 1, NW);
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t rb2 = (uint32_t)min(sd0 + p, a.H - 1) * (uint32_t)a.S;
+#pragma unroll
+            for (int c = 0; c < CD; ++c) {
+                const int ch = min(lane + 64 * c, a.S / 16 - 1);
+                qsd[p][c] = ldg16_stream(a.shd + (rb2 + (uint32_t)ch * 16u));
+            }
+        }
+    }
     compiler_fence();  // keep every load above in the entry block
 
     // ---- R: workgroup e computes router logit e; its waves split the row
@@ -332,6 +408,24 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
             vb = get_tag(src);
         }
+    } else if constexpr (SH) {
+        // the waves that do not poll quantize x for the shared expert into
+        // LDS (eight values per thread), as bf16 of the E4M3FN codes
+        const int npw = (a.E + 63) / 64;
+        const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
+        for (int t = iw * 64 + lane; t < a.H / 8; t += nidle * 64) {
+            const uint4 v = *reinterpret_cast<const uint4*>(a.x + 8 * t);
+            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+            uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t bits = (j & 1) ? in[j >> 1] >> 16 : in[j >> 1] & 0xffffu;
+                cw[j >> 2] |= fp8_act_code(bf16_bits_to_f32(bits), a.su_in) << (8 * (j & 3));
+            }
+            const uint2 b0 = fp8x4_bf16(cw[0]), b1 = fp8x4_bf16(cw[1]);
+            *reinterpret_cast<uint4*>(&s_xb[4 * t]) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+            if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
+        }
     }
     __syncthreads();
     Q4MOE_PHASE(2);
@@ -396,6 +490,29 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     compiler_fence();
+
+    // ---- shared expert up: u = (W x) * s_w * s_in for this segment's row
+    // (its weights arrived during the routing), h = relu(u)^2, and the h
+    // code into LDS for the publish
+    if constexpr (SH) {
+        const int nck = a.H / 16;
+        float acc = 0.f;
+#pragma unroll
+        for (int c = 0; c < CS; ++c) {
+            const int chr = li + 32 * c, ch = min(chr, nck - 1);
+            const uint4* xp = reinterpret_cast<const uint4*>(&s_xb[8 * ch]);
+            const float p = fp8_chunk_bf16(qsu[c], xp[0], xp[1]);
+            acc += chr < nck ? p : 0.f;
+        }
+        acc = seg_sum_last<32>(acc);
+        if (li == 31 && shr < 4 * sq1) {
+            const float r = fmaxf(acc * (a.su_w * a.su_in), 0.f), h = r * r;
+            const uint32_t code = fp8_act_code(h, a.sd_in);
+            reinterpret_cast<uint8_t*>(s_shq)[shr - 4 * sq0] = (uint8_t)code;
+            a.sh_h[shr] = h;
+            a.sh_hq[shr] = (uint8_t)code;
+        }
+    }
 
     // activations of this lane's up chunks, from LDS
     uint32_t xa[C][16];
@@ -503,6 +620,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.h_tag + ((size_t)rp * a.K + slot) * a.I + r, v, ep);
             a.h[(size_t)slot * a.I + r] = v;
         }
+        if constexpr (SH) {  // the shared expert's h codes, four per value
+            if (j < sq1 - sq0) {
+                const float v = __uint_as_float(s_shq[j]);
+#pragma unroll
+                for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.hq_tag + (size_t)rp * (a.S / 4) + sq0 + j, v, ep);
+            }
+        }
     }
     {
         // the slots sl0 .. sl1 are adjacent in the [K][I] layout, so their h
@@ -513,10 +637,30 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             if ((int)threadIdx.x + 512 * m < nh) pend |= 1u << m;
+        // shared expert: thread t also polls h-code quads t and t + 512
+        const unsigned long long* srcq = a.hq_tag + (size_t)rep * (a.S / 4);
+        if constexpr (SH) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+                if ((int)threadIdx.x + 512 * m < a.S / 4) pend |= 1u << (16 + m);
+        }
         for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
-            unsigned long long v[16];
+            unsigned long long v[16], vq[2];
 #pragma unroll
             for (int m = 0; m < 16; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + threadIdx.x + 512 * m) : 0ull;
+            if constexpr (SH) {
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    vq[m] = (pend >> (16 + m)) & 1u ? get_tag(srcq + threadIdx.x + 512 * m) : 0ull;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    if (((pend >> (16 + m)) & 1u) && tag_is(vq[m], ep)) {
+                        const int q = threadIdx.x + 512 * m;
+                        *reinterpret_cast<uint2*>(&s_shb[2 * q]) = fp8x4_bf16((uint32_t)vq[m]);
+                        pend &= ~(1u << (16 + m));
+                    }
+                }
+            }
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
@@ -628,6 +772,28 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         const float wg = wsel[dslot] * gdn;
         if ((lane & 7) == 7 && drow0 + rl < a.H) put_tag(a.z_tag + (uint32_t)(dslot * a.H + drow0 + rl), wg * zs, ep);
     }
+    // ---- shared expert down: z = (W h) * s_w * s_in for the wave's (at
+    // most two) rows, published as slot K
+    if constexpr (SH) {
+        const int nck2 = a.S / 16;
+        float zsh[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < CD; ++c) {
+                const int chr = lane + 64 * c, ch = min(chr, nck2 - 1);
+                const uint4* hp = reinterpret_cast<const uint4*>(&s_shb[8 * ch]);
+                const float q = fp8_chunk_bf16(qsd[p][c], hp[0], hp[1]);
+                acc += chr < nck2 ? q : 0.f;
+            }
+            zsh[p] = seg_sum_last<64>(acc);
+        }
+        const float sc = a.sd_w * a.sd_in;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            if (lane == 63 && sd0 + p < sd1) put_tag(a.z_tag + (uint32_t)(a.K * a.H + sd0 + p), zsh[p] * sc, ep);
+    }
     Q4MOE_PHASE(6);
 
     // ---- C: block b of 64 rows is combined by workgroup b * grid / nblocks
@@ -635,19 +801,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     for (int b = wave; b < nb; b += kWaves) {
         if ((int)((long long)b * gridDim.x / nb) != (int)blockIdx.x) continue;
         const int r = b * kRowBlock + lane;
-        float part[8];
+        constexpr int NS = SH ? 9 : 8;       // routed slots, then the shared expert
+        const int ns = a.K + (SH ? 1 : 0);
+        float part[NS];
         uint32_t pend = 0;
-        for (int s2 = 0; s2 < a.K; ++s2) pend |= 1u << s2;
+        for (int s2 = 0; s2 < ns; ++s2) pend |= 1u << s2;
         if (r >= a.H) pend = 0;
         // every load of a poll leaves before any is waited for (rows and
         // slots clamped into the array, so the load count is fixed)
         const unsigned long long* zr = a.z_tag + min(r, a.H - 1);
         for (uint32_t polls = 0;; ++polls) {
-            unsigned long long v[8];
+            unsigned long long v[NS];
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) v[s2] = get_tag(zr + (size_t)min(s2, a.K - 1) * a.H);
+            for (int s2 = 0; s2 < NS; ++s2) v[s2] = get_tag(zr + (size_t)min(s2, ns - 1) * a.H);
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2) {
+            for (int s2 = 0; s2 < NS; ++s2) {
                 if (((pend >> s2) & 1u) && tag_is(v[s2], ep)) {
                     part[s2] = tag_value(v[s2]);
                     pend &= ~(1u << s2);
@@ -663,8 +831,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         if (r < a.H) {
             float yv = 0.f;
 #pragma unroll
-            for (int s2 = 0; s2 < 8; ++s2)
-                if (s2 < a.K) yv += (pend >> s2) & 1u ? 0.f : part[s2];
+            for (int s2 = 0; s2 < NS; ++s2)
+                if (s2 < ns) yv += (pend >> s2) & 1u ? 0.f : part[s2];
             a.y32[r] = yv;
             a.y[r] = (uint16_t)f32_to_bf16_rne(yv);
         }

@@ -168,25 +168,6 @@ __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a) {
 // of v kept; scale 0 gives magnitude 0.
 // ---------------------------------------------------------------------------
 
-// E4M3FN byte nearest (ties to even) to a finite d >= 0, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3fn_rne_sat(float d) {
-    if (!(d < 448.0f)) return 0x7Eu;  // [448, inf) and NaN
-    if (d < 0.015625f) {              // below 2^-6: subnormal steps of 2^-9
-        return (uint32_t)__builtin_rintf(d * 512.0f);  // exact scaling; 8 -> 0x08 = 2^-6
-    }
-    const uint32_t u = __float_as_uint(d);
-    int e = (int)(u >> 23) - 127;  // -6 .. 8
-    uint32_t m = (u >> 20) & 7u;
-    const uint32_t rem = u & 0xFFFFFu;
-    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
-    if (m == 8u) {
-        m = 0u;
-        ++e;
-    }
-    const uint32_t b = ((uint32_t)(e + 7) << 3) | m;
-    return b > 0x7Eu ? 0x7Eu : b;
-}
-
 // The E2M1 code of |v| on the grid scaled by s is the number of midpoints
 // t_j = mids_j * s (exact: mids have at most 3 significant bits) that |v|
 // passes, a tie going to the even code: up at an odd j, down at an even j.

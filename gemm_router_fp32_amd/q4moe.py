@@ -40,6 +40,16 @@ class W4A4Taps(ctypes.Structure):
                 ("h32", _sz), ("hq_codes", _sz), ("hq_scales", _sz), ("y32", _sz)]
 
 
+class SharedFp8S(ctypes.Structure):
+    _fields_ = [("hidden", _i32), ("inter", _i32), ("up_codes", _p), ("down_codes", _p),
+                ("up_wscale", ctypes.c_float), ("up_iscale", ctypes.c_float),
+                ("down_wscale", ctypes.c_float), ("down_iscale", ctypes.c_float)]
+
+
+class SharedTaps(ctypes.Structure):
+    _fields_ = [("y32", _sz), ("h", _sz), ("xq", _sz), ("sh_h32", _sz), ("sh_hq", _sz)]
+
+
 class Q4moeError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"{msg} (status {status})")
@@ -56,6 +66,9 @@ _SIGS = {
     "q4moe_w4a16_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a16_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_decode_taps": (_i32, [_p, _p, _i32, _p]),
+    "q4moe_w4a16_decode_shared_ws_bytes": (_sz, [_p, _p, _p, _i32]),
+    "q4moe_w4a16_decode_shared": (_i32, [_p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
+    "q4moe_w4a16_decode_shared_taps": (_i32, [_p, _p, _p, _i32, _p]),
     "q4moe_w4a4_grouped_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_grouped": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_grouped_taps": (_i32, [_p, _p, _i32, _p]),
@@ -122,6 +135,17 @@ class Experts:
                           None if down_gscale is None else down_gscale.data_ptr())
 
 
+class SharedFp8:
+    """FP8 per-tensor W8A8 shared expert: up_codes [inter, hidden] and
+    down_codes [hidden, inter] uint8 E4M3FN tensors, four fp32 scales."""
+    def __init__(self, up_codes, down_codes, up_wscale, up_iscale, down_wscale, down_iscale):
+        self.t = (up_codes, down_codes)
+        I, H = up_codes.shape
+        self.hidden, self.inter = H, I
+        self.s = SharedFp8S(H, I, up_codes.data_ptr(), down_codes.data_ptr(), float(up_wscale),
+                            float(up_iscale), float(down_wscale), float(down_iscale))
+
+
 class QMat:
     def __init__(self, fmt, codes, scales, gscale=None):
         self.t = (codes, scales, gscale)
@@ -171,6 +195,28 @@ def q4moe_w4a16_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=
         ws = workspace(q4moe_w4a16_decode_ws_bytes(router, experts, n_tok), x.device)
     _check(lib().q4moe_w4a16_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                     _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4moe_w4a16_decode_shared_ws_bytes(router, experts, shared, n_tok):
+    return lib().q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                                    ctypes.byref(shared.s), n_tok)
+
+
+def q4moe_w4a16_decode_shared_taps(router, experts, shared, n_tok):
+    t = SharedTaps()
+    _check(lib().q4moe_w4a16_decode_shared_taps(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                                ctypes.byref(shared.s), n_tok, ctypes.byref(t)))
+    return t
+
+
+def q4moe_w4a16_decode_shared(router, experts, shared, x, y, ids=None, w=None, ws=None, stream=None):
+    n_tok = x.shape[0]
+    if ws is None:
+        ws = workspace(q4moe_w4a16_decode_shared_ws_bytes(router, experts, shared, n_tok), x.device)
+    _check(lib().q4moe_w4a16_decode_shared(ctypes.byref(router.s), ctypes.byref(experts.s), ctypes.byref(shared.s),
+                                           _ptr(x), n_tok, _ptr(y), _ptr(ids), _ptr(w), _ptr(ws), ws.numel(),
+                                           _stream(stream)))
     return ws
 
 

@@ -143,6 +143,44 @@ typedef struct { size_t y32, h; } q4moe_decode_taps;
 q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts* ex,
                                      int32_t n_tok, q4moe_decode_taps* out);
 
+/* FP8 per-tensor W8A8 shared expert ([W] Step 3: shared experts go to FP8,
+ * they run on every token; [C] precision table: shared experts FP8
+ * per-tensor W8A8).  up_codes E4M3FN [inter][hidden], down_codes E4M3FN
+ * [hidden][inter], row-major, 16-byte aligned; hidden equal to the routed
+ * experts', inter a multiple of 64 up to 4096.  up_wscale / down_wscale:
+ * fp32 weight scale per tensor; up_iscale / down_iscale: fp32 static input
+ * scale per tensor (x into up, h into down), finite and non-zero.  An
+ * activation v is coded as the E4M3FN value nearest fl32(v / iscale) (ties
+ * to even, saturating at 448, sign kept); u = (W q) * wscale * iscale.  The
+ * MLP is relu(up x)^2 then down, as for the routed experts. */
+typedef struct {
+    int32_t hidden, inter;
+    const uint8_t* up_codes;
+    const uint8_t* down_codes;
+    float up_wscale, up_iscale, down_wscale, down_iscale;
+} q4moe_shared_fp8;
+
+/* q4moe_w4a16_decode plus the shared expert, in the same single launch:
+ * y = sum_i w_i z_i + z_shared, rounded once to bf16.  n_tok must be 1 and
+ * the routed experts NVFP4; otherwise, or where the single launch does not
+ * fit the device, Q4MOE_EUNSUPPORTED.  The shared expert's weights are read
+ * from the start of the launch, while the router runs. */
+size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
+                                          const q4moe_shared_fp8* sh, int32_t n_tok);
+q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_experts* ex,
+                                       const q4moe_shared_fp8* sh, const uint16_t* x_bf16,
+                                       int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w,
+                                       void* ws, size_t ws_bytes, void* stream);
+
+/* Byte offsets of the values q4moe_w4a16_decode_shared leaves in its
+ * workspace: y32 and h as in q4moe_decode_taps; xq uint8 [hidden] (x
+ * codes), sh_h32 fp32 [inter] (relu(u)^2, the h quantizer's input), sh_hq
+ * uint8 [inter] (h codes). */
+typedef struct { size_t y32, h, xq, sh_h32, sh_hq; } q4moe_shared_taps;
+q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                            const q4moe_shared_fp8* sh, int32_t n_tok,
+                                            q4moe_shared_taps* out);
+
 /* W4A4 routed-MoE chunk of n_tok tokens (1 <= n_tok <= 65536), NVFP4 only
  * ([W] Step 3: routed experts take 4-bit weights and activations, the
  * activations quantized on the fly per block of 16 with an E4M3FN scale

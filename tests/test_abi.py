@@ -110,3 +110,36 @@ def test_router_validation(L):
     assert L.q4moe_router_topk(ctypes.byref(_router(E=300)), A16, 1, A16, A16, None, A16, 1 << 20, None) == g.EINVAL
     assert L.q4moe_router_topk(ctypes.byref(r), A16, 1, A16 + 2, A16, None, A16, 1 << 20, None) == g.EALIGN
     assert L.q4moe_router_topk(ctypes.byref(r), A16, 1, A16, A16, None, A16, 8, None) == g.EWORKSPACE
+
+
+def _shared(H=2688, S=3712, up=A16, dn=A16, sc=(2.0 ** -8, 2.0 ** -6, 2.0 ** -8, 2.0 ** -5)):
+    return g.SharedFp8S(H, S, up, dn, *sc)
+
+
+def _decode_sh(L, r, ex, sh, T=1, x=A16, ws=A16, wsb=1 << 30):
+    shp = None if sh is None else ctypes.byref(sh)
+    return L.q4moe_w4a16_decode_shared(ctypes.byref(r), ctypes.byref(ex), shp, x, T, A16, None, None, ws, wsb, None)
+
+
+def test_decode_shared_validation(L):
+    # every call here fails validation, so nothing reaches a device
+    r, ex = _router(), _experts()
+    assert _decode_sh(L, r, ex, None) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(H=2560)) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(S=3700)) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(S=8192)) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(up=None)) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(dn=A16 + 8)) == g.EALIGN
+    assert _decode_sh(L, r, ex, _shared(sc=(1.0, 0.0, 1.0, 1.0))) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(sc=(1.0, 1.0, float("inf"), 1.0))) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(), T=2) == g.EUNSUPPORTED
+    assert _decode_sh(L, r, _experts(fmt=2), _shared()) == g.EUNSUPPORTED
+    sh = _shared()
+    need = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)
+    plain = L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+    assert need > plain
+    assert _decode_sh(L, r, ex, sh, wsb=need - 1) == g.EWORKSPACE
+    t = g.SharedTaps()
+    assert L.q4moe_w4a16_decode_shared_taps(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1,
+                                            ctypes.byref(t)) == g.OK
+    assert 0 < t.xq < t.sh_h32 < t.sh_hq < need and t.y32 < need

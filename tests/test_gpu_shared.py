@@ -1,0 +1,122 @@
+"""GPU parity of the FP8 per-tensor W8A8 shared expert inside the
+single-token decode launch, through the C-ABI, stage by stage against the
+oracle on the same seeded inputs:
+
+1. routing exact (ids) and gates to 1e-5;
+2. x codes bit-exact against the oracle's quantizer of the same x;
+3. the h tap (fp32 relu(u)^2) within the fp32 output gate of the oracle's
+   up projection fed the GPU's x codes;
+4. h codes bit-exact against the oracle's quantizer applied to the GPU's h;
+5. y within the output gate of the oracle's routed output plus its shared
+   down projection fed the GPU's h codes, and y == RNE(y32) bit for bit.
+
+Stage-wise because a code decision taken on an fp32 value that lies within
+rounding of a midpoint may differ between the fp32 kernel and the fp64
+oracle; each stage is compared on the same quantized input."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_router_fp32_amd as g
+import oracle
+import synth
+from gpu_util import DEV, dev, host, upload_bank, upload_router
+from inputs import SEED, layer
+from q4moe_testutil import bf16_bits_to_f64, bf16_rne_of_f32, gate_f32, gate_out
+
+pytestmark = pytest.mark.gpu
+
+K = 6
+FAM_SH = 3
+
+
+def upload_shared(sh):
+    return g.SharedFp8(dev(sh["up_codes"]), dev(sh["down_codes"]), sh["up_wscale"], sh["up_iscale"],
+                       sh["down_wscale"], sh["down_iscale"])
+
+
+def run_shared(router, experts, shared, x_np, ws=None):
+    x = dev(x_np)
+    y = torch.empty((1, experts.hidden), dtype=torch.int16, device=DEV)
+    ids = torch.empty((1, router.top_k), dtype=torch.int32, device=DEV)
+    w = torch.empty((1, router.top_k), dtype=torch.float32, device=DEV)
+    ws = g.q4moe_w4a16_decode_shared(router, experts, shared, x, y, ids, w, ws=ws)
+    torch.cuda.synchronize()
+    t = g.q4moe_w4a16_decode_shared_taps(router, experts, shared, 1)
+    wsh = host(ws)
+    H, S = experts.hidden, shared.inter
+    return dict(y=host(y, np.uint16)[0], ids=host(ids), w=host(w),
+                y32=wsh[t.y32: t.y32 + H * 4].view(np.float32).copy(),
+                xq=wsh[t.xq: t.xq + H].copy(),
+                h32=wsh[t.sh_h32: t.sh_h32 + S * 4].view(np.float32).copy(),
+                hq=wsh[t.sh_hq: t.sh_hq + S].copy(), ws=ws)
+
+
+def check_shared(L, sh, out):
+    r = L["route"]
+    assert np.array_equal(out["ids"], r["ids"])
+    np.testing.assert_allclose(out["w"], r["w"], rtol=1e-5)
+    x = L["x"][0]
+    xf = bf16_bits_to_f64(x).astype(np.float32)
+    assert np.array_equal(out["xq"], oracle.fp8_quant(xf, sh["up_iscale"])), "x codes differ"
+    u = oracle.fp8_gemv(sh["up_codes"], out["xq"], sh["up_wscale"], sh["up_iscale"])
+    ok, worst_h = gate_f32(out["h32"][None], (np.maximum(u, 0.0) ** 2)[None])
+    assert ok, f"h tap gate exceeded: worst {worst_h:.3f}"
+    assert np.array_equal(out["hq"], oracle.fp8_quant(out["h32"], sh["down_iscale"])), "h codes differ"
+    ob = oracle.Bank.from_dict(oracle.NVFP4, L["bank"])
+    yr, _ = oracle.moe_w4a16(ob, L["x"], r["ids"], r["w"])
+    z = oracle.fp8_gemv(sh["down_codes"], out["hq"], sh["down_wscale"], sh["down_iscale"])
+    yhat = yr[0] + z
+    ok, worst = gate_out(out["y"][None], yhat[None])
+    assert ok, f"bf16 output gate exceeded: worst {worst:.3f}"
+    ok32, worst32 = gate_f32(out["y32"][None], yhat[None])
+    assert ok32, f"fp32 output gate exceeded: worst {worst32:.3f}"
+    assert np.array_equal(out["y"], bf16_rne_of_f32(out["y32"]))
+    # the end-to-end oracle (its own x codes, fp64 u) agrees too
+    full = oracle.shared_fp8(sh, x)
+    ok_e2e, worst_e2e = gate_out(out["y"][None], (yr[0] + full["z"])[None])
+    return worst, worst32, worst_h, ok_e2e, worst_e2e
+
+
+@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (16, 256, 192, 64), (32, 512, 320, 192)])
+def test_decode_shared_small(E, H, I, S):
+    L = layer(SEED + S, synth.FAM_NVFP4, 0, E, H, I, 1, K, "nvfp4")
+    sh = synth.shared_fp8(SEED, FAM_SH, S, H, S)
+    out = run_shared(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), upload_shared(sh), L["x"])
+    check_shared(L, sh, out)
+
+
+@pytest.fixture(scope="module")
+def full_layer():
+    L = layer(SEED, synth.FAM_NVFP4, 0, 128, 2688, 1856, 1, K, "nvfp4")
+    sh = synth.shared_fp8(SEED, FAM_SH, 0, 2688, 3712)
+    return L, sh, upload_bank(L["bank"], "nvfp4"), upload_router(L["wg"], L["b"], K), upload_shared(sh)
+
+
+def test_decode_shared_full_layer(full_layer):
+    L, sh, ex, router, shd = full_layer
+    out = run_shared(router, ex, shd, L["x"])
+    worst, worst32, worst_h, ok_e2e, worst_e2e = check_shared(L, sh, out)
+    print(f"shared: worst bf16 ratio {worst:.3f}, fp32 {worst32:.4f}, h tap {worst_h:.5f}; "
+          f"end to end {'within' if ok_e2e else 'outside'} the gate ({worst_e2e:.3f})")
+    # a second call on the same workspace (next epoch) repeats bit for bit
+    again = run_shared(router, ex, shd, L["x"], ws=out["ws"])
+    assert np.array_equal(again["y32"].view(np.uint32), out["y32"].view(np.uint32))
+    assert g.q4moe_ws_check(out["ws"]) == 0
+
+
+def test_decode_shared_zero_weights_is_plain_decode(full_layer):
+    # all-zero shared weights contribute +0 to every row, so y32 equals the
+    # routed-only launch's bit for bit (same slot order, + 0)
+    L, sh, ex, router, _ = full_layer
+    zero = dict(sh, up_codes=np.zeros_like(sh["up_codes"]), down_codes=np.zeros_like(sh["down_codes"]))
+    out = run_shared(router, ex, upload_shared(zero), L["x"])
+    x = dev(L["x"])
+    y = torch.empty((1, ex.hidden), dtype=torch.int16, device=DEV)
+    ws = g.q4moe_w4a16_decode(router, ex, x, y)
+    torch.cuda.synchronize()
+    t = g.q4moe_w4a16_decode_taps(router, ex, 1)
+    y32 = host(ws)[t.y32: t.y32 + ex.hidden * 4].view(np.float32)
+    assert np.array_equal(out["y32"].view(np.uint32), y32.view(np.uint32))
+    assert np.array_equal(out["y"], host(y, np.uint16)[0])
+    assert not out["hq"].any() and not out["h32"].any()
