@@ -314,14 +314,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         sq0 = share_lo(nq, blockIdx.x, gridDim.x);
         sq1 = share_lo(nq, blockIdx.x + 1, gridDim.x);
         shr = 4 * sq0 + 2 * wave + seg;
+        sd0 = share_lo(a.H, gw, NW);
+        sd1 = share_lo(a.H, gw + 1, NW);
+    }
+    auto issue_sh_up = [&]() {
         const uint32_t rb = (uint32_t)(shr < 4 * sq1 ? shr : 0) * (uint32_t)a.H;
 #pragma unroll
         for (int c = 0; c < CS; ++c) {
             const int ch = min(li + 32 * c, a.H / 16 - 1);
             qsu[c] = ldg16_stream(a.shu + (rb + (uint32_t)ch * 16u));
         }
-        sd0 = share_lo(a.H, gw, NW);
-        sd1 = share_lo(a.H, gw + 1, NW);
+    };
+    auto issue_sh_dn = [&]() {
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
             const uint32_t rb2 = (uint32_t)min(sd0 + p, a.H - 1) * (uint32_t)a.S;
@@ -331,6 +335,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 qsd[p][c] = ldg16_stream(a.shd + (rb2 + (uint32_t)ch * 16u));
             }
         }
+    };
+    if constexpr (SH) {
+        issue_sh_up();
+        issue_sh_dn();
     }
     compiler_fence();  // keep every load above in the entry block
 
@@ -492,8 +500,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     compiler_fence();
 
     // ---- shared expert up: u = (W x) * s_w * s_in for this segment's row
-    // (its weights arrived during the routing), h = relu(u)^2, and the h
-    // code into LDS for the publish
+    // (its weights arrived during the routing), h = relu(u)^2; the
+    // workgroup's h codes are published at once, four per value, so that
+    // they have travelled by the time the down rows need them
     if constexpr (SH) {
         const int nck = a.H / 16;
         float acc = 0.f;
@@ -511,6 +520,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             reinterpret_cast<uint8_t*>(s_shq)[shr - 4 * sq0] = (uint8_t)code;
             a.sh_h[shr] = h;
             a.sh_hq[shr] = (uint8_t)code;
+        }
+        __syncthreads();
+        const int j = threadIdx.x;
+        if (j < sq1 - sq0) {
+            const float v = __uint_as_float(s_shq[j]);
+#pragma unroll
+            for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.hq_tag + (size_t)rp * (a.S / 4) + sq0 + j, v, ep);
         }
     }
 
@@ -578,10 +594,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // their registers are reused, waits for the down weights as well.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     compiler_fence();
+    // Shared expert: one poll of the h-code quads (t and t + 512 for thread
+    // t), issued before the down loads so that its results do not wait for
+    // them; its quads were published about a memory round trip earlier.
+    const unsigned long long* srcq = a.hq_tag + (size_t)rep * (a.S / 4);
+    unsigned long long vq[2];
+    if constexpr (SH) {
+#pragma unroll
+        for (int m = 0; m < 2; ++m) vq[m] = get_tag(srcq + min((int)threadIdx.x + 512 * m, a.S / 4 - 1));
+    }
+    compiler_fence();
     uint4 qd[kDownRows][C2];
     uint32_t sd[kDownRows][C2];
     float gdn = 1.0f;  // per-tensor scale of the down matrix (NVFP4)
-    if (dwave) {
+    // (with the shared expert every wave issues them, the few without down
+    // rows reading rows 0-7 of slot 0: loads under a branch would make the
+    // compiler wait for all of them before the shared expert's h codes)
+    if (SH || dwave) {
         const int drow = ids[dslot] * a.H;
         uint32_t dco[C2], dso[C2];
 #pragma unroll
@@ -620,13 +649,59 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.h_tag + ((size_t)rp * a.K + slot) * a.I + r, v, ep);
             a.h[(size_t)slot * a.I + r] = v;
         }
-        if constexpr (SH) {  // the shared expert's h codes, four per value
-            if (j < sq1 - sq0) {
-                const float v = __uint_as_float(s_shq[j]);
+    }
+    if constexpr (SH) {
+        // The shared expert's h codes into LDS (from the early poll; quads
+        // not yet there are polled again, which waits for the down
+        // weights), then its down rows, while the routed h travels.
+        uint32_t qp = 0;
 #pragma unroll
-                for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.hq_tag + (size_t)rp * (a.S / 4) + sq0 + j, v, ep);
+        for (int m = 0; m < 2; ++m) {
+            const int q = threadIdx.x + 512 * m;
+            if (q < a.S / 4) {
+                if (tag_is(vq[m], ep))
+                    *reinterpret_cast<uint2*>(&s_shb[2 * q]) = fp8x4_bf16((uint32_t)vq[m]);
+                else
+                    qp |= 1u << m;
             }
         }
+        for (uint32_t polls = 0; __any(qp != 0u); ++polls) {
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int q = threadIdx.x + 512 * m;
+                if ((qp >> m) & 1u) {
+                    const unsigned long long v = get_tag(srcq + q);
+                    if (tag_is(v, ep)) {
+                        *reinterpret_cast<uint2*>(&s_shb[2 * q]) = fp8x4_bf16((uint32_t)v);
+                        qp &= ~(1u << m);
+                    }
+                }
+            }
+            if (polls > kPollLimit) {
+                if (lane == 0) atomicOr(flags, 1u);
+                break;
+            }
+            if (__any(qp != 0u)) __builtin_amdgcn_s_sleep(1);
+        }
+        __syncthreads();
+        const int nck2 = a.S / 16;
+        float zsh[2];
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < CD; ++c) {
+                const int chr = lane + 64 * c, ch = min(chr, nck2 - 1);
+                const uint4* hp = reinterpret_cast<const uint4*>(&s_shb[8 * ch]);
+                const float q = fp8_chunk_bf16(qsd[p][c], hp[0], hp[1]);
+                acc += chr < nck2 ? q : 0.f;
+            }
+            zsh[p] = seg_sum_last<64>(acc);
+        }
+        const float sc = a.sd_w * a.sd_in;
+#pragma unroll
+        for (int p = 0; p < 2; ++p)
+            if (lane == 63 && sd0 + p < sd1) put_tag(a.z_tag + (uint32_t)(a.K * a.H + sd0 + p), zsh[p] * sc, ep);
     }
     {
         // the slots sl0 .. sl1 are adjacent in the [K][I] layout, so their h
@@ -637,30 +712,10 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
         for (int m = 0; m < 16; ++m)
             if ((int)threadIdx.x + 512 * m < nh) pend |= 1u << m;
-        // shared expert: thread t also polls h-code quads t and t + 512
-        const unsigned long long* srcq = a.hq_tag + (size_t)rep * (a.S / 4);
-        if constexpr (SH) {
-#pragma unroll
-            for (int m = 0; m < 2; ++m)
-                if ((int)threadIdx.x + 512 * m < a.S / 4) pend |= 1u << (16 + m);
-        }
         for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
-            unsigned long long v[16], vq[2];
+            unsigned long long v[16];
 #pragma unroll
             for (int m = 0; m < 16; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + threadIdx.x + 512 * m) : 0ull;
-            if constexpr (SH) {
-#pragma unroll
-                for (int m = 0; m < 2; ++m)
-                    vq[m] = (pend >> (16 + m)) & 1u ? get_tag(srcq + threadIdx.x + 512 * m) : 0ull;
-#pragma unroll
-                for (int m = 0; m < 2; ++m) {
-                    if (((pend >> (16 + m)) & 1u) && tag_is(vq[m], ep)) {
-                        const int q = threadIdx.x + 512 * m;
-                        *reinterpret_cast<uint2*>(&s_shb[2 * q]) = fp8x4_bf16((uint32_t)vq[m]);
-                        pend &= ~(1u << (16 + m));
-                    }
-                }
-            }
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
@@ -771,28 +826,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         const int rl = rows8_label(lane);
         const float wg = wsel[dslot] * gdn;
         if ((lane & 7) == 7 && drow0 + rl < a.H) put_tag(a.z_tag + (uint32_t)(dslot * a.H + drow0 + rl), wg * zs, ep);
-    }
-    // ---- shared expert down: z = (W h) * s_w * s_in for the wave's (at
-    // most two) rows, published as slot K
-    if constexpr (SH) {
-        const int nck2 = a.S / 16;
-        float zsh[2];
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            float acc = 0.f;
-#pragma unroll
-            for (int c = 0; c < CD; ++c) {
-                const int chr = lane + 64 * c, ch = min(chr, nck2 - 1);
-                const uint4* hp = reinterpret_cast<const uint4*>(&s_shb[8 * ch]);
-                const float q = fp8_chunk_bf16(qsd[p][c], hp[0], hp[1]);
-                acc += chr < nck2 ? q : 0.f;
-            }
-            zsh[p] = seg_sum_last<64>(acc);
-        }
-        const float sc = a.sd_w * a.sd_in;
-#pragma unroll
-        for (int p = 0; p < 2; ++p)
-            if (lane == 63 && sd0 + p < sd1) put_tag(a.z_tag + (uint32_t)(a.K * a.H + sd0 + p), zsh[p] * sc, ep);
     }
     Q4MOE_PHASE(6);
 
