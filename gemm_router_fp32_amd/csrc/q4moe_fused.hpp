@@ -299,12 +299,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // x into LDS once per workgroup (the up GEMV reads it from there)
     if ((int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
 
-    // Shared expert: its weights do not depend on the routing, so their
-    // loads leave now and stream while the router runs.  Workgroup b takes
-    // the up rows of h-code quads [sq0, sq1) (at most 16 rows: one per
-    // 32-lane segment, lane li reading chunks li + 32 c), and wave gw the
-    // (at most two) down rows [sd0, sd1), lane l reading chunks l + 64 c.
-    // Reads past a row's end are clamped into it and masked at use.
+    // Shared expert: its weights do not depend on the routing, so they
+    // stream while the router runs (the loads leave in two bursts, below).
+    // Workgroup b takes the up rows of h-code quads [sq0, sq1) (at most 16
+    // rows: one per 32-lane segment, lane li reading chunks li + 32 c), and
+    // wave gw the (at most two) down rows [sd0, sd1), lane l reading chunks
+    // l + 64 c.  Reads past a row's end are clamped into it and masked at use.
     constexpr int CS = SH ? 2 * C : 1;  // H / 16 <= 32 * CS
     constexpr int CD = SH ? 4 : 1;      // S / 16 <= 64 * CD
     uint4 qsu[CS], qsd[2][CD];
@@ -336,10 +336,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
         }
     };
-    if constexpr (SH) {
-        issue_sh_up();
-        issue_sh_dn();
-    }
+
     compiler_fence();  // keep every load above in the entry block
 
     // ---- R: workgroup e computes router logit e; its waves split the row
@@ -367,6 +364,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     Q4MOE_PHASE(1);
+    // Shared expert up rows: their loads leave once the router rows are in
+    // (workgroups past E wait for their unused router loads), so that the
+    // router's reads do not queue behind them in the memory system.
+    if constexpr (SH) {
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        issue_sh_up();
+    }
 
     // unit bookkeeping (routing-independent: done while the scores travel)
     const int RU = a.K * a.I;
@@ -437,6 +441,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
     __syncthreads();
     Q4MOE_PHASE(2);
+    // Shared expert down rows: after the score hand-off, for the same reason
+    // (two smaller bursts delay the routing less than one).
+    if constexpr (SH) issue_sh_dn();
     int* ids = s_ids_all[wave];
     float* wsel = s_w_all[wave];
 
