@@ -116,9 +116,10 @@ class Evictor:
         self.buf.sum()
 
 
-def build_stack(torch, g, synth, fmt, shared=False):
+def build_stack(torch, g, synth, fmt, shared=False, w4a4=False):
     """The 23 layers, resident; with `shared`, each layer also carries the
-    FP8 shared expert [S_SHARED x H] and runs the shared decode entry."""
+    FP8 shared expert [S_SHARED x H] and runs the shared decode entry; with
+    `w4a4`, each layer runs the single-token W4A4 decode entry."""
     from gpu_util import dev
     fam = synth.FAM_NVFP4 if fmt == "nvfp4" else synth.FAM_INT4
     layers, buf = [], None
@@ -140,15 +141,20 @@ def build_stack(torch, g, synth, fmt, shared=False):
             L["sh"] = g.SharedFp8(dev(sh["up_codes"]), dev(sh["down_codes"]), sh["up_wscale"], sh["up_iscale"],
                                   sh["down_wscale"], sh["down_iscale"])
             L["ws"] = g.workspace(g.q4moe_w4a16_decode_shared_ws_bytes(r, ex, L["sh"], 1))
+        elif w4a4:
+            L["w4a4"] = True
+            L["ws"] = g.workspace(g.q4moe_w4a4_decode_ws_bytes(r, ex, 1))
         else:
             L["ws"] = g.workspace(g.q4moe_w4a16_decode_ws_bytes(r, ex, 1))
         layers.append(L)
-    log(f"{fmt} stack{' + shared expert' if shared else ''} resident ({LAYERS} layers)")
+    log(f"{fmt} stack{' + shared expert' if shared else ''}{' (W4A4)' if w4a4 else ''} resident ({LAYERS} layers)")
     return layers
 
 
 def decode_call(g, L):
-    if "sh" in L:
+    if L.get("w4a4"):
+        g.q4moe_w4a4_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
+    elif "sh" in L:
         g.q4moe_w4a16_decode_shared(L["r"], L["ex"], L["sh"], L["x"], L["y"], ws=L["ws"])
     else:
         g.q4moe_w4a16_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
@@ -349,6 +355,17 @@ def main():
                                  "bytes_per_layer": bs, "shared_inter": S_SHARED, "flags": fs}
         log(f"nvfp4 + fp8 shared expert stack: {extra['shared_stack']}")
         del shl
+        torch.cuda.empty_cache()
+        a4l = build_stack(torch, g, synth, "nvfp4", w4a4=True)
+        msa, mka, fa, pera = time_stack(torch, g, a4l, args.steps, args.warmup)
+        ba = layer_bytes()
+        extra["w4a4_decode_stack"] = {"us_per_layer": round(1000.0 * msa / LAYERS, 3),
+                                      "hbm_gbps": round(ba / (msa / LAYERS * 1e-3) / 1e9, 1),
+                                      "tokens_per_s": round(1000.0 / msa, 1), "single_launch_us": round(mka * 1e3, 3),
+                                      "us_per_layer_spread": spread(pera / LAYERS), "bytes_per_layer": ba,
+                                      "flags": fa}
+        log(f"nvfp4 W4A4 single-token stack: {extra['w4a4_decode_stack']}")
+        del a4l
         torch.cuda.empty_cache()
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
 

@@ -111,11 +111,12 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, total;
+    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, xq_c, xq_s, hq_c, hq_s, total;
 };
 
-// S: the shared expert's intermediate size (0: no shared expert).
-DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0) {
+// S: the shared expert's intermediate size (0: no shared expert); a4: the
+// W4A4 single-token decode (NVFP4 activation code taps).
+DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
     size_t o = l.r.total;
@@ -133,6 +134,14 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0) {
     o += up_to((size_t)S * 4);
     l.sh_hq = o;
     o += up_to((size_t)S);
+    l.xq_c = o;    // W4A4 taps: x codes and scales, h codes and scales
+    o += up_to(a4 ? (size_t)H / 2 : 0);
+    l.xq_s = o;
+    o += up_to(a4 ? (size_t)H / 16 : 0);
+    l.hq_c = o;
+    o += up_to(a4 ? (size_t)K * I / 2 : 0);
+    l.hq_s = o;
+    o += up_to(a4 ? (size_t)K * I / 16 : 0);
     l.h = o;       // h tap
     o += up_to((size_t)T * K * I * 4);
     l.y32 = o;
@@ -159,28 +168,28 @@ int persistent_grid(K kernel, int block, int want) {
 // every workgroup is resident and every wait can be satisfied), cached per
 // device and kernel variant.
 constexpr int kMaxDevices = 64;
-constexpr int kFusedVariants = 32;
+constexpr int kFusedVariants = 32;  // 8 shapes x (plain, shared, W4A4)
 int g_fused_grid[kMaxDevices][kFusedVariants];
 
-template <int FMT, int C, int C2, bool SH>
+template <int FMT, int C, int C2, bool SH, bool A4>
 int fused_grid(int dev, int variant) {
     if (dev < 0 || dev >= kMaxDevices) return 0;
     int& cached = g_fused_grid[dev][variant];
     if (cached != 0) return cached;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<FMT, C, C2, SH>, 64 * kWaves, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_fused<FMT, C, C2, SH, A4>, 64 * kWaves, 0) !=
         hipSuccess)
         return 0;
     cached = cus * (per_cu < 1 ? 0 : 1);
     return cached;
 }
 
-template <int FMT, int C, int C2, bool SH>
+template <int FMT, int C, int C2, bool SH, bool A4>
 q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
-    const int grid = fused_grid<FMT, C, C2, SH>(dev, variant);
+    const int grid = fused_grid<FMT, C, C2, SH, A4>(dev, variant);
     // The router needs one workgroup per expert; every wave's up rows must fit
     // in kMaxUp passes (all loads in flight at once), a workgroup stages at
     // most kMaxWgUp up rows, every down unit (kDownRows rows of one slot)
@@ -195,24 +204,24 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     // shared expert: at most 4 h-code quads (16 up rows) per workgroup and
     // two down rows per wave
     if (SH && (a.S / 4 > 4LL * grid || a.H > 2 * nw)) return Q4MOE_EUNSUPPORTED;
-    hipLaunchKernelGGL((k_decode_fused<FMT, C, C2, SH>), dim3(grid), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL((k_decode_fused<FMT, C, C2, SH, A4>), dim3(grid), dim3(64 * kWaves), 0, s, a);
     return launched("fused decode");
 }
 
-template <int FMT, bool SH = false>
+template <int FMT, bool SH = false, bool A4 = false>
 q4moe_status launch_fused(const FusedArgs& a, hipStream_t s) {
     const int C = (a.H / 32 + 31) / 32, C2 = (a.I / 32 + 63) / 64;
     const int v = (C - 1) * 2 + (C2 - 1);
-    const int slot = v + (SH ? 8 : 0);  // grid cache entry
+    const int slot = v + (SH ? 8 : 0) + (A4 ? 16 : 0);  // grid cache entry
     switch (v) {
-        case 0: return launch_fused_v<FMT, 1, 1, SH>(a, s, slot);
-        case 1: return launch_fused_v<FMT, 1, 2, SH>(a, s, slot);
-        case 2: return launch_fused_v<FMT, 2, 1, SH>(a, s, slot);
-        case 3: return launch_fused_v<FMT, 2, 2, SH>(a, s, slot);
-        case 4: return launch_fused_v<FMT, 3, 1, SH>(a, s, slot);
-        case 5: return launch_fused_v<FMT, 3, 2, SH>(a, s, slot);
-        case 6: return launch_fused_v<FMT, 4, 1, SH>(a, s, slot);
-        case 7: return launch_fused_v<FMT, 4, 2, SH>(a, s, slot);
+        case 0: return launch_fused_v<FMT, 1, 1, SH, A4>(a, s, slot);
+        case 1: return launch_fused_v<FMT, 1, 2, SH, A4>(a, s, slot);
+        case 2: return launch_fused_v<FMT, 2, 1, SH, A4>(a, s, slot);
+        case 3: return launch_fused_v<FMT, 2, 2, SH, A4>(a, s, slot);
+        case 4: return launch_fused_v<FMT, 3, 1, SH, A4>(a, s, slot);
+        case 5: return launch_fused_v<FMT, 3, 2, SH, A4>(a, s, slot);
+        case 6: return launch_fused_v<FMT, 4, 1, SH, A4>(a, s, slot);
+        case 7: return launch_fused_v<FMT, 4, 2, SH, A4>(a, s, slot);
     }
     return Q4MOE_EUNSUPPORTED;
 }
@@ -514,18 +523,21 @@ q4moe_status check_shared(const q4moe_shared_fp8* sh, const q4moe_experts* ex, i
     return Q4MOE_OK;
 }
 
+// a4: the W4A4 single-token decode (activations quantized to NVFP4).
 q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
                          const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w,
-                         void* ws, size_t ws_bytes, void* stream) {
+                         void* ws, size_t ws_bytes, void* stream, bool a4 = false) {
     q4moe_status st = check_router(r);
     if (st != Q4MOE_OK) return st;
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
     if (sh && (st = check_shared(sh, ex, n_tok)) != Q4MOE_OK) return st;
+    if (a4 && ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode takes NVFP4 experts only");
+    if (a4 && n_tok != 1) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode runs one token (n_tok = %d)", n_tok);
     if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
     if ((ids && !aligned(ids, 4)) || (w && !aligned(w, 4))) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh ? sh->inter : 0);
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh ? sh->inter : 0, a4);
     if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
     if ((st = device_ready()) != Q4MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
@@ -562,6 +574,17 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
         f.hq_tag = nullptr;
         f.sh_xq = f.sh_hq = nullptr;
         f.sh_h = nullptr;
+        f.xq_codes = f.xq_scales = f.hq_codes = f.hq_scales = nullptr;
+        if (a4) {
+            f.xq_codes = at<uint8_t>(ws, l.xq_c);
+            f.xq_scales = at<uint8_t>(ws, l.xq_s);
+            f.hq_codes = at<uint8_t>(ws, l.hq_c);
+            f.hq_scales = at<uint8_t>(ws, l.hq_s);
+            st = launch_fused<FMT_NVFP4, false, true>(f, s);
+            if (st == Q4MOE_EUNSUPPORTED)
+                return fail(st, "the W4A4 decode's single launch does not fit this device and shape");
+            return st;
+        }
         if (sh) {
             f.S = sh->inter;
             f.shu = sh->up_codes;
@@ -656,6 +679,30 @@ q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_expert
                                        void* stream) {
     if (!sh) return fail(Q4MOE_EINVAL, "shared expert descriptor is NULL");
     return decode_impl(r, ex, sh, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
+size_t q4moe_w4a4_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
+    if (!r || !ex || n_tok < 1) return 0;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, true).total;
+}
+
+q4moe_status q4moe_w4a4_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                               int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
+                               size_t ws_bytes, void* stream) {
+    return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream, true);
+}
+
+q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
+                                    q4moe_w4a4_token_taps* out) {
+    if (!r || !ex || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, true);
+    out->y32 = l.y32;
+    out->h32 = l.h;
+    out->xq_codes = l.xq_c;
+    out->xq_scales = l.xq_s;
+    out->hq_codes = l.hq_c;
+    out->hq_scales = l.hq_s;
+    return Q4MOE_OK;
 }
 
 q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,

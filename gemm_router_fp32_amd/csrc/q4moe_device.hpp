@@ -59,6 +59,65 @@ __device__ __forceinline__ f32x2 fp4x2_f32(uint32_t v) {
     return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(v, 1.0f, sel);
 }
 
+// The E2M1 code of |v| on the grid scaled by s is the number of midpoints
+// t_j = mids_j * s (exact: mids have at most 3 significant bits) that |v|
+// passes, a tie going to the even code: up at an odd j, down at an even j.
+// The thresholds increase, so three comparisons find the count (a binary
+// search: j = 3, then 1 or 5, then 0, 2, 4 or 6).  Scale 0 gives code 0 for
+// every value: the thresholds are then NaN and every comparison is false
+// (as for a NaN value).
+struct E2m1Thresholds {
+    float t[7];
+};
+__device__ __forceinline__ E2m1Thresholds e2m1_thresholds(float s) {
+    const float sc = s == 0.f ? __builtin_nanf("") : s;
+    return {{0.25f * sc, 0.75f * sc, 1.25f * sc, 1.75f * sc, 2.5f * sc, 3.5f * sc, 5.0f * sc}};
+}
+__device__ __forceinline__ uint32_t e2m1_code(float mag, const E2m1Thresholds& th) {
+    const uint32_t b2 = mag >= th.t[3] ? 1u : 0u;
+    const uint32_t b1 = mag >= (b2 ? th.t[5] : th.t[1]) ? 1u : 0u;
+    const float tl = b2 ? (b1 ? th.t[6] : th.t[4]) : (b1 ? th.t[2] : th.t[0]);
+    const uint32_t b0 = mag > tl ? 1u : 0u;
+    return (b2 << 2) | (b1 << 1) | b0;
+}
+
+// NVFP4 quantization of one block of 16 values (the activation quantizer:
+// scale byte = E4M3FN nearest-even of fl32(amax / 6), saturating at 448;
+// codes = nearest E2M1 of |v| / scale, ties to the even code, sign kept),
+// codes packed low nibble first; and the block's dequantized values
+// e2m1 * e4m3 (at most 6 significant bits: exact in fp32 and in bf16).
+struct Nvfp4Block {
+    uint32_t sb;
+    uint32_t code[2];
+};
+__device__ __forceinline__ Nvfp4Block nvfp4_quant16(const float (&v)[16]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    Nvfp4Block b;
+    b.sb = e4m3fn_rne_sat(__fdiv_rn(amax, 6.0f));
+    const E2m1Thresholds th = e2m1_thresholds(e4m3fn_to_f32(b.sb));
+    b.code[0] = b.code[1] = 0u;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+        b.code[k >> 3] |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * (k & 7));
+    return b;
+}
+__device__ __forceinline__ void nvfp4_dequant16(const Nvfp4Block& b, float (&out)[16]) {
+    const float s = e4m3fn_to_f32(b.sb);
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const f32x2 p[4] = {fp4x2_f32<0>(b.code[w]), fp4x2_f32<1>(b.code[w]), fp4x2_f32<2>(b.code[w]),
+                            fp4x2_f32<3>(b.code[w])};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            out[8 * w + 2 * j] = p[j][0] * s;
+            out[8 * w + 2 * j + 1] = p[j][1] * s;
+        }
+    }
+}
+
+
 // Two E2M1 codes -> bf16 pair (every E2M1 value is exact in bf16).
 template <int sel>
 __device__ __forceinline__ bf16x2 fp4x2_bf16(uint32_t v) {

@@ -98,6 +98,11 @@ struct FusedArgs {
     uint8_t* sh_xq;               // [H] tap: x codes
     float* sh_h;                  // [S] tap: relu(u)^2 before quantization
     uint8_t* sh_hq;               // [S] tap: h codes
+    // W4A4 (the A4 variants): taps of the NVFP4 activation codes
+    uint8_t* xq_codes;            // [H/2]
+    uint8_t* xq_scales;           // [H/16]
+    uint8_t* hq_codes;            // [K][I/2]
+    uint8_t* hq_scales;           // [K][I/16]
 };
 
 __device__ __forceinline__ unsigned long long tagged(float v, uint32_t ep) {
@@ -245,7 +250,11 @@ __device__ __forceinline__ uint2 fp8x4_bf16(uint32_t v) {
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v, 1.0f, true)));
 }
 
-template <int FMT, int C, int C2, bool SH>
+// A4: W4A4, the activations (x into up, h into down) quantized to NVFP4 on
+// the fly: x by the waves that do not poll the scores, h by every workgroup
+// for the slots it uses, once the h hand-off is in; both replaced in LDS by
+// their exact dequantized values, so the GEMVs themselves are unchanged.
+template <int FMT, int C, int C2, bool SH, bool A4>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __shared__ float s_part[kWaves];
     __shared__ float s_keys[256], s_scores[256];
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
 
     // x into LDS once per workgroup (the up GEMV reads it from there)
-    if ((int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+    if (!A4 && (int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
 
     // Shared expert: its weights do not depend on the routing, so they
     // stream while the router runs (the loads leave in two bursts, below).
@@ -437,6 +446,33 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             const uint2 b0 = fp8x4_bf16(cw[0]), b1 = fp8x4_bf16(cw[1]);
             *reinterpret_cast<uint4*>(&s_xb[4 * t]) = make_uint4(b0.x, b0.y, b1.x, b1.y);
             if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
+        }
+    } else if constexpr (A4) {
+        // the waves that do not poll quantize x to NVFP4, one block of 16
+        // per thread, into LDS as bf16 of the dequantized values
+        const int npw = (a.E + 63) / 64;
+        const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
+        for (int t = iw * 64 + lane; t < a.H / 16; t += nidle * 64) {
+            const uint4 v0 = *reinterpret_cast<const uint4*>(a.x + 16 * t);
+            const uint4 v1 = *reinterpret_cast<const uint4*>(a.x + 16 * t + 8);
+            const uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            float f[16];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                f[2 * j] = bf16_bits_to_f32(in[j] & 0xffffu);
+                f[2 * j + 1] = bf16_bits_to_f32(in[j] >> 16);
+            }
+            const Nvfp4Block b = nvfp4_quant16(f);
+            nvfp4_dequant16(b, f);
+            uint32_t o[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
+            s_x[2 * t] = make_uint4(o[0], o[1], o[2], o[3]);
+            s_x[2 * t + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+            if (blockIdx.x == 0) {
+                *reinterpret_cast<uint2*>(a.xq_codes + 8 * t) = make_uint2(b.code[0], b.code[1]);
+                a.xq_scales[t] = (uint8_t)b.sb;
+            }
         }
     }
     __syncthreads();
@@ -750,6 +786,34 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     __syncthreads();
+    if constexpr (A4) {
+        // h of the workgroup's slots to NVFP4, in place (block t of the run
+        // for thread t; a block never straddles two slots, I % 16 == 0); the
+        // workgroup holding a slot's first down unit writes its code taps
+        const int nh = (sl1 - sl0 + 1) * a.I;
+        for (int t = threadIdx.x; t < nh / 16; t += 64 * kWaves) {
+            float4* hp = reinterpret_cast<float4*>(&s_h[16 * t]);
+            float f[16];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float4 v = hp[k];
+                f[4 * k] = v.x;
+                f[4 * k + 1] = v.y;
+                f[4 * k + 2] = v.z;
+                f[4 * k + 3] = v.w;
+            }
+            const Nvfp4Block b = nvfp4_quant16(f);
+            nvfp4_dequant16(b, f);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) hp[k] = make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+            const int slot = sl0 + (16 * t) / a.I, col = 16 * t - (slot - sl0) * a.I;
+            if ((slot * dpu) / kWaves == (int)blockIdx.x) {
+                *reinterpret_cast<uint2*>(a.hq_codes + (size_t)slot * (a.I / 2) + col / 2) = make_uint2(b.code[0], b.code[1]);
+                a.hq_scales[(size_t)slot * (a.I / 16) + col / 16] = (uint8_t)b.sb;
+            }
+        }
+        __syncthreads();
+    }
     Q4MOE_PHASE(5);
 
     // ---- D: a wave computes z = w * g * (W_down h) for its 8 rows of slot

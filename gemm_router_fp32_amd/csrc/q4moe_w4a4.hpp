@@ -168,28 +168,6 @@ __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a) {
 // of v kept; scale 0 gives magnitude 0.
 // ---------------------------------------------------------------------------
 
-// The E2M1 code of |v| on the grid scaled by s is the number of midpoints
-// t_j = mids_j * s (exact: mids have at most 3 significant bits) that |v|
-// passes, a tie going to the even code: up at an odd j, down at an even j.
-// The thresholds increase, so three comparisons find the count (a binary
-// search: j = 3, then 1 or 5, then 0, 2, 4 or 6).  Scale 0 gives code 0 for
-// every value: the thresholds are then NaN and every comparison is false
-// (as for a NaN value).
-struct E2m1Thresholds {
-    float t[7];
-};
-__device__ __forceinline__ E2m1Thresholds e2m1_thresholds(float s) {
-    const float sc = s == 0.f ? __builtin_nanf("") : s;
-    return {{0.25f * sc, 0.75f * sc, 1.25f * sc, 1.75f * sc, 2.5f * sc, 3.5f * sc, 5.0f * sc}};
-}
-__device__ __forceinline__ uint32_t e2m1_code(float mag, const E2m1Thresholds& th) {
-    const uint32_t b2 = mag >= th.t[3] ? 1u : 0u;
-    const uint32_t b1 = mag >= (b2 ? th.t[5] : th.t[1]) ? 1u : 0u;
-    const float tl = b2 ? (b1 ? th.t[6] : th.t[4]) : (b1 ? th.t[2] : th.t[0]);
-    const uint32_t b0 = mag > tl ? 1u : 0u;
-    return (b2 << 2) | (b1 << 1) | b0;
-}
-
 struct QuantArgs {
     int rows, cols;
     const void* v;      // bf16 bits (BF16_IN) or fp32

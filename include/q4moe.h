@@ -181,6 +181,27 @@ q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_e
                                             const q4moe_shared_fp8* sh, int32_t n_tok,
                                             q4moe_shared_taps* out);
 
+/* W4A4 routed-MoE decode of one token in a single launch ([W] Step 3: the
+ * routed experts take 4-bit weights and activations; the MTP drafter's
+ * experts are NVFP4 W4A4 too, [C] and the pages' MTP passage): as
+ * q4moe_w4a16_decode, with x and h quantized to NVFP4 on the fly (per 16, an
+ * E4M3FN scale amax/6 and E2M1 codes, as in q4moe_w4a4_grouped) and the
+ * GEMVs run on their exact dequantized values.  NVFP4 experts and n_tok = 1
+ * only, else Q4MOE_EUNSUPPORTED.  ids/w nullable. */
+size_t q4moe_w4a4_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
+q4moe_status q4moe_w4a4_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                               int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
+                               size_t ws_bytes, void* stream);
+
+/* Byte offsets of the values q4moe_w4a4_decode leaves in its workspace:
+ * y32 fp32 [hidden]; h32 fp32 [top_k][inter] (relu(u)^2 before
+ * quantization, slot order); xq_codes [hidden/2], xq_scales [hidden/16];
+ * hq_codes [top_k][inter/2], hq_scales [top_k][inter/16] (slot order;
+ * codes low nibble first). */
+typedef struct { size_t y32, h32, xq_codes, xq_scales, hq_codes, hq_scales; } q4moe_w4a4_token_taps;
+q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
+                                    q4moe_w4a4_token_taps* out);
+
 /* W4A4 routed-MoE chunk of n_tok tokens (1 <= n_tok <= 65536), NVFP4 only
  * ([W] Step 3: routed experts take 4-bit weights and activations, the
  * activations quantized on the fly per block of 16 with an E4M3FN scale

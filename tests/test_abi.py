@@ -143,3 +143,20 @@ def test_decode_shared_validation(L):
     assert L.q4moe_w4a16_decode_shared_taps(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1,
                                             ctypes.byref(t)) == g.OK
     assert 0 < t.xq < t.sh_h32 < t.sh_hq < need and t.y32 < need
+
+
+def test_w4a4_decode_validation(L):
+    r, ex = _router(), _experts()
+
+    def call(ex_, T=1, wsb=1 << 30):
+        return L.q4moe_w4a4_decode(ctypes.byref(r), ctypes.byref(ex_), A16, T, A16, None, None, A16, wsb, None)
+
+    assert call(ex, T=2) == g.EUNSUPPORTED
+    assert call(_experts(fmt=2)) == g.EUNSUPPORTED
+    assert call(ex, T=0) == g.EINVAL
+    need = L.q4moe_w4a4_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+    assert need > L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+    assert call(ex, wsb=need - 1) == g.EWORKSPACE
+    t = g.W4A4TokenTaps()
+    assert L.q4moe_w4a4_decode_taps(ctypes.byref(r), ctypes.byref(ex), 1, ctypes.byref(t)) == g.OK
+    assert t.xq_codes < t.xq_scales < t.hq_codes < t.hq_scales < need
