@@ -103,6 +103,34 @@ __device__ __forceinline__ Nvfp4Block nvfp4_quant16(const float (&v)[16]) {
         b.code[k >> 3] |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * (k & 7));
     return b;
 }
+// The same for half a block per lane: lanes 2k and 2k + 1 hold the two
+// halves of one block (and are both active); the block maximum comes from
+// the partner lane (quad_perm [1,0,3,2]).  code packs the lane's 8 codes.
+struct Nvfp4Half {
+    uint32_t sb, code;
+};
+__device__ __forceinline__ Nvfp4Half nvfp4_quant8_pair(const float (&v)[8]) {
+    float amax = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, true)));
+    Nvfp4Half b;
+    b.sb = e4m3fn_rne_sat(__fdiv_rn(amax, 6.0f));
+    const E2m1Thresholds th = e2m1_thresholds(e4m3fn_to_f32(b.sb));
+    b.code = 0u;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) b.code |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * k);
+    return b;
+}
+__device__ __forceinline__ void nvfp4_dequant8(const Nvfp4Half& b, float (&out)[8]) {
+    const float s = e4m3fn_to_f32(b.sb);
+    const f32x2 p[4] = {fp4x2_f32<0>(b.code), fp4x2_f32<1>(b.code), fp4x2_f32<2>(b.code), fp4x2_f32<3>(b.code)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        out[2 * j] = p[j][0] * s;
+        out[2 * j + 1] = p[j][1] * s;
+    }
+}
 __device__ __forceinline__ void nvfp4_dequant16(const Nvfp4Block& b, float (&out)[16]) {
     const float s = e4m3fn_to_f32(b.sb);
 #pragma unroll

@@ -448,30 +448,29 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
         }
     } else if constexpr (A4) {
-        // the waves that do not poll quantize x to NVFP4, one block of 16
-        // per thread, into LDS as bf16 of the dequantized values
+        // the waves that do not poll quantize x to NVFP4, half a block of
+        // 16 per thread (lane pairs share a block), into LDS as bf16 of the
+        // dequantized values
         const int npw = (a.E + 63) / 64;
         const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
-        for (int t = iw * 64 + lane; t < a.H / 16; t += nidle * 64) {
-            const uint4 v0 = *reinterpret_cast<const uint4*>(a.x + 16 * t);
-            const uint4 v1 = *reinterpret_cast<const uint4*>(a.x + 16 * t + 8);
-            const uint32_t in[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            float f[16];
+        for (int t = iw * 64 + lane; t < a.H / 8; t += nidle * 64) {
+            const uint4 v = *reinterpret_cast<const uint4*>(a.x + 8 * t);
+            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
+            float f[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < 4; ++j) {
                 f[2 * j] = bf16_bits_to_f32(in[j] & 0xffffu);
                 f[2 * j + 1] = bf16_bits_to_f32(in[j] >> 16);
             }
-            const Nvfp4Block b = nvfp4_quant16(f);
-            nvfp4_dequant16(b, f);
-            uint32_t o[8];
+            const Nvfp4Half b = nvfp4_quant8_pair(f);
+            nvfp4_dequant8(b, f);
+            uint32_t o[4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
-            s_x[2 * t] = make_uint4(o[0], o[1], o[2], o[3]);
-            s_x[2 * t + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+            for (int j = 0; j < 4; ++j) o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
+            s_x[t] = make_uint4(o[0], o[1], o[2], o[3]);
             if (blockIdx.x == 0) {
-                *reinterpret_cast<uint2*>(a.xq_codes + 8 * t) = make_uint2(b.code[0], b.code[1]);
-                a.xq_scales[t] = (uint8_t)b.sb;
+                *reinterpret_cast<uint32_t*>(a.xq_codes + 4 * t) = b.code;
+                if ((t & 1) == 0) a.xq_scales[t / 2] = (uint8_t)b.sb;
             }
         }
     }
@@ -787,29 +786,23 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
     __syncthreads();
     if constexpr (A4) {
-        // h of the workgroup's slots to NVFP4, in place (block t of the run
-        // for thread t; a block never straddles two slots, I % 16 == 0); the
-        // workgroup holding a slot's first down unit writes its code taps
+        // h of the workgroup's slots to NVFP4, in place (half block t of the
+        // run for thread t, lane pairs sharing a block; a block never
+        // straddles two slots, I % 16 == 0); the workgroup holding a slot's
+        // first down unit writes its code taps
         const int nh = (sl1 - sl0 + 1) * a.I;
-        for (int t = threadIdx.x; t < nh / 16; t += 64 * kWaves) {
-            float4* hp = reinterpret_cast<float4*>(&s_h[16 * t]);
-            float f[16];
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const float4 v = hp[k];
-                f[4 * k] = v.x;
-                f[4 * k + 1] = v.y;
-                f[4 * k + 2] = v.z;
-                f[4 * k + 3] = v.w;
-            }
-            const Nvfp4Block b = nvfp4_quant16(f);
-            nvfp4_dequant16(b, f);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) hp[k] = make_float4(f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
-            const int slot = sl0 + (16 * t) / a.I, col = 16 * t - (slot - sl0) * a.I;
+        for (int t = threadIdx.x; t < nh / 8; t += 64 * kWaves) {
+            float4* hp = reinterpret_cast<float4*>(&s_h[8 * t]);
+            const float4 v0 = hp[0], v1 = hp[1];
+            float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+            const Nvfp4Half b = nvfp4_quant8_pair(f);
+            nvfp4_dequant8(b, f);
+            hp[0] = make_float4(f[0], f[1], f[2], f[3]);
+            hp[1] = make_float4(f[4], f[5], f[6], f[7]);
+            const int slot = sl0 + (8 * t) / a.I, col = 8 * t - (slot - sl0) * a.I;
             if ((slot * dpu) / kWaves == (int)blockIdx.x) {
-                *reinterpret_cast<uint2*>(a.hq_codes + (size_t)slot * (a.I / 2) + col / 2) = make_uint2(b.code[0], b.code[1]);
-                a.hq_scales[(size_t)slot * (a.I / 16) + col / 16] = (uint8_t)b.sb;
+                *reinterpret_cast<uint32_t*>(a.hq_codes + (size_t)slot * (a.I / 2) + col / 2) = b.code;
+                if ((t & 1) == 0) a.hq_scales[(size_t)slot * (a.I / 16) + col / 16] = (uint8_t)b.sb;
             }
         }
         __syncthreads();
