@@ -136,23 +136,25 @@ def build_stack(torch, g, synth, fmt, shared=False, w4a4=False):
             ex = g.Experts(g.INT4_G64, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"])
         r = g.Router(dev(wg), dev(b), K)
         L = dict(ex=ex, r=r, x=dev(x), y=torch.empty((1, H), dtype=torch.int16, device="cuda"))
+        L["w4a4"] = w4a4
         if shared:
             sh = synth.shared_fp8(SEED, fam, li, H, S_SHARED)
             L["sh"] = g.SharedFp8(dev(sh["up_codes"]), dev(sh["down_codes"]), sh["up_wscale"], sh["up_iscale"],
                                   sh["down_wscale"], sh["down_iscale"])
-            L["ws"] = g.workspace(g.q4moe_w4a16_decode_shared_ws_bytes(r, ex, L["sh"], 1))
-        elif w4a4:
-            L["w4a4"] = True
-            L["ws"] = g.workspace(g.q4moe_w4a4_decode_ws_bytes(r, ex, 1))
+            wsb = (g.q4moe_w4a4_decode_shared_ws_bytes if w4a4 else g.q4moe_w4a16_decode_shared_ws_bytes)(
+                r, ex, L["sh"], 1)
         else:
-            L["ws"] = g.workspace(g.q4moe_w4a16_decode_ws_bytes(r, ex, 1))
+            wsb = (g.q4moe_w4a4_decode_ws_bytes if w4a4 else g.q4moe_w4a16_decode_ws_bytes)(r, ex, 1)
+        L["ws"] = g.workspace(wsb)
         layers.append(L)
     log(f"{fmt} stack{' + shared expert' if shared else ''}{' (W4A4)' if w4a4 else ''} resident ({LAYERS} layers)")
     return layers
 
 
 def decode_call(g, L):
-    if L.get("w4a4"):
+    if L["w4a4"] and "sh" in L:
+        g.q4moe_w4a4_decode_shared(L["r"], L["ex"], L["sh"], L["x"], L["y"], ws=L["ws"])
+    elif L["w4a4"]:
         g.q4moe_w4a4_decode(L["r"], L["ex"], L["x"], L["y"], ws=L["ws"])
     elif "sh" in L:
         g.q4moe_w4a16_decode_shared(L["r"], L["ex"], L["sh"], L["x"], L["y"], ws=L["ws"])
@@ -366,6 +368,16 @@ def main():
                                       "flags": fa}
         log(f"nvfp4 W4A4 single-token stack: {extra['w4a4_decode_stack']}")
         del a4l
+        torch.cuda.empty_cache()
+        a4s = build_stack(torch, g, synth, "nvfp4", shared=True, w4a4=True)
+        msb, mkb, fb, perb = time_stack(torch, g, a4s, args.steps, args.warmup)
+        extra["w4a4_shared_stack"] = {"us_per_layer": round(1000.0 * msb / LAYERS, 3),
+                                      "hbm_gbps": round(bs / (msb / LAYERS * 1e-3) / 1e9, 1),
+                                      "tokens_per_s": round(1000.0 / msb, 1), "single_launch_us": round(mkb * 1e3, 3),
+                                      "us_per_layer_spread": spread(perb / LAYERS), "bytes_per_layer": bs,
+                                      "flags": fb}
+        log(f"nvfp4 W4A4 + fp8 shared expert single-token stack: {extra['w4a4_shared_stack']}")
+        del a4s
         torch.cuda.empty_cache()
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
 

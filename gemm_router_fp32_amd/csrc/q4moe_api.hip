@@ -580,10 +580,6 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
             f.xq_scales = at<uint8_t>(ws, l.xq_s);
             f.hq_codes = at<uint8_t>(ws, l.hq_c);
             f.hq_scales = at<uint8_t>(ws, l.hq_s);
-            st = launch_fused<FMT_NVFP4, false, true>(f, s);
-            if (st == Q4MOE_EUNSUPPORTED)
-                return fail(st, "the W4A4 decode's single launch does not fit this device and shape");
-            return st;
         }
         if (sh) {
             f.S = sh->inter;
@@ -597,9 +593,12 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
             f.sh_xq = at<uint8_t>(ws, l.sh_xq);
             f.sh_h = at<float>(ws, l.sh_h);
             f.sh_hq = at<uint8_t>(ws, l.sh_hq);
-            st = launch_fused<FMT_NVFP4, true>(f, s);
+        }
+        if (sh || a4) {  // these variants have no multi-launch fallback
+            st = sh ? (a4 ? launch_fused<FMT_NVFP4, true, true>(f, s) : launch_fused<FMT_NVFP4, true, false>(f, s))
+                    : launch_fused<FMT_NVFP4, false, true>(f, s);
             if (st == Q4MOE_EUNSUPPORTED)
-                return fail(st, "the shared expert's single launch does not fit this device and shape");
+                return fail(st, "the single launch does not fit this device and shape");
             return st;
         }
         st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
@@ -702,6 +701,35 @@ q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* 
     out->xq_scales = l.xq_s;
     out->hq_codes = l.hq_c;
     out->hq_scales = l.hq_s;
+    return Q4MOE_OK;
+}
+
+size_t q4moe_w4a4_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
+                                         const q4moe_shared_fp8* sh, int32_t n_tok) {
+    if (!r || !ex || !sh || n_tok < 1) return 0;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter, true).total;
+}
+
+q4moe_status q4moe_w4a4_decode_shared(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
+                                      const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids,
+                                      float* w, void* ws, size_t ws_bytes, void* stream) {
+    if (!sh) return fail(Q4MOE_EINVAL, "shared expert descriptor is NULL");
+    return decode_impl(r, ex, sh, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream, true);
+}
+
+q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                           const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_w4a4_shared_taps* out) {
+    if (!r || !ex || !sh || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter, true);
+    out->y32 = l.y32;
+    out->h32 = l.h;
+    out->xq_codes = l.xq_c;
+    out->xq_scales = l.xq_s;
+    out->hq_codes = l.hq_c;
+    out->hq_scales = l.hq_s;
+    out->sh_xq = l.sh_xq;
+    out->sh_h32 = l.sh_h;
+    out->sh_hq = l.sh_hq;
     return Q4MOE_OK;
 }
 

@@ -429,28 +429,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
             vb = get_tag(src);
         }
-    } else if constexpr (SH) {
-        // the waves that do not poll quantize x for the shared expert into
-        // LDS (eight values per thread), as bf16 of the E4M3FN codes
-        const int npw = (a.E + 63) / 64;
-        const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
-        for (int t = iw * 64 + lane; t < a.H / 8; t += nidle * 64) {
-            const uint4 v = *reinterpret_cast<const uint4*>(a.x + 8 * t);
-            const uint32_t in[4] = {v.x, v.y, v.z, v.w};
-            uint32_t cw[2] = {0u, 0u};
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t bits = (j & 1) ? in[j >> 1] >> 16 : in[j >> 1] & 0xffffu;
-                cw[j >> 2] |= fp8_act_code(bf16_bits_to_f32(bits), a.su_in) << (8 * (j & 3));
-            }
-            const uint2 b0 = fp8x4_bf16(cw[0]), b1 = fp8x4_bf16(cw[1]);
-            *reinterpret_cast<uint4*>(&s_xb[4 * t]) = make_uint4(b0.x, b0.y, b1.x, b1.y);
-            if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
-        }
-    } else if constexpr (A4) {
-        // the waves that do not poll quantize x to NVFP4, half a block of
-        // 16 per thread (lane pairs share a block), into LDS as bf16 of the
-        // dequantized values
+    } else if constexpr (SH || A4) {
+        // The waves that do not poll quantize x, eight values per thread:
+        // for the shared expert to E4M3FN codes (into LDS as their bf16
+        // values), for W4A4 to NVFP4 (lane pairs share a block of 16; into
+        // LDS as bf16 of the exact dequantized values).
         const int npw = (a.E + 63) / 64;
         const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
         for (int t = iw * 64 + lane; t < a.H / 8; t += nidle * 64) {
@@ -462,15 +445,26 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 f[2 * j] = bf16_bits_to_f32(in[j] & 0xffffu);
                 f[2 * j + 1] = bf16_bits_to_f32(in[j] >> 16);
             }
-            const Nvfp4Half b = nvfp4_quant8_pair(f);
-            nvfp4_dequant8(b, f);
-            uint32_t o[4];
+            if constexpr (SH) {
+                uint32_t cw[2] = {0u, 0u};
 #pragma unroll
-            for (int j = 0; j < 4; ++j) o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
-            s_x[t] = make_uint4(o[0], o[1], o[2], o[3]);
-            if (blockIdx.x == 0) {
-                *reinterpret_cast<uint32_t*>(a.xq_codes + 4 * t) = b.code;
-                if ((t & 1) == 0) a.xq_scales[t / 2] = (uint8_t)b.sb;
+                for (int j = 0; j < 8; ++j) cw[j >> 2] |= fp8_act_code(f[j], a.su_in) << (8 * (j & 3));
+                const uint2 b0 = fp8x4_bf16(cw[0]), b1 = fp8x4_bf16(cw[1]);
+                *reinterpret_cast<uint4*>(&s_xb[4 * t]) = make_uint4(b0.x, b0.y, b1.x, b1.y);
+                if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
+            }
+            if constexpr (A4) {
+                const Nvfp4Half b = nvfp4_quant8_pair(f);
+                nvfp4_dequant8(b, f);
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
+                s_x[t] = make_uint4(o[0], o[1], o[2], o[3]);
+                if (blockIdx.x == 0) {
+                    *reinterpret_cast<uint32_t*>(a.xq_codes + 4 * t) = b.code;
+                    if ((t & 1) == 0) a.xq_scales[t / 2] = (uint8_t)b.sb;
+                }
             }
         }
     }

@@ -55,6 +55,11 @@ class W4A4TokenTaps(ctypes.Structure):
                 ("hq_scales", _sz)]
 
 
+class W4A4SharedTaps(ctypes.Structure):
+    _fields_ = [("y32", _sz), ("h32", _sz), ("xq_codes", _sz), ("xq_scales", _sz), ("hq_codes", _sz),
+                ("hq_scales", _sz), ("sh_xq", _sz), ("sh_h32", _sz), ("sh_hq", _sz)]
+
+
 class Q4moeError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"{msg} (status {status})")
@@ -74,6 +79,9 @@ _SIGS = {
     "q4moe_w4a4_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_taps": (_i32, [_p, _p, _i32, _p]),
+    "q4moe_w4a4_decode_shared_ws_bytes": (_sz, [_p, _p, _p, _i32]),
+    "q4moe_w4a4_decode_shared": (_i32, [_p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
+    "q4moe_w4a4_decode_shared_taps": (_i32, [_p, _p, _p, _i32, _p]),
     "q4moe_w4a16_decode_shared_ws_bytes": (_sz, [_p, _p, _p, _i32]),
     "q4moe_w4a16_decode_shared": (_i32, [_p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_decode_shared_taps": (_i32, [_p, _p, _p, _i32, _p]),
@@ -222,6 +230,28 @@ def q4moe_w4a4_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=N
         ws = workspace(q4moe_w4a4_decode_ws_bytes(router, experts, n_tok), x.device)
     _check(lib().q4moe_w4a4_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                    _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4moe_w4a4_decode_shared_ws_bytes(router, experts, shared, n_tok):
+    return lib().q4moe_w4a4_decode_shared_ws_bytes(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                                   ctypes.byref(shared.s), n_tok)
+
+
+def q4moe_w4a4_decode_shared_taps(router, experts, shared, n_tok):
+    t = W4A4SharedTaps()
+    _check(lib().q4moe_w4a4_decode_shared_taps(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                               ctypes.byref(shared.s), n_tok, ctypes.byref(t)))
+    return t
+
+
+def q4moe_w4a4_decode_shared(router, experts, shared, x, y, ids=None, w=None, ws=None, stream=None):
+    n_tok = x.shape[0]
+    if ws is None:
+        ws = workspace(q4moe_w4a4_decode_shared_ws_bytes(router, experts, shared, n_tok), x.device)
+    _check(lib().q4moe_w4a4_decode_shared(ctypes.byref(router.s), ctypes.byref(experts.s), ctypes.byref(shared.s),
+                                          _ptr(x), n_tok, _ptr(y), _ptr(ids), _ptr(w), _ptr(ws), ws.numel(),
+                                          _stream(stream)))
     return ws
 
 

@@ -202,6 +202,24 @@ typedef struct { size_t y32, h32, xq_codes, xq_scales, hq_codes, hq_scales; } q4
 q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
                                     q4moe_w4a4_token_taps* out);
 
+/* The MoE block of the W4A4 checkpoint ([W] Step 3; [C] precision table:
+ * routed experts NVFP4 W4A4, shared experts FP8 per-tensor W8A8) for one
+ * token in one launch: q4moe_w4a4_decode plus the shared expert of
+ * q4moe_w4a16_decode_shared, y = sum_i w_i z_i + z_shared rounded once. */
+size_t q4moe_w4a4_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
+                                         const q4moe_shared_fp8* sh, int32_t n_tok);
+q4moe_status q4moe_w4a4_decode_shared(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
+                                      const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids,
+                                      float* w, void* ws, size_t ws_bytes, void* stream);
+
+/* Its taps: those of q4moe_w4a4_token_taps and, for the shared expert, sh_xq
+ * uint8 [hidden], sh_h32 fp32 [inter], sh_hq uint8 [inter]. */
+typedef struct {
+    size_t y32, h32, xq_codes, xq_scales, hq_codes, hq_scales, sh_xq, sh_h32, sh_hq;
+} q4moe_w4a4_shared_taps;
+q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                           const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_w4a4_shared_taps* out);
+
 /* W4A4 routed-MoE chunk of n_tok tokens (1 <= n_tok <= 65536), NVFP4 only
  * ([W] Step 3: routed experts take 4-bit weights and activations, the
  * activations quantized on the fly per block of 16 with an E4M3FN scale

@@ -160,3 +160,18 @@ def test_w4a4_decode_validation(L):
     t = g.W4A4TokenTaps()
     assert L.q4moe_w4a4_decode_taps(ctypes.byref(r), ctypes.byref(ex), 1, ctypes.byref(t)) == g.OK
     assert t.xq_codes < t.xq_scales < t.hq_codes < t.hq_scales < need
+
+
+def test_w4a4_decode_shared_validation(L):
+    r, ex, sh = _router(), _experts(), _shared()
+    def call(ex_, sh_, T=1, wsb=1 << 30):
+        shp = None if sh_ is None else ctypes.byref(sh_)
+        return L.q4moe_w4a4_decode_shared(ctypes.byref(r), ctypes.byref(ex_), shp, A16, T, A16, None, None, A16, wsb,
+                                          None)
+    assert call(ex, None) == g.EINVAL
+    assert call(ex, sh, T=2) == g.EUNSUPPORTED
+    assert call(_experts(fmt=2), sh) == g.EUNSUPPORTED
+    assert call(ex, _shared(S=100)) == g.EINVAL
+    need = L.q4moe_w4a4_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)
+    assert need > L.q4moe_w4a4_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+    assert call(ex, sh, wsb=need - 1) == g.EWORKSPACE

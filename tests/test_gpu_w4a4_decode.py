@@ -105,3 +105,66 @@ def test_w4a4_decode_exact_activations_equal_w4a16():
     t = g.q4moe_w4a16_decode_taps(router, ex, 1)
     h16 = host(ws)[t.h: t.h + K * 192 * 4].view(np.float32).reshape(K, 192)
     assert np.array_equal(a4["h32"].view(np.uint32), h16.view(np.uint32))
+
+
+# --- with the FP8 shared expert (the W4A4 checkpoint's whole MoE block) -------
+
+def run_w4a4_shared(router, ex, sh_dev, x_np):
+    H, I, S = ex.hidden, ex.inter, sh_dev.inter
+    y = torch.empty((1, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((1, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((1, K), dtype=torch.float32, device=DEV)
+    ws = g.q4moe_w4a4_decode_shared(router, ex, sh_dev, dev(x_np), y, ids, w)
+    torch.cuda.synchronize()
+    t = g.q4moe_w4a4_decode_shared_taps(router, ex, sh_dev, 1)
+    b = host(ws)
+
+    def view(off, n, dt):
+        return b[off: off + n * np.dtype(dt).itemsize].view(dt).copy()
+
+    return dict(y=host(y, np.uint16), ids=host(ids), w=host(w),
+                y32=view(t.y32, H, np.float32).reshape(1, H),
+                h32=view(t.h32, K * I, np.float32).reshape(K, I),
+                xq_codes=view(t.xq_codes, H // 2, np.uint8).reshape(1, H // 2),
+                xq_scales=view(t.xq_scales, H // 16, np.uint8).reshape(1, H // 16),
+                hq_codes=view(t.hq_codes, K * I // 2, np.uint8).reshape(K, I // 2),
+                hq_scales=view(t.hq_scales, K * I // 16, np.uint8).reshape(K, I // 16),
+                sh_xq=view(t.sh_xq, H, np.uint8), sh_h32=view(t.sh_h32, S, np.float32),
+                sh_hq=view(t.sh_hq, S, np.uint8))
+
+
+@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (128, 2688, 1856, 3712)])
+def test_w4a4_decode_with_shared_expert(E, H, I, S):
+    from test_gpu_shared import upload_shared
+    L = layer(SEED + S, synth.FAM_W4A4, 1, E, H, I, 1, K, "nvfp4")
+    sh = synth.shared_fp8(SEED, synth.FAM_W4A4, S, H, S)
+    out = run_w4a4_shared(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), upload_shared(sh),
+                          L["x"])
+    r = L["route"]
+    assert np.array_equal(out["ids"], r["ids"])
+    np.testing.assert_allclose(out["w"], r["w"], rtol=1e-5)
+    ob = oracle.Bank.from_dict(oracle.NVFP4, L["bank"])
+    xf = bf16_bits_to_f64(L["x"]).astype(np.float32)
+    # routed stages
+    xc, xs = oracle.quant_nvfp4(xf)
+    assert np.array_equal(out["xq_codes"], xc) and np.array_equal(out["xq_scales"], xs)
+    u = oracle.w4a4_up(ob, r["ids"], out["xq_codes"], out["xq_scales"])[0]
+    ok, worst_h = gate_f32(out["h32"], np.maximum(u, 0.0) ** 2)
+    assert ok, f"h gate exceeded ({worst_h:.3f})"
+    hc, hs = oracle.quant_nvfp4(out["h32"])
+    assert np.array_equal(out["hq_codes"], hc) and np.array_equal(out["hq_scales"], hs)
+    # shared stages
+    assert np.array_equal(out["sh_xq"], oracle.fp8_quant(xf[0], sh["up_iscale"]))
+    us = oracle.fp8_gemv(sh["up_codes"], out["sh_xq"], sh["up_wscale"], sh["up_iscale"])
+    ok, worst_sh = gate_f32(out["sh_h32"][None], (np.maximum(us, 0.0) ** 2)[None])
+    assert ok, f"shared h gate exceeded ({worst_sh:.3f})"
+    assert np.array_equal(out["sh_hq"], oracle.fp8_quant(out["sh_h32"], sh["down_iscale"]))
+    # output: routed down + combine on the GPU's h codes, plus the shared down
+    yhat = oracle.w4a4_down_combine(ob, r["ids"], r["w"], out["hq_codes"], out["hq_scales"])[0]
+    yhat = yhat + oracle.fp8_gemv(sh["down_codes"], out["sh_hq"], sh["down_wscale"], sh["down_iscale"])
+    ok, worst = gate_out(out["y"], yhat[None])
+    assert ok, f"bf16 output gate exceeded: worst {worst:.3f}"
+    ok32, worst32 = gate_f32(out["y32"], yhat[None])
+    assert ok32, f"fp32 output gate exceeded: worst {worst32:.3f}"
+    assert np.array_equal(out["y"], bf16_rne_of_f32(out["y32"]))
+    print(f"w4a4 + shared E={E}: worst bf16 ratio {worst:.3f}, h {worst_h:.5f}, shared h {worst_sh:.5f}")
