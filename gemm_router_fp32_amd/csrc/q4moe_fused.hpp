@@ -307,6 +307,18 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 
     // x into LDS once per workgroup (the up GEMV reads it from there)
     if (!A4 && (int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+    // x pieces the waves that will not poll the scores quantize during the
+    // score hand-off (eight values each, at most two per thread: H / 8 <= 512
+    // pieces over at least four such waves), loaded now with the router's
+    // loads; every thread loads, clamped into x, and the pollers' are unused
+    const int npw = (a.E + 63) / 64;
+    const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
+    uint4 xqv[2];
+    if constexpr (SH || A4) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            xqv[i] = *reinterpret_cast<const uint4*>(a.x + 8 * min(iw * 64 + lane + i * nidle * 64, a.H / 8 - 1));
+    }
 
     // Shared expert: its weights do not depend on the routing, so they
     // stream while the router runs (the loads leave in two bursts, below).
@@ -434,10 +446,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         // for the shared expert to E4M3FN codes (into LDS as their bf16
         // values), for W4A4 to NVFP4 (lane pairs share a block of 16; into
         // LDS as bf16 of the exact dequantized values).
-        const int npw = (a.E + 63) / 64;
-        const int iw = wave < 2 ? wave : wave - npw, nidle = kWaves - npw;
-        for (int t = iw * 64 + lane; t < a.H / 8; t += nidle * 64) {
-            const uint4 v = *reinterpret_cast<const uint4*>(a.x + 8 * t);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int t = iw * 64 + lane + i * nidle * 64;
+            if (t >= a.H / 8) break;
+            const uint4 v = xqv[i];
             const uint32_t in[4] = {v.x, v.y, v.z, v.w};
             float f[8];
 #pragma unroll
