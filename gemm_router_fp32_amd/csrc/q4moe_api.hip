@@ -204,6 +204,12 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     // shared expert: at most 4 h-code quads (16 up rows) per workgroup and
     // two down rows per wave
     if (SH && (a.S / 4 > 4LL * grid || a.H > 2 * nw)) return Q4MOE_EUNSUPPORTED;
+    // W4A4: a workgroup's up rows are whole 16-row blocks
+    if (A4) {
+        const long long wg_rows = 16 * ((RU / 16 + grid - 1) / grid);
+        if (RU % 16 != 0 || wg_rows > kMaxWgUp || (wg_rows + kWaves - 1) / kWaves > 2 * kMaxUp)
+            return Q4MOE_EUNSUPPORTED;
+    }
     hipLaunchKernelGGL((k_decode_fused<FMT, C, C2, SH, A4>), dim3(grid), dim3(64 * kWaves), 0, s, a);
     return launched("fused decode");
 }

@@ -395,8 +395,21 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 
     // unit bookkeeping (routing-independent: done while the scores travel)
     const int RU = a.K * a.I;
-    const int u0 = share_lo(RU, gw, NW), u1 = share_lo(RU, gw + 1, NW);
-    const int wu0 = share_lo(RU, blockIdx.x * kWaves, NW), wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
+    int u0, u1, wu0, wu1;
+    if constexpr (A4) {
+        // W4A4: a workgroup owns whole 16-row blocks of h (the quantizer's
+        // blocks), so that it can quantize them itself before publishing
+        const int nbk = RU / 16;
+        wu0 = 16 * share_lo(nbk, blockIdx.x, gridDim.x);
+        wu1 = 16 * share_lo(nbk, blockIdx.x + 1, gridDim.x);
+        u0 = wu0 + share_lo(wu1 - wu0, wave, kWaves);
+        u1 = wu0 + share_lo(wu1 - wu0, wave + 1, kWaves);
+    } else {
+        u0 = share_lo(RU, gw, NW);
+        u1 = share_lo(RU, gw + 1, NW);
+        wu0 = share_lo(RU, blockIdx.x * kWaves, NW);
+        wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
+    }
     // A wave's up units span at most two slots: slot(u) = us0 + (u >= ubnd).
     const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
     const int n_up_pass = (u1 - u0 + 1) / 2;  // <= kMaxUp (checked on the host)
@@ -694,9 +707,32 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             const int u = wu0 + j;
             const int slot = u / a.I, r = u - slot * a.I;
             const float v = s_hrow[j];
+            if constexpr (!A4) {
 #pragma unroll
-            for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.h_tag + ((size_t)rp * a.K + slot) * a.I + r, v, ep);
+                for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.h_tag + ((size_t)rp * a.K + slot) * a.I + r, v, ep);
+            }
             a.h[(size_t)slot * a.I + r] = v;
+        }
+        if constexpr (A4) {
+            // the workgroup's h blocks to NVFP4 (lane pairs: half a block
+            // each), published as one (8 codes, epoch) value per half block
+            // and one (scale, epoch) value per block, kReplicas copies each
+            // (per copy: K I / 8 code values, then K I / 16 scale values)
+            if (j < (wu1 - wu0) / 8) {
+                float f[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) f[k] = s_hrow[8 * j + k];
+                const Nvfp4Half b = nvfp4_quant8_pair(f);
+                const int hb = wu0 / 8 + j;  // global half-block index (slot-major)
+                const size_t per = (size_t)(RU / 8 + RU / 16);
+#pragma unroll
+                for (int rp = 0; rp < kReplicas; ++rp) {
+                    put_tag(a.h_tag + rp * per + hb, __uint_as_float(b.code), ep);
+                    if ((j & 1) == 0) put_tag(a.h_tag + rp * per + RU / 8 + hb / 2, __uint_as_float(b.sb), ep);
+                }
+                *reinterpret_cast<uint32_t*>(a.hq_codes + (size_t)hb * 4) = b.code;
+                if ((j & 1) == 0) a.hq_scales[hb / 2] = (uint8_t)b.sb;
+            }
         }
     }
     if constexpr (SH) {
@@ -752,7 +788,58 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         for (int p = 0; p < 2; ++p)
             if (lane == 63 && sd0 + p < sd1) put_tag(a.z_tag + (uint32_t)(a.K * a.H + sd0 + p), zsh[p] * sc, ep);
     }
-    {
+    if constexpr (A4) {
+        // W4A4: the NVFP4 h of slots sl0 .. sl1 (one run of at most 1024
+        // half blocks), thread t taking half blocks t and t + 512: its codes
+        // and its block's scale, decoded exactly into LDS as fp32
+        const int nhb = (sl1 - sl0 + 1) * a.I / 8, hb0 = sl0 * a.I / 8;
+        const size_t per = (size_t)(RU / 8 + RU / 16);
+        const unsigned long long* src = a.h_tag + rep * per;
+        uint32_t pend = 0;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+            if ((int)threadIdx.x + 512 * m < nhb) pend |= 5u << m;  // bit m: codes, bit m + 2: scale
+        uint32_t cw[2] = {0u, 0u}, sw[2] = {0u, 0u};
+        for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
+            unsigned long long v[4];
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                const int hb = hb0 + (int)threadIdx.x + 512 * m;
+                v[m] = (pend >> m) & 1u ? get_tag(src + hb) : 0ull;
+                v[m + 2] = (pend >> (m + 2)) & 1u ? get_tag(src + RU / 8 + hb / 2) : 0ull;
+            }
+#pragma unroll
+            for (int m = 0; m < 2; ++m) {
+                if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
+                    cw[m] = (uint32_t)v[m];
+                    pend &= ~(1u << m);
+                }
+                if (((pend >> (m + 2)) & 1u) && tag_is(v[m + 2], ep)) {
+                    sw[m] = (uint32_t)v[m + 2];
+                    pend &= ~(1u << (m + 2));
+                }
+            }
+            if (polls > kPollLimit) {
+                if (lane == 0) atomicOr(flags, 1u);
+                break;
+            }
+            if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
+        }
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+            const int t = (int)threadIdx.x + 512 * m;
+            if (t < nhb) {
+                Nvfp4Half b;
+                b.code = cw[m];
+                b.sb = sw[m] & 0xffu;
+                float f[8];
+                nvfp4_dequant8(b, f);
+                float4* hp = reinterpret_cast<float4*>(&s_h[8 * t]);
+                hp[0] = make_float4(f[0], f[1], f[2], f[3]);
+                hp[1] = make_float4(f[4], f[5], f[6], f[7]);
+            }
+        }
+    } else {
         // the slots sl0 .. sl1 are adjacent in the [K][I] layout, so their h
         // is one run of nh <= 2 * 4096 = 16 * 512 values
         const int nh = (sl1 - sl0 + 1) * a.I;
@@ -792,28 +879,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     __syncthreads();
-    if constexpr (A4) {
-        // h of the workgroup's slots to NVFP4, in place (half block t of the
-        // run for thread t, lane pairs sharing a block; a block never
-        // straddles two slots, I % 16 == 0); the workgroup holding a slot's
-        // first down unit writes its code taps
-        const int nh = (sl1 - sl0 + 1) * a.I;
-        for (int t = threadIdx.x; t < nh / 8; t += 64 * kWaves) {
-            float4* hp = reinterpret_cast<float4*>(&s_h[8 * t]);
-            const float4 v0 = hp[0], v1 = hp[1];
-            float f[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-            const Nvfp4Half b = nvfp4_quant8_pair(f);
-            nvfp4_dequant8(b, f);
-            hp[0] = make_float4(f[0], f[1], f[2], f[3]);
-            hp[1] = make_float4(f[4], f[5], f[6], f[7]);
-            const int slot = sl0 + (8 * t) / a.I, col = 8 * t - (slot - sl0) * a.I;
-            if ((slot * dpu) / kWaves == (int)blockIdx.x) {
-                *reinterpret_cast<uint32_t*>(a.hq_codes + (size_t)slot * (a.I / 2) + col / 2) = b.code;
-                if ((t & 1) == 0) a.hq_scales[(size_t)slot * (a.I / 16) + col / 16] = (uint8_t)b.sb;
-            }
-        }
-        __syncthreads();
-    }
     Q4MOE_PHASE(5);
 
     // ---- D: a wave computes z = w * g * (W_down h) for its 8 rows of slot
