@@ -390,7 +390,7 @@ def main():
     from gemm_router_fp32_amd.pmc_traffic import read_traffic
     # HBM bytes per launch from the committed counter passes (None once the
     # kernel's sources differ from the ones the counters were taken on)
-    traffic = read_traffic(os.path.join(ROOT, TRAFFIC_PROFILE), "k_decode_fused<1,3,1,false>")
+    traffic = read_traffic(os.path.join(ROOT, TRAFFIC_PROFILE), "k_decode_fused<1,3,1,false,false>")
     out = {
         "metric": METRIC,
         "value": round(us_layer, 4),
