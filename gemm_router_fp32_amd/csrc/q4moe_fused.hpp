@@ -834,9 +834,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 b.sb = sw[m] & 0xffu;
                 float f[8];
                 nvfp4_dequant8(b, f);
-                float4* hp = reinterpret_cast<float4*>(&s_h[8 * t]);
-                hp[0] = make_float4(f[0], f[1], f[2], f[3]);
-                hp[1] = make_float4(f[4], f[5], f[6], f[7]);
+                // as bf16 pairs (exact: at most 6 significant bits)
+                uint32_t o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
+                reinterpret_cast<uint4*>(s_h)[t] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
     } else {
@@ -887,7 +890,35 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // store.
     if (dwave) {
         float zp[kDownRows];  // this lane's part of each row
-        if constexpr (FMT == FMT_NVFP4) {
+        if constexpr (A4) {
+            // W4A4: h is exact in bf16, so one dot2 per weight pair
+            uint32_t hb[C2][16];
+#pragma unroll
+            for (int c = 0; c < C2; ++c) {
+                const int ch = min(lane * C2 + c, nchI - 1);
+                const uint4* hp = reinterpret_cast<const uint4*>(s_h) + ((dslot - sl0) * a.I + ch * 32) / 8;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const uint4 v = hp[k];
+                    hb[c][4 * k + 0] = v.x;
+                    hb[c][4 * k + 1] = v.y;
+                    hb[c][4 * k + 2] = v.z;
+                    hb[c][4 * k + 3] = v.w;
+                }
+            }
+#pragma unroll
+            for (int p = 0; p < kDownRows; ++p) {
+                float zz = 0.f;
+#pragma unroll
+                for (int c = 0; c < C2; ++c) {
+                    const bool chok = lane * C2 + c < nchI;
+                    const f32x2 sp = e4m3fn_x2_f32(sd[p][c]);
+                    const float s0 = chok ? sp[0] : 0.f, s1 = chok ? sp[1] : 0.f;
+                    zz += nvfp4_chunk_bf16(qd[p][c], hb[c], s0, s1);
+                }
+                zp[p] = zz;
+            }
+        } else if constexpr (FMT == FMT_NVFP4) {
             float hv[C2][32];
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
