@@ -1,4 +1,4 @@
-// One-launch W4A16 routed-MoE decode of a single token on gfx950.
+// One-launch routed-MoE decode of a single token on gfx950.
 //
 // Batch-1 decode reads every active weight once and does almost no
 // arithmetic per byte ("Let's optimize Nemotron 3.5 Lightning - a worklog",
@@ -40,6 +40,17 @@
 // its XCD), so no single line or memory channel serves the whole chip.
 // Every poll is bounded; on expiry the kernel flags the workspace and carries
 // on, so it always ends.
+//
+// Two variants ride on the same phases ("Let's optimize Nemotron 3.5
+// Lightning - a worklog", Step 3; the W4A4 model card's precision table):
+//   SH  the FP8 per-tensor W8A8 shared expert: its weights stream while the
+//       router runs, x is coded during the score hand-off, its h codes are
+//       exchanged four per value ahead of the routed h, its down rows run
+//       during the routed h hand-off, and its z is one more combine slot.
+//   A4  W4A4 routed experts: x and h quantized to NVFP4 inside the launch
+//       (h by the workgroup that makes it, which then publishes codes and
+//       scales instead of fp32 h), the GEMVs running on the exact bf16
+//       values of the quantized activations.
 #pragma once
 
 #include "q4moe_kernels.hpp"
