@@ -78,7 +78,8 @@ def check_shared(L, sh, out):
     return worst, worst32, worst_h, ok_e2e, worst_e2e
 
 
-@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (16, 256, 192, 64), (32, 512, 320, 192)])
+@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (16, 256, 192, 64), (32, 512, 320, 192),
+                                     (200, 2688, 256, 4096)])
 def test_decode_shared_small(E, H, I, S):
     L = layer(SEED + S, synth.FAM_NVFP4, 0, E, H, I, 1, K, "nvfp4")
     sh = synth.shared_fp8(SEED, FAM_SH, S, H, S)

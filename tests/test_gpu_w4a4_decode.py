@@ -69,8 +69,10 @@ def check_w4a4_decode(L, out):
     return worst, worst_h, ok_e, worst_e, flips
 
 
-@pytest.mark.parametrize("E,H,I", [(16, 256, 192), (32, 512, 320)])
+@pytest.mark.parametrize("E,H,I", [(16, 256, 192), (32, 512, 320), (200, 2688, 256)])
 def test_w4a4_decode_small(E, H, I):
+    # (200, 2688): four polling waves, so the four others quantize x's 336
+    # pieces in two passes
     L = layer(SEED + H, synth.FAM_W4A4, 0, E, H, I, 1, K, "nvfp4")
     out = run_w4a4_decode(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), L["x"])
     check_w4a4_decode(L, out)
@@ -133,7 +135,7 @@ def run_w4a4_shared(router, ex, sh_dev, x_np):
                 sh_hq=view(t.sh_hq, S, np.uint8))
 
 
-@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (128, 2688, 1856, 3712)])
+@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (200, 2688, 256, 192), (128, 2688, 1856, 3712)])
 def test_w4a4_decode_with_shared_expert(E, H, I, S):
     from test_gpu_shared import upload_shared
     L = layer(SEED + S, synth.FAM_W4A4, 1, E, H, I, 1, K, "nvfp4")
