@@ -71,6 +71,11 @@ def lib():
         L.q4o_fp8_quant.argtypes = [i32, p, f, p]
         L.q4o_fp8_gemv.argtypes = [i32, i32, p, p, f, f, p]
         L.q4o_shared_fp8.argtypes = [ctypes.POINTER(_Shared), p, p, p, p, p, p]
+        L.q4o_quant_weights_nvfp4.argtypes = [i32, i32, p, i32, p, p, p]
+        L.q4o_wq_gscale.restype = f
+        L.q4o_wq_gscale.argtypes = [ctypes.c_int64, p]
+        L.q4o_wq_block.restype = u32
+        L.q4o_wq_block.argtypes = [p, f, ctypes.c_int, p]
         _LIB = L
     return _LIB
 
@@ -287,3 +292,24 @@ def shared_fp8(sh, x):
     z = np.zeros(H, np.float64)
     lib().q4o_shared_fp8(ctypes.byref(d), _p(x), _p(xq), _p(u), _p(h32), _p(hq), _p(z))
     return {"xq": xq, "u": u, "h32": h32, "hq": hq, "z": z}
+
+
+# --- NVFP4 weight quantizer --------------------------------------------------
+
+def quant_weights_nvfp4(w_bits, mse=False):
+    """bf16 bits [rows, cols] -> (codes [rows, cols/2], scales [rows, cols/16], g)."""
+    w = _c(np.atleast_2d(w_bits), np.uint16)
+    rows, cols = w.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    scales = np.zeros((rows, cols // 16), np.uint8)
+    g = np.zeros(1, np.float32)
+    lib().q4o_quant_weights_nvfp4(rows, cols, _p(w), int(bool(mse)), _p(codes), _p(scales), _p(g))
+    return codes, scales, np.float32(g[0])
+
+
+def wq_block(w16_bits, g, mse=False):
+    """One block of 16: (scale byte, 8 code bytes)."""
+    w = _c(w16_bits, np.uint16).reshape(16)
+    c = np.zeros(8, np.uint8)
+    b = lib().q4o_wq_block(_p(w), float(g), int(bool(mse)), _p(c))
+    return b, c

@@ -482,3 +482,104 @@ void q4o_shared_fp8(const q4o_shared* sh, const uint16_t* x, uint8_t* xq, double
     q4o_fp8_gemv(H, S, sh->down_codes, hq, sh->down_wscale, sh->down_iscale, z);
     free(xf);
 }
+
+/* ---- NVFP4 weight quantizer ---------------------------------------------
+ * [W] Step 1 (NVFP4: 4-bit E2M1 values, an FP8 scale per 16, built with
+ * ModelOpt) and the recipe table's weight-scale selection (max-based, or an
+ * MSE per-block search over FP8 scale values).  Readings:
+ *  - per-tensor scale g = fl32(amax / 2688) (2688 = 6 * 448, the largest
+ *    E2M1 value times the largest E4M3FN value), g = 1 for an all-zero
+ *    tensor; decoded weight = e2m1 * e4m3(b) * g (as the GEMVs decode it);
+ *  - eff(b) = fl32(e4m3(b) * g); the code of w under b is the E2M1 magnitude
+ *    nearest the exact quotient |w| / eff(b), ties to the even code,
+ *    saturating at 6, with w's sign bit;
+ *  - max-based: b = E4M3FN nearest-even (saturating) of
+ *    fl32(bamax / fl32(6 * g)), bamax the block's largest |w|;
+ *  - MSE: b minimises err(b) = sum over the block, in element order, of
+ *    fl32(d * d), d = fl32(|w| - fl32(e2m1(code) * eff(b))), each step
+ *    rounded to fp32, over every positive finite E4M3FN byte 0x01..0x7E;
+ *    the lowest byte among equal minima; an all-zero block takes b = 0.
+ *  The error is taken in fp32 because the GPU takes the same decision in
+ *  fp32: both sides must round the same way for the choice to agree. */
+
+static const float kMid32[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+static const float kGrid32[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+
+/* Nearest E2M1 magnitude code of the exact quotient mag / eff (mid * eff is
+ * exact in fp64: 3 + 24 significant bits). */
+static uint32_t wq_code(float mag, float eff) {
+    uint32_t c = 0;
+    for (int j = 0; j < 7; ++j) {
+        double t = (double)kMid32[j] * (double)eff;
+        int up = ((double)mag > t) || ((double)mag == t && ((j + 1) % 2 == 0));
+        if (up) c = (uint32_t)(j + 1);
+    }
+    return c;
+}
+
+static float wq_err(const float* mag, float eff) {
+    float acc = 0.0f;
+    for (int k = 0; k < 16; ++k) {
+        volatile float q = kGrid32[wq_code(mag[k], eff)] * eff;
+        volatile float d = mag[k] - q;
+        volatile float sq = d * d;
+        acc = acc + sq;
+    }
+    return acc;
+}
+
+float q4o_wq_gscale(int64_t n, const uint16_t* w) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = fabsf((float)q4o_bf16(w[i]));
+        if (v > amax) amax = v;
+    }
+    return amax > 0.0f ? amax / 2688.0f : 1.0f;
+}
+
+/* One block of 16 bf16 weights: scale byte and 16 codes (low nibble first
+ * in 8 bytes). */
+uint32_t q4o_wq_block(const uint16_t* w, float g, int mse, uint8_t* codes8) {
+    float mag[16];
+    float bamax = 0.0f;
+    uint32_t sign[16];
+    for (int k = 0; k < 16; ++k) {
+        float v = (float)q4o_bf16(w[k]);
+        mag[k] = fabsf(v);
+        sign[k] = signbit(v) ? 8u : 0u;
+        if (mag[k] > bamax) bamax = mag[k];
+    }
+    uint32_t b = 0;
+    if (bamax > 0.0f) {
+        volatile float six_g = 6.0f * g;
+        volatile float t = bamax / six_g;
+        b = q4o_e4m3fn_from(t);
+        if (mse) {
+            float best = INFINITY;
+            for (uint32_t c = 1; c <= 0x7Eu; ++c) {
+                volatile float eff = (float)q4o_e4m3fn(c) * g;
+                float e = wq_err(mag, eff);
+                if (e < best) {
+                    best = e;
+                    b = c;
+                }
+            }
+        }
+    }
+    volatile float eff = (float)q4o_e4m3fn(b) * g;
+    for (int k = 0; k < 8; ++k) codes8[k] = 0;
+    for (int k = 0; k < 16; ++k) {
+        uint32_t c = (b == 0 ? 0u : wq_code(mag[k], eff)) | sign[k];
+        codes8[k / 2] |= (uint8_t)(k % 2 == 0 ? c : c << 4);
+    }
+    return b;
+}
+
+void q4o_quant_weights_nvfp4(int32_t rows, int32_t cols, const uint16_t* w, int32_t mse, uint8_t* codes,
+                             uint8_t* scales, float* gscale) {
+    const float g = q4o_wq_gscale((int64_t)rows * cols, w);
+    *gscale = g;
+    const int64_t nb = (int64_t)rows * cols / 16;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nb; ++i) scales[i] = (uint8_t)q4o_wq_block(w + 16 * i, g, mse, codes + 8 * i);
+}

@@ -143,6 +143,15 @@ void q4o_fp8_gemv(int32_t rows, int32_t cols, const uint8_t* w, const uint8_t* a
 void q4o_shared_fp8(const q4o_shared* sh, const uint16_t* x, uint8_t* xq, double* u, float* h32,
                     uint8_t* hq, double* z);
 
+/* NVFP4 weight quantizer of a bf16 matrix [rows][cols] (cols % 16 == 0):
+ * codes [rows][cols/2], scales [rows][cols/16], per-tensor g.  mse = 0:
+ * max-based block scales; mse = 1: per-block search over every positive
+ * finite E4M3FN scale (readings in q4moe_oracle.c).  Also its pieces. */
+void q4o_quant_weights_nvfp4(int32_t rows, int32_t cols, const uint16_t* w, int32_t mse, uint8_t* codes,
+                             uint8_t* scales, float* gscale);
+float q4o_wq_gscale(int64_t n, const uint16_t* w);
+uint32_t q4o_wq_block(const uint16_t* w, float g, int mse, uint8_t* codes8);
+
 /* bf16 bit pattern nearest to v (RNE), for chaining an oracle output. */
 uint32_t q4o_bf16_from(double v);
 
