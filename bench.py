@@ -281,6 +281,35 @@ def bench_verify(torch, g, synth, steps, stack_layer0):
             "lm_head_us_spread": spread(t_head), "cold": True, "reps": reps}
 
 
+def bench_wquant(torch, g, synth, steps):
+    """NVFP4 weight quantizer on one expert's up_proj (1856 x 2688 bf16):
+    µs per matrix in both scale modes; bytes = bf16 in + codes and scales out."""
+    from gpu_util import dev
+    w = dev(synth.bf16_normal(synth.key(SEED, 4, 0, 0), I * H, 0.0, 0.02).reshape(I, H))
+    codes = torch.empty((I, H // 2), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((I, H // 16), dtype=torch.uint8, device="cuda")
+    gs = torch.empty(1, dtype=torch.float32, device="cuda")
+    ws = g.workspace(g.q4moe_quantize_weights_ws_bytes(I, H))
+    nbytes = I * H * 2 + I * H // 2 + I * H // 16 + 4
+    out = {"matrix": [I, H], "bytes": nbytes, "warm": True}
+    for name, mode in (("max", g.WQ_MAX), ("mse", g.WQ_MSE)):
+        for _ in range(3):
+            g.q4moe_quantize_weights(w, codes, scales, gs, mode=mode, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(5, steps // 5)
+        e0.record()
+        for _ in range(reps):
+            g.q4moe_quantize_weights(w, codes, scales, gs, mode=mode, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = 1000.0 * e0.elapsed_time(e1) / reps
+        out[f"{name}_us"] = round(us, 2)
+        out[f"{name}_gbps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+    log(f"weight quantizer: {out}")
+    return out
+
+
 def cpu_baseline(seconds):
     """The oracle, as it stands, on layers of the NVFP4 stack until `seconds`
     of CPU work have run; returns microseconds per layer."""
@@ -380,6 +409,7 @@ def main():
         del a4s
         torch.cuda.empty_cache()
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
+        extra["weight_quantizer"] = bench_wquant(torch, g, synth, args.steps)
 
     cpu = None
     if not args.skip_cpu:

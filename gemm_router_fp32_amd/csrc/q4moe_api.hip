@@ -11,6 +11,7 @@
 #include "q4moe.h"
 #include "q4moe_fused.hpp"
 #include "q4moe_w4a4.hpp"
+#include "q4moe_wquant.hpp"
 
 using namespace q4moe;
 
@@ -737,6 +738,48 @@ q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_ex
     out->sh_h32 = l.sh_h;
     out->sh_hq = l.sh_hq;
     return Q4MOE_OK;
+}
+
+size_t q4moe_quantize_weights_ws_bytes(int32_t rows, int32_t cols) {
+    (void)rows;
+    (void)cols;
+    return (size_t)kWqMaxBlocks * sizeof(float);
+}
+
+q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_t cols, int32_t mode,
+                                    uint8_t* codes, uint8_t* scales, float* gscale, void* ws, size_t ws_bytes,
+                                    void* stream) {
+    if (!w_bf16 || !codes || !scales || !gscale) return fail(Q4MOE_EINVAL, "w / codes / scales / gscale is NULL");
+    if (rows < 1 || cols < 16 || cols % 16 != 0 || (long long)rows * cols > (1LL << 34))
+        return fail(Q4MOE_EINVAL, "shape %d x %d: rows >= 1, cols a positive multiple of 16, at most 2^34 weights",
+                    rows, cols);
+    if (mode != Q4MOE_WQ_MAX && mode != Q4MOE_WQ_MSE) return fail(Q4MOE_EINVAL, "unknown scale mode %d", mode);
+    if (!aligned(w_bf16, 16) || !aligned(codes, 8) || !aligned(gscale, 4))
+        return fail(Q4MOE_EALIGN, "w not 16-byte, codes not 8-byte or gscale not 4-byte aligned");
+    q4moe_status st = check_ws(ws, ws_bytes, q4moe_quantize_weights_ws_bytes(rows, cols));
+    if (st != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const size_t n8 = (size_t)rows * cols / 8, nblocks = (size_t)rows * cols / 16;
+    const int grid1 = (int)std::min<size_t>(kWqMaxBlocks, (n8 + 255) / 256);
+    float* partial = static_cast<float*>(ws);
+    hipLaunchKernelGGL(k_wq_amax, dim3(grid1), dim3(256), 0, s, reinterpret_cast<const uint4*>(w_bf16), n8, partial);
+    if ((st = launched("weight quantizer maximum")) != Q4MOE_OK) return st;
+    WqArgs a;
+    a.w = reinterpret_cast<const uint4*>(w_bf16);
+    a.nblocks = nblocks;
+    a.partial = partial;
+    a.npartial = grid1;
+    a.mse = mode;
+    a.codes = codes;
+    a.scales = scales;
+    a.gscale = gscale;
+    const dim3 grid2((unsigned)((nblocks + 255) / 256));
+    if (mode == Q4MOE_WQ_MSE)
+        hipLaunchKernelGGL(k_wq_quant<true>, grid2, dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_wq_quant<false>, grid2, dim3(256), 0, s, a);
+    return launched("weight quantizer");
 }
 
 q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,

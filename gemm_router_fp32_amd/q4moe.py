@@ -79,6 +79,8 @@ _SIGS = {
     "q4moe_w4a4_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_taps": (_i32, [_p, _p, _i32, _p]),
+    "q4moe_quantize_weights_ws_bytes": (_sz, [_i32, _i32]),
+    "q4moe_quantize_weights": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_shared_ws_bytes": (_sz, [_p, _p, _p, _i32]),
     "q4moe_w4a4_decode_shared": (_i32, [_p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_shared_taps": (_i32, [_p, _p, _p, _i32, _p]),
@@ -230,6 +232,24 @@ def q4moe_w4a4_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=N
         ws = workspace(q4moe_w4a4_decode_ws_bytes(router, experts, n_tok), x.device)
     _check(lib().q4moe_w4a4_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                    _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+WQ_MAX, WQ_MSE = 0, 1
+
+
+def q4moe_quantize_weights_ws_bytes(rows, cols):
+    return lib().q4moe_quantize_weights_ws_bytes(rows, cols)
+
+
+def q4moe_quantize_weights(w, codes, scales, gscale, mode=WQ_MAX, ws=None, stream=None):
+    """w: bf16 bits [rows, cols] (int16 tensor); codes uint8 [rows, cols/2];
+    scales uint8 [rows, cols/16]; gscale float32 [1]."""
+    rows, cols = w.shape
+    if ws is None:
+        ws = workspace(q4moe_quantize_weights_ws_bytes(rows, cols), w.device)
+    _check(lib().q4moe_quantize_weights(_ptr(w), rows, cols, mode, _ptr(codes), _ptr(scales), _ptr(gscale),
+                                        _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

@@ -220,6 +220,27 @@ typedef struct {
 q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                            const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_w4a4_shared_taps* out);
 
+/* NVFP4 weight quantizer ([W] Step 1: NVFP4 weights, E2M1 values with an
+ * FP8 (E4M3) scale per 16, built with ModelOpt; the recipe table's
+ * weight-scale selection: max-based, or an MSE per-block search over FP8
+ * scale values).  bf16 w [rows][cols] (cols % 16 == 0, 16-byte aligned) ->
+ * codes [rows][cols/2] (low nibble first, 8-byte aligned), E4M3FN scales
+ * [rows][cols/16], and the fp32 per-tensor scale *gscale (device memory),
+ * such that weight = e2m1 * e4m3 * g as every decoder here reads it.
+ *   g = fl32(amax / 2688) (1 for an all-zero tensor); eff(b) = fl32(e4m3(b) g);
+ *   the code of w under b is the E2M1 magnitude nearest |w| / eff(b) (the
+ *   exact quotient), ties to the even code, saturating at 6, sign of w kept;
+ *   Q4MOE_WQ_MAX: b = E4M3FN nearest-even of fl32(bamax / fl32(6 g));
+ *   Q4MOE_WQ_MSE: b in 0x01..0x7E minimising the block's squared error
+ *   (summed in element order, every step rounded to fp32), the lowest byte
+ *   among equal minima; an all-zero block takes b = 0.
+ * Two launches; the workspace holds the first one's partial maxima. */
+enum { Q4MOE_WQ_MAX = 0, Q4MOE_WQ_MSE = 1 };
+size_t q4moe_quantize_weights_ws_bytes(int32_t rows, int32_t cols);
+q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_t cols, int32_t mode,
+                                    uint8_t* codes, uint8_t* scales, float* gscale, void* ws, size_t ws_bytes,
+                                    void* stream);
+
 /* W4A4 routed-MoE chunk of n_tok tokens (1 <= n_tok <= 65536), NVFP4 only
  * ([W] Step 3: routed experts take 4-bit weights and activations, the
  * activations quantized on the fly per block of 16 with an E4M3FN scale

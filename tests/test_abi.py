@@ -175,3 +175,19 @@ def test_w4a4_decode_shared_validation(L):
     need = L.q4moe_w4a4_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)
     assert need > L.q4moe_w4a4_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
     assert call(ex, sh, wsb=need - 1) == g.EWORKSPACE
+
+
+def test_quantize_weights_validation(L):
+    need = L.q4moe_quantize_weights_ws_bytes(64, 2688)
+    assert need > 0
+
+    def call(rows=64, cols=2688, mode=0, w=A16, codes=A16, wsb=need):
+        return L.q4moe_quantize_weights(w, rows, cols, mode, codes, A16, A16, A16, wsb, None)
+
+    assert call(cols=40) == g.EINVAL
+    assert call(rows=0) == g.EINVAL
+    assert call(mode=2) == g.EINVAL
+    assert call(w=None) == g.EINVAL
+    assert call(w=A16 + 8) == g.EALIGN
+    assert call(codes=A16 + 4) == g.EALIGN
+    assert call(wsb=need - 1) == g.EWORKSPACE
