@@ -310,6 +310,48 @@ def bench_wquant(torch, g, synth, steps):
     return out
 
 
+def bench_mid_batch(torch, g, synth, steps, counts=(1, 2, 4, 8, 16, 32, 64, 128, 256)):
+    """W4A4 MoE layer (full shapes) at T tokens through the grouped MFMA
+    pipeline, and at T = 1 through the one-launch decode: µs per layer and
+    per token, warm (one bank; the crossover in T is what is measured)."""
+    from gpu_util import dev
+    bank = synth.expert_bank(SEED, synth.FAM_W4A4, 1, E, H, I, "nvfp4")
+    t = {k: dev(v) for k, v in bank.items()}
+    ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
+                   t["up_gscale"], t["down_gscale"])
+    wg, b = synth.router(SEED, synth.FAM_W4A4, 1, E, H, 0.5 / np.sqrt(H))
+    r = g.Router(dev(wg), dev(b), K)
+    out = {"grouped_us": {}, "grouped_us_per_token": {}, "warm": True}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = max(5, steps // 5)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return 1000.0 * e0.elapsed_time(e1) / reps
+
+    for T in counts:
+        x = dev(synth.x_rows(SEED, synth.FAM_W4A4, 1, H, [0] * T))
+        y = torch.empty((T, H), dtype=torch.int16, device="cuda")
+        ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+        ws = g.workspace(g.q4moe_w4a4_grouped_ws_bytes(r, ex, T))
+        us = timed(lambda: g.q4moe_w4a4_grouped(r, ex, x, y, ids, w, ws=ws))
+        out["grouped_us"][T] = round(us, 2)
+        out["grouped_us_per_token"][T] = round(us / T, 2)
+        if T == 1:
+            ws1 = g.workspace(g.q4moe_w4a4_decode_ws_bytes(r, ex, 1))
+            out["one_launch_us_T1"] = round(timed(lambda: g.q4moe_w4a4_decode(r, ex, x, y, ws=ws1)), 2)
+    log(f"mid-batch W4A4: {out}")
+    return out
+
+
 def cpu_baseline(seconds):
     """The oracle, as it stands, on layers of the NVFP4 stack until `seconds`
     of CPU work have run; returns microseconds per layer."""
@@ -410,6 +452,7 @@ def main():
         torch.cuda.empty_cache()
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
         extra["weight_quantizer"] = bench_wquant(torch, g, synth, args.steps)
+        extra["mid_batch_w4a4"] = bench_mid_batch(torch, g, synth, args.steps)
 
     cpu = None
     if not args.skip_cpu:

@@ -109,3 +109,17 @@ def test_w4a4_full_chunk_sampled():
     wh, wy = _check(bank, wg, b, x, r, out, K, sample=np.sort(sample))
     print(f"full: tokens resampled {sum(a > 0 for a in att)}, per-expert counts min {counts.min()} "
           f"max {counts.max()} mean {counts.mean():.1f} std {counts.std():.1f}; h {wh:.3f}, y {wy:.3f}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 8, 37, 200])
+def test_w4a4_mid_batch(T):
+    # the token counts between one-token decode and a prefill chunk: few rows
+    # per expert, most experts idle or with one row (full shapes)
+    E, H, I, K = 128, 2688, 1856, 6
+    bank = synth.expert_bank(SEED + T, synth.FAM_W4A4, 1, E, H, I, "nvfp4")
+    wg, b = synth.router(SEED + T, synth.FAM_W4A4, 1, E, H, 0.5 / np.sqrt(H))
+    x, r, _ = x_with_clear_routing(SEED + T, synth.FAM_W4A4, 1, wg, b, T, K)
+    out = _run(upload_router(wg, b, K), upload_bank(bank, "nvfp4"), x, K)
+    sample = None if T <= 8 else np.sort(np.random.default_rng(T).choice(T, 8, replace=False))
+    wh, wy = _check(bank, wg, b, x, r, out, K, sample=sample)
+    print(f"T={T}: experts used {int((np.diff(out['offsets']) > 0).sum())}; h {wh:.3f}, y {wy:.3f}")
