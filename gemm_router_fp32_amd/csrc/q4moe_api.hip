@@ -782,6 +782,34 @@ q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_
     return launched("weight quantizer");
 }
 
+size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
+    if (!r || !ex || n_tok < 1) return 0;
+    const size_t one = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, 1, 0, true).total;
+    const size_t grouped = w4a4_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
+    return std::max(one, grouped);
+}
+
+q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16, int32_t n_tok,
+                            uint16_t* y_bf16, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream) {
+    q4moe_status st = check_w4a4(r, ex, n_tok);
+    if (st != Q4MOE_OK) return st;
+    if (!x_bf16 || !y_bf16 || !ids || !w) return fail(Q4MOE_EINVAL, "x / y / ids / w is NULL");
+    if ((st = check_ws(ws, ws_bytes, q4moe_w4a4_moe_ws_bytes(r, ex, n_tok))) != Q4MOE_OK) return st;
+    if (n_tok <= Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS) {
+        // one single-token launch per token, in order on the stream (each
+        // call advances the workspace's epoch, so the calls can share it)
+        const size_t H = (size_t)ex->hidden, K = (size_t)r->top_k;
+        for (int32_t t = 0; t < n_tok; ++t) {
+            st = decode_impl(r, ex, nullptr, x_bf16 + t * H, 1, y_bf16 + t * H, ids + t * K, w + t * K, ws, ws_bytes,
+                             stream, true);
+            if (st == Q4MOE_EUNSUPPORTED && t == 0) break;  // the shape does not fit one launch: grouped path
+            if (st != Q4MOE_OK) return st;
+        }
+        if (st == Q4MOE_OK) return st;
+    }
+    return q4moe_w4a4_grouped(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
 q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                             const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_shared_taps* out) {
     if (!r || !ex || !sh || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");

@@ -79,6 +79,8 @@ _SIGS = {
     "q4moe_w4a4_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_taps": (_i32, [_p, _p, _i32, _p]),
+    "q4moe_w4a4_moe_ws_bytes": (_sz, [_p, _p, _i32]),
+    "q4moe_w4a4_moe": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_quantize_weights_ws_bytes": (_sz, [_i32, _i32]),
     "q4moe_quantize_weights": (_i32, [_p, _i32, _i32, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_shared_ws_bytes": (_sz, [_p, _p, _p, _i32]),
@@ -232,6 +234,19 @@ def q4moe_w4a4_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=N
         ws = workspace(q4moe_w4a4_decode_ws_bytes(router, experts, n_tok), x.device)
     _check(lib().q4moe_w4a4_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                    _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4moe_w4a4_moe_ws_bytes(router, experts, n_tok):
+    return lib().q4moe_w4a4_moe_ws_bytes(ctypes.byref(router.s), ctypes.byref(experts.s), n_tok)
+
+
+def q4moe_w4a4_moe(router, experts, x, y, ids, w, ws=None, stream=None):
+    n_tok = x.shape[0]
+    if ws is None:
+        ws = workspace(q4moe_w4a4_moe_ws_bytes(router, experts, n_tok), x.device)
+    _check(lib().q4moe_w4a4_moe(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y), _ptr(ids),
+                                _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

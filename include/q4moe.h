@@ -220,6 +220,18 @@ typedef struct {
 q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                            const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_w4a4_shared_taps* out);
 
+/* W4A4 routed-MoE layer for any token count, choosing the kernels by the
+ * count (mid-batch decode: the pages point at choosing the GEMM backend per
+ * batch size): up to Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS tokens run one
+ * single-token launch each (q4moe_w4a4_decode), more tokens the grouped MFMA
+ * pipeline (q4moe_w4a4_grouped); measured on MI355X at the full shapes, the
+ * single-token launches are faster per token up to 5 tokens.  The results
+ * are those of the entry point used.  ids / w are required. */
+#define Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS 5
+size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
+q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16, int32_t n_tok,
+                            uint16_t* y_bf16, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
+
 /* NVFP4 weight quantizer ([W] Step 1: NVFP4 weights, E2M1 values with an
  * FP8 (E4M3) scale per 16, built with ModelOpt; the recipe table's
  * weight-scale selection: max-based, or an MSE per-block search over FP8

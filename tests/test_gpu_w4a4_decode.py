@@ -170,3 +170,27 @@ def test_w4a4_decode_with_shared_expert(E, H, I, S):
     assert ok32, f"fp32 output gate exceeded: worst {worst32:.3f}"
     assert np.array_equal(out["y"], bf16_rne_of_f32(out["y32"]))
     print(f"w4a4 + shared E={E}: worst bf16 ratio {worst:.3f}, h {worst_h:.5f}, shared h {worst_sh:.5f}")
+
+
+@pytest.mark.parametrize("T", [3, 6])
+def test_w4a4_moe_selects_by_token_count(T):
+    # up to 5 tokens: one single-token launch per token; more: the grouped
+    # pipeline.  Either way the output is that entry point's, bit for bit.
+    H = 2688
+    L = layer(SEED + 11, synth.FAM_W4A4, 2, 128, H, 1856, T, K, "nvfp4")
+    router, ex = upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4")
+    x = dev(L["x"])
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    g.q4moe_w4a4_moe(router, ex, x, y, ids, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(ids), L["route"]["ids"])
+    y2 = torch.empty_like(y)
+    if T <= 5:
+        for t in range(T):
+            g.q4moe_w4a4_decode(router, ex, x[t:t + 1], y2[t:t + 1])
+    else:
+        g.q4moe_w4a4_grouped(router, ex, x, y2, torch.empty_like(ids), torch.empty_like(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), host(y2))
