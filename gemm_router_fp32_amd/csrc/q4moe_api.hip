@@ -613,9 +613,10 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
     }
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
-    if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;
-
     if (ex->fmt == Q4MOE_NVFP4) {  // each distinct expert streamed once, on MFMA
+        // the logits here; the top-k inside the up kernel (one launch fewer)
+        hipLaunchKernelGGL(k_router_logits, dim3(ra.E, (ra.T + 3) / 4), dim3(256), 0, s, ra);
+        if ((st = launched("router logits")) != Q4MOE_OK) return st;
         SmallMoeArgs b;
         b.E = ex->n_experts;
         b.H = ex->hidden;
@@ -635,8 +636,10 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
         b.zw = at<float>(ws, l.zw);
         b.y32 = at<float>(ws, l.y32);
         b.y = y_bf16;
+        b.ra = ra;
         return launch_small(b, s);
     }
+    if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;
 
     MoeArgs a;
     a.fmt = ex->fmt;

@@ -87,12 +87,12 @@ __global__ __launch_bounds__(256) void k_router_logits(RouterArgs a) {
 }
 
 // Sigmoid scores, selection key score + bias, top-K by key (largest first,
-// equal keys -> lower index), gates = selected scores / their sum.
-// One wave per token (E <= 256: four experts per lane); grid ceil(T/4).
-__global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wave;
-    if (t >= a.T) return;  // wave-uniform
+// equal keys -> lower index), gates = selected scores / their sum, for token
+// t by one wave (E <= 256: four experts per lane).  Writes a.ids / a.w (and
+// the caller's copies) when `global`, and lds_ids / lds_w when not null.
+__device__ __forceinline__ void topk_token(const RouterArgs& a, int t, bool global, int32_t* lds_ids,
+                                           float* lds_w) {
+    const int lane = threadIdx.x & 63;
     float s[4], key[4];
     bool live[4];
 #pragma unroll
@@ -151,11 +151,24 @@ __global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
             }
         const float wv = ws / ssum;
         const size_t o = (size_t)t * a.K + lane;
-        a.ids[o] = wi;
-        a.w[o] = wv;
-        if (a.ids_out) a.ids_out[o] = wi;
-        if (a.w_out) a.w_out[o] = wv;
+        if (global) {
+            a.ids[o] = wi;
+            a.w[o] = wv;
+            if (a.ids_out) a.ids_out[o] = wi;
+            if (a.w_out) a.w_out[o] = wv;
+        }
+        if (lds_ids) {
+            lds_ids[lane] = wi;
+            lds_w[lane] = wv;
+        }
     }
+}
+
+// One wave per token; grid ceil(T/4).
+__global__ __launch_bounds__(256) void k_topk(RouterArgs a) {
+    const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+    if (t >= a.T) return;  // wave-uniform
+    topk_token(a, t, true, nullptr, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -711,14 +724,17 @@ struct SmallMoeArgs {
     float* zw;           // [T*K][H] fp32: w * g * z per pair
     float* y32;          // [T][H]
     uint16_t* y;         // [T][H] bf16
+    // routing done by k_small_up itself from the logits (the top-k of every
+    // token in every workgroup; workgroup (0, 0) stores it for the others)
+    RouterArgs ra;
 };
 
 // The expert of pair p, and whether p is the first pair that selected it.
-__device__ __forceinline__ int small_expert(const SmallMoeArgs& a, int p, bool& leader) {
-    const int e = min(max(a.ids[p], 0), a.E - 1);  // routing ids are always in range; never read outside the bank
+__device__ __forceinline__ int small_expert(const SmallMoeArgs& a, const int32_t* ids, int p, bool& leader) {
+    const int e = min(max(ids[p], 0), a.E - 1);  // routing ids are always in range; never read outside the bank
     leader = true;
     for (int q = 0; q < p; ++q)
-        if (min(max(a.ids[q], 0), a.E - 1) == e) leader = false;
+        if (min(max(ids[q], 0), a.E - 1) == e) leader = false;
     return e;
 }
 
@@ -867,8 +883,16 @@ __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
     __shared__ float s_amax[4][4];
     __shared__ int s_exp[4];
     __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][NJ * 8];  // each wave's group scales (16 rows)
+    __shared__ int32_t s_ids[kSmallT * 8];
+    __shared__ float s_w[kSmallT * 8];
+    // routing: wave t takes token t (every workgroup, so no top-k launch)
+    if ((int)(threadIdx.x >> 6) < a.T) {
+        const int t = threadIdx.x >> 6;
+        topk_token(a.ra, t, blockIdx.x == 0 && blockIdx.y == 0, &s_ids[t * a.K], &s_w[t * a.K]);
+    }
+    __syncthreads();
     bool leader;
-    const int e = small_expert(a, blockIdx.y, leader);
+    const int e = small_expert(a, s_ids, blockIdx.y, leader);
     if (!leader) return;  // uniform
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m16 = lane & 15, kq = lane >> 4;
@@ -885,7 +909,7 @@ __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
     if (n < a.T) {
         int pp = -1;
         for (int sl = 0; sl < a.K; ++sl)
-            if (min(max(a.ids[n * a.K + sl], 0), a.E - 1) == e) pp = n * a.K + sl;
+            if (min(max(s_ids[n * a.K + sl], 0), a.E - 1) == e) pp = n * a.K + sl;
         if (pp >= 0) {
             const float sc = ldexpf(a.upg[e], -s_exp[n]);
 #pragma unroll
@@ -915,7 +939,7 @@ __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
     constexpr bool kScaleLds = NJ <= 24;
     __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][kScaleLds ? NJ * 8 : 1];
     bool leader;
-    const int e = small_expert(a, blockIdx.y, leader);
+    const int e = small_expert(a, a.ids, blockIdx.y, leader);
     if (!leader) return;  // uniform
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m16 = lane & 15, kq = lane >> 4;
