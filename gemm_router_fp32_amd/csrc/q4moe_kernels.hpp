@@ -244,9 +244,11 @@ __device__ __forceinline__ void load_x_chunk(const uint16_t* xrow, int ch, uint3
 }
 
 __device__ __forceinline__ float pair_sum_bf16(const uint32_t* xa) {
+    // one dot2 with (1, 1) per pair: 16 instructions instead of 64 converts
+    // and adds (the products are exact, the sum is fp32)
     float s = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s += bf16_bits_to_f32(xa[j] & 0xffffu) + bf16_bits_to_f32(xa[j] >> 16);
+    for (int j = 0; j < 16; ++j) s = dot2_bf16(as_bf16x2(xa[j]), as_bf16x2(0x3F803F80u), s);
     return s;
 }
 
