@@ -22,7 +22,7 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 # the fused decode kernel and the device helpers it inlines
-KERNEL_SOURCES = ("csrc/q4moe_fused.hpp", "csrc/q4moe_device.hpp")
+KERNEL_SOURCES = ("csrc/q4moe_fused.hpp", "csrc/q4moe_device.hpp", "csrc/q4moe_kernels.hpp")
 
 
 def source_sha256():
