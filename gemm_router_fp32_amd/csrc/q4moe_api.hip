@@ -12,6 +12,7 @@
 #include "q4moe_fused.hpp"
 #include "q4moe_w4a4.hpp"
 #include "q4moe_wquant.hpp"
+#include "q4moe_shared.hpp"
 
 using namespace q4moe;
 
@@ -112,7 +113,7 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, xq_c, xq_s, hq_c, hq_s, total;
+    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s, total;
 };
 
 // S: the shared expert's intermediate size (0: no shared expert); a4: the
@@ -129,12 +130,14 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     o += up_to((size_t)(K + (S > 0 ? 1 : 0)) * H * 8);
     l.hq_tag = o;  // shared expert: (four h codes, epoch), kReplicas copies
     o += up_to((size_t)kReplicas * (S / 4) * 8);
-    l.sh_xq = o;   // shared expert taps
-    o += up_to(S > 0 ? (size_t)H : 0);
+    l.sh_xq = o;   // shared expert taps [T][H], [T][S], [T][S], and its z [T][H]
+    o += up_to(S > 0 ? (size_t)T * H : 0);
     l.sh_h = o;
-    o += up_to((size_t)S * 4);
+    o += up_to((size_t)T * S * 4);
     l.sh_hq = o;
-    o += up_to((size_t)S);
+    o += up_to((size_t)T * S);
+    l.sh_z = o;
+    o += up_to(S > 0 && T > 1 ? (size_t)T * H * 4 : 0);
     l.xq_c = o;    // W4A4 taps: x codes and scales, h codes and scales
     o += up_to(a4 ? (size_t)H / 2 : 0);
     l.xq_s = o;
@@ -526,7 +529,7 @@ q4moe_status check_shared(const q4moe_shared_fp8* sh, const q4moe_experts* ex, i
     for (float v : sc)
         if (!std::isfinite(v) || v == 0.0f) return fail(Q4MOE_EINVAL, "shared expert scales must be finite and non-zero");
     if (ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs with NVFP4 routed experts");
-    if (n_tok != 1) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs for one token (n_tok = %d)", n_tok);
+    if (n_tok > kSmallT) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs for up to %d tokens", kSmallT);
     return Q4MOE_OK;
 }
 
@@ -613,6 +616,41 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
     }
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
+    const float* zsh = nullptr;
+    if (sh) {  // 2-4 tokens: the shared expert's own two launches first
+        SharedSmallArgs q;
+        q.T = n_tok;
+        q.H = ex->hidden;
+        q.S = sh->inter;
+        q.x = x_bf16;
+        q.shu = sh->up_codes;
+        q.shd = sh->down_codes;
+        q.su_w = sh->up_wscale;
+        q.su_in = sh->up_iscale;
+        q.sd_w = sh->down_wscale;
+        q.sd_in = sh->down_iscale;
+        q.xq = at<uint8_t>(ws, l.sh_xq);
+        q.h = at<float>(ws, l.sh_h);
+        q.hq = at<uint8_t>(ws, l.sh_hq);
+        q.z = at<float>(ws, l.sh_z);
+        const int chu = (q.H / 16 + 63) / 64, chd = (q.S / 16 + 63) / 64;  // 1..4 each
+        const dim3 gu((q.S + kShRowsPerWg - 1) / kShRowsPerWg), gd((q.H + kShRowsPerWg - 1) / kShRowsPerWg);
+        switch (chu) {
+            case 1: hipLaunchKernelGGL(k_shared_up<1>, gu, dim3(256), 0, s, q); break;
+            case 2: hipLaunchKernelGGL(k_shared_up<2>, gu, dim3(256), 0, s, q); break;
+            case 3: hipLaunchKernelGGL(k_shared_up<3>, gu, dim3(256), 0, s, q); break;
+            default: hipLaunchKernelGGL(k_shared_up<4>, gu, dim3(256), 0, s, q); break;
+        }
+        if ((st = launched("shared expert up")) != Q4MOE_OK) return st;
+        switch (chd) {
+            case 1: hipLaunchKernelGGL(k_shared_down<1>, gd, dim3(256), 0, s, q); break;
+            case 2: hipLaunchKernelGGL(k_shared_down<2>, gd, dim3(256), 0, s, q); break;
+            case 3: hipLaunchKernelGGL(k_shared_down<3>, gd, dim3(256), 0, s, q); break;
+            default: hipLaunchKernelGGL(k_shared_down<4>, gd, dim3(256), 0, s, q); break;
+        }
+        if ((st = launched("shared expert down")) != Q4MOE_OK) return st;
+        zsh = q.z;
+    }
     if (ex->fmt == Q4MOE_NVFP4) {  // each distinct expert streamed once, on MFMA
         // the logits here; the top-k inside the up kernel (one launch fewer)
         hipLaunchKernelGGL(k_router_logits, dim3(ra.E, (ra.T + 3) / 4), dim3(256), 0, s, ra);
@@ -637,6 +675,7 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
         b.y32 = at<float>(ws, l.y32);
         b.y = y_bf16;
         b.ra = ra;
+        b.zsh = zsh;
         return launch_small(b, s);
     }
     if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;

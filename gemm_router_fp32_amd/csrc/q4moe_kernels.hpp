@@ -729,6 +729,7 @@ struct SmallMoeArgs {
     // routing done by k_small_up itself from the logits (the top-k of every
     // token in every workgroup; workgroup (0, 0) stores it for the others)
     RouterArgs ra;
+    const float* zsh;    // [T][H] the shared expert's output (nullable)
 };
 
 // The expert of pair p, and whether p is the first pair that selected it.
@@ -997,6 +998,7 @@ __global__ __launch_bounds__(256) void k_small_combine(SmallMoeArgs a) {
     const int t = i / a.H, r = i - t * a.H;
     float acc = 0.f;
     for (int sl = 0; sl < a.K; ++sl) acc += a.zw[(size_t)(t * a.K + sl) * a.H + r];
+    if (a.zsh) acc += a.zsh[i];  // the shared expert, after the routed slots
     a.y32[i] = acc;
     a.y[i] = (uint16_t)f32_to_bf16_rne(acc);
 }

@@ -160,11 +160,13 @@ typedef struct {
     float up_wscale, up_iscale, down_wscale, down_iscale;
 } q4moe_shared_fp8;
 
-/* q4moe_w4a16_decode plus the shared expert, in the same single launch:
- * y = sum_i w_i z_i + z_shared, rounded once to bf16.  n_tok must be 1 and
- * the routed experts NVFP4; otherwise, or where the single launch does not
- * fit the device, Q4MOE_EUNSUPPORTED.  The shared expert's weights are read
- * from the start of the launch, while the router runs. */
+/* q4moe_w4a16_decode plus the shared expert: y = sum_i w_i z_i + z_shared,
+ * rounded once to bf16.  NVFP4 routed experts and 1 <= n_tok <= 4, else
+ * Q4MOE_EUNSUPPORTED.  One token: the same single launch, whose shared
+ * weights are read while the router runs (EUNSUPPORTED where that launch
+ * does not fit the device); 2-4 tokens: two launches for the shared expert
+ * (each weight row read once for all tokens) before the small-batch routed
+ * kernels, whose combine adds its output. */
 size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
                                           const q4moe_shared_fp8* sh, int32_t n_tok);
 q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_experts* ex,
@@ -173,9 +175,9 @@ q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_expert
                                        void* ws, size_t ws_bytes, void* stream);
 
 /* Byte offsets of the values q4moe_w4a16_decode_shared leaves in its
- * workspace: y32 and h as in q4moe_decode_taps; xq uint8 [hidden] (x
- * codes), sh_h32 fp32 [inter] (relu(u)^2, the h quantizer's input), sh_hq
- * uint8 [inter] (h codes). */
+ * workspace: y32 and h as in q4moe_decode_taps; xq uint8 [n_tok][hidden] (x
+ * codes), sh_h32 fp32 [n_tok][inter] (relu(u)^2, the h quantizer's input),
+ * sh_hq uint8 [n_tok][inter] (h codes). */
 typedef struct { size_t y32, h, xq, sh_h32, sh_hq; } q4moe_shared_taps;
 q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                             const q4moe_shared_fp8* sh, int32_t n_tok,

@@ -132,7 +132,7 @@ def test_decode_shared_validation(L):
     assert _decode_sh(L, r, ex, _shared(dn=A16 + 8)) == g.EALIGN
     assert _decode_sh(L, r, ex, _shared(sc=(1.0, 0.0, 1.0, 1.0))) == g.EINVAL
     assert _decode_sh(L, r, ex, _shared(sc=(1.0, 1.0, float("inf"), 1.0))) == g.EINVAL
-    assert _decode_sh(L, r, ex, _shared(), T=2) == g.EUNSUPPORTED
+    assert _decode_sh(L, r, ex, _shared(), T=5) == g.EINVAL
     assert _decode_sh(L, r, _experts(fmt=2), _shared()) == g.EUNSUPPORTED
     sh = _shared()
     need = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)
@@ -143,6 +143,13 @@ def test_decode_shared_validation(L):
     assert L.q4moe_w4a16_decode_shared_taps(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1,
                                             ctypes.byref(t)) == g.OK
     assert 0 < t.xq < t.sh_h32 < t.sh_hq < need and t.y32 < need
+    # 2-4 tokens: per-token taps and the shared output buffer
+    need4 = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 4)
+    assert L.q4moe_w4a16_decode_shared_taps(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 4,
+                                            ctypes.byref(t)) == g.OK
+    assert t.sh_h32 - t.xq >= 4 * 2688 and t.sh_hq - t.sh_h32 >= 4 * 3712 * 4
+    assert t.sh_hq + 4 * 3712 + 4 * 2688 * 4 <= need4
+    assert _decode_sh(L, r, ex, sh, T=4, wsb=need4 - 1) == g.EWORKSPACE
 
 
 def test_w4a4_decode_validation(L):

@@ -1,6 +1,7 @@
-"""GPU parity of the FP8 per-tensor W8A8 shared expert inside the
-single-token decode launch, through the C-ABI, stage by stage against the
-oracle on the same seeded inputs:
+"""GPU parity of the FP8 per-tensor W8A8 shared expert, through the C-ABI:
+inside the single-token decode launch, and in its own two launches beside
+the 2-4-token kernels; stage by stage against the oracle on the same seeded
+inputs:
 
 1. routing exact (ids) and gates to 1e-5;
 2. x codes bit-exact against the oracle's quantizer of the same x;
@@ -121,3 +122,75 @@ def test_decode_shared_zero_weights_is_plain_decode(full_layer):
     assert np.array_equal(out["y32"].view(np.uint32), y32.view(np.uint32))
     assert np.array_equal(out["y"], host(y, np.uint16)[0])
     assert not out["hq"].any() and not out["h32"].any()
+
+
+def run_shared_multi(router, experts, shared, x_np):
+    T = x_np.shape[0]
+    x = dev(x_np)
+    y = torch.empty((T, experts.hidden), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, router.top_k), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, router.top_k), dtype=torch.float32, device=DEV)
+    ws = g.q4moe_w4a16_decode_shared(router, experts, shared, x, y, ids, w)
+    torch.cuda.synchronize()
+    t = g.q4moe_w4a16_decode_shared_taps(router, experts, shared, T)
+    wsh = host(ws)
+    H, S = experts.hidden, shared.inter
+    return dict(y=host(y, np.uint16), ids=host(ids), w=host(w),
+                y32=wsh[t.y32: t.y32 + T * H * 4].view(np.float32).reshape(T, H).copy(),
+                xq=wsh[t.xq: t.xq + T * H].reshape(T, H).copy(),
+                h32=wsh[t.sh_h32: t.sh_h32 + T * S * 4].view(np.float32).reshape(T, S).copy(),
+                hq=wsh[t.sh_hq: t.sh_hq + T * S].reshape(T, S).copy())
+
+
+def check_shared_multi(L, sh, out):
+    r = L["route"]
+    assert np.array_equal(out["ids"], r["ids"])
+    np.testing.assert_allclose(out["w"], r["w"], rtol=1e-5)
+    ob = oracle.Bank.from_dict(oracle.NVFP4, L["bank"])
+    yr, _ = oracle.moe_w4a16(ob, L["x"], r["ids"], r["w"])
+    worst = 0.0
+    for t in range(L["x"].shape[0]):
+        xf = bf16_bits_to_f64(L["x"][t]).astype(np.float32)
+        assert np.array_equal(out["xq"][t], oracle.fp8_quant(xf, sh["up_iscale"])), f"token {t}: x codes differ"
+        u = oracle.fp8_gemv(sh["up_codes"], out["xq"][t], sh["up_wscale"], sh["up_iscale"])
+        ok, worst_h = gate_f32(out["h32"][t][None], (np.maximum(u, 0.0) ** 2)[None])
+        assert ok, f"token {t}: h tap gate exceeded: worst {worst_h:.3f}"
+        assert np.array_equal(out["hq"][t], oracle.fp8_quant(out["h32"][t], sh["down_iscale"])), \
+            f"token {t}: h codes differ"
+        z = oracle.fp8_gemv(sh["down_codes"], out["hq"][t], sh["down_wscale"], sh["down_iscale"])
+        yhat = yr[t] + z
+        ok, wt = gate_out(out["y"][t][None], yhat[None])
+        assert ok, f"token {t}: bf16 output gate exceeded: worst {wt:.3f}"
+        ok32, _ = gate_f32(out["y32"][t][None], yhat[None])
+        assert ok32, f"token {t}: fp32 output gate exceeded"
+        worst = max(worst, wt)
+    assert np.array_equal(out["y"], bf16_rne_of_f32(out["y32"]))
+    return worst
+
+
+@pytest.mark.parametrize("T", [2, 3, 4])
+@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (32, 512, 320, 192), (64, 1024, 256, 4096)])
+def test_decode_shared_multi_token(T, E, H, I, S):
+    L = layer(SEED + 7 * T + S, synth.FAM_NVFP4, 0, E, H, I, T, K, "nvfp4")
+    sh = synth.shared_fp8(SEED, FAM_SH, S + T, H, S)
+    out = run_shared_multi(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), upload_shared(sh),
+                           L["x"])
+    check_shared_multi(L, sh, out)
+
+
+def test_decode_shared_multi_token_full_layer(full_layer):
+    L1, sh, ex, router, shd = full_layer
+    L = layer(SEED + 1, synth.FAM_NVFP4, 0, 128, 2688, 1856, 4, K, "nvfp4")
+    ex4 = upload_bank(L["bank"], "nvfp4")
+    out = run_shared_multi(upload_router(L["wg"], L["b"], K), ex4, shd, L["x"])
+    worst = check_shared_multi(L, sh, out)
+    print(f"shared, 4 tokens: worst bf16 ratio {worst:.3f}")
+    # all-zero shared weights: y32 equals the routed-only path's bit for bit
+    zero = dict(sh, up_codes=np.zeros_like(sh["up_codes"]), down_codes=np.zeros_like(sh["down_codes"]))
+    outz = run_shared_multi(upload_router(L["wg"], L["b"], K), ex4, upload_shared(zero), L["x"])
+    y = torch.empty((4, ex4.hidden), dtype=torch.int16, device=DEV)
+    ws = g.q4moe_w4a16_decode(upload_router(L["wg"], L["b"], K), ex4, dev(L["x"]), y)
+    torch.cuda.synchronize()
+    t = g.q4moe_w4a16_decode_taps(upload_router(L["wg"], L["b"], K), ex4, 4)
+    y32 = host(ws)[t.y32: t.y32 + 4 * ex4.hidden * 4].view(np.float32).reshape(4, -1)
+    assert np.array_equal(outz["y32"].view(np.uint32), y32.view(np.uint32))
