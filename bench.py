@@ -116,10 +116,11 @@ class Evictor:
         self.buf.sum()
 
 
-def build_stack(torch, g, synth, fmt, shared=False, w4a4=False):
+def build_stack(torch, g, synth, fmt, shared=False, w4a4=False, n_tok=1):
     """The 23 layers, resident; with `shared`, each layer also carries the
     FP8 shared expert [S_SHARED x H] and runs the shared decode entry; with
-    `w4a4`, each layer runs the single-token W4A4 decode entry."""
+    `w4a4`, each layer runs the single-token W4A4 decode entry; `n_tok`
+    tokens per call."""
     from gpu_util import dev
     fam = synth.FAM_NVFP4 if fmt == "nvfp4" else synth.FAM_INT4
     layers, buf = [], None
@@ -127,7 +128,7 @@ def build_stack(torch, g, synth, fmt, shared=False, w4a4=False):
         bank = synth.expert_bank(SEED, fam, li, E, H, I, fmt, out=buf)
         buf = bank
         wg, b = synth.router(SEED, fam, li, E, H)
-        x = synth.x_rows(SEED, fam, li, H, [0])
+        x = synth.x_rows(SEED, fam, li, H, list(range(n_tok)))
         t = {k: dev(v) for k, v in bank.items()}
         if fmt == "nvfp4":
             ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
@@ -135,16 +136,16 @@ def build_stack(torch, g, synth, fmt, shared=False, w4a4=False):
         else:
             ex = g.Experts(g.INT4_G64, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"])
         r = g.Router(dev(wg), dev(b), K)
-        L = dict(ex=ex, r=r, x=dev(x), y=torch.empty((1, H), dtype=torch.int16, device="cuda"))
+        L = dict(ex=ex, r=r, x=dev(x), y=torch.empty((n_tok, H), dtype=torch.int16, device="cuda"))
         L["w4a4"] = w4a4
         if shared:
             sh = synth.shared_fp8(SEED, fam, li, H, S_SHARED)
             L["sh"] = g.SharedFp8(dev(sh["up_codes"]), dev(sh["down_codes"]), sh["up_wscale"], sh["up_iscale"],
                                   sh["down_wscale"], sh["down_iscale"])
             wsb = (g.q4moe_w4a4_decode_shared_ws_bytes if w4a4 else g.q4moe_w4a16_decode_shared_ws_bytes)(
-                r, ex, L["sh"], 1)
+                r, ex, L["sh"], n_tok)
         else:
-            wsb = (g.q4moe_w4a4_decode_ws_bytes if w4a4 else g.q4moe_w4a16_decode_ws_bytes)(r, ex, 1)
+            wsb = (g.q4moe_w4a4_decode_ws_bytes if w4a4 else g.q4moe_w4a16_decode_ws_bytes)(r, ex, n_tok)
         L["ws"] = g.workspace(wsb)
         layers.append(L)
     log(f"{fmt} stack{' + shared expert' if shared else ''}{' (W4A4)' if w4a4 else ''} resident ({LAYERS} layers)")
@@ -428,6 +429,16 @@ def main():
                                  "bytes_per_layer": bs, "shared_inter": S_SHARED, "flags": fs}
         log(f"nvfp4 + fp8 shared expert stack: {extra['shared_stack']}")
         del shl
+        torch.cuda.empty_cache()
+        sh4 = build_stack(torch, g, synth, "nvfp4", shared=True, n_tok=4)
+        ms4s, mk4s, f4s, per4s = time_stack(torch, g, sh4, args.steps, args.warmup)
+        extra["shared_stack_4tok"] = {"us_per_layer": round(1000.0 * ms4s / LAYERS, 3),
+                                      "tokens_per_s": round(4000.0 / ms4s, 1),
+                                      "single_call_us": round(mk4s * 1e3, 3),
+                                      "us_per_layer_spread": spread(per4s / LAYERS), "n_tok": 4,
+                                      "shared_inter": S_SHARED, "flags": f4s}
+        log(f"nvfp4 + fp8 shared expert stack, 4 tokens per call: {extra['shared_stack_4tok']}")
+        del sh4
         torch.cuda.empty_cache()
         a4l = build_stack(torch, g, synth, "nvfp4", w4a4=True)
         msa, mka, fa, pera = time_stack(torch, g, a4l, args.steps, args.warmup)

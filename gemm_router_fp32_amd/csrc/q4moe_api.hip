@@ -617,7 +617,7 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
     const float* zsh = nullptr;
-    if (sh) {  // 2-4 tokens: the shared expert's own two launches first
+    if (sh) {  // 2-4 tokens: the shared expert's own three launches first
         SharedSmallArgs q;
         q.T = n_tok;
         q.H = ex->hidden;
@@ -635,6 +635,8 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
         q.z = at<float>(ws, l.sh_z);
         const int chu = (q.H / 16 + 63) / 64, chd = (q.S / 16 + 63) / 64;  // 1..4 each
         const dim3 gu((q.S + kShRowsPerWg - 1) / kShRowsPerWg), gd((q.H + kShRowsPerWg - 1) / kShRowsPerWg);
+        hipLaunchKernelGGL(k_shared_xcode, dim3((q.T * q.H / 8 + 255) / 256), dim3(256), 0, s, q);
+        if ((st = launched("shared expert x codes")) != Q4MOE_OK) return st;
         switch (chu) {
             case 1: hipLaunchKernelGGL(k_shared_up<1>, gu, dim3(256), 0, s, q); break;
             case 2: hipLaunchKernelGGL(k_shared_up<2>, gu, dim3(256), 0, s, q); break;

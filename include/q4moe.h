@@ -164,7 +164,7 @@ typedef struct {
  * rounded once to bf16.  NVFP4 routed experts and 1 <= n_tok <= 4, else
  * Q4MOE_EUNSUPPORTED.  One token: the same single launch, whose shared
  * weights are read while the router runs (EUNSUPPORTED where that launch
- * does not fit the device); 2-4 tokens: two launches for the shared expert
+ * does not fit the device); 2-4 tokens: three launches for the shared expert
  * (each weight row read once for all tokens) before the small-batch routed
  * kernels, whose combine adds its output. */
 size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
