@@ -169,10 +169,22 @@ def check_shared_multi(L, sh, out):
 
 
 @pytest.mark.parametrize("T", [2, 3, 4])
-@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (32, 512, 320, 192), (64, 1024, 256, 4096)])
+@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (32, 512, 320, 192), (64, 1024, 256, 4096),
+                                     (16, 256, 192, 64)])
 def test_decode_shared_multi_token(T, E, H, I, S):
     L = layer(SEED + 7 * T + S, synth.FAM_NVFP4, 0, E, H, I, T, K, "nvfp4")
     sh = synth.shared_fp8(SEED, FAM_SH, S + T, H, S)
+    out = run_shared_multi(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), upload_shared(sh),
+                           L["x"])
+    check_shared_multi(L, sh, out)
+
+
+def test_decode_shared_multi_token_max_size():
+    # every dimension at the library's limit (4096): the widest small-batch
+    # instances and full LDS staging of 4 tokens x 4096 codes in both
+    # shared-expert kernels
+    L = layer(SEED + 4096, synth.FAM_NVFP4, 0, 16, 4096, 4096, 4, K, "nvfp4")
+    sh = synth.shared_fp8(SEED, FAM_SH, 4096, 4096, 4096)
     out = run_shared_multi(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), upload_shared(sh),
                            L["x"])
     check_shared_multi(L, sh, out)
