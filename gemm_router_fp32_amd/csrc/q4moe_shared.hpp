@@ -47,7 +47,7 @@ __device__ __forceinline__ void fp8_rows_load(const uint8_t* w, int row0, int ro
 }
 
 // The four rows against the T activation rows act [T][cols] (bf16 pairs in
-// LDS, pitch cols / 2 dwords); lane 63 returns out[k][t].
+// LDS, pitch cols / 2 dwords); lane 63 returns out[k][t] (0 for t >= T).
 template <int CH>
 __device__ __forceinline__ void fp8_rows_dot(const uint4 (&q)[4][CH], int cols, const uint32_t* act, int T,
                                              float (&out)[4][4]) {
@@ -73,8 +73,22 @@ __device__ __forceinline__ void fp8_rows_dot(const uint4 (&q)[4][CH], int cols, 
 #pragma unroll
     for (int k = 0; k < 4; ++k)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            if (t < T) out[k][t] = seg_sum_last<64>(acc[k][t]);
+        for (int t = 0; t < 4; ++t) out[k][t] = t < T ? seg_sum_last<64>(acc[k][t]) : 0.f;
+}
+
+// The sixteen sums held by lane 63 spread over lanes 0..15 (lane 4 k + t
+// takes out[k][t]), so that the epilogue runs on 16 lanes at once.
+__device__ __forceinline__ float spread_sums(const float (&out)[4][4]) {
+    const int lane = threadIdx.x & 63;
+    float mine = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const float v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(out[k][t]), 63));
+            mine = lane == 4 * k + t ? v : mine;
+        }
+    return mine;
 }
 
 // x of every token coded to E4M3FN once, before the up kernel (coding it in
@@ -130,17 +144,12 @@ __global__ __launch_bounds__(256) void k_shared_up(SharedSmallArgs a) {
     float u[4][4];
     fp8_rows_dot<CH>(q, a.H, s_x, a.T, u);
     const float sc = a.su_w * a.su_in;
-    if (lane == 63) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int row = row0 + k;
-            if (row >= a.S) break;
-            for (int t = 0; t < a.T; ++t) {
-                const float r = fmaxf(u[k][t] * sc, 0.f), hv = r * r;
-                a.h[(size_t)t * a.S + row] = hv;
-                a.hq[(size_t)t * a.S + row] = (uint8_t)fp8_act_code(hv, a.sd_in);
-            }
-        }
+    const float um = spread_sums(u);
+    const int row = row0 + (lane >> 2), t = lane & 3;
+    if (lane < 16 && t < a.T && row < a.S) {
+        const float r = fmaxf(um * sc, 0.f), hv = r * r;
+        a.h[(size_t)t * a.S + row] = hv;
+        a.hq[(size_t)t * a.S + row] = (uint8_t)fp8_act_code(hv, a.sd_in);
     }
 }
 
@@ -158,14 +167,9 @@ __global__ __launch_bounds__(256) void k_shared_down(SharedSmallArgs a) {
     float zz[4][4];
     fp8_rows_dot<CH>(q, a.S, s_h, a.T, zz);
     const float sc = a.sd_w * a.sd_in;
-    if (lane == 63) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int row = row0 + k;
-            if (row >= a.H) break;
-            for (int t = 0; t < a.T; ++t) a.z[(size_t)t * a.H + row] = zz[k][t] * sc;
-        }
-    }
+    const float zm = spread_sums(zz);
+    const int row = row0 + (lane >> 2), t = lane & 3;
+    if (lane < 16 && t < a.T && row < a.H) a.z[(size_t)t * a.H + row] = zm * sc;
 }
 
 }  // namespace q4moe
