@@ -76,6 +76,9 @@ def lib():
         L.q4o_wq_gscale.argtypes = [ctypes.c_int64, p]
         L.q4o_wq_block.restype = u32
         L.q4o_wq_block.argtypes = [p, f, ctypes.c_int, p]
+        L.q4o_wq_codes_excess.restype = d
+        L.q4o_wq_codes_excess.argtypes = [p, f, u32, p]
+        L.q4o_wq_codes_excess_blocks.argtypes = [ctypes.c_int64, p, f, p, p, p]
         _LIB = L
     return _LIB
 
@@ -313,3 +316,17 @@ def wq_block(w16_bits, g, mse=False):
     c = np.zeros(8, np.uint8)
     b = lib().q4o_wq_block(_p(w), float(g), int(bool(mse)), _p(c))
     return b, c
+
+
+def wq_codes_excess(w_bits, g, scales):
+    """For bf16 weights [rows, cols] and given block scale bytes [rows, cols/16]:
+    the codes those bytes give (the quantizer's code rule), and per block how
+    much the exact squared error exceeds the block's exact MSE minimum."""
+    w = _c(np.atleast_2d(w_bits), np.uint16)
+    rows, cols = w.shape
+    sc = _c(scales, np.uint8).reshape(-1)
+    assert sc.size == rows * cols // 16
+    codes = np.zeros(rows * cols // 2, np.uint8)
+    excess = np.zeros(sc.size)
+    lib().q4o_wq_codes_excess_blocks(sc.size, _p(w), float(g), _p(sc), _p(codes), _p(excess))
+    return codes.reshape(rows, cols // 2), excess.reshape(rows, cols // 16)

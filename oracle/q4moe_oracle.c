@@ -10,6 +10,7 @@
 #include "q4moe_oracle.h"
 
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -495,15 +496,12 @@ void q4o_shared_fp8(const q4o_shared* sh, const uint16_t* x, uint8_t* xq, double
  *    saturating at 6, with w's sign bit;
  *  - max-based: b = E4M3FN nearest-even (saturating) of
  *    fl32(bamax / fl32(6 * g)), bamax the block's largest |w|;
- *  - MSE: b minimises err(b) = sum over the block, in element order, of
- *    fl32(d * d), d = fl32(|w| - fl32(e2m1(code) * eff(b))), each step
- *    rounded to fp32, over every positive finite E4M3FN byte 0x01..0x7E;
- *    the lowest byte among equal minima; an all-zero block takes b = 0.
- *  The error is taken in fp32 because the GPU takes the same decision in
- *  fp32: both sides must round the same way for the choice to agree. */
+ *  - MSE: b minimises the block's exact squared error
+ *    sum_k (|w_k| - q_k(b))^2, q_k(b) = e2m1(code_k) * eff(b), over every
+ *    positive finite E4M3FN byte 0x01..0x7E; the lowest byte among equal
+ *    minima; an all-zero block takes b = 0. */
 
 static const float kMid32[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
-static const float kGrid32[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
 
 /* Nearest E2M1 magnitude code of the exact quotient mag / eff (mid * eff is
  * exact in fp64: 3 + 24 significant bits). */
@@ -517,16 +515,64 @@ static uint32_t wq_code(float mag, float eff) {
     return c;
 }
 
-static float wq_err(const float* mag, float eff) {
-    float acc = 0.0f;
+/* Twice the E2M1 magnitude of code c (an integer: 0, 1, 2, 3, 4, 6, 8, 12). */
+static const int kTwiceE2m1[8] = {0, 1, 2, 3, 4, 6, 8, 12};
+
+/* The MSE objective, exactly.  Expanding the square,
+ *   sum_k (|w_k| - q_k)^2 = sum_k w_k^2 + F(b),  F(b) = sum_k q_k (q_k - 2 |w_k|),
+ * and the first sum does not depend on b, so comparing F compares errors.
+ * A term is 0 unless code_k != 0, which needs |w_k| > eff / 4.  Write
+ * eff = M * 2^E (M an integer below 2^24); every such |w_k| (8 significant
+ * bits, at least 2^-2 of eff) is then an integer multiple W_k of 2^E, and
+ * with c_k = 2 e2m1(code_k):
+ *   F(b) = P * 2^(2E - 2),  P = sum_k c_k M (c_k M - 4 W_k),
+ * an exact integer: c_k M < 2^28 and, for the tensor's own g (bamax <= 2688 g,
+ * eff >= 2^-9 g), W_k < 2^45, so P < 2^80 (values that would leave the
+ * checked range W_k < 2^50 stop the program).  The value is held as (P, E);
+ * for one g the exponents E of the 126 scale bytes span at most 19 binades,
+ * so aligning two values multiplies P by at most 2^38 and stays below 2^127. */
+typedef struct {
+    __int128 p;
+    int e;
+} wq_obj;
+
+static wq_obj wq_objective(const float* mag, float eff) {
+    wq_obj o = {0, 0};
+    if (!(eff > 0.0f)) return o; /* an underflowed scale decodes every code to 0: F = 0 */
+    int ex;
+    double f = frexp((double)eff, &ex);           /* eff = f * 2^ex, f in [0.5, 1) */
+    int64_t M = (int64_t)ldexp(f, 24);            /* exact: eff has at most 24 bits */
+    o.e = ex - 24;
     for (int k = 0; k < 16; ++k) {
-        volatile float q = kGrid32[wq_code(mag[k], eff)] * eff;
-        volatile float d = mag[k] - q;
-        volatile float sq = d * d;
-        acc = acc + sq;
+        uint32_t code = wq_code(mag[k], eff);
+        if (code == 0) continue;
+        double wq = ldexp((double)mag[k], -o.e);  /* W_k, exact (see above) */
+        if (wq != floor(wq) || wq >= 0x1p50) {
+            fprintf(stderr, "q4o_wq: block value outside the exact range of the MSE objective\n");
+            abort();
+        }
+        __int128 cm = (__int128)kTwiceE2m1[code] * M;
+        o.p += cm * (cm - 4 * (__int128)(int64_t)wq);
     }
-    return acc;
+    return o;
 }
+
+/* a - b for F values, exactly, as (P, E) at the smaller exponent. */
+static wq_obj wq_sub(wq_obj a, wq_obj b) {
+    if (a.p == 0) a.e = b.e;
+    if (b.p == 0) b.e = a.e;
+    wq_obj d;
+    d.e = a.e < b.e ? a.e : b.e;
+    __int128 pa = a.p, pb = b.p;
+    for (int i = 0; i < 2 * (a.e - d.e); ++i) pa *= 2;
+    for (int i = 0; i < 2 * (b.e - d.e); ++i) pb *= 2;
+    d.p = pa - pb;
+    return d;
+}
+
+static int wq_less(wq_obj a, wq_obj b) { return wq_sub(a, b).p < 0; }
+
+static double wq_to_double(wq_obj a) { return ldexp((double)a.p, 2 * a.e - 2); }
 
 float q4o_wq_gscale(int64_t n, const uint16_t* w) {
     float amax = 0.0f;
@@ -555,12 +601,12 @@ uint32_t q4o_wq_block(const uint16_t* w, float g, int mse, uint8_t* codes8) {
         volatile float t = bamax / six_g;
         b = q4o_e4m3fn_from(t);
         if (mse) {
-            float best = INFINITY;
+            wq_obj best = {0, 0};
             for (uint32_t c = 1; c <= 0x7Eu; ++c) {
                 volatile float eff = (float)q4o_e4m3fn(c) * g;
-                float e = wq_err(mag, eff);
-                if (e < best) {
-                    best = e;
+                wq_obj o = wq_objective(mag, eff);
+                if (c == 1 || wq_less(o, best)) { /* strictly less: the lowest byte keeps a tie */
+                    best = o;
                     b = c;
                 }
             }
@@ -582,4 +628,39 @@ void q4o_quant_weights_nvfp4(int32_t rows, int32_t cols, const uint16_t* w, int3
     const int64_t nb = (int64_t)rows * cols / 16;
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < nb; ++i) scales[i] = (uint8_t)q4o_wq_block(w + 16 * i, g, mse, codes + 8 * i);
+}
+
+/* Codes of a block under a given scale byte b (the rule above), and the
+ * amount by which b's exact squared error exceeds the block's exact MSE
+ * minimum (F(b) - min F, exact, rounded once to fp64).  For checking a
+ * quantizer that takes the same decision by another evaluation. */
+double q4o_wq_codes_excess(const uint16_t* w, float g, uint32_t b, uint8_t* codes8) {
+    float mag[16];
+    uint32_t sign[16];
+    for (int k = 0; k < 16; ++k) {
+        float v = (float)q4o_bf16(w[k]);
+        mag[k] = fabsf(v);
+        sign[k] = signbit(v) ? 8u : 0u;
+    }
+    volatile float eff = (float)q4o_e4m3fn(b) * g;
+    for (int k = 0; k < 8; ++k) codes8[k] = 0;
+    for (int k = 0; k < 16; ++k) {
+        uint32_t c = (b == 0 ? 0u : wq_code(mag[k], eff)) | sign[k];
+        codes8[k / 2] |= (uint8_t)(k % 2 == 0 ? c : c << 4);
+    }
+    if (b == 0 || b > 0x7Eu) return 0.0;
+    wq_obj mine = wq_objective(mag, eff), best = mine;
+    for (uint32_t c = 1; c <= 0x7Eu; ++c) {
+        volatile float e2 = (float)q4o_e4m3fn(c) * g;
+        wq_obj o = wq_objective(mag, e2);
+        if (wq_less(o, best)) best = o;
+    }
+    return wq_to_double(wq_sub(mine, best));
+}
+
+void q4o_wq_codes_excess_blocks(int64_t nblocks, const uint16_t* w, float g, const uint8_t* scales,
+                                uint8_t* codes, double* excess) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < nblocks; ++i)
+        excess[i] = q4o_wq_codes_excess(w + 16 * i, g, scales[i], codes + 8 * i);
 }

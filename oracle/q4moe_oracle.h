@@ -151,6 +151,11 @@ void q4o_quant_weights_nvfp4(int32_t rows, int32_t cols, const uint16_t* w, int3
                              uint8_t* scales, float* gscale);
 float q4o_wq_gscale(int64_t n, const uint16_t* w);
 uint32_t q4o_wq_block(const uint16_t* w, float g, int mse, uint8_t* codes8);
+/* The codes of one block under scale byte b, and how much b's exact squared
+ * error exceeds the block's exact minimum over the bytes 0x01..0x7E. */
+double q4o_wq_codes_excess(const uint16_t* w, float g, uint32_t b, uint8_t* codes8);
+void q4o_wq_codes_excess_blocks(int64_t nblocks, const uint16_t* w, float g, const uint8_t* scales,
+                                uint8_t* codes, double* excess);
 
 /* bf16 bit pattern nearest to v (RNE), for chaining an oracle output. */
 uint32_t q4o_bf16_from(double v);
