@@ -31,7 +31,7 @@ q4moe_status fail(q4moe_status s, const char* fmt, ...) {
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 constexpr size_t kAlign = 256;
-size_t up_to(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
+constexpr size_t up_to(size_t n, size_t a = kAlign) { return (n + a - 1) / a * a; }
 
 constexpr int kMaxDim = 4096;
 
@@ -92,15 +92,29 @@ q4moe_status check_experts(const q4moe_experts* ex, const q4moe_router* r) {
 // Workspace layouts
 // ---------------------------------------------------------------------------
 
+// Every workspace starts with the same prefix at the same offsets, whatever
+// the entry point, shape or token count: the control words, then the tag
+// area of the one-launch decode, sized for the largest supported shapes.
+// Only the one-launch decode writes the tag area, and it accepts a tag only
+// when it carries the current call's epoch (one more than the last completed
+// call's), so values of earlier calls never match and no other entry point
+// can leave a value there that a later one-launch call would take.  Each
+// entry point's own scratch follows the prefix.
+constexpr int kMaxExperts = 256, kMaxTopK = 8;
+constexpr size_t kScTagOff = up_to(CTRL_WORDS * 4);
+constexpr size_t kHTagOff = kScTagOff + up_to((size_t)kReplicas * kMaxExperts * 8);
+constexpr size_t kZTagOff = kHTagOff + up_to((size_t)kReplicas * kMaxTopK * kMaxDim * 8);
+constexpr size_t kHqTagOff = kZTagOff + up_to((size_t)(kMaxTopK + 1) * kMaxDim * 8);
+constexpr size_t kPrefixBytes = kHqTagOff + up_to((size_t)kReplicas * (kMaxDim / 4) * 8);
+
 struct RouterWs {
     size_t ctrl, logits, ids, w, total;
 };
 
 RouterWs router_ws(int E, int K, int T) {
     RouterWs l;
-    size_t o = 0;
-    l.ctrl = o;
-    o += up_to(CTRL_WORDS * 4);
+    size_t o = kPrefixBytes;
+    l.ctrl = 0;
     l.logits = o;
     o += up_to((size_t)T * E * 4);
     l.ids = o;
@@ -121,15 +135,12 @@ struct DecodeWs {
 DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
+    // the one-launch decode's tags, in the common prefix:
+    l.sc_tag = kScTagOff;  // (score, epoch) pairs [kReplicas][E]
+    l.h_tag = kHTagOff;    // (h, epoch) pairs [kReplicas][K][I] (W4A4: codes and scales)
+    l.z_tag = kZTagOff;    // (w * g * z, epoch) pairs [K + 1][H]; slot K: the shared expert
+    l.hq_tag = kHqTagOff;  // shared expert: (four h codes, epoch) [kReplicas][S / 4]
     size_t o = l.r.total;
-    l.sc_tag = o;  // single-token launch: (score, epoch) pairs, kReplicas copies
-    o += up_to((size_t)kReplicas * E * 8);
-    l.h_tag = o;   // (h, epoch) pairs, kReplicas copies
-    o += up_to((size_t)kReplicas * K * I * 8);
-    l.z_tag = o;   // (w * g * z, epoch) pairs; slot K: the shared expert
-    o += up_to((size_t)(K + (S > 0 ? 1 : 0)) * H * 8);
-    l.hq_tag = o;  // shared expert: (four h codes, epoch), kReplicas copies
-    o += up_to((size_t)kReplicas * (S / 4) * 8);
     l.sh_xq = o;   // shared expert taps [T][H], [T][S], [T][S], and its z [T][H]
     o += up_to(S > 0 ? (size_t)T * H : 0);
     l.sh_h = o;
@@ -137,7 +148,7 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     l.sh_hq = o;
     o += up_to((size_t)T * S);
     l.sh_z = o;
-    o += up_to(S > 0 && T > 1 ? (size_t)T * H * 4 : 0);
+    o += up_to(S > 0 ? (size_t)T * H * 4 : 0);
     l.xq_c = o;    // W4A4 taps: x codes and scales, h codes and scales
     o += up_to(a4 ? (size_t)H / 2 : 0);
     l.xq_s = o;
@@ -288,7 +299,7 @@ struct GemvWs {
 GemvWs gemv_ws(int T) {
     GemvWs l;
     l.ctrl = 0;
-    l.keys = up_to(CTRL_WORDS * 4);
+    l.keys = kPrefixBytes;
     l.total = l.keys + up_to((size_t)kMaxGemvBlocks * T * 8);
     return l;
 }
@@ -604,20 +615,24 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
             f.sh_h = at<float>(ws, l.sh_h);
             f.sh_hq = at<uint8_t>(ws, l.sh_hq);
         }
-        if (sh || a4) {  // these variants have no multi-launch fallback
-            st = sh ? (a4 ? launch_fused<FMT_NVFP4, true, true>(f, s) : launch_fused<FMT_NVFP4, true, false>(f, s))
-                    : launch_fused<FMT_NVFP4, false, true>(f, s);
+        if (a4) {  // the W4A4 decode has no multi-launch form
+            st = sh ? launch_fused<FMT_NVFP4, true, true>(f, s) : launch_fused<FMT_NVFP4, false, true>(f, s);
             if (st == Q4MOE_EUNSUPPORTED)
                 return fail(st, "the single launch does not fit this device and shape");
             return st;
         }
-        st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
+        // where the single launch does not fit the device and shape, the
+        // multi-launch path below takes the token
+        if (sh)
+            st = launch_fused<FMT_NVFP4, true, false>(f, s);
+        else
+            st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
         if (st != Q4MOE_EUNSUPPORTED) return st;
     }
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
     const float* zsh = nullptr;
-    if (sh) {  // 2-4 tokens: the shared expert's own three launches first
+    if (sh) {  // the shared expert's own three launches first
         SharedSmallArgs q;
         q.T = n_tok;
         q.H = ex->hidden;
@@ -787,7 +802,7 @@ q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_ex
 size_t q4moe_quantize_weights_ws_bytes(int32_t rows, int32_t cols) {
     (void)rows;
     (void)cols;
-    return (size_t)kWqMaxBlocks * sizeof(float);
+    return kPrefixBytes + (size_t)kWqMaxBlocks * sizeof(float);
 }
 
 q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_t cols, int32_t mode,
@@ -806,7 +821,7 @@ q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_
     hipStream_t s = (hipStream_t)stream;
     const size_t n8 = (size_t)rows * cols / 8, nblocks = (size_t)rows * cols / 16;
     const int grid1 = (int)std::min<size_t>(kWqMaxBlocks, (n8 + 255) / 256);
-    float* partial = static_cast<float*>(ws);
+    float* partial = at<float>(ws, kPrefixBytes);
     hipLaunchKernelGGL(k_wq_amax, dim3(grid1), dim3(256), 0, s, reinterpret_cast<const uint4*>(w_bf16), n8, partial);
     if ((st = launched("weight quantizer maximum")) != Q4MOE_OK) return st;
     WqArgs a;

@@ -424,10 +424,23 @@ struct GemvArgs {
     unsigned long long* keys;  // [gridDim][T] workspace: each workgroup's best key per token
 };
 
-// Order-preserving map of fp32 onto uint32 (larger float -> larger integer).
+// Order-preserving map of fp32 onto uint32 (larger float -> larger integer;
+// -0 and +0 are equal numbers and map alike).
 __device__ __forceinline__ uint32_t f32_order(float f) {
-    const uint32_t u = __float_as_uint(f);
+    uint32_t u = __float_as_uint(f);
+    if ((u << 1) == 0u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Exponent s of the power of two 2^s that puts a row's largest magnitude mx
+// in [2^14, 2^15) before the row is rounded to fp16 (0 for a zero, infinite
+// or NaN maximum).  s is at most 127 so that 2^s stays finite in fp32: a row
+// of bf16 subnormals (multiples of 2^-133) then lands on multiples of 2^-6,
+// still exact in fp16.  Results are scaled back by ldexp(result, -s) before
+// any other factor, so the way back is exact unless the result itself
+// underflows.
+__device__ __forceinline__ int fp16_stage_exp(float mx) {
+    return (mx > 0.f && mx < __builtin_inff()) ? min(14 - ilogbf(mx), 127) : 0;
 }
 
 typedef float f32x4g __attribute__((ext_vector_type(4)));
@@ -589,8 +602,7 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
         if (threadIdx.x < T) {
             const float mx = fmaxf(fmaxf(s_amax[0][threadIdx.x], s_amax[1][threadIdx.x]),
                                    fmaxf(s_amax[2][threadIdx.x], s_amax[3][threadIdx.x]));
-            // scale 2^(14 - ilogb(max)); no scaling for 0, inf or NaN
-            s_exp[threadIdx.x] = (mx > 0.f && mx <= 3.4e38f) ? 14 - ilogbf(mx) : 0;
+            s_exp[threadIdx.x] = fp16_stage_exp(mx);
         }
         __syncthreads();
 #pragma unroll
@@ -629,10 +641,10 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
                                                       cols, &xs[0][0], m16, kq, x_setup, sblk, (uint32_t)(grp0 * 16),
                                                       grp0 * 16 + 16 <= a.rows);
     const float g = *a.gscale;
-    float unscale = 0.f;
+    int unexp = 0;
 #pragma unroll
     for (int t = 0; t < T; ++t)
-        if (n == t) unscale = ldexpf(g, -s_exp[t]);
+        if (n == t) unexp = -s_exp[t];
     for (; grp < groups; grp += gridDim.x * 4) {
         if (grp != blockIdx.x * 4 + wave) {
             const uint32_t r = (uint32_t)min(grp * 16 + m16, a.rows - 1);
@@ -645,7 +657,7 @@ __global__ __launch_bounds__(256, 3) void k_gemv_mfma(GemvArgs a) {
             for (int rr = 0; rr < 4; ++rr) {
                 const int row = grp * 16 + 4 * kq + rr;
                 if (row < a.rows) {
-                    const float l = acc[rr] * unscale;
+                    const float l = ldexpf(acc[rr], unexp) * g;
                     a.logits[(size_t)n * a.rows + row] = l;
                     const unsigned long long key =
                         ((unsigned long long)f32_order(l) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)row);
@@ -754,8 +766,7 @@ __device__ __forceinline__ void block_amax4(float m[4], float (*s_amax)[4], int*
     if (threadIdx.x < 4) {
         const float mx = fmaxf(fmaxf(s_amax[0][threadIdx.x], s_amax[1][threadIdx.x]),
                                fmaxf(s_amax[2][threadIdx.x], s_amax[3][threadIdx.x]));
-        // scale 2^(14 - ilogb(max)) puts the largest magnitude in [2^14, 2^15)
-        s_exp[threadIdx.x] = (mx > 0.f && mx <= 3.4e38f) ? 14 - ilogbf(mx) : 0;
+        s_exp[threadIdx.x] = fp16_stage_exp(mx);
     }
     __syncthreads();
 }
@@ -914,12 +925,13 @@ __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
         for (int sl = 0; sl < a.K; ++sl)
             if (min(max(s_ids[n * a.K + sl], 0), a.E - 1) == e) pp = n * a.K + sl;
         if (pp >= 0) {
-            const float sc = ldexpf(a.upg[e], -s_exp[n]);
+            const float ge = a.upg[e];
+            const int unexp = -s_exp[n];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rr = blockIdx.x * 64 + wave * 16 + 4 * kq + r;
                 if (rr < a.I) {
-                    const float u = fmaxf(acc[r] * sc, 0.f);
+                    const float u = fmaxf(ldexpf(acc[r], unexp) * ge, 0.f);
                     a.h[(size_t)pp * a.I + rr] = u * u;
                 }
             }
@@ -982,11 +994,12 @@ __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
 #pragma unroll
         for (int c = 1; c < kSmallT; ++c)
             if (c == n) pp = cols[c];
-        const float sc = ldexpf(a.w[pp] * a.dng[e], -s_exp[n]);
+        const float wg = a.w[pp] * a.dng[e];
+        const int unexp = -s_exp[n];
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int rr = blockIdx.x * 64 + wave * 16 + 4 * kq + r;
-            if (rr < a.H) a.zw[(size_t)pp * a.H + rr] = z[r] * sc;
+            if (rr < a.H) a.zw[(size_t)pp * a.H + rr] = ldexpf(z[r], unexp) * wg;
         }
     }
 }

@@ -46,11 +46,26 @@
  *    problem.  Nothing throws, aborts or prints.
  *  - Alignment: code arrays, x, y, logits and workspaces 16-byte aligned;
  *    scale arrays 4-byte aligned.
- *  - Workspaces: size from the matching *_ws_bytes() call; zero-filled before
- *    the first use (q4moe_ws_init).  Every call leaves the workspace's
- *    control words zero again, so one workspace serves any number of calls
- *    issued in order on one stream; calls that overlap in time must use
- *    different workspaces.
+ *  - Workspaces: size from the matching *_ws_bytes() call; zero-filled once
+ *    before the first use (q4moe_ws_init).  Every workspace starts with the
+ *    same prefix at the same offsets: control words, then the epoch-tagged
+ *    hand-off values of the one-launch decode, sized for the largest
+ *    supported shapes (about 2.4 MB).  Only the one-launch decode writes the
+ *    prefix, and each of its calls accepts only values tagged with its own
+ *    epoch (one more than the last completed call's); every other entry
+ *    point keeps its scratch after the prefix.  So one workspace, sized for
+ *    the largest call it serves, takes any sequence of calls of any entry
+ *    points, shapes and token counts issued in order on one stream; calls
+ *    that overlap in time must use different workspaces.
+ *  - The one-launch decode (n_tok = 1 in q4moe_w4a16_decode and its shared
+ *    and W4A4 variants) is a persistent kernel whose workgroups wait on one
+ *    another: it launches one workgroup per compute unit and needs all of
+ *    them resident at once, so the device must not be shared with work that
+ *    holds compute units for the whole call.  Every wait is bounded: if one
+ *    expires (a workgroup that never became resident, or a workspace that is
+ *    not zero-filled), the kernel still ends and the call has returned OK,
+ *    but bit 0 of the workspace flags is set and y is not valid.  Read the
+ *    flags with q4moe_ws_check (sticky until q4moe_ws_init).
  */
 #ifndef Q4MOE_H
 #define Q4MOE_H
@@ -246,8 +261,11 @@ q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, cons
  *   exact quotient), ties to the even code, saturating at 6, sign of w kept;
  *   Q4MOE_WQ_MAX: b = E4M3FN nearest-even of fl32(bamax / fl32(6 g));
  *   Q4MOE_WQ_MSE: b in 0x01..0x7E minimising the block's squared error
- *   (summed in element order, every step rounded to fp32), the lowest byte
- *   among equal minima; an all-zero block takes b = 0.
+ *   sum (|w| - e2m1(code) * eff(b))^2, the lowest byte among equal minima;
+ *   an all-zero block takes b = 0.  The search evaluates the error in fp32
+ *   (summed in element order): where two bytes' exact errors differ by less
+ *   than that evaluation's rounding (at most about 2^-15 of the block's
+ *   sum w^2), it may keep the other byte.
  * Two launches; the workspace holds the first one's partial maxima. */
 enum { Q4MOE_WQ_MAX = 0, Q4MOE_WQ_MSE = 1 };
 size_t q4moe_quantize_weights_ws_bytes(int32_t rows, int32_t cols);

@@ -40,6 +40,11 @@ FAM_NVFP4, FAM_INT4, FAM_W4A4 = 0, 1, 2
 # E4M3FN bytes of 2^k for k = -4..2 (exponent field k+7, mantissa 0).
 NVFP4_SCALE_BYTES = np.array([(k + 7) << 3 for k in range(-4, 3)], dtype=np.uint8)
 
+# Every finite E4M3FN byte (both signs, subnormals, zeros and 448): all but
+# the two NaN encodings S.1111.111.  An alternative block-scale table for
+# edge-case parity runs.
+E4M3_FINITE_BYTES = np.array([b for b in range(256) if (b & 0x7F) != 0x7F], dtype=np.uint8)
+
 # FP8 shared-expert weight bytes: both signs, exponent fields 1..10, every
 # mantissa (magnitudes 2^-6 .. 15), so no NaN and no subnormal.
 FP8_WEIGHT_BYTES = np.array([(sg << 7) | (e << 3) | m for sg in (0, 1) for e in range(1, 11) for m in range(8)],
@@ -165,10 +170,10 @@ def router(seed, fam, layer, E, H, sigma_g=0.02):
 
 
 def nvfp4_matrix(seed, fam, layer, s_codes, s_scales, index, rows, cols, pool=None,
-                 out_codes=None, out_scales=None):
+                 out_codes=None, out_scales=None, scale_bytes=NVFP4_SCALE_BYTES):
     codes = bytes_(key(seed, fam, layer, s_codes, index), rows * cols // 2, pool, out_codes)
     scales = choice_bytes(key(seed, fam, layer, s_scales, index), rows * cols // 16,
-                          NVFP4_SCALE_BYTES, pool, out_scales)
+                          scale_bytes, pool, out_scales)
     return codes.reshape(rows, cols // 2), scales.reshape(rows, cols // 16)
 
 
@@ -194,16 +199,22 @@ def bank_arrays(E, H, I, fmt, alloc=np.zeros):
     }
 
 
-def expert_bank(seed, fam, layer, E, H, I, fmt, experts=None, gscale=1.0 / 64, out=None):
+def expert_bank(seed, fam, layer, E, H, I, fmt, experts=None, gscale=1.0 / 64, out=None,
+                scale_bytes=NVFP4_SCALE_BYTES):
     """Expert bank as a dict of expert-major numpy arrays.
 
     fmt: "nvfp4" or "int4".  `experts` restricts generation to a subset of
     expert indices (the other entries are left as they are), which lets a
     consumer regenerate only the experts a token selected.  `out` reuses the
     arrays of an earlier bank of the same shape.  NVFP4 per-tensor scales are
-    `gscale`; int4 tensors carry none (stored as 1.0).
+    `gscale`, block scales drawn uniformly from `scale_bytes`; int4 tensors
+    carry none (stored as 1.0).
     """
-    mat = nvfp4_matrix if fmt == "nvfp4" else int4_matrix
+    if fmt == "nvfp4":
+        def mat(*a):
+            return nvfp4_matrix(*a, scale_bytes=scale_bytes)
+    else:
+        mat = int4_matrix
     bank = bank_arrays(E, H, I, fmt) if out is None else out
     bank["up_gscale"][:] = gscale if fmt == "nvfp4" else 1.0
     bank["down_gscale"][:] = gscale if fmt == "nvfp4" else 1.0
@@ -220,10 +231,11 @@ def expert_bank(seed, fam, layer, E, H, I, fmt, experts=None, gscale=1.0 / 64, o
     return bank
 
 
-def lm_head(seed, fam, layer, V, H, gscale=1.0 / 64):
+def lm_head(seed, fam, layer, V, H, gscale=1.0 / 64, scale_bytes=NVFP4_SCALE_BYTES):
     """NVFP4 lm_head [V, H]: codes, scales, per-tensor fp32 scale."""
     with ThreadPoolExecutor(NTHREADS) as pool:
-        codes, scales = nvfp4_matrix(seed, fam, layer, S_LM_CODES, S_LM_SCALES, 0, V, H, pool)
+        codes, scales = nvfp4_matrix(seed, fam, layer, S_LM_CODES, S_LM_SCALES, 0, V, H, pool,
+                                     scale_bytes=scale_bytes)
     return codes, scales, np.float32(gscale)
 
 

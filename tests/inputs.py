@@ -10,11 +10,15 @@ GAP = 1e-4
 SEED = 20261202
 
 
-def x_with_clear_routing(seed, fam, layer, wg, b, T, k, max_attempts=64):
+def x_with_clear_routing(seed, fam, layer, wg, b, T, k, max_attempts=64, transform=None):
+    """x rows (bf16 bits) whose routing has no near tie; `transform` (bits ->
+    bits) is applied to each draw before the routing is checked."""
     H = wg.shape[1]
     attempts = [0] * T
     for _ in range(max_attempts):
         x = synth.x_rows(seed, fam, layer, H, attempts)
+        if transform is not None:
+            x = transform(x)
         r = oracle.router(wg, b, x, k)
         bad = [t for t in range(T) if r["gap"][t] < GAP]
         if not bad:

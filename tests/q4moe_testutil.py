@@ -127,3 +127,18 @@ def bf16_rne_of_f32(a):
     u = np.asarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
     r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
     return r.astype(np.uint16)
+
+
+def unfloored_errors(y_bf16_bits, yhat):
+    """Errors the floored gate does not show: the largest relative error
+    |y - yhat| / |yhat| over nonzero yhat, the same after taking off half a
+    bf16 ulp of yhat (the output rounding), and the normwise error
+    ||y - yhat||_2 / ||yhat||_2."""
+    y = bf16_bits_to_f64(y_bf16_bits).astype(np.float64)
+    yhat = np.asarray(yhat, dtype=np.float64)
+    nz = yhat != 0
+    err = np.abs(y - yhat)
+    rel = float((err[nz] / np.abs(yhat[nz])).max()) if nz.any() else 0.0
+    rel_r = float((np.maximum(err - half_ulp_bf16(yhat), 0.0)[nz] / np.abs(yhat[nz])).max()) if nz.any() else 0.0
+    norm = float(np.linalg.norm(y - yhat) / max(np.linalg.norm(yhat), 1e-300))
+    return rel, rel_r, norm

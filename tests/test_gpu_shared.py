@@ -88,6 +88,16 @@ def test_decode_shared_small(E, H, I, S):
     check_shared(L, sh, out)
 
 
+def test_decode_shared_one_token_without_single_launch():
+    # top-8 routing at hidden 2688 needs 8 x 336 down units, more than the
+    # 2048 waves of the single launch: one token then takes the shared
+    # expert's own launches and the small-batch kernels
+    L = layer(SEED + 8, synth.FAM_NVFP4, 0, 16, 2688, 256, 1, 8, "nvfp4")
+    sh = synth.shared_fp8(SEED, FAM_SH, 8, 2688, 256)
+    out = run_shared(upload_router(L["wg"], L["b"], 8), upload_bank(L["bank"], "nvfp4"), upload_shared(sh), L["x"])
+    check_shared(L, sh, out)
+
+
 @pytest.fixture(scope="module")
 def full_layer():
     L = layer(SEED, synth.FAM_NVFP4, 0, 128, 2688, 1856, 1, K, "nvfp4")

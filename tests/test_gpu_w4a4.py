@@ -98,15 +98,15 @@ def test_w4a4_small_ragged():
     print(f"small: h {wh:.3f}, y {wy:.3f}; end-to-end ratio {worst_e2e:.3f}, h code bytes differing {flips}")
 
 
-def test_w4a4_full_chunk_sampled():
+def test_w4a4_full_chunk():
+    # every one of the 1024 tokens, every stage
     T, E, H, I, K = 1024, 128, 2688, 1856, 6
     bank = synth.expert_bank(SEED, synth.FAM_W4A4, 0, E, H, I, "nvfp4")
     wg, b = synth.router(SEED, synth.FAM_W4A4, 0, E, H, 0.5 / np.sqrt(H))
     x, r, att = x_with_clear_routing(SEED, synth.FAM_W4A4, 0, wg, b, T, K)
     out = _run(upload_router(wg, b, K), upload_bank(bank, "nvfp4"), x, K)
     counts = np.diff(out["offsets"])
-    sample = np.random.default_rng(0).choice(T, 12, replace=False)
-    wh, wy = _check(bank, wg, b, x, r, out, K, sample=np.sort(sample))
+    wh, wy = _check(bank, wg, b, x, r, out, K)
     print(f"full: tokens resampled {sum(a > 0 for a in att)}, per-expert counts min {counts.min()} "
           f"max {counts.max()} mean {counts.mean():.1f} std {counts.std():.1f}; h {wh:.3f}, y {wy:.3f}")
 
@@ -120,6 +120,5 @@ def test_w4a4_mid_batch(T):
     wg, b = synth.router(SEED + T, synth.FAM_W4A4, 1, E, H, 0.5 / np.sqrt(H))
     x, r, _ = x_with_clear_routing(SEED + T, synth.FAM_W4A4, 1, wg, b, T, K)
     out = _run(upload_router(wg, b, K), upload_bank(bank, "nvfp4"), x, K)
-    sample = None if T <= 8 else np.sort(np.random.default_rng(T).choice(T, 8, replace=False))
-    wh, wy = _check(bank, wg, b, x, r, out, K, sample=sample)
+    wh, wy = _check(bank, wg, b, x, r, out, K)
     print(f"T={T}: experts used {int((np.diff(out['offsets']) > 0).sum())}; h {wh:.3f}, y {wy:.3f}")
