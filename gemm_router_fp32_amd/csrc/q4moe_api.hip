@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "q4moe.h"
 #include "q4moe_fused.hpp"
@@ -730,6 +731,59 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
                                 int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
                                 size_t ws_bytes, void* stream) {
     return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The decode without a caller workspace: its workspace is a file-scope
+// device array, one copy per GPU, zero-filled when the code object is
+// loaded and kept until the process ends.  Its device address on each GPU
+// is looked up once (with that GPU current) and used from then on; the
+// array's name in host code is only a stand-in for the symbol.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = 3u << 20;  // the prefix (~2.4 MB) plus room for 1-4 tokens
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+q4moe_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(Q4MOE_EDEVICE, "no HIP device: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(Q4MOE_EDEVICE, "device index %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(Q4MOE_EDEVICE, "static scratch address on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return Q4MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+q4moe_status q4moe_w4a16_decode_noalloc(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                                        int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* stream) {
+    q4moe_status st = check_router(r);
+    if (st != Q4MOE_OK) return st;
+    if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
+    if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    const size_t need = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
+    if (need > kNoAllocScratchBytes)
+        return fail(Q4MOE_EWORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", need,
+                    kNoAllocScratchBytes);
+    void* ws = nullptr;
+    if ((st = scratch_for_current_device(&ws)) != Q4MOE_OK) return st;
+    return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, kNoAllocScratchBytes, stream);
 }
 
 size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,

@@ -76,6 +76,7 @@ _SIGS = {
     "q4moe_w4a16_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a16_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_decode_taps": (_i32, [_p, _p, _i32, _p]),
+    "q4moe_w4a16_decode_noalloc": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p]),
     "q4moe_w4a4_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_taps": (_i32, [_p, _p, _i32, _p]),
@@ -216,6 +217,12 @@ def q4moe_w4a16_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=
     _check(lib().q4moe_w4a16_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                     _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
     return ws
+
+
+def q4moe_w4a16_decode_noalloc(router, experts, x, y, ids=None, w=None, stream=None):
+    """q4moe_w4a16_decode on the library's static per-GPU scratch (no workspace)."""
+    _check(lib().q4moe_w4a16_decode_noalloc(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), x.shape[0],
+                                            _ptr(y), _ptr(ids), _ptr(w), _stream(stream)))
 
 
 def q4moe_w4a4_decode_ws_bytes(router, experts, n_tok):

@@ -151,6 +151,20 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex,
                                 const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
                                 int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
 
+/* q4moe_w4a16_decode for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): no
+ * workspace argument; the library's own static scratch of 3 MiB per GPU
+ * (device memory held from load until the process ends) serves as the
+ * workspace.  It allocates nothing.  Shapes whose workspace would exceed the
+ * scratch return Q4MOE_EWORKSPACE (1-4 tokens of the 128 x 2688 x 1856
+ * top-6 layer take about 3.0 MB).  Every call on a GPU shares that GPU's
+ * scratch: calls that overlap in time on one GPU race and must not be
+ * issued (calls in order on one stream are fine).  The expired-wait flag of
+ * the one-launch decode is kept in the scratch and not reported. */
+q4moe_status q4moe_w4a16_decode_noalloc(const q4moe_router* r, const q4moe_experts* ex,
+                                        const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
+                                        int32_t* ids, float* w, void* stream);
+
 /* Byte offsets, inside a decode workspace, of values the decode leaves there
  * after each call: y32 fp32 [n_tok][hidden] (y before rounding) and
  * h fp32 [n_tok*top_k][inter] (relu(u)^2, rows ordered (token, slot)). */

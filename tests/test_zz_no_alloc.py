@@ -1,0 +1,66 @@
+"""The decode entry point that allocates nothing (static per-GPU scratch)
+against the decode with a caller workspace, through the C-ABI: bit for bit
+on two calls in a row, the second with a smaller input (4 tokens through the
+small-batch kernels, then 1 token through the one-launch decode), then the
+one-token call again (the scratch keeps the epoch of the call before)."""
+import numpy as np
+import pytest
+import torch
+
+import gemm_router_fp32_amd as g
+import synth
+from gpu_util import DEV, dev, host, upload_bank, upload_router
+from inputs import SEED, layer
+
+pytestmark = pytest.mark.gpu
+
+E, H, I, K = 128, 2688, 1856, 6
+
+
+def _noalloc(router, ex, x_np):
+    T = x_np.shape[0]
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    g.q4moe_w4a16_decode_noalloc(router, ex, dev(x_np), y, ids, w)
+    torch.cuda.synchronize()
+    return host(y, np.uint16), host(ids), host(w)
+
+
+def _with_ws(router, ex, x_np):
+    T = x_np.shape[0]
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    ws = g.q4moe_w4a16_decode(router, ex, dev(x_np), y, ids, w)
+    torch.cuda.synchronize()
+    assert g.q4moe_ws_check(ws) == 0
+    return host(y, np.uint16), host(ids), host(w)
+
+
+def _same(a, b):
+    return all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "int4"])
+def test_noalloc_matches_workspace_entry_point(fmt):
+    fam = synth.FAM_NVFP4 if fmt == "nvfp4" else synth.FAM_INT4
+    L = layer(SEED, fam, 5, E, H, I, 4, K, fmt)
+    ex, router = upload_bank(L["bank"], fmt), upload_router(L["wg"], L["b"], K)
+    x4, x1 = L["x"], L["x"][:1]
+    print(f"no-alloc decode {fmt}: 4 tokens, then 1 token twice", flush=True)
+    ref4, ref1 = _with_ws(router, ex, x4), _with_ws(router, ex, x1)
+    assert _same(_noalloc(router, ex, x4), ref4)
+    assert _same(_noalloc(router, ex, x1), ref1)
+    assert _same(_noalloc(router, ex, x1), ref1)
+    assert np.array_equal(ref4[1], L["route"]["ids"])
+
+
+def test_noalloc_rejects_shapes_beyond_the_scratch():
+    # top-8 of 128 with hidden and inter 4096 at 4 tokens needs about 3.6 MB
+    big = g.ExpertsS(g.NVFP4, 128, 4096, 4096, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20, 1 << 20)
+    r = g.RouterS(1 << 20, 1 << 20, 128, 4096, 8)
+    import ctypes
+    L = g.lib()
+    st = L.q4moe_w4a16_decode_noalloc(ctypes.byref(r), ctypes.byref(big), 1 << 20, 4, 1 << 20, None, None, None)
+    assert st == g.EWORKSPACE and b"static scratch" in L.q4moe_last_error()
