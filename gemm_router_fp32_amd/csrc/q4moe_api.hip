@@ -214,7 +214,7 @@ q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     const long long RU = (long long)a.K * a.I;
     const long long nw = (long long)grid * kWaves;
     const long long dpu = (a.H + kDownRows - 1) / kDownRows;
-    if (grid < a.E || (RU + nw - 1) / nw > 2 * kMaxUp || (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw ||
+    if (grid < a.E || grid > CTRL_WORDS - FW_EPOCH || (RU + nw - 1) / nw > 2 * kMaxUp || (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw ||
         dpu < kWaves - 1)
         return Q4MOE_EUNSUPPORTED;
     // shared expert: at most 4 h-code quads (16 up rows) per workgroup and

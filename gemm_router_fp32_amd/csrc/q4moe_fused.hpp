@@ -33,9 +33,9 @@
 // and readers poll the values until they carry the current epoch.  No
 // counters, no store-completion waits and no agent-scope fences (which
 // write back or invalidate a whole L2 on this part) sit on the critical
-// path.  The epoch advances by one per call: the last workgroup to finish
-// stores it, so stale values of earlier calls never match and nothing has to
-// be cleared.  Values many workgroups read (scores, h) and the epoch word are
+// path.  The epoch advances by one per call (each workgroup keeps its own
+// copy and advances it early in the call), so stale values of earlier calls
+// never match and nothing has to be cleared.  Values many workgroups read (scores, h) and the epoch word are
 // kept in kReplicas copies, copy b % kReplicas for workgroup b (which is also
 // its XCD), so no single line or memory channel serves the whole chip.
 // Every poll is bounded; on expiry the kernel flags the workspace and carries
@@ -59,6 +59,9 @@
 #ifndef Q4MOE_PHASE
 #define Q4MOE_PHASE(i)
 #endif
+#ifndef Q4MOE_WAVE_MARK
+#define Q4MOE_WAVE_MARK(i)
+#endif
 
 namespace q4moe {
 
@@ -72,8 +75,7 @@ constexpr uint32_t kPollLimit = 200000;  // polls (each at least one memory roun
 
 // Workspace control words of the fused decode.
 enum : int {
-    FW_EXIT = 3,    // workgroups finished
-    FW_EPOCH = 8,   // [kReplicas]: epoch of the last completed call
+    FW_EPOCH = 256,  // [grid]: workgroup b's epoch of the last call (at most CTRL_WORDS - FW_EPOCH workgroups)
 };
 
 struct FusedArgs {
@@ -130,56 +132,85 @@ __device__ __forceinline__ float tag_value(unsigned long long t) { return __uint
 
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
-// Exact fp32 top-k of E <= 64 * NQ keys by one wave: expert e sits in lane
-// e % 64, register e / 64, as the order-preserving integer image of its key
-// (NaN keys and padding at INT_MIN, never chosen).  Each round takes the wave
-// maximum and then the lowest expert index holding it (the lowest set bit of
-// the first non-empty ballot, found without branches), so equal keys go to
-// the lower index exactly as the definition says.  The rounds form a rolled
-// loop over K that leaves pick i in lane i; lane i then reads its score and
-// divides it by the sum of the K picked scores (summed in pick order), into
-// this wave's LDS slots.
-template <int NQ>
-__device__ __forceinline__ void wave_topk(const FusedArgs& a, const float* s_keys, const float* s_scores,
-                                          int* s_ids, float* s_w) {
+// Exact fp32 top-k by rank, in two stages.  Each key is held as a 64-bit
+// composite: the order-preserving integer image of the key in the high half
+// (NaN at INT_MIN, below every key) and 2^32 - 1 - e in the low half, so
+// that of two keys the one earlier in the selection order (the larger key;
+// for equal keys the lower expert index) has the larger composite, and no
+// two composites are equal.  An expert's rank is the number of composites
+// above its own; the experts of rank < K are the selection, in rank order.
+//  1. Wave w ranks the G = EP / 8 composites of experts w G .. w G + G - 1
+//     among themselves (EP = E rounded up to 64, 128 or 256; slots past E
+//     hold composites below every key), P = 64 / G lanes per expert, each
+//     counting over G / P of them, and writes its K largest in order to its
+//     list.
+//  2. Each entry of the lists is counted against the entries of all lists
+//     (eight lanes per entry, one list each).  For an entry whose rank among
+//     all experts is below K that count is its rank (every expert above it
+//     is in the first K of its own group, so in a list); for any other entry
+//     the count is at least K.
+// Every comparison within a stage is independent, and the lists are small.
+// The gates (topk_gates) are taken later, off the path to the up loads.
+__device__ __forceinline__ long long topk_comp(float key, int e) {
+    const uint32_t ko = (uint32_t)key_order(key);
+    return (long long)(((unsigned long long)ko << 32) | (unsigned long long)(0xFFFFFFFFu - (uint32_t)e));
+}
+
+template <int EP>
+__device__ __forceinline__ void topk_stage1(const FusedArgs& a, const long long* s_comp, long long (*s_list)[8]) {
+    constexpr int G = EP / kWaves;  // 8, 16 or 32 experts per wave
+    constexpr int P = 64 / G;       // lanes per expert: 8, 4 or 2
+    constexpr int NC = G / P;       // composites each lane compares: 1, 4 or 16
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int e = wave * G + lane / P, part = lane % P;
+    const long long ce = s_comp[e];
+    const long long* src = s_comp + wave * G + part * NC;
+    int rank = 0;
+#pragma unroll
+    for (int j = 0; j < NC; ++j) rank += src[j] > ce ? 1 : 0;
+    if constexpr (P >= 2) rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    if constexpr (P >= 4) rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+    if constexpr (P >= 8) rank += __shfl_xor(rank, 4, 64);
+    if (part == 0 && rank < a.K) s_list[wave][rank] = ce;
+}
+
+__device__ __forceinline__ void topk_stage2(const FusedArgs& a, long long (*s_list)[8], const float* s_scores,
+                                            int* s_ids, float* s_sc) {
+    // thread t: entry t / 8 of the lists (list (t / 8) / K, position
+    // (t / 8) % K), counted against list t % 8; the 8 lanes of an entry are
+    // adjacent, so the 8 counts are summed with lane moves
+    const int t = threadIdx.x, ent = t >> 3, part = t & 7;
+    const int nc = kWaves * a.K;
+    const int en = ent < nc ? ent : 0;  // threads past the entries count entry 0 and write nothing
+    const long long c = s_list[en / a.K][en % a.K];
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        if (q < a.K) rank += s_list[part][q] > c ? 1 : 0;
+    rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+    rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+    rank += __shfl_xor(rank, 4, 64);
+    if (part == 0 && ent < nc && rank < a.K) {
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)(unsigned long long)c);
+        s_ids[rank] = e;
+        s_sc[rank] = s_scores[e];
+        if ((int)((unsigned long long)c >> 32) == INT_MIN) atomicOr(a.ctrl + CTRL_FLAGS, 2u);  // a NaN key chosen
+    }
+}
+
+// The gates of one wave's copy: lane i < K takes the i-th selected score
+// over the sum of the K selected scores, summed in selection order.
+__device__ __forceinline__ void topk_gates(const FusedArgs& a, const float* s_sc, float* s_w) {
     const int lane = threadIdx.x & 63;
-    int key[NQ];
+    const float4 p0 = reinterpret_cast<const float4*>(s_sc)[0], p1 = reinterpret_cast<const float4*>(s_sc)[1];
+    const float sc[8] = {p0.x, p0.y, p0.z, p0.w, p1.x, p1.y, p1.z, p1.w};
+    float ssum = 0.f, mine = 0.f;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-        const int e = lane + 64 * q;
-        const float kv = s_keys[e];  // e < 256: inside the array; past E masked
-        key[q] = e < a.E ? key_order(kv) : INT_MIN;
+    for (int i = 0; i < 8; ++i) {
+        if (i < a.K) ssum += sc[i];
+        mine = lane == i ? sc[i] : mine;
     }
-    int my = 0;         // lane i: pick i
-    bool lost = false;  // fewer than K keys that are not NaN
-#pragma nounroll
-    for (int i = 0; i < a.K; ++i) {
-        int m = key[0];
-#pragma unroll
-        for (int q = 1; q < NQ; ++q) m = max(m, key[q]);
-        m = wave_max_i32(m);
-        // lowest index holding m: an empty ballot counts as 1024
-        int best = 1024;
-#pragma unroll
-        for (int q = 0; q < NQ; ++q)
-            best = min(best, 64 * q + (int)__builtin_ctzg((unsigned long long)__ballot(key[q] == m), 1024));
-        lost = lost || m == INT_MIN;
-        best = m == INT_MIN ? 0 : best;  // only NaN keys left: keep every read inside the bank
-#pragma unroll
-        for (int q = 0; q < NQ; ++q) key[q] = lane + 64 * q == best ? INT_MIN : key[q];
-        my = lane == i ? best : my;
-    }
-    if (lost && lane == 0) atomicOr(a.ctrl + CTRL_FLAGS, 2u);
-    const float sc_my = s_scores[my];
-    const float msc = lane < a.K ? sc_my : 0.f;
-    float ssum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-        if (i < a.K) ssum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, msc), i));
-    if (lane < a.K) {
-        s_ids[lane] = my;
-        s_w[lane] = msc / ssum;
-    }
+    if (lane < a.K) s_w[lane] = mine / ssum;
     __builtin_amdgcn_wave_barrier();
 }
 
@@ -268,9 +299,12 @@ __device__ __forceinline__ uint2 fp8x4_bf16(uint32_t v) {
 template <int FMT, int C, int C2, bool SH, bool A4>
 __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __shared__ float s_part[kWaves];
-    __shared__ float s_keys[256], s_scores[256];
-    __shared__ int s_ids_all[kWaves][8];
-    __shared__ float s_w_all[kWaves][8];
+    __shared__ __attribute__((aligned(16))) long long s_comp[256];  // selection composites (key, index)
+    __shared__ float s_scores[256];
+    __shared__ long long s_list[kWaves][8];  // each wave's K largest composites, in order
+    __shared__ int s_sel_ids[8];
+    __shared__ __attribute__((aligned(16))) float s_sel_sc[8];
+    __shared__ float s_w_all[kWaves][8];  // each wave's copy of the gates
     __shared__ float s_h[2 * 4096];     // h of the (at most two, adjacent) slots this workgroup's down rows use
     uint16_t* const s_h16 = reinterpret_cast<uint16_t*>(s_h);  // int4: bf16 hi halves, then lo halves
     __shared__ float s_hrow[kMaxWgUp];  // this workgroup's up results, before they are published
@@ -289,10 +323,15 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     const int rep = blockIdx.x % kReplicas;
 
     Q4MOE_PHASE(0);
-    // This call's epoch (the last completed call's + 1).  Every wave loads it
-    // and first uses it after the router, so nothing waits for it here.
+    // selection slots past E: composites below every key (never chosen)
+    if ((int)threadIdx.x >= a.E && threadIdx.x < 256) s_comp[threadIdx.x] = topk_comp(__builtin_nanf(""), threadIdx.x);
+    // This call's epoch: one more than the last call's.  Each workgroup keeps
+    // its own copy in word FW_EPOCH + b, which only workgroup b of each call
+    // reads and writes; every call runs every workgroup once, so all copies
+    // advance together and stay equal.  Every wave loads it and first uses it
+    // after the router, so nothing waits for it here.
     const uint32_t ep =
-        __hip_atomic_load(a.ctrl + FW_EPOCH + rep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+        __hip_atomic_load(a.ctrl + FW_EPOCH + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     // Thread 128 + e polls the score of expert e: waves 2 and up store
     // nothing in the router phase, so their poll results do not wait for
     // the score stores to complete.
@@ -435,35 +474,27 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     const int wdu0 = blockIdx.x * kWaves, wdu1 = min(wdu0 + kWaves, n_du);
     const int sl0 = wdu1 > wdu0 ? wdu0 / dpu : 0, sl1 = wdu1 > wdu0 ? (wdu1 - 1) / dpu : -1;
 
-    // ---- S: poll the scores (one copy per workgroup), form the keys.  The
-    // polling waves keep two polls in flight (every lane loads every time, so
-    // each check waits for the older poll only) and so see a score about
-    // half a memory round trip sooner than with one poll at a time.
+    // ---- S: poll the scores (one copy per workgroup), form the keys.  One
+    // poll in flight at a time, so that the loop ends with nothing
+    // outstanding: a poll left in flight would hold up the next wait on the
+    // wave's memory counter (register reuse makes the compiler place one at
+    // the top-k), and with it the whole workgroup at the next barrier.
     if (wave >= 2 && wave < 2 + (a.E + 63) / 64) {
         const unsigned long long* src = a.sc_tag + rep * a.E + (poller ? pe : 0);
         bool have = !poller;
-        auto take = [&](unsigned long long v) {
+        for (uint32_t polls = 0;; ++polls) {
+            const unsigned long long v = get_tag(src);
             if (!have && tag_is(v, ep)) {
                 const float sc = tag_value(v);
                 s_scores[pe] = sc;
-                s_keys[pe] = sc + bias;
+                s_comp[pe] = topk_comp(sc + bias, pe);
                 have = true;
             }
-        };
-        // (one exit per round: a second exit makes the compiler copy the
-        // poll registers, which waits for the newer poll as well)
-        unsigned long long va = get_tag(src);
-        unsigned long long vb = get_tag(src);
-        for (uint32_t polls = 0;; ++polls) {
-            take(va);
-            va = get_tag(src);
-            take(vb);
             if (!__any(!have)) break;
             if (polls > kPollLimit) {
                 if (lane == 0) atomicOr(flags, 1u);
                 break;
             }
-            vb = get_tag(src);
         }
     } else if constexpr (SH || A4) {
         // The waves that do not poll quantize x, eight values per thread:
@@ -505,26 +536,34 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
         }
     }
+    // Every wave holds its epoch value before this barrier (the empty asm
+    // takes it as an input, so its load has returned): the workgroup's copy
+    // can then advance after the next barrier without any wave reading the
+    // new value.
+    asm volatile("" ::"v"(ep));
     __syncthreads();
     Q4MOE_PHASE(2);
     // Shared expert down rows: after the score hand-off, for the same reason
     // (two smaller bursts delay the routing less than one).
     if constexpr (SH) issue_sh_dn();
-    int* ids = s_ids_all[wave];
-    float* wsel = s_w_all[wave];
-
-    if (a.E <= 64 * 2)
-        wave_topk<2>(a, s_keys, s_scores, ids, wsel);
+    Q4MOE_WAVE_MARK(0);
+    if (a.E <= 64)
+        topk_stage1<64>(a, s_comp, s_list);
+    else if (a.E <= 128)
+        topk_stage1<128>(a, s_comp, s_list);
     else
-        wave_topk<4>(a, s_keys, s_scores, ids, wsel);
-    if (gw == 0 && lane < a.K) {
-        const int id = ids[lane];
-        const float wv = wsel[lane];
-        a.ids[lane] = id;
-        a.w[lane] = wv;
-        if (a.ids_out) a.ids_out[lane] = id;
-        if (a.w_out) a.w_out[lane] = wv;
-    }
+        topk_stage1<256>(a, s_comp, s_list);
+    Q4MOE_WAVE_MARK(1);
+    __syncthreads();
+    topk_stage2(a, s_list, s_scores, s_sel_ids, s_sel_sc);
+    Q4MOE_WAVE_MARK(2);
+    __syncthreads();
+    int* ids = s_sel_ids;
+    float* wsel = s_w_all[wave];
+    Q4MOE_WAVE_MARK(3);
+    // the workgroup's epoch copy advances now, long before the kernel ends,
+    // so nothing is left for its last instructions
+    if (threadIdx.x == 0) __hip_atomic_store(a.ctrl + FW_EPOCH + blockIdx.x, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Q4MOE_PHASE(3);
 
     // ---- U: issue the loads of this wave's up rows.  Every lane issues every
@@ -571,6 +610,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     compiler_fence();
+    Q4MOE_PHASE(8);
+    // the gates, while the up rows travel
+    topk_gates(a, s_sel_sc, wsel);
+    if (gw == 0 && lane < a.K) {
+        const int id = ids[lane];
+        const float wv = wsel[lane];
+        a.ids[lane] = id;
+        a.w[lane] = wv;
+        if (a.ids_out) a.ids_out[lane] = id;
+        if (a.w_out) a.w_out[lane] = wv;
+    }
 
     // ---- shared expert up: u = (W x) * s_w * s_in for this segment's row
     // (its weights arrived during the routing), h = relu(u)^2; the
@@ -667,6 +717,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // their registers are reused, waits for the down weights as well.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     compiler_fence();
+    Q4MOE_PHASE(9);
     // Shared expert: one poll of the h-code quads (t and t + 512 for thread
     // t), issued before the down loads so that its results do not wait for
     // them; its quads were published about a memory round trip earlier.
@@ -1050,15 +1101,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
     Q4MOE_PHASE(7);
 
-    // ---- exit: the last workgroup out advances the epoch
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const uint32_t done = atomicAdd(a.ctrl + FW_EXIT, 1u);
-        if (done == gridDim.x - 1) {
-            for (int i = 0; i < kReplicas; ++i) atomicExch(a.ctrl + FW_EPOCH + i, ep);
-            atomicExch(a.ctrl + FW_EXIT, 0u);
-        }
-    }
+    Q4MOE_PHASE(10);
 }
 
 }  // namespace q4moe

@@ -16,7 +16,7 @@ namespace q4moe {
 enum : int { FMT_NVFP4 = 1, FMT_INT4 = 2 };
 
 // Control words at the start of every workspace.
-enum : int { CTRL_TICKET = 0, CTRL_FLAGS = 1, CTRL_WORDS = 256 };
+enum : int { CTRL_TICKET = 0, CTRL_FLAGS = 1, CTRL_WORDS = 1024 };
 
 // ---------------------------------------------------------------------------
 // Router ("Quantization (PTQ + QAD)", Precision Recipes: router compute FP32;

@@ -65,7 +65,9 @@
  *    expires (a workgroup that never became resident, or a workspace that is
  *    not zero-filled), the kernel still ends and the call has returned OK,
  *    but bit 0 of the workspace flags is set and y is not valid.  Read the
- *    flags with q4moe_ws_check (sticky until q4moe_ws_init).
+ *    flags with q4moe_ws_check (sticky until q4moe_ws_init).  A workspace
+ *    whose control words were disturbed (shared by calls that overlapped,
+ *    or overwritten) keeps failing this way until q4moe_ws_init.
  */
 #ifndef Q4MOE_H
 #define Q4MOE_H

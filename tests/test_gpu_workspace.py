@@ -8,10 +8,11 @@ through a sequence of entry points, token counts and paths, and check each
 one-token result bit for bit against the same call on a fresh workspace.
 
 The timeout test forces the one-launch decode's waits to give up from the
-host: the epoch replicas in the control words are seeded inconsistent, so
-that the workgroups of one call disagree on its epoch and some hand-offs
-never match.  Every wait is bounded, so the kernel still ends; the call
-returns OK and the workspace flag reports the expired waits."""
+host: one workgroup's epoch copy in the control words is seeded apart from
+the others, so that the workgroups of one call disagree on its epoch and
+some hand-offs never match.  Every wait is bounded, so the kernel still
+ends; the call returns OK and the workspace flag reports the expired
+waits."""
 import numpy as np
 import pytest
 import torch
@@ -24,7 +25,7 @@ from inputs import SEED, layer, x_with_clear_routing
 pytestmark = pytest.mark.gpu
 
 E, H, I, K = 128, 2688, 1856, 6
-FW_EPOCH = 8  # control word index of the first epoch replica
+FW_EPOCH = 256  # control word index of workgroup 0's epoch copy
 
 
 @pytest.fixture(scope="module")
@@ -92,18 +93,53 @@ def test_decode_bounded_waits_forced_from_host(full_layer):
     x1 = L["x"][:1]
     ref = _decode(g.q4moe_w4a16_decode, router, ex, x1, None)
     ws = g.workspace(g.q4moe_w4a16_decode_ws_bytes(router, ex, 1))
-    # epoch replicas that disagree: the workgroups reading replica 0 take
-    # epoch 1001, the others epoch 1, so hand-offs between the two groups
-    # never match and those waits expire (each after its bounded count)
-    ctrl = ws[:64].view(torch.int32)
+    # epoch copies that disagree: workgroup 0 takes epoch 1001, the others
+    # epoch 1, so hand-offs between workgroup 0 and the others never match
+    # and those waits expire (each after its bounded count)
+    ctrl = ws[:4096].view(torch.int32)
     ctrl[FW_EPOCH] = 1000
     torch.cuda.synchronize()
-    print("one-launch decode with inconsistent epoch replicas (waits expire by design)", flush=True)
+    print("one-launch decode with inconsistent epoch copies (waits expire by design)", flush=True)
     _decode(g.q4moe_w4a16_decode, router, ex, x1, ws)  # returns: every wait is bounded
     assert g.q4moe_ws_check(ws) & 1, "expired waits are reported through the workspace flag"
-    # the last workgroup made the replicas consistent again, at an epoch no
-    # stale value carries: the next call is correct (the flag stays set)
-    assert _same(_decode(g.q4moe_w4a16_decode, router, ex, x1, ws), ref)
+    # a workspace disturbed this way is re-initialised; then calls are correct
     g.q4moe_ws_init(ws)
     assert _same(_decode(g.q4moe_w4a16_decode, router, ex, x1, ws), ref)
     assert g.q4moe_ws_check(ws) == 0
+
+
+@pytest.mark.parametrize("variant", ["w4a16", "int4", "w4a4", "shared", "w4a4_shared"])
+def test_one_launch_repeated_calls(variant):
+    # every call of the one-launch decode advances the epoch of each of its
+    # workgroups; repeated calls on one workspace and on fresh workspaces
+    # must all finish within their waits and agree bit for bit
+    fmt = "int4" if variant == "int4" else "nvfp4"
+    fam = synth.FAM_INT4 if fmt == "int4" else synth.FAM_W4A4
+    L = layer(SEED + 3, fam, 4, 16, H, I, 1, K, fmt)
+    ex, router = upload_bank(L["bank"], fmt), upload_router(L["wg"], L["b"], K)
+    args, fn, wsb = (), g.q4moe_w4a16_decode, g.q4moe_w4a16_decode_ws_bytes
+    if variant in ("shared", "w4a4_shared"):
+        sh = synth.shared_fp8(SEED, 3, 4, H, 512)
+        shd = g.SharedFp8(dev(sh["up_codes"]), dev(sh["down_codes"]), sh["up_wscale"], sh["up_iscale"],
+                          sh["down_wscale"], sh["down_iscale"])
+        args = (shd,)
+        fn = g.q4moe_w4a16_decode_shared if variant == "shared" else g.q4moe_w4a4_decode_shared
+        wsb = g.q4moe_w4a16_decode_shared_ws_bytes if variant == "shared" else g.q4moe_w4a4_decode_shared_ws_bytes
+    elif variant == "w4a4":
+        fn, wsb = g.q4moe_w4a4_decode, g.q4moe_w4a4_decode_ws_bytes
+    x = dev(L["x"])
+
+    def call(ws):
+        y = torch.empty((1, H), dtype=torch.int16, device=DEV)
+        fn(router, ex, *args, x, y, ws=ws)
+        torch.cuda.synchronize()
+        assert g.q4moe_ws_check(ws) == 0, "a bounded wait expired"
+        return host(y, np.uint16)
+
+    print(f"{variant}: 12 calls on one workspace, 4 on fresh ones", flush=True)
+    ws = g.workspace(wsb(router, ex, *args, 1))
+    first = call(ws)
+    for _ in range(11):
+        assert np.array_equal(call(ws), first)
+    for _ in range(4):
+        assert np.array_equal(call(g.workspace(wsb(router, ex, *args, 1))), first)
