@@ -170,27 +170,26 @@ __device__ __forceinline__ void topk_stage1(const FusedArgs& a, const long long*
     for (int j = 0; j < NC; ++j) rank += src[j] > ce ? 1 : 0;
     if constexpr (P >= 2) rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
     if constexpr (P >= 4) rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
-    if constexpr (P >= 8) rank += __shfl_xor(rank, 4, 64);
+    if constexpr (P >= 8) rank += __builtin_amdgcn_mov_dpp(rank, 0x141, 0xF, 0xF, true);  // row_half_mirror
     if (part == 0 && rank < a.K) s_list[wave][rank] = ce;
 }
 
 __device__ __forceinline__ void topk_stage2(const FusedArgs& a, long long (*s_list)[8], const float* s_scores,
                                             int* s_ids, float* s_sc) {
-    // thread t: entry t / 8 of the lists (list (t / 8) / K, position
-    // (t / 8) % K), counted against list t % 8; the 8 lanes of an entry are
-    // adjacent, so the 8 counts are summed with lane moves
-    const int t = threadIdx.x, ent = t >> 3, part = t & 7;
-    const int nc = kWaves * a.K;
-    const int en = ent < nc ? ent : 0;  // threads past the entries count entry 0 and write nothing
-    const long long c = s_list[en / a.K][en % a.K];
+    // thread t: position (t >> 3) & 7 of list t >> 6 (positions past K hold
+    // nothing and write nothing), counted against list t & 7; the 8 lanes of
+    // an entry are adjacent, so the 8 counts are summed with lane moves
+    const int t = threadIdx.x, lst = t >> 6, pos = (t >> 3) & 7, part = t & 7;
+    const bool valid = pos < a.K;
+    const long long c = s_list[lst][valid ? pos : 0];
     int rank = 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
         if (q < a.K) rank += s_list[part][q] > c ? 1 : 0;
-    rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-    rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
-    rank += __shfl_xor(rank, 4, 64);
-    if (part == 0 && ent < nc && rank < a.K) {
+    rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+    rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, true);   // [2,3,0,1]
+    rank += __builtin_amdgcn_mov_dpp(rank, 0x141, 0xF, 0xF, true);  // row_half_mirror: the other quad of the 8
+    if (part == 0 && valid && rank < a.K) {
         const int e = (int)(0xFFFFFFFFu - (uint32_t)(unsigned long long)c);
         s_ids[rank] = e;
         s_sc[rank] = s_scores[e];
