@@ -12,6 +12,7 @@
 #include "q4moe.h"
 #include "q4moe_fused.hpp"
 #include "q4moe_w4a4.hpp"
+#include "q4moe_grouped16.hpp"
 #include "q4moe_wquant.hpp"
 #include "q4moe_shared.hpp"
 
@@ -128,7 +129,10 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s, total;
+    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s;
+    // the grouped path (more than kSmallT tokens): dispatch, fp16 staging
+    size_t counts, offsets, lists, perm, inv, act, n_act, x16, xexp, h16, hexp;
+    size_t total;
 };
 
 // S: the shared expert's intermediate size (0: no shared expert); a4: the
@@ -164,6 +168,24 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     o += up_to((size_t)T * H * 4);
     l.zw = o;      // multi-token path: w * g * z per (token, slot) pair
     o += up_to((size_t)T * K * H * 4);
+    // the grouped path's own buffers (none for kSmallT tokens or fewer)
+    const bool grouped = T > kSmallT;
+    const size_t rows = grouped ? (size_t)T * K : 0;
+    auto take = [&](size_t& off, size_t bytes) {
+        off = o;
+        o += up_to(bytes);
+    };
+    take(l.counts, grouped ? (size_t)E * 4 : 0);
+    take(l.offsets, grouped ? (size_t)(E + 1) * 4 : 0);
+    take(l.lists, grouped ? (size_t)E * T * 4 : 0);
+    take(l.perm, rows * 4);
+    take(l.inv, rows * 4);
+    take(l.act, grouped ? (size_t)E * 16 : 0);
+    take(l.n_act, grouped ? 4 : 0);
+    take(l.x16, grouped ? (size_t)T * H * 2 : 0);
+    take(l.xexp, grouped ? (size_t)T * 4 : 0);
+    take(l.h16, rows * 2 * I * 2);
+    take(l.hexp, rows * 4);
     l.total = o;
     return l;
 }
@@ -417,6 +439,103 @@ q4moe_status launch_small(const SmallMoeArgs& a, hipStream_t s) {
     return launched("small-batch combine");
 }
 
+// The grouped W4A16 path for more than kSmallT tokens (hidden and inter
+// multiples of 64): router, dispatch, fp16 staging, two grouped MFMA GEMMs
+// and the combine, in order on one stream.
+q4moe_status launch_grouped16(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x, int T, uint16_t* y,
+                              int32_t* ids_out, float* w_out, void* ws, const DecodeWs& l, hipStream_t s) {
+    const int E = r->n_experts, H = ex->hidden, I = ex->inter, K = r->top_k;
+    RouterArgs ra = router_args(r, x, T, ws, l.r, ids_out, w_out, nullptr);
+    q4moe_status st = launch_router(ra, s);
+    if (st != Q4MOE_OK) return st;
+
+    DispatchArgs da;
+    da.ids = ra.ids;
+    da.T = T;
+    da.K = K;
+    da.E = E;
+    da.counts = at<int32_t>(ws, l.counts);
+    da.lists = at<int32_t>(ws, l.lists);
+    da.offsets = at<int32_t>(ws, l.offsets);
+    da.perm = at<int32_t>(ws, l.perm);
+    da.inv = at<int32_t>(ws, l.inv);
+    da.act = at<int4>(ws, l.act);
+    da.n_act = at<int32_t>(ws, l.n_act);
+    hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(64), 0, s, da);
+    if ((st = launched("dispatch")) != Q4MOE_OK) return st;
+    hipLaunchKernelGGL(k_dispatch_scan, dim3(E), dim3(256), 0, s, da);
+    if ((st = launched("dispatch scan")) != Q4MOE_OK) return st;
+
+    StageArgs sx;
+    sx.cols = H;
+    sx.xb = x;
+    sx.hf = nullptr;
+    sx.out = at<_Float16>(ws, l.x16);
+    sx.exps = at<int32_t>(ws, l.xexp);
+    hipLaunchKernelGGL(k_stage_x16, dim3(T), dim3(256), 0, s, sx);
+    if ((st = launched("x staging")) != Q4MOE_OK) return st;
+
+    const bool nv = ex->fmt == Q4MOE_NVFP4;
+    GemmA16Args gu;
+    gu.N = I;
+    gu.Kd = H;
+    gu.K = K;
+    gu.wc = ex->up_codes;
+    gu.wsc = static_cast<const uint8_t*>(ex->up_scales);
+    gu.wg = ex->up_gscale;
+    gu.a16 = sx.out;
+    gu.aexp = sx.exps;
+    gu.act = da.act;
+    gu.n_act = da.n_act;
+    gu.perm = da.perm;
+    gu.gate = ra.w;
+    gu.out = at<float>(ws, l.h);
+    const dim3 grid_up((I + kGemmBN - 1) / kGemmBN, E);
+    const size_t lds_up = (size_t)kGemmBN * (nv ? H / 16 : H / 32) + 16;
+    if (nv)
+        hipLaunchKernelGGL((k_grouped_a16<EPI_UP, FMT_NVFP4>), grid_up, dim3(256), lds_up, s, gu);
+    else
+        hipLaunchKernelGGL((k_grouped_a16<EPI_UP, FMT_INT4>), grid_up, dim3(256), lds_up, s, gu);
+    if ((st = launched("grouped up gemm")) != Q4MOE_OK) return st;
+
+    StageArgs sh;
+    sh.cols = I;
+    sh.xb = nullptr;
+    sh.hf = gu.out;
+    sh.out = at<_Float16>(ws, l.h16);
+    sh.exps = at<int32_t>(ws, l.hexp);
+    hipLaunchKernelGGL(k_stage_h16, dim3(T * K), dim3(256), 0, s, sh);
+    if ((st = launched("h staging")) != Q4MOE_OK) return st;
+
+    GemmA16Args gd = gu;
+    gd.N = H;
+    gd.Kd = I;
+    gd.wc = ex->down_codes;
+    gd.wsc = static_cast<const uint8_t*>(ex->down_scales);
+    gd.wg = ex->down_gscale;
+    gd.a16 = sh.out;
+    gd.aexp = sh.exps;
+    gd.out = at<float>(ws, l.zw);
+    const dim3 grid_dn((H + kGemmBN - 1) / kGemmBN, E);
+    const size_t lds_dn = (size_t)kGemmBN * (nv ? I / 16 : I / 32) + 16;
+    if (nv)
+        hipLaunchKernelGGL((k_grouped_a16<EPI_DOWN, FMT_NVFP4>), grid_dn, dim3(256), lds_dn, s, gd);
+    else
+        hipLaunchKernelGGL((k_grouped_a16<EPI_DOWN, FMT_INT4>), grid_dn, dim3(256), lds_dn, s, gd);
+    if ((st = launched("grouped down gemm")) != Q4MOE_OK) return st;
+
+    SmallMoeArgs b;
+    b.T = T;
+    b.H = H;
+    b.K = K;
+    b.zw = gd.out;
+    b.y32 = at<float>(ws, l.y32);
+    b.y = y;
+    b.zsh = nullptr;
+    hipLaunchKernelGGL(k_small_combine, dim3((T * H + 255) / 256), dim3(256), 0, s, b);
+    return launched("combine");
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -552,8 +671,11 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
     q4moe_status st = check_router(r);
     if (st != Q4MOE_OK) return st;
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
-    if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    if (n_tok < 1 || n_tok > 65536) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 65536]", n_tok);
     if (sh && (st = check_shared(sh, ex, n_tok)) != Q4MOE_OK) return st;
+    if (n_tok > kSmallT && (ex->hidden % 64 != 0 || ex->inter % 64 != 0))
+        return fail(Q4MOE_EUNSUPPORTED, "more than %d tokens need hidden and inter multiples of 64 (got %d, %d)",
+                    kSmallT, ex->hidden, ex->inter);
     if (a4 && ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode takes NVFP4 experts only");
     if (a4 && n_tok != 1) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode runs one token (n_tok = %d)", n_tok);
     if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
@@ -630,6 +752,8 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
             st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
         if (st != Q4MOE_EUNSUPPORTED) return st;
     }
+
+    if (n_tok > kSmallT) return launch_grouped16(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, l, s);
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
     const float* zsh = nullptr;
@@ -991,6 +1115,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     da.offsets = at<int32_t>(ws, l.offsets);
     da.perm = at<int32_t>(ws, l.perm);
     da.inv = at<int32_t>(ws, l.inv);
+    da.act = nullptr;
+    da.n_act = nullptr;
     hipLaunchKernelGGL(k_dispatch, dim3(E), dim3(64), 0, s, da);
     if ((st = launched("dispatch")) != Q4MOE_OK) return st;
     hipLaunchKernelGGL(k_dispatch_scan, dim3(E), dim3(256), 0, s, da);

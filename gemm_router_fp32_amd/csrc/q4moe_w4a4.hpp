@@ -101,6 +101,10 @@ struct DispatchArgs {
     int32_t* offsets;    // [E+1]
     int32_t* perm;       // [T*K]   dispatch row -> pair
     int32_t* inv;        // [T*K]   pair -> dispatch row
+    // (nullable) the experts with at least one row, in expert order:
+    // act[j] = (expert, first dispatch row, rows, 0) for j < n_act[0]
+    int4* act;
+    int32_t* n_act;
 };
 
 __global__ __launch_bounds__(64) void k_dispatch(DispatchArgs a) {
@@ -135,20 +139,27 @@ __global__ __launch_bounds__(64) void k_dispatch(DispatchArgs a) {
 }
 
 // Offsets (exclusive scan of the counts), the dispatch permutation and its
-// inverse.  Workgroup e (grid E) loads all counts, scans them in LDS and
-// writes expert e's part of the permutation.
+// inverse, and (when asked) the list of experts that have rows.  Workgroup e
+// (grid E) loads all counts, scans them in LDS and writes expert e's part of
+// the permutation and its entry of the list.
 __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a) {
-    __shared__ int s_cnt[256], s_off[257];
+    __shared__ int s_cnt[256], s_off[257], s_rank;
     const int e = blockIdx.x;
     for (int i = threadIdx.x; i < a.E; i += 256) s_cnt[i] = a.counts[i];
     __syncthreads();
     if (threadIdx.x == 0) {
-        int o = 0;
+        int o = 0, nact = 0;
         for (int i = 0; i < a.E; ++i) {
             s_off[i] = o;
             o += s_cnt[i];
+            if (i == e) s_rank = nact;
+            nact += s_cnt[i] > 0;
         }
         s_off[a.E] = o;
+        if (a.act) {
+            if (s_cnt[e] > 0) a.act[s_rank] = make_int4(e, s_off[e], s_cnt[e], 0);
+            if (e == 0) a.n_act[0] = nact;
+        }
     }
     __syncthreads();
     if (e == 0)

@@ -144,10 +144,17 @@ q4moe_status q4moe_router_topk(const q4moe_router* r, const uint16_t* x_bf16, in
  * INT4_G64 int4 * bf16 ([W] Step 1; [G] What was changed).  No workspace. */
 q4moe_status q4moe_dequant_ref(const q4moe_qmat* m, float* out, void* stream);
 
-/* W4A16 routed-MoE decode of n_tok tokens (1 <= n_tok <= 4) through one
- * layer ([W] Step 1 and Interlude; Step 5 for n_tok = 4): router top-k,
- * up GEMV, relu^2, down GEMV, weighted combine.  x bf16 [n_tok][hidden],
- * y bf16 [n_tok][hidden]; ids/w (nullable) receive the routing. */
+/* W4A16 routed-MoE decode of n_tok tokens (1 <= n_tok <= 65536) through
+ * one layer ([W] Step 1 and Interlude; Step 5 for n_tok = 4; "Coming in Part
+ * 2: filling the GPU" for many concurrent tokens): router top-k, up GEMV,
+ * relu^2, down GEMV, weighted combine.  x bf16 [n_tok][hidden], y bf16
+ * [n_tok][hidden]; ids/w (nullable) receive the routing.
+ * By token count: 1 -> one persistent launch; 2-4 -> small-batch kernels
+ * that stream each selected expert once for all tokens; more -> the grouped
+ * path (per-expert dispatch lists, grouped GEMMs on fp16 MFMA with x staged
+ * exactly and h carried as fp16 hi + lo, about 22 bits), which needs hidden
+ * and inter multiples of 64 (else Q4MOE_EUNSUPPORTED).  Every path
+ * accumulates in fp32 and rounds y once. */
 size_t q4moe_w4a16_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
 q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex,
                                 const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
@@ -169,7 +176,8 @@ q4moe_status q4moe_w4a16_decode_noalloc(const q4moe_router* r, const q4moe_exper
 
 /* Byte offsets, inside a decode workspace, of values the decode leaves there
  * after each call: y32 fp32 [n_tok][hidden] (y before rounding) and
- * h fp32 [n_tok*top_k][inter] (relu(u)^2, rows ordered (token, slot)). */
+ * h fp32 [n_tok*top_k][inter] (relu(u)^2, rows ordered (token, slot)),
+ * for every token count. */
 typedef struct { size_t y32, h; } q4moe_decode_taps;
 q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts* ex,
                                      int32_t n_tok, q4moe_decode_taps* out);

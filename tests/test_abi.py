@@ -61,7 +61,10 @@ def test_decode_validation(L):
     assert _decode(L, _router(k=9), ex) == g.EINVAL
     assert _decode(L, _router(wg=None), ex) == g.EINVAL
     assert _decode(L, r, ex, T=0) == g.EINVAL
-    assert _decode(L, r, ex, T=5) == g.EINVAL
+    assert _decode(L, r, ex, T=65537) == g.EINVAL
+    # more than 4 tokens take the grouped path: hidden and inter multiples of 64
+    assert _decode(L, r, _experts(I=1856 + 32), T=5) == g.EUNSUPPORTED
+    assert b"multiples of 64" in L.q4moe_last_error()
     assert _decode(L, r, _experts(I=1850)) == g.EINVAL
     assert _decode(L, r, _experts(fmt=7)) == g.EINVAL
     assert _decode(L, r, _experts(gs=None)) == g.EINVAL
@@ -132,7 +135,7 @@ def test_decode_shared_validation(L):
     assert _decode_sh(L, r, ex, _shared(dn=A16 + 8)) == g.EALIGN
     assert _decode_sh(L, r, ex, _shared(sc=(1.0, 0.0, 1.0, 1.0))) == g.EINVAL
     assert _decode_sh(L, r, ex, _shared(sc=(1.0, 1.0, float("inf"), 1.0))) == g.EINVAL
-    assert _decode_sh(L, r, ex, _shared(), T=5) == g.EINVAL
+    assert _decode_sh(L, r, ex, _shared(), T=5) == g.EUNSUPPORTED
     assert _decode_sh(L, r, _experts(fmt=2), _shared()) == g.EUNSUPPORTED
     sh = _shared()
     need = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)
