@@ -311,45 +311,55 @@ def bench_wquant(torch, g, synth, steps):
     return out
 
 
-def bench_mid_batch(torch, g, synth, steps, counts=(1, 2, 4, 8, 16, 32, 64, 128, 256)):
-    """W4A4 MoE layer (full shapes) at T tokens through the grouped MFMA
-    pipeline, and at T = 1 through the one-launch decode: µs per layer and
-    per token, warm (one bank; the crossover in T is what is measured)."""
+MID_COUNTS = (1, 2, 3, 4, 5, 8, 16, 32, 64, 128, 256)
+
+
+def bench_mid_batch(torch, g, synth, steps, fmt, layer=None):
+    """One routed-MoE layer (full shapes) at T tokens, cold (1 GiB read
+    before every rep, so no weight is left in the MALL or the L2s): µs per
+    call through the decode entry point (which picks its path by T) and
+    through the grouped path, the experts the T tokens select, and the HBM
+    rate of the decode entry on their weights.  fmt "nvfp4" / "int4": the
+    W4A16 entries on the stack's first layer; "w4a4": q4moe_w4a4_moe (one
+    launch per token up to Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS) and
+    q4moe_w4a4_grouped on a bank routed with logits ~N(0, 0.5^2)."""
     from gpu_util import dev
-    bank = synth.expert_bank(SEED, synth.FAM_W4A4, 1, E, H, I, "nvfp4")
-    t = {k: dev(v) for k, v in bank.items()}
-    ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
-                   t["up_gscale"], t["down_gscale"])
-    wg, b = synth.router(SEED, synth.FAM_W4A4, 1, E, H, 0.5 / np.sqrt(H))
-    r = g.Router(dev(wg), dev(b), K)
-    out = {"grouped_us": {}, "grouped_us_per_token": {}, "warm": True}
-
-    def timed(fn):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = max(5, steps // 5)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return 1000.0 * e0.elapsed_time(e1) / reps
-
-    for T in counts:
-        x = dev(synth.x_rows(SEED, synth.FAM_W4A4, 1, H, [0] * T))
+    fam = {"nvfp4": synth.FAM_NVFP4, "int4": synth.FAM_INT4, "w4a4": synth.FAM_W4A4}[fmt]
+    if fmt == "w4a4":
+        bank = synth.expert_bank(SEED, fam, 1, E, H, I, "nvfp4")
+        t = {k: dev(v) for k, v in bank.items()}
+        ex = g.Experts(g.NVFP4, t["up_codes"], t["up_scales"], t["down_codes"], t["down_scales"],
+                       t["up_gscale"], t["down_gscale"])
+        wg, b = synth.router(SEED, fam, 1, E, H, 0.5 / np.sqrt(H))
+        r = g.Router(dev(wg), dev(b), K)
+        entry, entry_ws = g.q4moe_w4a4_moe, g.q4moe_w4a4_moe_ws_bytes
+        grouped, grouped_ws = g.q4moe_w4a4_grouped, g.q4moe_w4a4_grouped_ws_bytes
+    else:
+        ex, r = layer["ex"], layer["r"]
+        entry, entry_ws = g.q4moe_w4a16_decode, g.q4moe_w4a16_decode_ws_bytes
+        grouped, grouped_ws = g.q4moe_w4a16_grouped, g.q4moe_w4a16_grouped_ws_bytes
+    timer, evict = Timer(torch), Evictor(torch)
+    reps = max(5, steps // 10)
+    out = {"cold": True, "reps": reps, "decode_us": {}, "grouped_us": {}, "decode_us_per_token": {},
+           "experts_read": {}, "decode_hbm_gbps": {}}
+    for T in MID_COUNTS:
+        x = dev(synth.x_rows(SEED, fam, 1, H, [0] * T))
         y = torch.empty((T, H), dtype=torch.int16, device="cuda")
         ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
         w = torch.empty((T, K), dtype=torch.float32, device="cuda")
-        ws = g.workspace(g.q4moe_w4a4_grouped_ws_bytes(r, ex, T))
-        us = timed(lambda: g.q4moe_w4a4_grouped(r, ex, x, y, ids, w, ws=ws))
-        out["grouped_us"][T] = round(us, 2)
-        out["grouped_us_per_token"][T] = round(us / T, 2)
-        if T == 1:
-            ws1 = g.workspace(g.q4moe_w4a4_decode_ws_bytes(r, ex, 1))
-            out["one_launch_us_T1"] = round(timed(lambda: g.q4moe_w4a4_decode(r, ex, x, y, ws=ws1)), 2)
-    log(f"mid-batch W4A4: {out}")
+        ws = g.workspace(max(entry_ws(r, ex, T), grouped_ws(r, ex, T)))
+        calls = {"decode_us": lambda: entry(r, ex, x, y, ids, w, ws=ws),
+                 "grouped_us": lambda: grouped(r, ex, x, y, ids, w, ws=ws)}
+        for name, fn in calls.items():
+            fn()
+            out[name][T] = round(float(np.median(timer.each(fn, reps, evict))) * 1e3, 2)
+        n = len(np.unique(ids.cpu().numpy()))
+        out["experts_read"][T] = n
+        out["decode_us_per_token"][T] = round(out["decode_us"][T] / T, 2)
+        nbytes = layer_bytes("int4" if fmt == "int4" else "nvfp4", n, T)
+        out["decode_hbm_gbps"][T] = round(nbytes / (out["decode_us"][T] * 1e-6) / 1e9, 1)
+        del ws
+    log(f"mid-batch {fmt}: {out}")
     return out
 
 
@@ -406,6 +416,7 @@ def main():
     if not args.only_stack:
         extra["verify_step"] = bench_verify(torch, g, synth, args.steps, layers[0])
         log(f"verify step: {extra['verify_step']}")
+        extra["mid_batch_nvfp4"] = bench_mid_batch(torch, g, synth, args.steps, "nvfp4", layers[0])
         del layers
         torch.cuda.empty_cache()
         int4 = build_stack(torch, g, synth, "int4")
@@ -417,6 +428,7 @@ def main():
                                "us_per_layer_spread": spread(per4 / LAYERS),
                                "bytes_per_layer": b4, "flags": f4}
         log(f"int4 stack: {extra['int4_stack']}")
+        extra["mid_batch_int4"] = bench_mid_batch(torch, g, synth, args.steps, "int4", int4[0])
         del int4
         torch.cuda.empty_cache()
         shl = build_stack(torch, g, synth, "nvfp4", shared=True)
@@ -463,7 +475,7 @@ def main():
         torch.cuda.empty_cache()
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
         extra["weight_quantizer"] = bench_wquant(torch, g, synth, args.steps)
-        extra["mid_batch_w4a4"] = bench_mid_batch(torch, g, synth, args.steps)
+        extra["mid_batch_w4a4"] = bench_mid_batch(torch, g, synth, args.steps, "w4a4")
 
     cpu = None
     if not args.skip_cpu:

@@ -136,8 +136,10 @@ struct DecodeWs {
 };
 
 // S: the shared expert's intermediate size (0: no shared expert); a4: the
-// W4A4 single-token decode (NVFP4 activation code taps).
-DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false) {
+// W4A4 single-token decode (NVFP4 activation code taps); grouped: the
+// grouped path's buffers whatever T (they follow every other buffer, so the
+// tap offsets do not depend on it).
+DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false, bool grouped = false) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
     // the one-launch decode's tags, in the common prefix:
@@ -169,7 +171,7 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     l.zw = o;      // multi-token path: w * g * z per (token, slot) pair
     o += up_to((size_t)T * K * H * 4);
     // the grouped path's own buffers (none for kSmallT tokens or fewer)
-    const bool grouped = T > kSmallT;
+    grouped = grouped || T > kSmallT;
     const size_t rows = grouped ? (size_t)T * K : 0;
     auto take = [&](size_t& off, size_t bytes) {
         off = o;
@@ -664,27 +666,30 @@ q4moe_status check_shared(const q4moe_shared_fp8* sh, const q4moe_experts* ex, i
     return Q4MOE_OK;
 }
 
-// a4: the W4A4 single-token decode (activations quantized to NVFP4).
+// a4: the W4A4 single-token decode (activations quantized to NVFP4);
+// grouped: the grouped W4A16 path whatever the token count.
 q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
                          const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w,
-                         void* ws, size_t ws_bytes, void* stream, bool a4 = false) {
+                         void* ws, size_t ws_bytes, void* stream, bool a4 = false, bool grouped = false) {
     q4moe_status st = check_router(r);
     if (st != Q4MOE_OK) return st;
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 65536) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 65536]", n_tok);
     if (sh && (st = check_shared(sh, ex, n_tok)) != Q4MOE_OK) return st;
-    if (n_tok > kSmallT && (ex->hidden % 64 != 0 || ex->inter % 64 != 0))
-        return fail(Q4MOE_EUNSUPPORTED, "more than %d tokens need hidden and inter multiples of 64 (got %d, %d)",
-                    kSmallT, ex->hidden, ex->inter);
+    grouped = grouped || n_tok > kSmallT;
+    if (grouped && (ex->hidden % 64 != 0 || ex->inter % 64 != 0))
+        return fail(Q4MOE_EUNSUPPORTED, "the grouped path (and more than %d tokens) needs hidden and inter "
+                    "multiples of 64 (got %d, %d)", kSmallT, ex->hidden, ex->inter);
     if (a4 && ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode takes NVFP4 experts only");
     if (a4 && n_tok != 1) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode runs one token (n_tok = %d)", n_tok);
     if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
     if ((ids && !aligned(ids, 4)) || (w && !aligned(w, 4))) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh ? sh->inter : 0, a4);
+    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh ? sh->inter : 0, a4, grouped);
     if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
     if ((st = device_ready()) != Q4MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
+    if (grouped) return launch_grouped16(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, l, s);
 
     if (n_tok == 1) {  // one persistent launch for the whole layer
         FusedArgs f;
@@ -752,8 +757,6 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
             st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
         if (st != Q4MOE_EUNSUPPORTED) return st;
     }
-
-    if (n_tok > kSmallT) return launch_grouped16(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, l, s);
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
     const float* zsh = nullptr;
@@ -855,6 +858,17 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
                                 int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
                                 size_t ws_bytes, void* stream) {
     return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
+size_t q4moe_w4a16_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
+    if (!r || !ex || n_tok < 1) return 0;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, false, true).total;
+}
+
+q4moe_status q4moe_w4a16_grouped(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
+                                 int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
+                                 size_t ws_bytes, void* stream) {
+    return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream, false, true);
 }
 
 }  // extern "C"

@@ -77,6 +77,8 @@ _SIGS = {
     "q4moe_w4a16_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_decode_taps": (_i32, [_p, _p, _i32, _p]),
     "q4moe_w4a16_decode_noalloc": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p]),
+    "q4moe_w4a16_grouped_ws_bytes": (_sz, [_p, _p, _i32]),
+    "q4moe_w4a16_grouped": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_taps": (_i32, [_p, _p, _i32, _p]),
@@ -216,6 +218,19 @@ def q4moe_w4a16_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=
         ws = workspace(q4moe_w4a16_decode_ws_bytes(router, experts, n_tok), x.device)
     _check(lib().q4moe_w4a16_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                     _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4moe_w4a16_grouped_ws_bytes(router, experts, n_tok):
+    return lib().q4moe_w4a16_grouped_ws_bytes(ctypes.byref(router.s), ctypes.byref(experts.s), n_tok)
+
+
+def q4moe_w4a16_grouped(router, experts, x, y, ids=None, w=None, ws=None, stream=None):
+    n_tok = x.shape[0]
+    if ws is None:
+        ws = workspace(q4moe_w4a16_grouped_ws_bytes(router, experts, n_tok), x.device)
+    _check(lib().q4moe_w4a16_grouped(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
+                                     _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

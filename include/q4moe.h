@@ -160,6 +160,18 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex,
                                 const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
                                 int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
 
+/* The grouped W4A16 path of q4moe_w4a16_decode for any token count
+ * (1 <= n_tok <= 65536; hidden and inter multiples of 64, else
+ * Q4MOE_EUNSUPPORTED): the same arguments, results and precision as
+ * q4moe_w4a16_decode above four tokens, where that entry point takes this
+ * path itself.  Exposed so that a caller can choose the backend per batch
+ * size ("Quantization (PTQ + QAD)", Deployment and Serving).  Its workspace
+ * holds the q4moe_w4a16_decode_taps values at the same offsets. */
+size_t q4moe_w4a16_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
+q4moe_status q4moe_w4a16_grouped(const q4moe_router* r, const q4moe_experts* ex,
+                                 const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
+                                 int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
+
 /* q4moe_w4a16_decode for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): no
  * workspace argument; the library's own static scratch of 3 MiB per GPU

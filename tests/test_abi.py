@@ -65,6 +65,15 @@ def test_decode_validation(L):
     # more than 4 tokens take the grouped path: hidden and inter multiples of 64
     assert _decode(L, r, _experts(I=1856 + 32), T=5) == g.EUNSUPPORTED
     assert b"multiples of 64" in L.q4moe_last_error()
+    # the grouped entry point: the same rule at any token count
+    assert L.q4moe_w4a16_grouped(ctypes.byref(r), ctypes.byref(_experts(I=1856 + 32)), A16, 1, A16, None, None,
+                                 A16, 1 << 30, None) == g.EUNSUPPORTED
+    assert L.q4moe_w4a16_grouped(ctypes.byref(r), ctypes.byref(ex), A16, 0, A16, None, None, A16, 1 << 30,
+                                 None) == g.EINVAL
+    gneed = L.q4moe_w4a16_grouped_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 2)
+    assert gneed > L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 2)
+    assert L.q4moe_w4a16_grouped(ctypes.byref(r), ctypes.byref(ex), A16, 2, A16, None, None, A16, gneed - 1,
+                                 None) == g.EWORKSPACE
     assert _decode(L, r, _experts(I=1850)) == g.EINVAL
     assert _decode(L, r, _experts(fmt=7)) == g.EINVAL
     assert _decode(L, r, _experts(gs=None)) == g.EINVAL

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import host, run_decode, upload_bank, upload_router, ws_view
+from gpu_util import DEV, dev, host, run_decode, upload_bank, upload_router, ws_view
 from inputs import SEED, layer, x_with_clear_routing
 from q4moe_testutil import bf16_rne_of_f32, gate_f32, gate_out, unfloored_errors
 
@@ -123,3 +123,22 @@ def test_midbatch_workspace_reuse_and_determinism(full_layer):
     run_decode(router, ex, L["x"][:8], ws=a["ws"])
     b = run_decode(router, ex, L["x"][:37], ws=a["ws"])
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["y32"].view(np.uint32), b["y32"].view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4])
+def test_grouped_entry_few_tokens(full_layer, T):
+    # the grouped path called directly at 1-4 tokens (where the decode entry
+    # takes the single-launch or small-batch kernels)
+    import torch
+    L, ex, router = full_layer
+    Lt = dict(L, x=L["x"][:T], route={k: v[:T] for k, v in L["route"].items()})
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    print(f"grouped entry {L['fmt']} T={T}", flush=True)
+    ws = g.q4moe_w4a16_grouped(router, ex, dev(Lt["x"]), y, ids, w)
+    torch.cuda.synchronize()
+    taps = g.q4moe_w4a16_decode_taps(router, ex, T)
+    y32 = ws_view(host(ws), taps.y32, T * H, np.float32).reshape(T, H)
+    out = dict(y=host(y, np.uint16), ids=host(ids), w=host(w), y32=y32, ws=ws)
+    _check(Lt, out, router, ex, f"{L['fmt']} grouped entry T={T}")
