@@ -321,8 +321,8 @@ def bench_mid_batch(torch, g, synth, steps, fmt, layer=None):
     through the grouped path, the experts the T tokens select, and the HBM
     rate of the decode entry on their weights.  fmt "nvfp4" / "int4": the
     W4A16 entries on the stack's first layer; "w4a4": q4moe_w4a4_moe (one
-    launch per token up to Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS) and
-    q4moe_w4a4_grouped on a bank routed with logits ~N(0, 0.5^2)."""
+    launch for one token, the small-batch kernels up to
+    Q4MOE_W4A4_SMALL_MAX_TOKENS) and q4moe_w4a4_grouped on a bank routed with logits ~N(0, 0.5^2)."""
     from gpu_util import dev
     fam = {"nvfp4": synth.FAM_NVFP4, "int4": synth.FAM_INT4, "w4a4": synth.FAM_W4A4}[fmt]
     if fmt == "w4a4":

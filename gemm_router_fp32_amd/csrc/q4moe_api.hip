@@ -135,10 +135,16 @@ struct DecodeWs {
     size_t total;
 };
 
+// Whether the W4A16 decode of T tokens takes the grouped path (measured
+// cold crossovers at the full shapes): NVFP4 above the 8-token small-batch
+// kernels, int4 above 2 tokens (its small-batch kernels stream each expert
+// once per token and slot).
+bool w4a16_grouped(int fmt, int T) { return fmt == Q4MOE_NVFP4 ? T > kSmallT8 : T > 2; }
+
 // S: the shared expert's intermediate size (0: no shared expert); a4: the
-// W4A4 single-token decode (NVFP4 activation code taps); grouped: the
-// grouped path's buffers whatever T (they follow every other buffer, so the
-// tap offsets do not depend on it).
+// W4A4 decode (NVFP4 activation code taps); grouped: the grouped path's
+// buffers (they follow every other buffer, so the tap offsets do not depend
+// on it).
 DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false, bool grouped = false) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
@@ -157,21 +163,20 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     l.sh_z = o;
     o += up_to(S > 0 ? (size_t)T * H * 4 : 0);
     l.xq_c = o;    // W4A4 taps: x codes and scales, h codes and scales
-    o += up_to(a4 ? (size_t)H / 2 : 0);
+    o += up_to(a4 ? (size_t)T * H / 2 : 0);
     l.xq_s = o;
-    o += up_to(a4 ? (size_t)H / 16 : 0);
+    o += up_to(a4 ? (size_t)T * H / 16 : 0);
     l.hq_c = o;
-    o += up_to(a4 ? (size_t)K * I / 2 : 0);
+    o += up_to(a4 ? (size_t)T * K * I / 2 : 0);
     l.hq_s = o;
-    o += up_to(a4 ? (size_t)K * I / 16 : 0);
+    o += up_to(a4 ? (size_t)T * K * I / 16 : 0);
     l.h = o;       // h tap
     o += up_to((size_t)T * K * I * 4);
     l.y32 = o;
     o += up_to((size_t)T * H * 4);
     l.zw = o;      // multi-token path: w * g * z per (token, slot) pair
     o += up_to((size_t)T * K * H * 4);
-    // the grouped path's own buffers (none for kSmallT tokens or fewer)
-    grouped = grouped || T > kSmallT;
+    // the grouped path's own buffers
     const size_t rows = grouped ? (size_t)T * K : 0;
     auto take = [&](size_t& off, size_t bytes) {
         off = o;
@@ -417,10 +422,11 @@ inline int small_nj(int cols) {
     return nj <= 8 ? 8 : nj <= 15 ? 15 : nj <= 16 ? 16 : nj <= 21 ? 21 : nj <= 24 ? 24 : 32;
 }
 
-q4moe_status launch_small(const SmallMoeArgs& a, hipStream_t s) {
+template <int TM, bool A4>
+q4moe_status launch_small_t(const SmallMoeArgs& a, hipStream_t s) {
     const int pairs = a.T * a.K;
     const dim3 gu((a.I + 63) / 64, pairs), gd((a.H + 63) / 64, pairs);
-#define Q4_SMALL(KERN, NJ, G) hipLaunchKernelGGL((KERN<NJ>), G, dim3(256), 0, s, a)
+#define Q4_SMALL(KERN, NJ, G) hipLaunchKernelGGL((KERN<NJ, TM, A4>), G, dim3(256), 0, s, a)
 #define Q4_SMALL_NJ(KERN, NJV, G)              \
     switch (NJV) {                             \
         case 8: Q4_SMALL(KERN, 8, G); break;   \
@@ -439,6 +445,13 @@ q4moe_status launch_small(const SmallMoeArgs& a, hipStream_t s) {
 #undef Q4_SMALL
     hipLaunchKernelGGL(k_small_combine, dim3((a.T * a.H + 255) / 256), dim3(256), 0, s, a);
     return launched("small-batch combine");
+}
+
+// The small-batch kernels for 1..8 tokens: the 4-token instances up to 4
+// tokens, the 8-token ones above; a4: the W4A4 form.
+q4moe_status launch_small(const SmallMoeArgs& a, bool a4, hipStream_t s) {
+    if (a.T <= kSmallT) return a4 ? launch_small_t<kSmallT, true>(a, s) : launch_small_t<kSmallT, false>(a, s);
+    return a4 ? launch_small_t<kSmallT8, true>(a, s) : launch_small_t<kSmallT8, false>(a, s);
 }
 
 // The grouped W4A16 path for more than kSmallT tokens (hidden and inter
@@ -635,7 +648,8 @@ q4moe_status q4moe_dequant_ref(const q4moe_qmat* m, float* out, void* stream) {
 
 size_t q4moe_w4a16_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, false,
+                     w4a16_grouped(ex->fmt, n_tok)).total;
 }
 
 q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
@@ -676,12 +690,13 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 65536) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 65536]", n_tok);
     if (sh && (st = check_shared(sh, ex, n_tok)) != Q4MOE_OK) return st;
-    grouped = grouped || n_tok > kSmallT;
+    grouped = grouped || (!a4 && w4a16_grouped(ex->fmt, n_tok));
     if (grouped && (ex->hidden % 64 != 0 || ex->inter % 64 != 0))
         return fail(Q4MOE_EUNSUPPORTED, "the grouped path (and more than %d tokens) needs hidden and inter "
                     "multiples of 64 (got %d, %d)", kSmallT, ex->hidden, ex->inter);
     if (a4 && ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode takes NVFP4 experts only");
-    if (a4 && n_tok != 1) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode runs one token (n_tok = %d)", n_tok);
+    if (a4 && n_tok > kSmallT8)
+        return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode runs up to %d tokens (n_tok = %d)", kSmallT8, n_tok);
     if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
     if ((ids && !aligned(ids, 4)) || (w && !aligned(w, 4))) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
@@ -743,15 +758,11 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
             f.sh_h = at<float>(ws, l.sh_h);
             f.sh_hq = at<uint8_t>(ws, l.sh_hq);
         }
-        if (a4) {  // the W4A4 decode has no multi-launch form
-            st = sh ? launch_fused<FMT_NVFP4, true, true>(f, s) : launch_fused<FMT_NVFP4, false, true>(f, s);
-            if (st == Q4MOE_EUNSUPPORTED)
-                return fail(st, "the single launch does not fit this device and shape");
-            return st;
-        }
         // where the single launch does not fit the device and shape, the
         // multi-launch path below takes the token
-        if (sh)
+        if (a4)
+            st = sh ? launch_fused<FMT_NVFP4, true, true>(f, s) : launch_fused<FMT_NVFP4, false, true>(f, s);
+        else if (sh)
             st = launch_fused<FMT_NVFP4, true, false>(f, s);
         else
             st = ex->fmt == Q4MOE_NVFP4 ? launch_fused<FMT_NVFP4>(f, s) : launch_fused<FMT_INT4>(f, s);
@@ -821,7 +832,11 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
         b.y = y_bf16;
         b.ra = ra;
         b.zsh = zsh;
-        return launch_small(b, s);
+        b.xq_codes = a4 ? at<uint8_t>(ws, l.xq_c) : nullptr;
+        b.xq_scales = a4 ? at<uint8_t>(ws, l.xq_s) : nullptr;
+        b.hq_codes = a4 ? at<uint8_t>(ws, l.hq_c) : nullptr;
+        b.hq_scales = a4 ? at<uint8_t>(ws, l.hq_s) : nullptr;
+        return launch_small(b, a4, s);
     }
     if ((st = launch_router(ra, s)) != Q4MOE_OK) return st;
 
@@ -882,7 +897,7 @@ q4moe_status q4moe_w4a16_grouped(const q4moe_router* r, const q4moe_experts* ex,
 // ---------------------------------------------------------------------------
 namespace {
 
-constexpr size_t kNoAllocScratchBytes = 3u << 20;  // the prefix (~2.4 MB) plus room for 1-4 tokens
+constexpr size_t kNoAllocScratchBytes = 7u << 19;  // 3.5 MiB: the prefix (~2.5 MB) plus room for 1-4 tokens
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 std::mutex g_scratch_mu;
@@ -915,7 +930,8 @@ q4moe_status q4moe_w4a16_decode_noalloc(const q4moe_router* r, const q4moe_exper
     if (st != Q4MOE_OK) return st;
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
-    const size_t need = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
+    const size_t need =
+        decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, false, w4a16_grouped(ex->fmt, n_tok)).total;
     if (need > kNoAllocScratchBytes)
         return fail(Q4MOE_EWORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", need,
                     kNoAllocScratchBytes);
@@ -1035,9 +1051,10 @@ q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_
 
 size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    const size_t one = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, 1, 0, true).total;
+    const size_t small =
+        decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, std::min<int32_t>(n_tok, kSmallT8), 0, true).total;
     const size_t grouped = w4a4_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
-    return std::max(one, grouped);
+    return std::max(small, grouped);
 }
 
 q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16, int32_t n_tok,
@@ -1046,17 +1063,10 @@ q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, cons
     if (st != Q4MOE_OK) return st;
     if (!x_bf16 || !y_bf16 || !ids || !w) return fail(Q4MOE_EINVAL, "x / y / ids / w is NULL");
     if ((st = check_ws(ws, ws_bytes, q4moe_w4a4_moe_ws_bytes(r, ex, n_tok))) != Q4MOE_OK) return st;
-    if (n_tok <= Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS) {
-        // one single-token launch per token, in order on the stream (each
-        // call advances the workspace's epoch, so the calls can share it)
-        const size_t H = (size_t)ex->hidden, K = (size_t)r->top_k;
-        for (int32_t t = 0; t < n_tok; ++t) {
-            st = decode_impl(r, ex, nullptr, x_bf16 + t * H, 1, y_bf16 + t * H, ids + t * K, w + t * K, ws, ws_bytes,
-                             stream, true);
-            if (st == Q4MOE_EUNSUPPORTED && t == 0) break;  // the shape does not fit one launch: grouped path
-            if (st != Q4MOE_OK) return st;
-        }
-        if (st == Q4MOE_OK) return st;
+    if (n_tok <= Q4MOE_W4A4_SMALL_MAX_TOKENS) {
+        // one token: the single launch; 2..8: the small-batch kernels
+        st = decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream, true);
+        if (st != Q4MOE_EUNSUPPORTED) return st;  // (EUNSUPPORTED: the shape does not fit them)
     }
     return q4moe_w4a4_grouped(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
 }

@@ -714,14 +714,18 @@ __global__ __launch_bounds__(256) void k_argmax_reduce(const unsigned long long*
 }
 
 // ---------------------------------------------------------------------------
-// Routed MoE for 2..4 tokens on MFMA (the four-token verify step of "Let's
-// optimize Nemotron 3.5 Lightning - a worklog", Step 5), NVFP4 weights.  Each
-// distinct selected expert is streamed once: the block set of the first
-// (token, slot) pair that selected it computes the expert for every token
-// (MFMA columns are free up to 16) and writes the results of every pair that
-// selected it.
+// Routed MoE for 2..8 tokens on MFMA (the four-token verify step of "Let's
+// optimize Nemotron 3.5 Lightning - a worklog", Step 5, and a few concurrent
+// sequences), NVFP4 weights.  Each distinct selected expert is streamed
+// once: the block set of the first (token, slot) pair that selected it
+// computes the expert for every token (MFMA columns are free up to 16) and
+// writes the results of every pair that selected it.  TM (4 or 8) is the
+// instance's token capacity.  A4: the W4A4 form (Step 3: activations
+// quantized to NVFP4 on the fly): x and h are quantized per 16-block and
+// their decoded values (e2m1 * e4m3, exact in fp16) are the MFMA columns.
 // ---------------------------------------------------------------------------
-constexpr int kSmallT = 4;  // tokens at most
+constexpr int kSmallT = 4;   // tokens at most for the small-batch W4A16 path
+constexpr int kSmallT8 = 8;  // capacity of the wider instances
 
 struct SmallMoeArgs {
     int E, H, I, K, T;
@@ -742,6 +746,12 @@ struct SmallMoeArgs {
     // token in every workgroup; workgroup (0, 0) stores it for the others)
     RouterArgs ra;
     const float* zsh;    // [T][H] the shared expert's output (nullable)
+    // A4 code taps: x codes [T][H/2] and scales [T][H/16], h codes
+    // [T*K][I/2] and scales [T*K][I/16] (unused otherwise)
+    uint8_t* xq_codes;
+    uint8_t* xq_scales;
+    uint8_t* hq_codes;
+    uint8_t* hq_scales;
 };
 
 // The expert of pair p, and whether p is the first pair that selected it.
@@ -753,17 +763,19 @@ __device__ __forceinline__ int small_expert(const SmallMoeArgs& a, const int32_t
     return e;
 }
 
-// Largest magnitude of each of the 4 rows' values (per-thread partials -> block).
-__device__ __forceinline__ void block_amax4(float m[4], float (*s_amax)[4], int* s_exp) {
+// Largest magnitude of each of TM rows' values (per-thread partials ->
+// block), turned into the row's fp16 staging exponent.
+template <int TM>
+__device__ __forceinline__ void block_amax(float (&m)[TM], float (*s_amax)[TM], int* s_exp) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < TM; ++t) {
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) m[t] = fmaxf(m[t], __shfl_xor(m[t], o, 64));
         if (lane == 0) s_amax[wave][t] = m[t];
     }
     __syncthreads();
-    if (threadIdx.x < 4) {
+    if (threadIdx.x < TM) {
         const float mx = fmaxf(fmaxf(s_amax[0][threadIdx.x], s_amax[1][threadIdx.x]),
                                fmaxf(s_amax[2][threadIdx.x], s_amax[3][threadIdx.x]));
         s_exp[threadIdx.x] = fp16_stage_exp(mx);
@@ -771,17 +783,41 @@ __device__ __forceinline__ void block_amax4(float m[4], float (*s_amax)[4], int*
     __syncthreads();
 }
 
-// Rows 0..3 of an LDS operand (pitch P fp16) from up to four bf16 rows of
-// `cols` values (row t at src + t * cols): row t is scaled by 2^s_exp[t],
-// the power of two that puts its largest magnitude in [2^14, 2^15), and
-// rounded to fp16 (exact for every bf16 value at least 2^-28 of that
-// maximum); rows past `rows` and columns past `cols` are zero.  One pass of
-// 16-byte loads, all in flight at once.
-template <int P>
+// NVFP4 quantization of a block of 16 values held by four adjacent lanes
+// (4 values each, the block's first lane at a multiple of 4): the block
+// maximum over the quad (quad_perm [1,0,3,2], then [2,3,0,1]); code packs
+// the lane's 4 codes.  The same rule as nvfp4_quant16.
+struct Nvfp4Quarter {
+    uint32_t sb, code;
+};
+__device__ __forceinline__ Nvfp4Quarter nvfp4_quant4_quad(const float (&v)[4]) {
+    float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, true)));
+    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x4E, 0xF, 0xF, true)));
+    Nvfp4Quarter b;
+    b.sb = e4m3fn_rne_sat(__fdiv_rn(amax, 6.0f));
+    const E2m1Thresholds th = e2m1_thresholds(e4m3fn_to_f32(b.sb));
+    b.code = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) b.code |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * k);
+    return b;
+}
+
+// Rows 0..TM-1 of an LDS operand (pitch P fp16) from up to TM bf16 rows of
+// `cols` values (row t at src + t * cols); rows past `rows` and columns past
+// `cols` are zero.  One pass of 16-byte loads, all in flight at once.
+//  - W4A16: row t is scaled by 2^s_exp[t], the power of two that puts its
+//    largest magnitude in [2^14, 2^15), and rounded to fp16 (exact for every
+//    bf16 value at least 2^-28 of that maximum);
+//  - A4: each 16-block is quantized to NVFP4 (two adjacent lanes per block)
+//    and its decoded values stored (exact in fp16); s_exp = 0; codes and
+//    scales go to xq_codes / xq_scales when they are not null.
+template <int P, int TM, bool A4>
 __device__ __forceinline__ void stage_bf16_rows(const uint16_t* src, int rows, int cols, _Float16* xs,
-                                                float (*s_amax)[4], int* s_exp) {
+                                                float (*s_amax)[TM], int* s_exp, uint8_t* xq_codes,
+                                                uint8_t* xq_scales) {
     typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-    constexpr int kXP = (4 * (P / 8) + 255) / 256;
+    constexpr int kXP = (TM * (P / 8) + 255) / 256;
     const int per = cols / 8, total = rows * per;
     uint4 v[kXP];
 #pragma unroll
@@ -789,55 +825,92 @@ __device__ __forceinline__ void stage_bf16_rows(const uint16_t* src, int rows, i
         const int p = threadIdx.x + 256 * i;
         v[i] = p < total ? *reinterpret_cast<const uint4*>(src + (size_t)p * 8) : make_uint4(0u, 0u, 0u, 0u);
     }
-    float m[4] = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (A4) {
+        if (threadIdx.x < TM) s_exp[threadIdx.x] = 0;
 #pragma unroll
-    for (int i = 0; i < kXP; ++i) {
-        const int t = (threadIdx.x + 256 * i) / per;
-        const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-        float mx = 0.f;
-#pragma unroll
-        for (int d = 0; d < 4; ++d)
-            mx = fmaxf(mx, fmaxf(fabsf(bf16_bits_to_f32(w[d] & 0xffffu)), fabsf(bf16_bits_to_f32(w[d] >> 16))));
-#pragma unroll
-        for (int tt = 0; tt < 4; ++tt)
-            if (t == tt) m[tt] = fmaxf(m[tt], mx);
-    }
-    block_amax4(m, s_amax, s_exp);
-#pragma unroll
-    for (int i = 0; i < kXP; ++i) {
-        const int p = threadIdx.x + 256 * i;
-        if (p < total) {
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
             const int t = p / per, k0 = (p - t * per) * 8;
-            const float sc = ldexpf(1.0f, s_exp[t]);
             const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-            h8 hv;
+            float f[8];
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
-                hv[2 * d] = (_Float16)(bf16_bits_to_f32(w[d] & 0xffffu) * sc);
-                hv[2 * d + 1] = (_Float16)(bf16_bits_to_f32(w[d] >> 16) * sc);
+                f[2 * d] = bf16_bits_to_f32(w[d] & 0xffffu);
+                f[2 * d + 1] = bf16_bits_to_f32(w[d] >> 16);
             }
-            *reinterpret_cast<h8*>(xs + t * P + k0) = hv;
+            const Nvfp4Half b = nvfp4_quant8_pair(f);  // (both lanes of a block run it)
+            float dq[8];
+            nvfp4_dequant8(b, dq);
+            if (p < total) {
+                h8 hv;
+#pragma unroll
+                for (int d = 0; d < 8; ++d) hv[d] = (_Float16)dq[d];
+                *reinterpret_cast<h8*>(xs + t * P + k0) = hv;
+                if (xq_codes) {
+                    *reinterpret_cast<uint32_t*>(xq_codes + (size_t)t * (cols / 2) + k0 / 2) = b.code;
+                    if ((p & 1) == 0) xq_scales[(size_t)t * (cols / 16) + k0 / 16] = (uint8_t)b.sb;
+                }
+            }
+        }
+    } else {
+        float m[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) m[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int t = (threadIdx.x + 256 * i) / per;
+            const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            float mx = 0.f;
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+                mx = fmaxf(mx, fmaxf(fabsf(bf16_bits_to_f32(w[d] & 0xffffu)), fabsf(bf16_bits_to_f32(w[d] >> 16))));
+#pragma unroll
+            for (int tt = 0; tt < TM; ++tt)
+                if (t == tt) m[tt] = fmaxf(m[tt], mx);
+        }
+        block_amax<TM>(m, s_amax, s_exp);
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            if (p < total) {
+                const int t = p / per, k0 = (p - t * per) * 8;
+                const float sc = ldexpf(1.0f, s_exp[t]);
+                const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+                h8 hv;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    hv[2 * d] = (_Float16)(bf16_bits_to_f32(w[d] & 0xffffu) * sc);
+                    hv[2 * d + 1] = (_Float16)(bf16_bits_to_f32(w[d] >> 16) * sc);
+                }
+                *reinterpret_cast<h8*>(xs + t * P + k0) = hv;
+            }
         }
     }
     // zeros: rows past `rows`, and columns past `cols` (8-aligned pieces)
     const h8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int i = threadIdx.x; i < 4 * (P / 8); i += 256) {
+    for (int i = threadIdx.x; i < TM * (P / 8); i += 256) {
         const int t = i / (P / 8), k0 = (i - t * (P / 8)) * 8;
         if (t >= rows || k0 >= cols) *reinterpret_cast<h8*>(xs + t * P + k0) = z;
     }
     __syncthreads();
 }
 
-// Columns c < nc of an LDS operand as fp16 hi (row c) and lo (row 4 + c)
-// parts of the fp32 rows src + col_off[c] (`cols` values): row c is scaled
-// by 2^s_exp[c] (largest magnitude into [2^14, 2^15)); hi = fp16(v), lo =
-// fp16(v - hi), so hi + lo carries v to about 2^-22.  Other rows and columns
-// past `cols` are zero.
-template <int P>
-__device__ __forceinline__ void stage_f32_hilo(const float* src, const size_t col_off[4], int nc, int cols,
-                                               _Float16* hs, float (*s_amax)[4], int* s_exp) {
+// Columns c < nc of an LDS operand as fp16 hi (row c) and lo (row TM + c)
+// parts of the fp32 rows src + col_off[c] (`cols` values); other rows and
+// columns past `cols` are zero.
+//  - W4A16: row c is scaled by 2^s_exp[c] (largest magnitude into [2^14,
+//    2^15)); hi = fp16(v), lo = fp16(v - hi), so hi + lo carries v to about
+//    2^-22;
+//  - A4: each 16-block is quantized to NVFP4 (four adjacent lanes per block)
+//    and hi holds its decoded values (exact in fp16), lo zero; s_exp = 0;
+//    codes and scales of column c go to row pair[c] of hq_codes / hq_scales
+//    when they are not null.
+template <int P, int TM, bool A4>
+__device__ __forceinline__ void stage_f32_hilo(const float* src, const size_t (&col_off)[TM], int nc, int cols,
+                                               _Float16* hs, float (*s_amax)[TM], int* s_exp,
+                                               const int (&pair)[TM], uint8_t* hq_codes, uint8_t* hq_scales) {
     typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-    constexpr int kXP = (4 * (P / 4) + 255) / 256;
+    constexpr int kXP = (TM * (P / 4) + 255) / 256;
     const int per = cols / 4, total = nc * per;
     float4 v[kXP];
 #pragma unroll
@@ -846,77 +919,109 @@ __device__ __forceinline__ void stage_f32_hilo(const float* src, const size_t co
         const int c = p / per;
         size_t off = col_off[0];
 #pragma unroll
-        for (int cc = 1; cc < 4; ++cc)
+        for (int cc = 1; cc < TM; ++cc)
             if (c == cc) off = col_off[cc];
         v[i] = p < total ? *reinterpret_cast<const float4*>(src + off + (size_t)(p - c * per) * 4)
                          : make_float4(0.f, 0.f, 0.f, 0.f);
     }
-    float m[4] = {0.f, 0.f, 0.f, 0.f};
+    const h4 z = {0, 0, 0, 0};
+    if constexpr (A4) {
+        if (threadIdx.x < TM) s_exp[threadIdx.x] = 0;
 #pragma unroll
-    for (int i = 0; i < kXP; ++i) {
-        const int c = (threadIdx.x + 256 * i) / per;
-        const float mx = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-            if (c == cc) m[cc] = fmaxf(m[cc], mx);
-    }
-    block_amax4(m, s_amax, s_exp);
-#pragma unroll
-    for (int i = 0; i < kXP; ++i) {
-        const int p = threadIdx.x + 256 * i;
-        if (p < total) {
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
             const int c = p / per, k0 = (p - c * per) * 4;
-            const float sc = ldexpf(1.0f, s_exp[c]);
-            const float f[4] = {v[i].x * sc, v[i].y * sc, v[i].z * sc, v[i].w * sc};
-            h4 hi, lo;
+            const float f[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+            const Nvfp4Quarter b = nvfp4_quant4_quad(f);  // (all four lanes of a block run it)
+            if (p < total) {
+                const float s = e4m3fn_to_f32(b.sb);
+                const f32x2 d0 = fp4x2_f32<0>(b.code), d1 = fp4x2_f32<1>(b.code);
+                const h4 hv = {(_Float16)(d0[0] * s), (_Float16)(d0[1] * s), (_Float16)(d1[0] * s),
+                               (_Float16)(d1[1] * s)};
+                *reinterpret_cast<h4*>(hs + c * P + k0) = hv;
+                *reinterpret_cast<h4*>(hs + (TM + c) * P + k0) = z;
+                if (hq_codes) {
+                    int pr = pair[0];
 #pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                hi[d] = (_Float16)f[d];
-                lo[d] = (_Float16)(f[d] - (float)hi[d]);
+                    for (int cc = 1; cc < TM; ++cc)
+                        if (c == cc) pr = pair[cc];
+                    *reinterpret_cast<uint16_t*>(hq_codes + (size_t)pr * (cols / 2) + k0 / 2) = (uint16_t)b.code;
+                    if ((p & 3) == 0) hq_scales[(size_t)pr * (cols / 16) + k0 / 16] = (uint8_t)b.sb;
+                }
             }
-            *reinterpret_cast<h4*>(hs + c * P + k0) = hi;
-            *reinterpret_cast<h4*>(hs + (4 + c) * P + k0) = lo;
+        }
+        __syncthreads();  // (s_exp)
+    } else {
+        float m[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t) m[t] = 0.f;
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int c = (threadIdx.x + 256 * i) / per;
+            const float mx = fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w)));
+#pragma unroll
+            for (int cc = 0; cc < TM; ++cc)
+                if (c == cc) m[cc] = fmaxf(m[cc], mx);
+        }
+        block_amax<TM>(m, s_amax, s_exp);
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int p = threadIdx.x + 256 * i;
+            if (p < total) {
+                const int c = p / per, k0 = (p - c * per) * 4;
+                const float sc = ldexpf(1.0f, s_exp[c]);
+                const float f[4] = {v[i].x * sc, v[i].y * sc, v[i].z * sc, v[i].w * sc};
+                h4 hi, lo;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    hi[d] = (_Float16)f[d];
+                    lo[d] = (_Float16)(f[d] - (float)hi[d]);
+                }
+                *reinterpret_cast<h4*>(hs + c * P + k0) = hi;
+                *reinterpret_cast<h4*>(hs + (TM + c) * P + k0) = lo;
+            }
         }
     }
-    const h4 z = {0, 0, 0, 0};
-    for (int i = threadIdx.x; i < 8 * (P / 4); i += 256) {
+    for (int i = threadIdx.x; i < 2 * TM * (P / 4); i += 256) {
         const int rr = i / (P / 4), k0 = (i - rr * (P / 4)) * 4;
-        if ((rr & 3) >= nc || k0 >= cols) *reinterpret_cast<h4*>(hs + rr * P + k0) = z;
+        if ((rr % TM) >= nc || k0 >= cols) *reinterpret_cast<h4*>(hs + rr * P + k0) = z;
     }
     __syncthreads();
 }
 
 // up: u = W_up[e] x_t for all tokens t, h[pair] = relu(g u)^2 for every pair
 // (t, slot) that selected e.  Grid (ceil(I/64), T*K): 64 rows per block, one
-// 16-row group per wave.  x goes to LDS as fp16 after a per-token power-of-two
-// scaling (as in the lm_head GEMV).
-template <int NJ>
+// 16-row group per wave.  x goes to LDS as fp16 (scaled per token by a power
+// of two, as in the lm_head GEMV; A4: NVFP4-quantized and decoded).
+template <int NJ, int TM, bool A4>
 __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
     constexpr int P = 128 * NJ + 8;
-    __shared__ __attribute__((aligned(16))) _Float16 xs[kSmallT][P];
-    __shared__ float s_amax[4][4];
-    __shared__ int s_exp[4];
+    __shared__ __attribute__((aligned(16))) _Float16 xs[TM][P];
+    __shared__ float s_amax[4][TM];
+    __shared__ int s_exp[TM];
     __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][NJ * 8];  // each wave's group scales (16 rows)
-    __shared__ int32_t s_ids[kSmallT * 8];
-    __shared__ float s_w[kSmallT * 8];
-    // routing: wave t takes token t (every workgroup, so no top-k launch)
-    if ((int)(threadIdx.x >> 6) < a.T) {
-        const int t = threadIdx.x >> 6;
+    __shared__ int32_t s_ids[TM * 8];
+    __shared__ float s_w[TM * 8];
+    // routing: wave w takes tokens w, w + 4 (every workgroup, so no top-k launch)
+    for (int t = (int)(threadIdx.x >> 6); t < a.T; t += 4)
         topk_token(a.ra, t, blockIdx.x == 0 && blockIdx.y == 0, &s_ids[t * a.K], &s_w[t * a.K]);
-    }
     __syncthreads();
     bool leader;
     const int e = small_expert(a, s_ids, blockIdx.y, leader);
     if (!leader) return;  // uniform
+    const bool tap = A4 && blockIdx.x == 0 && blockIdx.y == 0;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m16 = lane & 15, kq = lane >> 4;
     const int row = blockIdx.x * 64 + wave * 16 + m16;
     const uint32_t wrow = (uint32_t)e * a.I + min(row, a.I - 1);
     const int row0 = blockIdx.x * 64 + wave * 16;
     // x goes to LDS while the first weight batch is in flight
-    const f32x4g acc = mfma_gemv_group<NJ, kSmallT, P>(
+    const f32x4g acc = mfma_gemv_group<NJ, TM, P>(
         a.upc, a.ups, wrow, a.H, &xs[0][0], m16, kq,
-        [&] { stage_bf16_rows<P>(a.x, a.T, a.H, &xs[0][0], s_amax, s_exp); },
+        [&] {
+            stage_bf16_rows<P, TM, A4>(a.x, a.T, a.H, &xs[0][0], s_amax, s_exp, tap ? a.xq_codes : nullptr,
+                                       tap ? a.xq_scales : nullptr);
+        },
         reinterpret_cast<uint8_t*>(&s_sblk[wave][0]), (uint32_t)e * a.I + (uint32_t)row0, row0 + 16 <= a.I);
     // lane (n = m16, kq) holds rows 4 kq + r of token n
     const int n = m16;
@@ -942,14 +1047,14 @@ __global__ __launch_bounds__(256, 2) void k_small_up(SmallMoeArgs a) {
 // down: z = W_down[e] h_pair for every pair that selected e, zw[pair] =
 // w * g * z.  Grid (ceil(H/64), T*K).  Each pair's fp32 h is scaled by a power
 // of two and split into fp16 hi + lo (h' = hi + lo to about 2^-22), columns c
-// and 4 + c of the same MFMA, so h keeps nearly fp32 precision at no extra
-// MFMA cost.
-template <int NJ>
+// and TM + c of the same MFMA, so h keeps nearly fp32 precision at no extra
+// MFMA cost (A4: the decoded NVFP4 h in column c, column TM + c zero).
+template <int NJ, int TM, bool A4>
 __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
-    constexpr int P = 128 * NJ + (NJ < 32 ? 8 : 0);  // (the widest instance drops the pad to fit 64 KiB)
-    __shared__ __attribute__((aligned(16))) _Float16 hs[2 * kSmallT][P];
-    __shared__ float s_amax[4][4];
-    __shared__ int s_exp[4];
+    constexpr int P = 128 * NJ + 8;
+    __shared__ __attribute__((aligned(16))) _Float16 hs[2 * TM][P];
+    __shared__ float s_amax[4][TM];
+    __shared__ int s_exp[TM];
     // each wave's group scales (16 rows), where the instance has room for them
     constexpr bool kScaleLds = NJ <= 24;
     __shared__ __attribute__((aligned(16))) uint4 s_sblk[4][kScaleLds ? NJ * 8 : 1];
@@ -962,37 +1067,43 @@ __global__ __launch_bounds__(256, 2) void k_small_down(SmallMoeArgs a) {
     const uint32_t wrow = (uint32_t)e * a.H + min(row, a.H - 1);
     // columns: the pairs that selected e, in pair order (one per token at most)
     // (static indices only, so the list stays in registers)
-    int cols[kSmallT] = {0, 0, 0, 0};
+    int cols[TM];
+#pragma unroll
+    for (int c = 0; c < TM; ++c) cols[c] = 0;
     int nc = 0;
     for (int pp = 0; pp < a.T * a.K; ++pp) {
         if (min(max(a.ids[pp], 0), a.E - 1) == e) {
 #pragma unroll
-            for (int c = 0; c < kSmallT; ++c)
+            for (int c = 0; c < TM; ++c)
                 if (c == nc) cols[c] = pp;
-            nc = min(nc + 1, kSmallT);
+            nc = min(nc + 1, TM);
         }
     }
-    size_t col_off[kSmallT];
+    size_t col_off[TM];
 #pragma unroll
-    for (int c = 0; c < kSmallT; ++c) col_off[c] = (size_t)cols[c] * a.I;
+    for (int c = 0; c < TM; ++c) col_off[c] = (size_t)cols[c] * a.I;
+    const bool tap = A4 && blockIdx.x == 0;
     // h goes to LDS while the first weight batch is in flight
     // (the widest instances have no LDS left for the scale slice: their
     // scales load per piece)
     const int row0 = blockIdx.x * 64 + wave * 16;
-    const f32x4g acc = mfma_gemv_group<NJ, 2 * kSmallT, P>(
+    const f32x4g acc = mfma_gemv_group<NJ, 2 * TM, P>(
         a.dnc, a.dns, wrow, a.I, &hs[0][0], m16, kq,
-        [&] { stage_f32_hilo<P>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp); },
+        [&] {
+            stage_f32_hilo<P, TM, A4>(a.h, col_off, nc, a.I, &hs[0][0], s_amax, s_exp, cols,
+                                      tap ? a.hq_codes : nullptr, tap ? a.hq_scales : nullptr);
+        },
         reinterpret_cast<uint8_t*>(&s_sblk[wave][0]), (uint32_t)e * a.H + (uint32_t)row0,
         kScaleLds && row0 + 16 <= a.H);
-    // lane (n, kq) holds column n: hi for n < 4, lo for n >= 4; add lane n + 4's lo
+    // lane (n, kq) holds column n: hi for n < TM, lo for n >= TM; add lane n + TM's lo
     const int n = m16;
     float z[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) z[r] = acc[r] + __shfl(acc[r], (n < kSmallT) ? lane + kSmallT : lane, 64);
+    for (int r = 0; r < 4; ++r) z[r] = acc[r] + __shfl(acc[r], (n < TM) ? lane + TM : lane, 64);
     if (n < nc) {
         int pp = cols[0];
 #pragma unroll
-        for (int c = 1; c < kSmallT; ++c)
+        for (int c = 1; c < TM; ++c)
             if (c == n) pp = cols[c];
         const float wg = a.w[pp] * a.dng[e];
         const int unexp = -s_exp[n];

@@ -149,8 +149,9 @@ q4moe_status q4moe_dequant_ref(const q4moe_qmat* m, float* out, void* stream);
  * 2: filling the GPU" for many concurrent tokens): router top-k, up GEMV,
  * relu^2, down GEMV, weighted combine.  x bf16 [n_tok][hidden], y bf16
  * [n_tok][hidden]; ids/w (nullable) receive the routing.
- * By token count: 1 -> one persistent launch; 2-4 -> small-batch kernels
- * that stream each selected expert once for all tokens; more -> the grouped
+ * By token count: 1 -> one persistent launch; 2-4 (NVFP4; int4: 2) ->
+ * small-batch kernels that stream each selected expert once for all
+ * tokens (int4: once per token and slot); more -> the grouped
  * path (per-expert dispatch lists, grouped GEMMs on fp16 MFMA with x staged
  * exactly and h carried as fp16 hi + lo, about 22 bits), which needs hidden
  * and inter multiples of 64 (else Q4MOE_EUNSUPPORTED).  Every path
@@ -174,11 +175,11 @@ q4moe_status q4moe_w4a16_grouped(const q4moe_router* r, const q4moe_experts* ex,
 
 /* q4moe_w4a16_decode for callers that cannot allocate (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): no
- * workspace argument; the library's own static scratch of 3 MiB per GPU
+ * workspace argument; the library's own static scratch of 3.5 MiB per GPU
  * (device memory held from load until the process ends) serves as the
  * workspace.  It allocates nothing.  Shapes whose workspace would exceed the
  * scratch return Q4MOE_EWORKSPACE (1-4 tokens of the 128 x 2688 x 1856
- * top-6 layer take about 3.0 MB).  Every call on a GPU shares that GPU's
+ * top-6 layer take at most 3.02 MiB).  Every call on a GPU shares that GPU's
  * scratch: calls that overlap in time on one GPU race and must not be
  * issued (calls in order on one stream are fine).  The expired-wait flag of
  * the one-launch decode is kept in the scratch and not reported. */
@@ -234,31 +235,35 @@ q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_e
                                             const q4moe_shared_fp8* sh, int32_t n_tok,
                                             q4moe_shared_taps* out);
 
-/* W4A4 routed-MoE decode of one token in a single launch ([W] Step 3: the
+/* W4A4 routed-MoE decode of 1 <= n_tok <= 8 tokens ([W] Step 3: the
  * routed experts take 4-bit weights and activations; the MTP drafter's
  * experts are NVFP4 W4A4 too, [C] and the pages' MTP passage): as
  * q4moe_w4a16_decode, with x and h quantized to NVFP4 on the fly (per 16, an
  * E4M3FN scale amax/6 and E2M1 codes, as in q4moe_w4a4_grouped) and the
- * GEMVs run on their exact dequantized values.  NVFP4 experts and n_tok = 1
- * only, else Q4MOE_EUNSUPPORTED.  ids/w nullable. */
+ * GEMVs run on their exact dequantized values.  One token: a single launch;
+ * 2-8 tokens: the small-batch kernels, each selected expert streamed once
+ * for all tokens.  NVFP4 experts and n_tok <= 8 only, else
+ * Q4MOE_EUNSUPPORTED.  ids/w nullable. */
 size_t q4moe_w4a4_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
 q4moe_status q4moe_w4a4_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
                                int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
                                size_t ws_bytes, void* stream);
 
 /* Byte offsets of the values q4moe_w4a4_decode leaves in its workspace:
- * y32 fp32 [hidden]; h32 fp32 [top_k][inter] (relu(u)^2 before
- * quantization, slot order); xq_codes [hidden/2], xq_scales [hidden/16];
- * hq_codes [top_k][inter/2], hq_scales [top_k][inter/16] (slot order;
- * codes low nibble first). */
+ * y32 fp32 [n_tok][hidden]; h32 fp32 [n_tok*top_k][inter] (relu(u)^2
+ * before quantization, rows (token, slot)); xq_codes [n_tok][hidden/2],
+ * xq_scales [n_tok][hidden/16]; hq_codes [n_tok*top_k][inter/2], hq_scales
+ * [n_tok*top_k][inter/16] (rows (token, slot); codes low nibble first). */
 typedef struct { size_t y32, h32, xq_codes, xq_scales, hq_codes, hq_scales; } q4moe_w4a4_token_taps;
 q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
                                     q4moe_w4a4_token_taps* out);
 
 /* The MoE block of the W4A4 checkpoint ([W] Step 3; [C] precision table:
- * routed experts NVFP4 W4A4, shared experts FP8 per-tensor W8A8) for one
- * token in one launch: q4moe_w4a4_decode plus the shared expert of
- * q4moe_w4a16_decode_shared, y = sum_i w_i z_i + z_shared rounded once. */
+ * routed experts NVFP4 W4A4, shared experts FP8 per-tensor W8A8) for
+ * 1 <= n_tok <= 4 tokens: q4moe_w4a4_decode plus the shared expert of
+ * q4moe_w4a16_decode_shared, y = sum_i w_i z_i + z_shared rounded once.
+ * One token: one launch; 2-4: the shared expert's three launches, then the
+ * small-batch kernels. */
 size_t q4moe_w4a4_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
                                          const q4moe_shared_fp8* sh, int32_t n_tok);
 q4moe_status q4moe_w4a4_decode_shared(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
@@ -266,7 +271,8 @@ q4moe_status q4moe_w4a4_decode_shared(const q4moe_router* r, const q4moe_experts
                                       float* w, void* ws, size_t ws_bytes, void* stream);
 
 /* Its taps: those of q4moe_w4a4_token_taps and, for the shared expert, sh_xq
- * uint8 [hidden], sh_h32 fp32 [inter], sh_hq uint8 [inter]. */
+ * uint8 [n_tok][hidden], sh_h32 fp32 [n_tok][inter], sh_hq uint8
+ * [n_tok][inter]. */
 typedef struct {
     size_t y32, h32, xq_codes, xq_scales, hq_codes, hq_scales, sh_xq, sh_h32, sh_hq;
 } q4moe_w4a4_shared_taps;
@@ -275,12 +281,11 @@ q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_ex
 
 /* W4A4 routed-MoE layer for any token count, choosing the kernels by the
  * count (mid-batch decode: the pages point at choosing the GEMM backend per
- * batch size): up to Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS tokens run one
- * single-token launch each (q4moe_w4a4_decode), more tokens the grouped MFMA
- * pipeline (q4moe_w4a4_grouped); measured on MI355X at the full shapes, the
- * single-token launches are faster per token up to 5 tokens.  The results
- * are those of the entry point used.  ids / w are required. */
-#define Q4MOE_W4A4_ONE_LAUNCH_MAX_TOKENS 5
+ * batch size): up to Q4MOE_W4A4_SMALL_MAX_TOKENS tokens q4moe_w4a4_decode
+ * (one launch for one token, the small-batch kernels for 2-8), more tokens
+ * the grouped MFMA pipeline (q4moe_w4a4_grouped).  The results are those of
+ * the entry point used.  ids / w are required. */
+#define Q4MOE_W4A4_SMALL_MAX_TOKENS 8
 size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
 q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16, int32_t n_tok,
                             uint16_t* y_bf16, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);

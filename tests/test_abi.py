@@ -62,8 +62,8 @@ def test_decode_validation(L):
     assert _decode(L, _router(wg=None), ex) == g.EINVAL
     assert _decode(L, r, ex, T=0) == g.EINVAL
     assert _decode(L, r, ex, T=65537) == g.EINVAL
-    # more than 4 tokens take the grouped path: hidden and inter multiples of 64
-    assert _decode(L, r, _experts(I=1856 + 32), T=5) == g.EUNSUPPORTED
+    # NVFP4 above 8 tokens takes the grouped path: hidden and inter multiples of 64
+    assert _decode(L, r, _experts(I=1856 + 32), T=9) == g.EUNSUPPORTED
     assert b"multiples of 64" in L.q4moe_last_error()
     # the grouped entry point: the same rule at any token count
     assert L.q4moe_w4a16_grouped(ctypes.byref(r), ctypes.byref(_experts(I=1856 + 32)), A16, 1, A16, None, None,
@@ -170,7 +170,7 @@ def test_w4a4_decode_validation(L):
     def call(ex_, T=1, wsb=1 << 30):
         return L.q4moe_w4a4_decode(ctypes.byref(r), ctypes.byref(ex_), A16, T, A16, None, None, A16, wsb, None)
 
-    assert call(ex, T=2) == g.EUNSUPPORTED
+    assert call(ex, T=9) == g.EUNSUPPORTED
     assert call(_experts(fmt=2)) == g.EUNSUPPORTED
     assert call(ex, T=0) == g.EINVAL
     need = L.q4moe_w4a4_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
@@ -188,7 +188,7 @@ def test_w4a4_decode_shared_validation(L):
         return L.q4moe_w4a4_decode_shared(ctypes.byref(r), ctypes.byref(ex_), shp, A16, T, A16, None, None, A16, wsb,
                                           None)
     assert call(ex, None) == g.EINVAL
-    assert call(ex, sh, T=2) == g.EUNSUPPORTED
+    assert call(ex, sh, T=5) == g.EUNSUPPORTED
     assert call(_experts(fmt=2), sh) == g.EUNSUPPORTED
     assert call(ex, _shared(S=100)) == g.EINVAL
     need = L.q4moe_w4a4_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)

@@ -1,8 +1,11 @@
-"""GPU parity of the W4A16 decode above four tokens (the grouped path: per-
-expert dispatch, grouped MFMA GEMMs with fp16 activations), NVFP4 and
-int4-g64, against the oracle on every token: ids bit-exact, gates within
-1e-5, y within the output gate, y equal to the nearest-even bf16 of its fp32
-value, and the h tap (pair order) within 2e-3 of the oracle's relu(u)^2."""
+"""GPU parity of the W4A16 decode above four tokens, NVFP4 and int4-g64,
+against the oracle on every token: ids bit-exact, gates within 1e-5, y
+within the output gate, y equal to the nearest-even bf16 of its fp32 value,
+and the h tap (pair order) within 2e-3 of the oracle's relu(u)^2.  The
+decode entry takes the 8-token small-batch kernels for NVFP4 at 5-8 tokens
+and the grouped path (per-expert dispatch, grouped MFMA GEMMs with fp16
+activations) above that and for int4 from 3 tokens; the grouped entry point
+is also run directly at 1-8 tokens."""
 import numpy as np
 import pytest
 
@@ -125,7 +128,7 @@ def test_midbatch_workspace_reuse_and_determinism(full_layer):
     assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["y32"].view(np.uint32), b["y32"].view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [1, 2, 4])
+@pytest.mark.parametrize("T", [1, 2, 4, 5, 8])
 def test_grouped_entry_few_tokens(full_layer, T):
     # the grouped path called directly at 1-4 tokens (where the decode entry
     # takes the single-launch or small-batch kernels)

@@ -24,35 +24,37 @@ K = 6
 
 def run_w4a4_decode(router, ex, x_np, ws=None):
     H, I = ex.hidden, ex.inter
-    y = torch.empty((1, H), dtype=torch.int16, device=DEV)
-    ids = torch.empty((1, K), dtype=torch.int32, device=DEV)
-    w = torch.empty((1, K), dtype=torch.float32, device=DEV)
+    T = x_np.shape[0]
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
     ws = g.q4moe_w4a4_decode(router, ex, dev(x_np), y, ids, w, ws=ws)
     torch.cuda.synchronize()
-    t = g.q4moe_w4a4_decode_taps(router, ex, 1)
+    t = g.q4moe_w4a4_decode_taps(router, ex, T)
     b = host(ws)
 
     def view(off, n, dt):
         return b[off: off + n * np.dtype(dt).itemsize].view(dt).copy()
 
     return dict(y=host(y, np.uint16), ids=host(ids), w=host(w), ws=ws,
-                y32=view(t.y32, H, np.float32).reshape(1, H),
-                h32=view(t.h32, K * I, np.float32).reshape(K, I),
-                xq_codes=view(t.xq_codes, H // 2, np.uint8).reshape(1, H // 2),
-                xq_scales=view(t.xq_scales, H // 16, np.uint8).reshape(1, H // 16),
-                hq_codes=view(t.hq_codes, K * I // 2, np.uint8).reshape(K, I // 2),
-                hq_scales=view(t.hq_scales, K * I // 16, np.uint8).reshape(K, I // 16))
+                y32=view(t.y32, T * H, np.float32).reshape(T, H),
+                h32=view(t.h32, T * K * I, np.float32).reshape(T * K, I),
+                xq_codes=view(t.xq_codes, T * H // 2, np.uint8).reshape(T, H // 2),
+                xq_scales=view(t.xq_scales, T * H // 16, np.uint8).reshape(T, H // 16),
+                hq_codes=view(t.hq_codes, T * K * I // 2, np.uint8).reshape(T * K, I // 2),
+                hq_scales=view(t.hq_scales, T * K * I // 16, np.uint8).reshape(T * K, I // 16))
 
 
 def check_w4a4_decode(L, out):
     r = L["route"]
+    T = L["x"].shape[0]
     assert np.array_equal(out["ids"], r["ids"])
     np.testing.assert_allclose(out["w"], r["w"], rtol=1e-5)
     ob = oracle.Bank.from_dict(oracle.NVFP4, L["bank"])
     xc, xs = oracle.quant_nvfp4(bf16_bits_to_f64(L["x"]).astype(np.float32))
     assert np.array_equal(out["xq_codes"], xc) and np.array_equal(out["xq_scales"], xs), "x codes differ"
-    u = oracle.w4a4_up(ob, r["ids"], out["xq_codes"], out["xq_scales"])[0]  # [K][I]
-    ok, worst_h = gate_f32(out["h32"], np.maximum(u, 0.0) ** 2)
+    u = oracle.w4a4_up(ob, r["ids"], out["xq_codes"], out["xq_scales"])  # [T][K][I]
+    ok, worst_h = gate_f32(out["h32"], (np.maximum(u, 0.0) ** 2).reshape(T * K, -1))
     assert ok, f"h gate exceeded ({worst_h:.3f})"
     hc, hs = oracle.quant_nvfp4(out["h32"])
     assert np.array_equal(out["hq_codes"], hc) and np.array_equal(out["hq_scales"], hs), "h codes differ"
@@ -65,7 +67,7 @@ def check_w4a4_decode(L, out):
     # the end-to-end fp64 chain (its own h codes) is reported, not gated
     e2e = oracle.moe_w4a4(ob, L["x"], r["ids"], r["w"])
     ok_e, worst_e = gate_out(out["y"], e2e["y"])
-    flips = int((e2e["hq_codes"][0] != out["hq_codes"]).sum())
+    flips = int((e2e["hq_codes"].reshape(T * K, -1) != out["hq_codes"]).sum())
     return worst, worst_h, ok_e, worst_e, flips
 
 
@@ -113,32 +115,35 @@ def test_w4a4_decode_exact_activations_equal_w4a16():
 
 def run_w4a4_shared(router, ex, sh_dev, x_np):
     H, I, S = ex.hidden, ex.inter, sh_dev.inter
-    y = torch.empty((1, H), dtype=torch.int16, device=DEV)
-    ids = torch.empty((1, K), dtype=torch.int32, device=DEV)
-    w = torch.empty((1, K), dtype=torch.float32, device=DEV)
+    T = x_np.shape[0]
+    y = torch.empty((T, H), dtype=torch.int16, device=DEV)
+    ids = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
     ws = g.q4moe_w4a4_decode_shared(router, ex, sh_dev, dev(x_np), y, ids, w)
     torch.cuda.synchronize()
-    t = g.q4moe_w4a4_decode_shared_taps(router, ex, sh_dev, 1)
+    t = g.q4moe_w4a4_decode_shared_taps(router, ex, sh_dev, T)
     b = host(ws)
 
     def view(off, n, dt):
         return b[off: off + n * np.dtype(dt).itemsize].view(dt).copy()
 
     return dict(y=host(y, np.uint16), ids=host(ids), w=host(w),
-                y32=view(t.y32, H, np.float32).reshape(1, H),
-                h32=view(t.h32, K * I, np.float32).reshape(K, I),
-                xq_codes=view(t.xq_codes, H // 2, np.uint8).reshape(1, H // 2),
-                xq_scales=view(t.xq_scales, H // 16, np.uint8).reshape(1, H // 16),
-                hq_codes=view(t.hq_codes, K * I // 2, np.uint8).reshape(K, I // 2),
-                hq_scales=view(t.hq_scales, K * I // 16, np.uint8).reshape(K, I // 16),
-                sh_xq=view(t.sh_xq, H, np.uint8), sh_h32=view(t.sh_h32, S, np.float32),
-                sh_hq=view(t.sh_hq, S, np.uint8))
+                y32=view(t.y32, T * H, np.float32).reshape(T, H),
+                h32=view(t.h32, T * K * I, np.float32).reshape(T * K, I),
+                xq_codes=view(t.xq_codes, T * H // 2, np.uint8).reshape(T, H // 2),
+                xq_scales=view(t.xq_scales, T * H // 16, np.uint8).reshape(T, H // 16),
+                hq_codes=view(t.hq_codes, T * K * I // 2, np.uint8).reshape(T * K, I // 2),
+                hq_scales=view(t.hq_scales, T * K * I // 16, np.uint8).reshape(T * K, I // 16),
+                sh_xq=view(t.sh_xq, T * H, np.uint8).reshape(T, H),
+                sh_h32=view(t.sh_h32, T * S, np.float32).reshape(T, S),
+                sh_hq=view(t.sh_hq, T * S, np.uint8).reshape(T, S))
 
 
-@pytest.mark.parametrize("E,H,I,S", [(16, 256, 192, 128), (200, 2688, 256, 192), (128, 2688, 1856, 3712)])
-def test_w4a4_decode_with_shared_expert(E, H, I, S):
+@pytest.mark.parametrize("E,H,I,S,T", [(16, 256, 192, 128, 1), (200, 2688, 256, 192, 1), (128, 2688, 1856, 3712, 1),
+                                       (16, 256, 192, 128, 3), (128, 2688, 1856, 3712, 4)])
+def test_w4a4_decode_with_shared_expert(E, H, I, S, T):
     from test_gpu_shared import upload_shared
-    L = layer(SEED + S, synth.FAM_W4A4, 1, E, H, I, 1, K, "nvfp4")
+    L = layer(SEED + S, synth.FAM_W4A4, 1, E, H, I, T, K, "nvfp4")
     sh = synth.shared_fp8(SEED, synth.FAM_W4A4, S, H, S)
     out = run_w4a4_shared(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), upload_shared(sh),
                           L["x"])
@@ -150,32 +155,58 @@ def test_w4a4_decode_with_shared_expert(E, H, I, S):
     # routed stages
     xc, xs = oracle.quant_nvfp4(xf)
     assert np.array_equal(out["xq_codes"], xc) and np.array_equal(out["xq_scales"], xs)
-    u = oracle.w4a4_up(ob, r["ids"], out["xq_codes"], out["xq_scales"])[0]
+    u = oracle.w4a4_up(ob, r["ids"], out["xq_codes"], out["xq_scales"]).reshape(T * K, I)
     ok, worst_h = gate_f32(out["h32"], np.maximum(u, 0.0) ** 2)
     assert ok, f"h gate exceeded ({worst_h:.3f})"
     hc, hs = oracle.quant_nvfp4(out["h32"])
     assert np.array_equal(out["hq_codes"], hc) and np.array_equal(out["hq_scales"], hs)
-    # shared stages
-    assert np.array_equal(out["sh_xq"], oracle.fp8_quant(xf[0], sh["up_iscale"]))
-    us = oracle.fp8_gemv(sh["up_codes"], out["sh_xq"], sh["up_wscale"], sh["up_iscale"])
-    ok, worst_sh = gate_f32(out["sh_h32"][None], (np.maximum(us, 0.0) ** 2)[None])
-    assert ok, f"shared h gate exceeded ({worst_sh:.3f})"
-    assert np.array_equal(out["sh_hq"], oracle.fp8_quant(out["sh_h32"], sh["down_iscale"]))
-    # output: routed down + combine on the GPU's h codes, plus the shared down
-    yhat = oracle.w4a4_down_combine(ob, r["ids"], r["w"], out["hq_codes"], out["hq_scales"])[0]
-    yhat = yhat + oracle.fp8_gemv(sh["down_codes"], out["sh_hq"], sh["down_wscale"], sh["down_iscale"])
-    ok, worst = gate_out(out["y"], yhat[None])
+    # shared stages, token by token
+    yhat = oracle.w4a4_down_combine(ob, r["ids"], r["w"], out["hq_codes"], out["hq_scales"])
+    worst_sh = 0.0
+    for t in range(T):
+        assert np.array_equal(out["sh_xq"][t], oracle.fp8_quant(xf[t], sh["up_iscale"]))
+        us = oracle.fp8_gemv(sh["up_codes"], out["sh_xq"][t], sh["up_wscale"], sh["up_iscale"])
+        ok, wt = gate_f32(out["sh_h32"][t][None], (np.maximum(us, 0.0) ** 2)[None])
+        assert ok, f"shared h gate exceeded ({wt:.3f})"
+        worst_sh = max(worst_sh, wt)
+        assert np.array_equal(out["sh_hq"][t], oracle.fp8_quant(out["sh_h32"][t], sh["down_iscale"]))
+        # output: routed down + combine on the GPU's h codes, plus the shared down
+        yhat[t] = yhat[t] + oracle.fp8_gemv(sh["down_codes"], out["sh_hq"][t], sh["down_wscale"], sh["down_iscale"])
+    ok, worst = gate_out(out["y"], yhat)
     assert ok, f"bf16 output gate exceeded: worst {worst:.3f}"
-    ok32, worst32 = gate_f32(out["y32"], yhat[None])
+    ok32, worst32 = gate_f32(out["y32"], yhat)
     assert ok32, f"fp32 output gate exceeded: worst {worst32:.3f}"
     assert np.array_equal(out["y"], bf16_rne_of_f32(out["y32"]))
     print(f"w4a4 + shared E={E}: worst bf16 ratio {worst:.3f}, h {worst_h:.5f}, shared h {worst_sh:.5f}")
 
 
-@pytest.mark.parametrize("T", [3, 6])
+@pytest.mark.parametrize("T", [2, 3, 5, 8])
+@pytest.mark.parametrize("E,H,I", [(16, 256, 192), (12, 320, 448)])
+def test_w4a4_decode_few_tokens_small(T, E, H, I):
+    # 2-8 tokens: the small-batch kernels in their W4A4 form (4- and 8-token
+    # instances), stage by stage
+    L = layer(SEED + 3 * T + H, synth.FAM_W4A4, 0, E, H, I, T, K, "nvfp4")
+    print(f"w4a4 decode T={T} E={E} H={H} I={I}", flush=True)
+    out = run_w4a4_decode(upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4"), L["x"])
+    check_w4a4_decode(L, out)
+
+
+@pytest.mark.parametrize("T", [2, 4, 5, 8])
+def test_w4a4_decode_few_tokens_full_layer(T):
+    L = layer(SEED + T, synth.FAM_W4A4, 0, 128, 2688, 1856, T, K, "nvfp4")
+    router, ex = upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4")
+    print(f"w4a4 decode full layer T={T}", flush=True)
+    out = run_w4a4_decode(router, ex, L["x"])
+    worst, worst_h, ok_e, worst_e, flips = check_w4a4_decode(L, out)
+    print(f"w4a4 decode T={T}: worst bf16 ratio {worst:.3f}, h tap {worst_h:.5f}; end to end "
+          f"{'within' if ok_e else 'outside'} the gate ({worst_e:.3f}), {flips} h code bytes differ")
+
+
+@pytest.mark.parametrize("T", [3, 6, 9])
 def test_w4a4_moe_selects_by_token_count(T):
-    # up to 5 tokens: one single-token launch per token; more: the grouped
-    # pipeline.  Either way the output is that entry point's, bit for bit.
+    # up to 8 tokens: q4moe_w4a4_decode (the small-batch kernels); more: the
+    # grouped pipeline.  Either way the output is that entry point's, bit
+    # for bit.
     H = 2688
     L = layer(SEED + 11, synth.FAM_W4A4, 2, 128, H, 1856, T, K, "nvfp4")
     router, ex = upload_router(L["wg"], L["b"], K), upload_bank(L["bank"], "nvfp4")
@@ -187,9 +218,8 @@ def test_w4a4_moe_selects_by_token_count(T):
     torch.cuda.synchronize()
     assert np.array_equal(host(ids), L["route"]["ids"])
     y2 = torch.empty_like(y)
-    if T <= 5:
-        for t in range(T):
-            g.q4moe_w4a4_decode(router, ex, x[t:t + 1], y2[t:t + 1])
+    if T <= 8:
+        g.q4moe_w4a4_decode(router, ex, x, y2)
     else:
         g.q4moe_w4a4_grouped(router, ex, x, y2, torch.empty_like(ids), torch.empty_like(w))
     torch.cuda.synchronize()
