@@ -321,8 +321,9 @@ def bench_mid_batch(torch, g, synth, steps, fmt, layer=None):
     through the grouped path, the experts the T tokens select, and the HBM
     rate of the decode entry on their weights.  fmt "nvfp4" / "int4": the
     W4A16 entries on the stack's first layer; "w4a4": q4moe_w4a4_moe (one
-    launch for one token, the small-batch kernels up to
-    Q4MOE_W4A4_SMALL_MAX_TOKENS) and q4moe_w4a4_grouped on a bank routed with logits ~N(0, 0.5^2)."""
+    single-token launch per token up to Q4MOE_W4A4_PER_TOKEN_MAX_TOKENS),
+    q4moe_w4a4_decode (one launch for one token, the one-pass small-batch
+    kernels for 2-8) and q4moe_w4a4_grouped on a bank routed with logits ~N(0, 0.5^2)."""
     from gpu_util import dev
     fam = {"nvfp4": synth.FAM_NVFP4, "int4": synth.FAM_INT4, "w4a4": synth.FAM_W4A4}[fmt]
     if fmt == "w4a4":
@@ -342,14 +343,21 @@ def bench_mid_batch(torch, g, synth, steps, fmt, layer=None):
     reps = max(5, steps // 10)
     out = {"cold": True, "reps": reps, "decode_us": {}, "grouped_us": {}, "decode_us_per_token": {},
            "experts_read": {}, "decode_hbm_gbps": {}}
+    if fmt == "w4a4":
+        out["one_pass_small_us"] = {}
     for T in MID_COUNTS:
         x = dev(synth.x_rows(SEED, fam, 1, H, [0] * T))
         y = torch.empty((T, H), dtype=torch.int16, device="cuda")
         ids = torch.empty((T, K), dtype=torch.int32, device="cuda")
         w = torch.empty((T, K), dtype=torch.float32, device="cuda")
-        ws = g.workspace(max(entry_ws(r, ex, T), grouped_ws(r, ex, T)))
+        need = max(entry_ws(r, ex, T), grouped_ws(r, ex, T))
+        if fmt == "w4a4" and T <= 8:
+            need = max(need, g.q4moe_w4a4_decode_ws_bytes(r, ex, T))
+        ws = g.workspace(need)
         calls = {"decode_us": lambda: entry(r, ex, x, y, ids, w, ws=ws),
                  "grouped_us": lambda: grouped(r, ex, x, y, ids, w, ws=ws)}
+        if fmt == "w4a4" and T <= 8:
+            calls["one_pass_small_us"] = lambda: g.q4moe_w4a4_decode(r, ex, x, y, ids, w, ws=ws)
         for name, fn in calls.items():
             fn()
             out[name][T] = round(float(np.median(timer.each(fn, reps, evict))) * 1e3, 2)

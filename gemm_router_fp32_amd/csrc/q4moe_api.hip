@@ -136,10 +136,11 @@ struct DecodeWs {
 };
 
 // Whether the W4A16 decode of T tokens takes the grouped path (measured
-// cold crossovers at the full shapes): NVFP4 above the 8-token small-batch
-// kernels, int4 above 2 tokens (its small-batch kernels stream each expert
-// once per token and slot).
-bool w4a16_grouped(int fmt, int T) { return fmt == Q4MOE_NVFP4 ? T > kSmallT8 : T > 2; }
+// cold crossovers at the full shapes, 128 x 2688 x 1856 top-6): NVFP4 above
+// 4 tokens (at 5 tokens the grouped path takes 93 us, the 8-token
+// small-batch kernels 106 us), int4 above 2 (its small-batch kernels stream
+// each expert once per token and slot: 100 us against 87 us at 3 tokens).
+bool w4a16_grouped(int fmt, int T) { return fmt == Q4MOE_NVFP4 ? T > kSmallT : T > 2; }
 
 // S: the shared expert's intermediate size (0: no shared expert); a4: the
 // W4A4 decode (NVFP4 activation code taps); grouped: the grouped path's
@@ -447,11 +448,13 @@ q4moe_status launch_small_t(const SmallMoeArgs& a, hipStream_t s) {
     return launched("small-batch combine");
 }
 
-// The small-batch kernels for 1..8 tokens: the 4-token instances up to 4
-// tokens, the 8-token ones above; a4: the W4A4 form.
+// The small-batch kernels: up to 4 tokens the 4-token instances; the W4A4
+// form also takes 5..8 tokens with the 8-token instances (the W4A16 decode
+// sends more than 4 tokens to the grouped path).
 q4moe_status launch_small(const SmallMoeArgs& a, bool a4, hipStream_t s) {
     if (a.T <= kSmallT) return a4 ? launch_small_t<kSmallT, true>(a, s) : launch_small_t<kSmallT, false>(a, s);
-    return a4 ? launch_small_t<kSmallT8, true>(a, s) : launch_small_t<kSmallT8, false>(a, s);
+    if (!a4) return fail(Q4MOE_EUNSUPPORTED, "the W4A16 small-batch kernels take up to %d tokens", kSmallT);
+    return launch_small_t<kSmallT8, true>(a, s);
 }
 
 // The grouped W4A16 path for more than kSmallT tokens (hidden and inter
@@ -1051,8 +1054,7 @@ q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_
 
 size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    const size_t small =
-        decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, std::min<int32_t>(n_tok, kSmallT8), 0, true).total;
+    const size_t small = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, 1, 0, true).total;
     const size_t grouped = w4a4_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
     return std::max(small, grouped);
 }
@@ -1063,10 +1065,19 @@ q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, cons
     if (st != Q4MOE_OK) return st;
     if (!x_bf16 || !y_bf16 || !ids || !w) return fail(Q4MOE_EINVAL, "x / y / ids / w is NULL");
     if ((st = check_ws(ws, ws_bytes, q4moe_w4a4_moe_ws_bytes(r, ex, n_tok))) != Q4MOE_OK) return st;
-    if (n_tok <= Q4MOE_W4A4_SMALL_MAX_TOKENS) {
-        // one token: the single launch; 2..8: the small-batch kernels
-        st = decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream, true);
-        if (st != Q4MOE_EUNSUPPORTED) return st;  // (EUNSUPPORTED: the shape does not fit them)
+    if (n_tok <= Q4MOE_W4A4_PER_TOKEN_MAX_TOKENS) {
+        // one single-token launch per token, in order on the stream (each
+        // call advances the workspace's epoch, so the calls can share it);
+        // measured cold at the full shapes, these beat the one-pass
+        // small-batch kernels (2 tokens: 34 us against 50 us) and the grouped
+        // pipeline up to 7 tokens
+        const size_t H = (size_t)ex->hidden, K = (size_t)r->top_k;
+        for (int32_t t = 0; t < n_tok; ++t) {
+            st = decode_impl(r, ex, nullptr, x_bf16 + t * H, 1, y_bf16 + t * H, ids + t * K, w + t * K, ws, ws_bytes,
+                             stream, true);
+            if (st != Q4MOE_OK) return st;
+        }
+        return st;
     }
     return q4moe_w4a4_grouped(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
 }

@@ -281,11 +281,14 @@ q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_ex
 
 /* W4A4 routed-MoE layer for any token count, choosing the kernels by the
  * count (mid-batch decode: the pages point at choosing the GEMM backend per
- * batch size): up to Q4MOE_W4A4_SMALL_MAX_TOKENS tokens q4moe_w4a4_decode
- * (one launch for one token, the small-batch kernels for 2-8), more tokens
- * the grouped MFMA pipeline (q4moe_w4a4_grouped).  The results are those of
- * the entry point used.  ids / w are required. */
-#define Q4MOE_W4A4_SMALL_MAX_TOKENS 8
+ * batch size): up to Q4MOE_W4A4_PER_TOKEN_MAX_TOKENS tokens one
+ * single-token q4moe_w4a4_decode launch per token, more tokens the grouped
+ * MFMA pipeline (q4moe_w4a4_grouped).  Measured cold on MI355X at the full
+ * shapes (128 x 2688 x 1856, top-6), the single-token launches (about 18 us
+ * each) beat both the one-pass small-batch kernels of q4moe_w4a4_decode and
+ * the grouped pipeline up to 7 tokens.  The results are those of the entry
+ * point used.  ids / w are required. */
+#define Q4MOE_W4A4_PER_TOKEN_MAX_TOKENS 7
 size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok);
 q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16, int32_t n_tok,
                             uint16_t* y_bf16, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
