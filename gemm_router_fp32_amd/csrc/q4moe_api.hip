@@ -13,6 +13,7 @@
 #include "q4moe_fused.hpp"
 #include "q4moe_w4a4.hpp"
 #include "q4moe_grouped16.hpp"
+#include "q4moe_fp8gemv.hpp"
 #include "q4moe_wquant.hpp"
 #include "q4moe_shared.hpp"
 
@@ -332,6 +333,19 @@ GemvWs gemv_ws(int T) {
     l.ctrl = 0;
     l.keys = kPrefixBytes;
     l.total = l.keys + up_to((size_t)kMaxGemvBlocks * T * 8);
+    return l;
+}
+
+// The FP8 GEMV: the keys, then its activation code tap [T][cols].
+struct Fp8GemvWs {
+    size_t keys, xq, total;
+};
+
+Fp8GemvWs fp8_gemv_ws(int T, int cols) {
+    Fp8GemvWs l;
+    l.keys = kPrefixBytes;
+    l.xq = l.keys + up_to((size_t)kMaxGemvBlocks * T * 8);
+    l.total = l.xq + up_to((size_t)T * cols);
     return l;
 }
 
@@ -1292,6 +1306,85 @@ q4moe_status q4moe_w4a16_gemv(const q4moe_qmat* m, const uint16_t* x_bf16, int32
     if (argmax) {
         hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(256), 0, s, a.keys, grid, n_tok, argmax);
         return launched("lm_head argmax");
+    }
+    return Q4MOE_OK;
+}
+
+
+// --- FP8 W8A8 GEMV (the drafter's lm_head) ---------------------------------
+
+size_t q4moe_fp8_gemv_ws_bytes(const q4moe_fp8_mat* m, int32_t n_tok) {
+    if (!m || n_tok < 1 || m->cols < 1) return 0;
+    return fp8_gemv_ws(n_tok, m->cols).total;
+}
+
+q4moe_status q4moe_fp8_gemv_taps(const q4moe_fp8_mat* m, int32_t n_tok, size_t* xq) {
+    if (!m || !xq || n_tok < 1 || m->cols < 1) return fail(Q4MOE_EINVAL, "NULL argument or n_tok < 1");
+    *xq = fp8_gemv_ws(n_tok, m->cols).xq;
+    return Q4MOE_OK;
+}
+
+q4moe_status q4moe_fp8_gemv(const q4moe_fp8_mat* m, const uint16_t* x_bf16, int32_t n_tok, float* logits,
+                            int32_t* argmax, void* ws, size_t ws_bytes, void* stream) {
+    if (!m) return fail(Q4MOE_EINVAL, "matrix descriptor is NULL");
+    if (m->rows < 1 || m->cols < 64 || m->cols % 64 != 0 || m->cols > kMaxDim)
+        return fail(Q4MOE_EINVAL, "shape %d x %d: cols a multiple of 64 in [64, %d]", m->rows, m->cols, kMaxDim);
+    if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
+    if ((uint64_t)m->rows * (uint64_t)m->cols > 0xFFFFFFFFull)
+        return fail(Q4MOE_EUNSUPPORTED, "FP8 codes of %d x %d exceed 4 GiB", m->rows, m->cols);
+    if (!std::isfinite(m->wscale) || !std::isfinite(m->iscale) || m->wscale == 0.0f || m->iscale == 0.0f)
+        return fail(Q4MOE_EINVAL, "wscale / iscale must be finite and non-zero");
+    if (!m->codes || !x_bf16 || !logits) return fail(Q4MOE_EINVAL, "codes / x / logits is NULL");
+    if (!aligned(m->codes, 16) || !aligned(x_bf16, 16) || !aligned(logits, 16))
+        return fail(Q4MOE_EALIGN, "codes / x / logits not 16-byte aligned");
+    if (argmax && !aligned(argmax, 4)) return fail(Q4MOE_EALIGN, "argmax not 4-byte aligned");
+    Fp8GemvWs l = fp8_gemv_ws(n_tok, m->cols);
+    q4moe_status st = check_ws(ws, ws_bytes, l.total);
+    if (st != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    Fp8GemvArgs a;
+    a.rows = m->rows;
+    a.cols = m->cols;
+    a.T = n_tok;
+    a.codes = m->codes;
+    a.wscale = m->wscale;
+    a.iscale = m->iscale;
+    a.x = x_bf16;
+    a.logits = logits;
+    a.xq = at<uint8_t>(ws, l.xq);
+    a.keys = at<unsigned long long>(ws, l.keys);
+    hipStream_t s = (hipStream_t)stream;
+    const int nj = m->cols / 64;  // 64-column pieces per row: 1..64
+    const int groups = (m->rows + 15) / 16;
+    // NJ8: exact for the 2688-wide lm_head, else 16, 32, 48 or 64
+    const int NJ8 = nj == 42 ? 42 : (nj + 15) / 16 * 16;
+    int grid = 0;
+#define Q4_GEMV8(JJ, TT)                                                                             \
+    do {                                                                                             \
+        grid = persistent_grid(k_gemv_fp8<JJ, TT>, 256, std::min((groups + 3) / 4, kMaxGemvBlocks));  \
+        if (grid < 1) return fail(Q4MOE_EDEVICE, "occupancy query failed");                          \
+        hipLaunchKernelGGL((k_gemv_fp8<JJ, TT>), dim3(grid), dim3(256), 0, s, a);                    \
+    } while (0)
+#define Q4_GEMV8_T(JJ)                  \
+    switch (n_tok) {                    \
+        case 1: Q4_GEMV8(JJ, 1); break; \
+        case 2: Q4_GEMV8(JJ, 2); break; \
+        case 3: Q4_GEMV8(JJ, 3); break; \
+        default: Q4_GEMV8(JJ, 4); break; \
+    }
+    switch (NJ8) {
+        case 16: Q4_GEMV8_T(16); break;
+        case 32: Q4_GEMV8_T(32); break;
+        case 42: Q4_GEMV8_T(42); break;
+        case 48: Q4_GEMV8_T(48); break;
+        default: Q4_GEMV8_T(64); break;
+    }
+#undef Q4_GEMV8_T
+#undef Q4_GEMV8
+    if ((st = launched("fp8 gemv")) != Q4MOE_OK) return st;
+    if (argmax) {
+        hipLaunchKernelGGL(k_argmax_reduce, dim3(1), dim3(256), 0, s, a.keys, grid, n_tok, argmax);
+        return launched("fp8 gemv argmax");
     }
     return Q4MOE_OK;
 }

@@ -46,6 +46,11 @@ class SharedFp8S(ctypes.Structure):
                 ("down_wscale", ctypes.c_float), ("down_iscale", ctypes.c_float)]
 
 
+class Fp8MatS(ctypes.Structure):
+    _fields_ = [("rows", _i32), ("cols", _i32), ("codes", _p), ("wscale", ctypes.c_float),
+                ("iscale", ctypes.c_float)]
+
+
 class SharedTaps(ctypes.Structure):
     _fields_ = [("y32", _sz), ("h", _sz), ("xq", _sz), ("sh_h32", _sz), ("sh_hq", _sz)]
 
@@ -97,6 +102,9 @@ _SIGS = {
     "q4moe_w4a4_grouped_taps": (_i32, [_p, _p, _i32, _p]),
     "q4moe_w4a16_gemv_ws_bytes": (_sz, [_p, _i32]),
     "q4moe_w4a16_gemv": (_i32, [_p, _p, _i32, _p, _p, _p, _sz, _p]),
+    "q4moe_fp8_gemv_ws_bytes": (_sz, [_p, _i32]),
+    "q4moe_fp8_gemv": (_i32, [_p, _p, _i32, _p, _p, _p, _sz, _p]),
+    "q4moe_fp8_gemv_taps": (_i32, [_p, _i32, ctypes.POINTER(_sz)]),
     "q4moe_ws_init": (_i32, [_p, _sz, _p]),
     "q4moe_ws_check": (_i32, [_p, _sz, _p, _p]),
     "q4moe_status_str": (ctypes.c_char_p, [_i32]),
@@ -176,6 +184,15 @@ class QMat:
         self.fmt, self.rows, self.cols = fmt, rows, c2 * 2
         self.s = QMatS(fmt, rows, c2 * 2, codes.data_ptr(), scales.data_ptr(),
                        None if gscale is None else gscale.data_ptr())
+
+
+class Fp8Mat:
+    """FP8 per-tensor W8A8 matrix: codes [rows, cols] uint8 E4M3FN tensor,
+    fp32 weight scale and static input scale."""
+    def __init__(self, codes, wscale, iscale):
+        self.t = (codes,)
+        self.rows, self.cols = codes.shape
+        self.s = Fp8MatS(self.rows, self.cols, codes.data_ptr(), float(wscale), float(iscale))
 
 
 def workspace(nbytes, device="cuda"):
@@ -363,6 +380,26 @@ def q4moe_w4a16_gemv(qmat, x, logits, argmax=None, ws=None, stream=None):
         ws = workspace(q4moe_w4a16_gemv_ws_bytes(qmat, n_tok), x.device)
     _check(lib().q4moe_w4a16_gemv(ctypes.byref(qmat.s), _ptr(x), n_tok, _ptr(logits), _ptr(argmax), _ptr(ws),
                                   ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4moe_fp8_gemv_ws_bytes(mat, n_tok):
+    return lib().q4moe_fp8_gemv_ws_bytes(ctypes.byref(mat.s), n_tok)
+
+
+def q4moe_fp8_gemv_taps(mat, n_tok):
+    """Byte offset of the activation codes [n_tok][cols] in the workspace."""
+    off = _sz(0)
+    _check(lib().q4moe_fp8_gemv_taps(ctypes.byref(mat.s), n_tok, ctypes.byref(off)))
+    return off.value
+
+
+def q4moe_fp8_gemv(mat, x, logits, argmax=None, ws=None, stream=None):
+    n_tok = x.shape[0]
+    if ws is None:
+        ws = workspace(q4moe_fp8_gemv_ws_bytes(mat, n_tok), x.device)
+    _check(lib().q4moe_fp8_gemv(ctypes.byref(mat.s), _ptr(x), n_tok, _ptr(logits), _ptr(argmax), _ptr(ws),
+                                ws.numel(), _stream(stream)))
     return ws
 
 

@@ -293,6 +293,31 @@ size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, i
 q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16, int32_t n_tok,
                             uint16_t* y_bf16, int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
 
+/* FP8 per-tensor W8A8 matrix: the MTP drafter's lm_head ("Quantization
+ * (PTQ + QAD)", MTP Drafter Precision: the drafter shares the checkpoint's
+ * lm_head, quantized to FP8).  codes E4M3FN [rows][cols] row-major,
+ * 16-byte aligned, cols a multiple of 64 in [64, 4096], rows * cols < 2^32;
+ * wscale: fp32 weight scale per tensor; iscale: fp32 static input scale per
+ * tensor (finite, non-zero).  The same per-tensor W8A8 format as the shared
+ * expert: an activation v is coded as the E4M3FN value nearest
+ * fl32(v / iscale) (ties to even, saturating at 448, sign kept). */
+typedef struct {
+    int32_t rows, cols;
+    const uint8_t* codes;
+    float wscale, iscale;
+} q4moe_fp8_mat;
+
+/* FP8 GEMV + argmax for 1 <= n_tok <= 4 bf16 tokens x [n_tok][cols]:
+ * logits fp32 [n_tok][rows] = (sum_c e4m3(W[r][c]) e4m3(code(x[t][c]))) *
+ * wscale * iscale (each product exact, fp32 accumulation); argmax (nullable)
+ * int32 [n_tok]: the lowest row among each token's largest logits.  The
+ * workspace keeps the activation codes uint8 [n_tok][cols] at the offset
+ * q4moe_fp8_gemv_taps returns. */
+size_t q4moe_fp8_gemv_ws_bytes(const q4moe_fp8_mat* m, int32_t n_tok);
+q4moe_status q4moe_fp8_gemv(const q4moe_fp8_mat* m, const uint16_t* x_bf16, int32_t n_tok, float* logits,
+                            int32_t* argmax, void* ws, size_t ws_bytes, void* stream);
+q4moe_status q4moe_fp8_gemv_taps(const q4moe_fp8_mat* m, int32_t n_tok, size_t* xq);
+
 /* NVFP4 weight quantizer ([W] Step 1: NVFP4 weights, E2M1 values with an
  * FP8 (E4M3) scale per 16, built with ModelOpt; the recipe table's
  * weight-scale selection: max-based, or an MSE per-block search over FP8

@@ -13,7 +13,8 @@ with the shapes and value distributions of the workloads:
 * int4 group-64 matrices: uniform nibble codes (two's complement -8..7) and
   bf16 group scales |N(0, 0.01^2)| + 1e-3;
 * FP8 shared expert: E4M3FN weight bytes uniform over FP8_WEIGHT_BYTES and
-  fixed power-of-two per-tensor scales (FP8_SHARED_SCALES).
+  fixed power-of-two per-tensor scales (FP8_SHARED_SCALES); the FP8 lm_head
+  of the drafter the same way (FP8_LM_SCALES).
 
 Expert weights are the logical row-major layout: element (r, 2j) is the low
 nibble of byte r*cols/2 + j, scale (r, b) is entry r*(cols/block) + b.
@@ -32,6 +33,7 @@ _LIB = None
 # Stream identifiers (the third element of a key tuple).
 S_X, S_WG, S_BIAS, S_UP_CODES, S_UP_SCALES, S_DN_CODES, S_DN_SCALES, S_LM_CODES, S_LM_SCALES = range(1, 10)
 S_SH_UP, S_SH_DN = 10, 11
+S_LM_FP8 = 12
 # Workload families (the first element of a key tuple).  One-token and
 # four-token NVFP4 decode and the 23-layer NVFP4 stack share a family, so
 # layer 0 of the stack is the one-layer workload.
@@ -237,6 +239,19 @@ def lm_head(seed, fam, layer, V, H, gscale=1.0 / 64, scale_bytes=NVFP4_SCALE_BYT
         codes, scales = nvfp4_matrix(seed, fam, layer, S_LM_CODES, S_LM_SCALES, 0, V, H, pool,
                                      scale_bytes=scale_bytes)
     return codes, scales, np.float32(gscale)
+
+
+# Per-tensor scales of the synthetic FP8 lm_head (the input scale keeps
+# x / s inside the E4M3FN range for N(0, 1) activations).
+FP8_LM_SCALES = {"wscale": 2.0 ** -8, "iscale": 2.0 ** -6}
+
+
+def lm_head_fp8(seed, fam, layer, V, H):
+    """FP8 lm_head [V, H]: E4M3FN codes uniform over FP8_WEIGHT_BYTES and the
+    fp32 weight and input scales."""
+    with ThreadPoolExecutor(NTHREADS) as pool:
+        codes = choice_bytes(key(seed, fam, layer, S_LM_FP8), V * H, FP8_WEIGHT_BYTES, pool)
+    return codes.reshape(V, H), np.float32(FP8_LM_SCALES["wscale"]), np.float32(FP8_LM_SCALES["iscale"])
 
 
 def shared_fp8(seed, fam, layer, H, S):

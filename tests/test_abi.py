@@ -210,3 +210,29 @@ def test_quantize_weights_validation(L):
     assert call(w=A16 + 8) == g.EALIGN
     assert call(codes=A16 + 4) == g.EALIGN
     assert call(wsb=need - 1) == g.EWORKSPACE
+
+
+def test_fp8_gemv_validation(L):
+    # every call here fails validation, so nothing reaches a device
+    def mat(rows=1024, cols=2688, codes=A16, ws=2.0 ** -8, is_=2.0 ** -6):
+        return g.Fp8MatS(rows, cols, codes, ws, is_)
+
+    need = L.q4moe_fp8_gemv_ws_bytes(ctypes.byref(mat()), 4)
+
+    def call(m, T=1, x=A16, wsb=need, logits=A16):
+        return L.q4moe_fp8_gemv(ctypes.byref(m), x, T, logits, None, A16, wsb, None)
+
+    assert need > L.q4moe_fp8_gemv_ws_bytes(ctypes.byref(mat()), 1)
+    assert call(mat(cols=2600)) == g.EINVAL
+    assert call(mat(cols=8192)) == g.EINVAL
+    assert call(mat(), T=5) == g.EINVAL
+    assert call(mat(is_=0.0)) == g.EINVAL
+    assert call(mat(ws=float("nan"))) == g.EINVAL
+    assert call(mat(codes=None)) == g.EINVAL
+    assert call(mat(codes=A16 + 4)) == g.EALIGN
+    assert call(mat(), x=A16 + 2) == g.EALIGN
+    assert call(mat(), T=4, wsb=need - 1) == g.EWORKSPACE
+    assert call(mat(rows=1 << 21, cols=4096)) == g.EUNSUPPORTED
+    off = ctypes.c_size_t(0)
+    assert L.q4moe_fp8_gemv_taps(ctypes.byref(mat()), 4, ctypes.byref(off)) == g.OK
+    assert 0 < off.value and off.value + 4 * 2688 <= need
