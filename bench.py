@@ -282,6 +282,42 @@ def bench_verify(torch, g, synth, steps, stack_layer0):
             "lm_head_us_spread": spread(t_head), "cold": True, "reps": reps}
 
 
+def bench_spec_step(torch, g, synth, steps):
+    """One speculative decode step through one MoE layer (tests/spec_step.py):
+    three drafter passes (W4A4 NVFP4 MoE on one token, FP8 lm_head GEMV +
+    argmax), then the 4-token W4A16 NVFP4 verify MoE and the NVFP4 lm_head,
+    captured as one graph and replayed cold (1 GiB read before each
+    replay); the eager step and each stage are timed cold beside it."""
+    from spec_step import DRAFT_LAYER, SpecStep
+    st = SpecStep(torch, g, synth, SEED, x0=synth.x_rows(SEED, synth.FAM_W4A4, DRAFT_LAYER, H, [0])[0])
+    for _ in range(3):
+        st.step()
+    graph = st.capture()
+    timer, evict = Timer(torch), Evictor(torch)
+    reps = max(10, steps // 2)
+    t_graph = timer.each(graph.replay, reps, evict)
+    t_eager = timer.each(st.step, reps, evict)
+    t_draft = timer.each(lambda: st.draft(1), reps, evict)
+    t_moe = timer.each(lambda: g.q4moe_w4a4_decode(st.drouter, st.dex, st.xv[0:1], st.xv[1:2], st.d_ids[0:1],
+                                                   st.d_w[0:1], ws=st.d_ws[0]), reps, evict)
+    t_fp8 = timer.each(lambda: g.q4moe_fp8_gemv(st.fp8, st.xv[1:2], st.d_logits[0:1], st.d_am[0:1], ws=st.f_ws[0]),
+                       reps, evict)
+    t_verify = timer.each(st.verify, reps, evict)
+    fp8_bytes = V * H + H * 2 + V * 4
+    out = {"graph_step_us": round(float(np.median(t_graph)) * 1e3, 2), "graph_step_us_spread": spread(t_graph),
+           "eager_step_us": round(float(np.median(t_eager)) * 1e3, 2),
+           "draft_pass_us": round(float(np.median(t_draft)) * 1e3, 2),
+           "draft_moe_w4a4_us": round(float(np.median(t_moe)) * 1e3, 2),
+           "draft_lm_head_fp8_us": round(float(np.median(t_fp8)) * 1e3, 2),
+           "draft_lm_head_fp8_hbm_gbps": round(fp8_bytes / (float(np.median(t_fp8)) * 1e-3) / 1e9, 1),
+           "verify_us": round(float(np.median(t_verify)) * 1e3, 2),
+           "kernels_per_step": 3 * 3 + 4 + 2, "cold": True, "reps": reps}
+    del graph, st
+    torch.cuda.empty_cache()
+    log(f"speculative step: {out}")
+    return out
+
+
 def bench_wquant(torch, g, synth, steps):
     """NVFP4 weight quantizer on one expert's up_proj (1856 x 2688 bf16):
     µs per matrix in both scale modes; bytes = bf16 in + codes and scales out."""
@@ -481,6 +517,7 @@ def main():
         log(f"nvfp4 W4A4 + fp8 shared expert single-token stack: {extra['w4a4_shared_stack']}")
         del a4s
         torch.cuda.empty_cache()
+        extra["spec_step"] = bench_spec_step(torch, g, synth, args.steps)
         extra["w4a4_chunk"] = bench_w4a4(torch, g, synth, args.steps)
         extra["weight_quantizer"] = bench_wquant(torch, g, synth, args.steps)
         extra["mid_batch_w4a4"] = bench_mid_batch(torch, g, synth, args.steps, "w4a4")
