@@ -133,6 +133,8 @@ struct DecodeWs {
     size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s;
     // the grouped path (more than kSmallT tokens): dispatch, fp16 staging
     size_t counts, offsets, lists, perm, inv, act, n_act, x16, xexp, h16, hexp;
+    // the shared expert through the grouped GEMMs (one-expert dispatch)
+    size_t sh_act, sh_nact, sh_perm, sh_gate, sh_x16, sh_xexp, sh_h16, sh_hexp;
     size_t total;
 };
 
@@ -147,7 +149,8 @@ bool w4a16_grouped(int fmt, int T) { return fmt == Q4MOE_NVFP4 ? T > kSmallT : T
 // W4A4 decode (NVFP4 activation code taps); grouped: the grouped path's
 // buffers (they follow every other buffer, so the tap offsets do not depend
 // on it).
-DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false, bool grouped = false) {
+DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false, bool grouped = false,
+                   bool sh_grouped = false) {
     DecodeWs l;
     l.r = router_ws(E, K, T);
     // the one-launch decode's tags, in the common prefix:
@@ -195,6 +198,16 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     take(l.xexp, grouped ? (size_t)T * 4 : 0);
     take(l.h16, rows * 2 * I * 2);
     take(l.hexp, rows * 4);
+    // the shared expert's grouped buffers (after every other buffer)
+    const size_t st = sh_grouped ? (size_t)T : 0;
+    take(l.sh_act, sh_grouped ? 16 : 0);
+    take(l.sh_nact, sh_grouped ? 4 : 0);
+    take(l.sh_perm, st * 4);
+    take(l.sh_gate, st * 4);
+    take(l.sh_x16, st * H * 2);
+    take(l.sh_xexp, st * 4);
+    take(l.sh_h16, st * 2 * S * 2);
+    take(l.sh_hexp, st * 4);
     l.total = o;
     return l;
 }
@@ -475,7 +488,8 @@ q4moe_status launch_small(const SmallMoeArgs& a, bool a4, hipStream_t s) {
 // multiples of 64): router, dispatch, fp16 staging, two grouped MFMA GEMMs
 // and the combine, in order on one stream.
 q4moe_status launch_grouped16(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x, int T, uint16_t* y,
-                              int32_t* ids_out, float* w_out, void* ws, const DecodeWs& l, hipStream_t s) {
+                              int32_t* ids_out, float* w_out, void* ws, const DecodeWs& l, hipStream_t s,
+                              const float* zsh = nullptr) {
     const int E = r->n_experts, H = ex->hidden, I = ex->inter, K = r->top_k;
     RouterArgs ra = router_args(r, x, T, ws, l.r, ids_out, w_out, nullptr);
     q4moe_status st = launch_router(ra, s);
@@ -563,10 +577,158 @@ q4moe_status launch_grouped16(const q4moe_router* r, const q4moe_experts* ex, co
     b.zw = gd.out;
     b.y32 = at<float>(ws, l.y32);
     b.y = y;
-    b.zsh = nullptr;
+    b.zsh = zsh;
     hipLaunchKernelGGL(k_small_combine, dim3((T * H + 255) / 256), dim3(256), 0, s, b);
     return launched("combine");
 }
+
+// The shared expert as the grouped GEMMs see it: FP8 per-tensor W8A8, or a
+// 4-bit W4A16 expert (NVFP4 or int4-g64).
+struct SharedDense {
+    int wf, S;
+    const uint8_t *upc, *ups, *dnc, *dns;
+    const float *upg, *dng;
+    float up_gs, dn_gs, up_in, dn_in;  // FP8: weight scale * input scale, input scales
+};
+
+SharedDense shared_dense(const q4moe_shared_fp8* sh, const q4moe_experts* sh4) {
+    SharedDense d;
+    if (sh) {
+        d.wf = FMT_FP8;
+        d.S = sh->inter;
+        d.upc = sh->up_codes;
+        d.dnc = sh->down_codes;
+        d.ups = d.dns = nullptr;
+        d.upg = d.dng = nullptr;
+        d.up_gs = sh->up_wscale * sh->up_iscale;
+        d.dn_gs = sh->down_wscale * sh->down_iscale;
+        d.up_in = sh->up_iscale;
+        d.dn_in = sh->down_iscale;
+    } else {
+        d.wf = sh4->fmt == Q4MOE_NVFP4 ? FMT_NVFP4 : FMT_INT4;
+        d.S = sh4->inter;
+        d.upc = sh4->up_codes;
+        d.dnc = sh4->down_codes;
+        d.ups = static_cast<const uint8_t*>(sh4->up_scales);
+        d.dns = static_cast<const uint8_t*>(sh4->down_scales);
+        d.upg = sh4->up_gscale;
+        d.dng = sh4->down_gscale;
+        d.up_gs = d.dn_gs = d.up_in = d.dn_in = 1.0f;
+    }
+    return d;
+}
+
+// The shared expert for T tokens through the grouped GEMMs, as a one-expert
+// dispatch (every token a row with gate 1): zsh [T][H] = its output, with
+// the taps sh_xq / sh_hq (FP8 codes) and sh_h (relu(u)^2).  hidden a
+// multiple of 64.
+q4moe_status launch_shared_grouped(const SharedDense& d, const uint16_t* x, int T, int H, void* ws, const DecodeWs& l,
+                                   hipStream_t s) {
+    q4moe_status st;
+    int4* act = at<int4>(ws, l.sh_act);
+    int32_t* nact = at<int32_t>(ws, l.sh_nact);
+    int32_t* perm = at<int32_t>(ws, l.sh_perm);
+    float* gate = at<float>(ws, l.sh_gate);
+    hipLaunchKernelGGL(k_dispatch_all, dim3((T + 255) / 256), dim3(256), 0, s, T, act, nact, perm, gate);
+    if ((st = launched("shared expert dispatch")) != Q4MOE_OK) return st;
+    const bool f8 = d.wf == FMT_FP8;
+    StageArgs sx;
+    sx.cols = H;
+    sx.xb = x;
+    sx.hf = nullptr;
+    sx.out = at<_Float16>(ws, l.sh_x16);
+    sx.exps = at<int32_t>(ws, l.sh_xexp);
+    sx.iscale = d.up_in;
+    sx.codes = f8 ? at<uint8_t>(ws, l.sh_xq) : nullptr;
+    if (f8)
+        hipLaunchKernelGGL((k_stage_fp8<true>), dim3(T), dim3(256), 0, s, sx);
+    else
+        hipLaunchKernelGGL(k_stage_x16, dim3(T), dim3(256), 0, s, sx);
+    if ((st = launched("shared expert x staging")) != Q4MOE_OK) return st;
+    GemmA16Args gu;
+    gu.N = d.S;
+    gu.Kd = H;
+    gu.K = 1;
+    gu.wc = d.upc;
+    gu.wsc = d.ups;
+    gu.wg = d.upg;
+    gu.gs = d.up_gs;
+    gu.a16 = sx.out;
+    gu.aexp = sx.exps;
+    gu.act = act;
+    gu.n_act = nact;
+    gu.perm = perm;
+    gu.gate = gate;
+    gu.out = at<float>(ws, l.sh_h);
+    const dim3 grid_up((d.S + kGemmBN - 1) / kGemmBN, 1);
+    const size_t lds_up = d.wf == FMT_NVFP4 ? (size_t)kGemmBN * (H / 16) + 16 : d.wf == FMT_INT4 ? (size_t)kGemmBN * (H / 32) + 16 : 16;
+    if (d.wf == FMT_FP8)
+        hipLaunchKernelGGL((k_grouped_a16<EPI_UP, FMT_FP8>), grid_up, dim3(256), lds_up, s, gu);
+    else if (d.wf == FMT_NVFP4)
+        hipLaunchKernelGGL((k_grouped_a16<EPI_UP, FMT_NVFP4>), grid_up, dim3(256), lds_up, s, gu);
+    else
+        hipLaunchKernelGGL((k_grouped_a16<EPI_UP, FMT_INT4>), grid_up, dim3(256), lds_up, s, gu);
+    if ((st = launched("shared expert up gemm")) != Q4MOE_OK) return st;
+    StageArgs sh;
+    sh.cols = d.S;
+    sh.xb = nullptr;
+    sh.hf = gu.out;
+    sh.out = at<_Float16>(ws, l.sh_h16);
+    sh.exps = at<int32_t>(ws, l.sh_hexp);
+    sh.iscale = d.dn_in;
+    sh.codes = f8 ? at<uint8_t>(ws, l.sh_hq) : nullptr;
+    if (f8)
+        hipLaunchKernelGGL((k_stage_fp8<false>), dim3(T), dim3(256), 0, s, sh);
+    else
+        hipLaunchKernelGGL(k_stage_h16, dim3(T), dim3(256), 0, s, sh);
+    if ((st = launched("shared expert h staging")) != Q4MOE_OK) return st;
+    GemmA16Args gd = gu;
+    gd.N = H;
+    gd.Kd = d.S;
+    gd.wc = d.dnc;
+    gd.wsc = d.dns;
+    gd.wg = d.dng;
+    gd.gs = d.dn_gs;
+    gd.a16 = sh.out;
+    gd.aexp = sh.exps;
+    gd.out = at<float>(ws, l.sh_z);
+    const dim3 grid_dn((H + kGemmBN - 1) / kGemmBN, 1);
+    const size_t lds_dn = d.wf == FMT_NVFP4 ? (size_t)kGemmBN * (d.S / 16) + 16 : d.wf == FMT_INT4 ? (size_t)kGemmBN * (d.S / 32) + 16 : 16;
+    if (d.wf == FMT_FP8)
+        hipLaunchKernelGGL((k_grouped_a16<EPI_DOWN, FMT_FP8>), grid_dn, dim3(256), lds_dn, s, gd);
+    else if (d.wf == FMT_NVFP4)
+        hipLaunchKernelGGL((k_grouped_a16<EPI_DOWN, FMT_NVFP4>), grid_dn, dim3(256), lds_dn, s, gd);
+    else
+        hipLaunchKernelGGL((k_grouped_a16<EPI_DOWN, FMT_INT4>), grid_dn, dim3(256), lds_dn, s, gd);
+    return launched("shared expert down gemm");
+}
+
+// Which paths a decode call takes: the routed experts through the grouped
+// path, and the shared expert through the grouped GEMMs (the FP8 shared
+// expert's small-batch and one-launch forms cover NVFP4 routed experts up
+// to kSmallT tokens; the 4-bit shared expert always takes the grouped
+// GEMMs).  The small-batch kernels add a shared output in their combine, so
+// NVFP4 routed experts keep them up to kSmallT tokens.
+struct DecodePlan {
+    bool grouped, sh_grouped;
+};
+
+DecodePlan decode_plan(const q4moe_experts* ex, int T, bool fp8_shared, bool q4_shared, bool a4, bool force_grouped) {
+    DecodePlan p;
+    p.sh_grouped = !a4 && (q4_shared || (fp8_shared && (T > kSmallT || ex->fmt != Q4MOE_NVFP4)));
+    const bool small_ok = ex->fmt == Q4MOE_NVFP4 && T <= kSmallT;
+    p.grouped = force_grouped || (!a4 && w4a16_grouped(ex->fmt, T)) || (p.sh_grouped && !small_ok);
+    return p;
+}
+
+// The workspace layout of a decode call (as decode_impl plans it).
+DecodeWs decode_layout(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
+                       const q4moe_experts* sh4, int32_t n_tok, bool a4 = false, bool grouped = false) {
+    const DecodePlan p = decode_plan(ex, n_tok, sh != nullptr, sh4 != nullptr, a4, grouped);
+    const int S = sh ? sh->inter : sh4 ? sh4->inter : 0;
+    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, S, a4, p.grouped, p.sh_grouped);
+}
+
 
 }  // namespace
 
@@ -665,14 +827,13 @@ q4moe_status q4moe_dequant_ref(const q4moe_qmat* m, float* out, void* stream) {
 
 size_t q4moe_w4a16_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, false,
-                     w4a16_grouped(ex->fmt, n_tok)).total;
+    return decode_layout(r, ex, nullptr, nullptr, n_tok).total;
 }
 
 q4moe_status q4moe_w4a16_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
                                      q4moe_decode_taps* out) {
     if (!r || !ex || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok);
+    DecodeWs l = decode_layout(r, ex, nullptr, nullptr, n_tok);
     out->y32 = l.y32;
     out->h = l.h;
     return Q4MOE_OK;
@@ -692,8 +853,33 @@ q4moe_status check_shared(const q4moe_shared_fp8* sh, const q4moe_experts* ex, i
     const float sc[4] = {sh->up_wscale, sh->up_iscale, sh->down_wscale, sh->down_iscale};
     for (float v : sc)
         if (!std::isfinite(v) || v == 0.0f) return fail(Q4MOE_EINVAL, "shared expert scales must be finite and non-zero");
-    if (ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs with NVFP4 routed experts");
-    if (n_tok > kSmallT) return fail(Q4MOE_EUNSUPPORTED, "the shared expert runs for up to %d tokens", kSmallT);
+    (void)n_tok;
+    return Q4MOE_OK;
+}
+
+// The 4-bit W4A16 shared expert: an expert bank of one expert, NVFP4 or
+// int4-g64, the routed experts' hidden, inter a multiple of 64.
+q4moe_status check_shared_q4(const q4moe_experts* sh, const q4moe_experts* ex) {
+    if (!sh) return fail(Q4MOE_EINVAL, "shared expert descriptor is NULL");
+    if (sh->n_experts != 1) return fail(Q4MOE_EINVAL, "the shared expert is a bank of one expert (got %d)", sh->n_experts);
+    if (sh->fmt != Q4MOE_NVFP4 && sh->fmt != Q4MOE_INT4_G64)
+        return fail(Q4MOE_EINVAL, "unknown shared expert format %d", sh->fmt);
+    if (sh->hidden != ex->hidden)
+        return fail(Q4MOE_EINVAL, "shared expert hidden %d differs from the experts' %d", sh->hidden, ex->hidden);
+    if (sh->inter < 64 || sh->inter % 64 != 0 || sh->inter > kMaxDim)
+        return fail(Q4MOE_EINVAL, "shared expert inter %d must be a multiple of 64 in [64, %d]", sh->inter, kMaxDim);
+    if (!sh->up_codes || !sh->up_scales || !sh->down_codes || !sh->down_scales)
+        return fail(Q4MOE_EINVAL, "shared expert code / scale pointer is NULL");
+    if (sh->fmt == Q4MOE_NVFP4 && (!sh->up_gscale || !sh->down_gscale))
+        return fail(Q4MOE_EINVAL, "an NVFP4 shared expert needs up_gscale and down_gscale");
+    if (sh->fmt == Q4MOE_INT4_G64 && (sh->up_gscale || sh->down_gscale))
+        return fail(Q4MOE_EINVAL, "an INT4_G64 shared expert takes no per-tensor scale (pass NULL)");
+    if (!aligned(sh->up_codes, 16) || !aligned(sh->down_codes, 16))
+        return fail(Q4MOE_EALIGN, "shared expert codes not 16-byte aligned");
+    if (!aligned(sh->up_scales, 4) || !aligned(sh->down_scales, 4))
+        return fail(Q4MOE_EALIGN, "shared expert scales not 4-byte aligned");
+    if ((sh->up_gscale && !aligned(sh->up_gscale, 4)) || (sh->down_gscale && !aligned(sh->down_gscale, 4)))
+        return fail(Q4MOE_EALIGN, "shared expert gscale not 4-byte aligned");
     return Q4MOE_OK;
 }
 
@@ -701,29 +887,42 @@ q4moe_status check_shared(const q4moe_shared_fp8* sh, const q4moe_experts* ex, i
 // grouped: the grouped W4A16 path whatever the token count.
 q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
                          const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w,
-                         void* ws, size_t ws_bytes, void* stream, bool a4 = false, bool grouped = false) {
+                         void* ws, size_t ws_bytes, void* stream, bool a4 = false, bool force_grouped = false,
+                         const q4moe_experts* sh4 = nullptr) {
     q4moe_status st = check_router(r);
     if (st != Q4MOE_OK) return st;
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 65536) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 65536]", n_tok);
     if (sh && (st = check_shared(sh, ex, n_tok)) != Q4MOE_OK) return st;
-    grouped = grouped || (!a4 && w4a16_grouped(ex->fmt, n_tok));
-    if (grouped && (ex->hidden % 64 != 0 || ex->inter % 64 != 0))
-        return fail(Q4MOE_EUNSUPPORTED, "the grouped path (and more than %d tokens) needs hidden and inter "
-                    "multiples of 64 (got %d, %d)", kSmallT, ex->hidden, ex->inter);
+    if (sh4 && (st = check_shared_q4(sh4, ex)) != Q4MOE_OK) return st;
     if (a4 && ex->fmt != Q4MOE_NVFP4) return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode takes NVFP4 experts only");
     if (a4 && n_tok > kSmallT8)
         return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode runs up to %d tokens (n_tok = %d)", kSmallT8, n_tok);
+    if (a4 && sh && n_tok > kSmallT)
+        return fail(Q4MOE_EUNSUPPORTED, "the W4A4 decode with the shared expert runs up to %d tokens", kSmallT);
+    const DecodePlan plan = decode_plan(ex, n_tok, sh != nullptr, sh4 != nullptr, a4, force_grouped);
+    if (plan.grouped && (ex->hidden % 64 != 0 || ex->inter % 64 != 0))
+        return fail(Q4MOE_EUNSUPPORTED, "the grouped path (and more than %d tokens) needs hidden and inter "
+                    "multiples of 64 (got %d, %d)", kSmallT, ex->hidden, ex->inter);
+    if (plan.sh_grouped && ex->hidden % 64 != 0)
+        return fail(Q4MOE_EUNSUPPORTED, "the shared expert's grouped GEMMs need hidden a multiple of 64 (got %d)",
+                    ex->hidden);
     if (!x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "x / y is NULL");
     if (!aligned(x_bf16, 16) || !aligned(y_bf16, 16)) return fail(Q4MOE_EALIGN, "x / y not 16-byte aligned");
     if ((ids && !aligned(ids, 4)) || (w && !aligned(w, 4))) return fail(Q4MOE_EALIGN, "ids / w not 4-byte aligned");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh ? sh->inter : 0, a4, grouped);
+    const DecodeWs l = decode_layout(r, ex, sh, sh4, n_tok, a4, force_grouped);
     if ((st = check_ws(ws, ws_bytes, l.total)) != Q4MOE_OK) return st;
     if ((st = device_ready()) != Q4MOE_OK) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (grouped) return launch_grouped16(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, l, s);
+    const float* zsh = nullptr;
+    if (plan.sh_grouped) {
+        if ((st = launch_shared_grouped(shared_dense(sh, sh4), x_bf16, n_tok, ex->hidden, ws, l, s)) != Q4MOE_OK)
+            return st;
+        zsh = at<float>(ws, l.sh_z);
+    }
+    if (plan.grouped) return launch_grouped16(r, ex, x_bf16, n_tok, y_bf16, ids, w, ws, l, s, zsh);
 
-    if (n_tok == 1) {  // one persistent launch for the whole layer
+    if (n_tok == 1 && !plan.sh_grouped) {  // one persistent launch for the whole layer
         FusedArgs f;
         f.E = r->n_experts;
         f.H = ex->hidden;
@@ -787,8 +986,7 @@ q4moe_status decode_impl(const q4moe_router* r, const q4moe_experts* ex, const q
     }
 
     RouterArgs ra = router_args(r, x_bf16, n_tok, ws, l.r, ids, w, nullptr);
-    const float* zsh = nullptr;
-    if (sh) {  // the shared expert's own three launches first
+    if (sh && !plan.sh_grouped) {  // the shared expert's own three launches first
         SharedSmallArgs q;
         q.T = n_tok;
         q.H = ex->hidden;
@@ -894,7 +1092,7 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
 
 size_t q4moe_w4a16_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, false, true).total;
+    return decode_layout(r, ex, nullptr, nullptr, n_tok, false, true).total;
 }
 
 q4moe_status q4moe_w4a16_grouped(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
@@ -948,7 +1146,7 @@ q4moe_status q4moe_w4a16_decode_noalloc(const q4moe_router* r, const q4moe_exper
     if ((st = check_experts(ex, r)) != Q4MOE_OK) return st;
     if (n_tok < 1 || n_tok > 4) return fail(Q4MOE_EINVAL, "n_tok %d outside [1, 4]", n_tok);
     const size_t need =
-        decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, false, w4a16_grouped(ex->fmt, n_tok)).total;
+        decode_layout(r, ex, nullptr, nullptr, n_tok).total;
     if (need > kNoAllocScratchBytes)
         return fail(Q4MOE_EWORKSPACE, "this shape needs %zu bytes of scratch; the static scratch holds %zu", need,
                     kNoAllocScratchBytes);
@@ -960,7 +1158,7 @@ q4moe_status q4moe_w4a16_decode_noalloc(const q4moe_router* r, const q4moe_exper
 size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
                                           const q4moe_shared_fp8* sh, int32_t n_tok) {
     if (!r || !ex || !sh || n_tok < 1) return 0;
-    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter).total;
+    return decode_layout(r, ex, sh, nullptr, n_tok).total;
 }
 
 q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_experts* ex,
@@ -971,9 +1169,34 @@ q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_expert
     return decode_impl(r, ex, sh, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
 }
 
+size_t q4moe_w4a16_decode_shared_q4_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
+                                             const q4moe_experts* sh, int32_t n_tok) {
+    if (!r || !ex || !sh || n_tok < 1) return 0;
+    return decode_layout(r, ex, nullptr, sh, n_tok).total;
+}
+
+q4moe_status q4moe_w4a16_decode_shared_q4(const q4moe_router* r, const q4moe_experts* ex, const q4moe_experts* sh,
+                                          const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids,
+                                          float* w, void* ws, size_t ws_bytes, void* stream) {
+    if (!sh) return fail(Q4MOE_EINVAL, "shared expert descriptor is NULL");
+    return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream, false, false, sh);
+}
+
+q4moe_status q4moe_w4a16_decode_shared_q4_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                               const q4moe_experts* sh, int32_t n_tok, q4moe_shared_taps* out) {
+    if (!r || !ex || !sh || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
+    DecodeWs l = decode_layout(r, ex, nullptr, sh, n_tok);
+    out->y32 = l.y32;
+    out->h = l.h;
+    out->xq = 0;
+    out->sh_h32 = l.sh_h;
+    out->sh_hq = 0;
+    return Q4MOE_OK;
+}
+
 size_t q4moe_w4a4_decode_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, true).total;
+    return decode_layout(r, ex, nullptr, nullptr, n_tok, true).total;
 }
 
 q4moe_status q4moe_w4a4_decode(const q4moe_router* r, const q4moe_experts* ex, const uint16_t* x_bf16,
@@ -985,7 +1208,7 @@ q4moe_status q4moe_w4a4_decode(const q4moe_router* r, const q4moe_experts* ex, c
 q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok,
                                     q4moe_w4a4_token_taps* out) {
     if (!r || !ex || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, 0, true);
+    DecodeWs l = decode_layout(r, ex, nullptr, nullptr, n_tok, true);
     out->y32 = l.y32;
     out->h32 = l.h;
     out->xq_codes = l.xq_c;
@@ -998,7 +1221,7 @@ q4moe_status q4moe_w4a4_decode_taps(const q4moe_router* r, const q4moe_experts* 
 size_t q4moe_w4a4_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
                                          const q4moe_shared_fp8* sh, int32_t n_tok) {
     if (!r || !ex || !sh || n_tok < 1) return 0;
-    return decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter, true).total;
+    return decode_layout(r, ex, sh, nullptr, n_tok, true).total;
 }
 
 q4moe_status q4moe_w4a4_decode_shared(const q4moe_router* r, const q4moe_experts* ex, const q4moe_shared_fp8* sh,
@@ -1011,7 +1234,7 @@ q4moe_status q4moe_w4a4_decode_shared(const q4moe_router* r, const q4moe_experts
 q4moe_status q4moe_w4a4_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                            const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_w4a4_shared_taps* out) {
     if (!r || !ex || !sh || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter, true);
+    DecodeWs l = decode_layout(r, ex, sh, nullptr, n_tok, true);
     out->y32 = l.y32;
     out->h32 = l.h;
     out->xq_codes = l.xq_c;
@@ -1068,7 +1291,7 @@ q4moe_status q4moe_quantize_weights(const uint16_t* w_bf16, int32_t rows, int32_
 
 size_t q4moe_w4a4_moe_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {
     if (!r || !ex || n_tok < 1) return 0;
-    const size_t small = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, 1, 0, true).total;
+    const size_t small = decode_layout(r, ex, nullptr, nullptr, 1, true).total;
     const size_t grouped = w4a4_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok).total;
     return std::max(small, grouped);
 }
@@ -1099,7 +1322,7 @@ q4moe_status q4moe_w4a4_moe(const q4moe_router* r, const q4moe_experts* ex, cons
 q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                             const q4moe_shared_fp8* sh, int32_t n_tok, q4moe_shared_taps* out) {
     if (!r || !ex || !sh || !out || n_tok < 1) return fail(Q4MOE_EINVAL, "NULL descriptor or n_tok < 1");
-    DecodeWs l = decode_ws(r->n_experts, ex->hidden, ex->inter, r->top_k, n_tok, sh->inter);
+    DecodeWs l = decode_layout(r, ex, sh, nullptr, n_tok);
     out->y32 = l.y32;
     out->h = l.h;
     out->xq = l.sh_xq;

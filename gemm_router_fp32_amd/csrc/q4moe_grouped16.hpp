@@ -29,6 +29,7 @@
 //  - the epilogue undoes every power of two exactly.
 #pragma once
 
+#include "q4moe_fused.hpp"
 #include "q4moe_w4a4.hpp"
 
 namespace q4moe {
@@ -38,10 +39,12 @@ namespace q4moe {
 // ---------------------------------------------------------------------------
 struct StageArgs {
     int cols;
-    const uint16_t* xb;  // bf16 rows (k_stage_x16)
-    const float* hf;     // fp32 rows (k_stage_h16)
-    _Float16* out;       // x: [rows][cols]; h: [2 rows][cols], hi then lo of each row
-    int32_t* exps;       // [rows]: the power of two each row was scaled by
+    const uint16_t* xb;  // bf16 rows (k_stage_x16, k_stage_fp8<true>)
+    const float* hf;     // fp32 rows (k_stage_h16, k_stage_fp8<false>)
+    _Float16* out;       // x: [rows][cols]; h: [2 rows][cols], hi then lo of each row (FP8: [rows][cols])
+    int32_t* exps;       // [rows]: the power of two each row was scaled by (FP8: 0)
+    float iscale;        // FP8: the static input scale
+    uint8_t* codes;      // FP8: the E4M3FN codes [rows][cols] (nullable tap)
 };
 
 // Largest of the 256 threads' values, returned to every thread.
@@ -122,33 +125,87 @@ __global__ __launch_bounds__(256) void k_stage_h16(StageArgs a) {
     }
 }
 
+// FP8 per-tensor activation coding (the shared expert's W8A8 form): each
+// value v becomes the E4M3FN code of fl32(v / iscale) (nearest-even,
+// saturating at 448, sign kept), staged as its exact fp16 value; one
+// workgroup per row, 8 values per thread and pass.
+template <bool BF16_IN>
+__global__ __launch_bounds__(256) void k_stage_fp8(StageArgs a) {
+    typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+    const int r = blockIdx.x, per = a.cols / 8;
+    if (threadIdx.x == 0) a.exps[r] = 0;
+    for (int p = threadIdx.x; p < per; p += 256) {
+        float v[8];
+        if constexpr (BF16_IN) {
+            const uint4 q = *reinterpret_cast<const uint4*>(a.xb + (size_t)r * a.cols + 8 * p);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                v[2 * d] = bf16_bits_to_f32(w[d] & 0xffffu);
+                v[2 * d + 1] = bf16_bits_to_f32(w[d] >> 16);
+            }
+        } else {
+            const float4 q0 = *reinterpret_cast<const float4*>(a.hf + (size_t)r * a.cols + 8 * p);
+            const float4 q1 = *reinterpret_cast<const float4*>(a.hf + (size_t)r * a.cols + 8 * p + 4);
+            v[0] = q0.x; v[1] = q0.y; v[2] = q0.z; v[3] = q0.w;
+            v[4] = q1.x; v[5] = q1.y; v[6] = q1.z; v[7] = q1.w;
+        }
+        h8 hv;
+        uint32_t cw[2] = {0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const uint32_t c = fp8_act_code(v[k], a.iscale);
+            hv[k] = (_Float16)e4m3fn_to_f32(c);
+            cw[k >> 2] |= c << (8 * (k & 3));
+        }
+        *reinterpret_cast<h8*>(a.out + (size_t)r * a.cols + 8 * p) = hv;
+        if (a.codes) *reinterpret_cast<uint2*>(a.codes + (size_t)r * a.cols + 8 * p) = make_uint2(cw[0], cw[1]);
+    }
+}
+
+// A dense layer as a one-expert dispatch: every token is a row of expert 0
+// with gate 1 (the shared expert through the grouped GEMMs).
+__global__ __launch_bounds__(256) void k_dispatch_all(int T, int4* act, int32_t* n_act, int32_t* perm, float* gate) {
+    const int t = blockIdx.x * 256 + threadIdx.x;
+    if (t == 0) {
+        act[0] = make_int4(0, 0, T, 0);
+        n_act[0] = 1;
+    }
+    if (t < T) {
+        perm[t] = t;
+        gate[t] = 1.0f;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Grouped GEMM with fp16 activations: for expert e and a 128-column output
 // tile, out[pair][n] = epi(sum_k A[row][k] W_e[n][k]).  Workgroup: 4 waves,
 // wave w owns columns 32w..32w+31 (lane l: column l % 32, k half l / 32 of
 // each 256-wide chunk) and one 32-row A tile (v_mfma_f32_32x32x16_f16), in
-// M-tiles over the expert's rows: 32 tokens per tile for the up GEMM, 16
-// pairs (32 hi/lo rows) for the down GEMM.
+// M-tiles over the expert's rows: 32 rows per tile, or 16 pairs (32 hi/lo
+// rows) for the down GEMM of the 16-bit path.
 //
 // Weights stream straight into registers, two chunks ahead in a three-slot
-// ring (every weight row contributes one 128-byte line per chunk); the A
-// pieces (64 bytes of a row per thread and chunk) ride a ring of their own
-// and are copied into LDS once per workgroup.  MFMA step j (0..15) of a chunk
-// sums k 8j..8j+7 (lanes 0..31) and 128+8j..+7 (lanes 32..63) of both
-// operands.  int4 codes unpack as the pairs (e0,e4), (e1,e5), (e2,e6),
+// ring (every weight row contributes one 128-byte line per chunk, two for
+// FP8); the A pieces (64 bytes of a row per thread and chunk) ride a ring of
+// their own and are copied into LDS once per workgroup.  MFMA step j (0..15)
+// of a chunk sums k 8j..8j+7 (lanes 0..31) and 128+8j..+7 (lanes 32..63) of
+// both operands.  int4 codes unpack as the pairs (e0,e4), (e1,e5), (e2,e6),
 // (e3,e7) of each 8-code dword, so the A pieces are stored in that order.
 // The block scales of the workgroup's 128 weight rows are copied into LDS
-// once.  Loads past the end of a row (last chunk, and the prefetches of the
-// last two chunks) reread the row's last bytes and are given scale 0 (B) or
-// zeroed (A).  Workgroups map to the experts that have rows (the dispatch's
-// list), expert-major on the XCDs; the rest exit at once.
+// once (FP8 has one scale per tensor).  Loads past the end of a row (last
+// chunk, and the prefetches of the last two chunks) reread the row's last
+// bytes and are given scale 0 (B) or zeroed (A).  Workgroups map to the
+// experts that have rows (the dispatch's list), expert-major on the XCDs;
+// the rest exit at once.
 // ---------------------------------------------------------------------------
 struct GemmA16Args {
     int N, Kd, K;              // output columns (rows of W_e), reduction length, top-k
-    const uint8_t* wc;         // W codes [E][N][Kd/2]
+    const uint8_t* wc;         // W codes [E][N][Kd/2] (FP8: [E][N][Kd])
     const uint8_t* wsc;        // W scales: E4M3 [E][N][Kd/16] (NVFP4) or bf16 [E][N][Kd/64] (int4)
-    const float* wg;           // NVFP4 per-expert fp32 scale [E]; unused for int4
-    const _Float16* a16;       // A rows: x [T][Kd] (up) or h hi/lo [2 T K][Kd] (down)
+    const float* wg;           // NVFP4 per-expert fp32 scale [E]
+    float gs;                  // FP8: the weight scale times the input scale
+    const _Float16* a16;       // A rows: x [T][Kd] (up) or h [T K][Kd] (down; hi/lo [2 T K][Kd] but FP8)
     const int32_t* aexp;       // power of two of each staged row: [T] (up) or [T K] (down)
     const int4* act;           // experts with rows: (e, first dispatch row, rows, 0)
     const int32_t* n_act;      // their number
@@ -175,28 +232,48 @@ __device__ __forceinline__ f16x8 int4x8_f16(uint32_t w, f16x2 s) {
     return f16x8{p[0].x, p[0].y, p[1].x, p[1].y, p[2].x, p[2].y, p[3].x, p[3].y};
 }
 
+// Eight E4M3FN bytes (two dwords, natural order) as fp16, exact.
+__device__ __forceinline__ f16x8 fp8x8_f16(uint32_t w0, uint32_t w1) {
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return f16x8{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+template <int NP>
+struct BChunkN {
+    uint4 q[NP];
+};
+
 template <int EPI, int WF, typename F>
 __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0, int mv,
                                          _Float16 (*As)[kApitch], F&& after_first_issue) {
+    // HILO: the A rows come in hi/lo pairs (the 16-bit path's h); FP8
+    // weights: 16-byte pieces of 16 values, 8 per lane and chunk
+    constexpr bool HILO = EPI == EPI_DOWN && WF != FMT_FP8;
+    constexpr bool F8 = WF == FMT_FP8;
+    constexpr int NP = F8 ? 8 : 4, KPP = F8 ? 16 : 32;
     const int lane = threadIdx.x & 63;
+    const uint32_t row_bytes = F8 ? (uint32_t)a.Kd : (uint32_t)(a.Kd / 2);
     // the A row this thread stages (rows past the tile's last repeat it)
-    const int dr = x.row0 + m0 + min(EPI == EPI_UP ? x.ar : (x.ar >> 1), mv - 1);
+    const int dr = x.row0 + m0 + min(HILO ? (x.ar >> 1) : x.ar, mv - 1);
     const int pr = a.perm[dr];
     // weight pieces of chunk c (this lane's half), in the B ring
-    auto valid_pieces = [&](int c) { return min(4, max(0, (a.Kd - c * kGemmBK - 128 * x.hk) / 32)); };
-    auto load_b = [&](int c, BChunk& b) {
+    auto valid_pieces = [&](int c) { return min(NP, max(0, (a.Kd - c * kGemmBK - 128 * x.hk) / KPP)); };
+    auto load_b = [&](int c, BChunkN<NP>& b) {
         const int v = valid_pieces(c);
-        const uint32_t c_last = x.wc_off + a.Kd / 2 - 16;
-        const uint32_t base = x.wc_off + c * (kGemmBK / 2) + 64 * x.hk;
+        const uint32_t c_last = x.wc_off + row_bytes - 16;
+        const uint32_t base = x.wc_off + (uint32_t)c * (F8 ? kGemmBK : kGemmBK / 2) + (F8 ? 128 : 64) * x.hk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) b.q[i] = ldg16(a.wc + (i < v ? base + 16 * i : c_last));
+        for (int i = 0; i < NP; ++i) b.q[i] = ldg16(a.wc + (i < v ? base + 16 * i : c_last));
     };
-    BChunk bb[3];
+    BChunkN<NP> bb[3];
     load_b(0, bb[0]);
     __builtin_amdgcn_sched_barrier(0);
     load_b(1, bb[1]);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t arow = EPI == EPI_UP ? (uint32_t)(pr / a.K) : (uint32_t)(2 * pr + (x.ar & 1));
+    const uint32_t arow = EPI == EPI_UP ? (uint32_t)(pr / a.K) : HILO ? (uint32_t)(2 * pr + (x.ar & 1)) : (uint32_t)pr;
     const _Float16* asrc = a.a16 + (size_t)arow * a.Kd;
     uint4 qa[3][4];
     auto load_a = [&](int c, uint4 (&q)[4]) {
@@ -215,7 +292,7 @@ __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 
-    auto step = [&](const int c, const BChunk& bc, BChunk& bn, const uint4 (&qc)[4], uint4 (&qn)[4]) {
+    auto step = [&](const int c, const BChunkN<NP>& bc, BChunkN<NP>& bn, const uint4 (&qc)[4], uint4 (&qn)[4]) {
         __syncthreads();  // every wave is done with the last chunk's A
         const bool a_ok = c * kGemmBK + 32 * x.ap < a.Kd;
 #pragma unroll
@@ -245,7 +322,7 @@ __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0
             sc[1] = e4m3x2_f16<true>(s0);
             sc[2] = e4m3x2_f16<false>(s1);
             sc[3] = e4m3x2_f16<true>(s1);
-        } else {
+        } else if constexpr (WF == FMT_INT4) {
             // groups 4c + 2hk and 4c + 2hk + 1 (pieces 0-1 and 2-3)
             const int grp = 4 * c + 2 * x.hk;
             const uint16_t* srow = reinterpret_cast<const uint16_t*>(g_gemm_sct + x.sc_row);
@@ -254,12 +331,19 @@ __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0
             sc[0] = sc[1] = f16x2{g0, g0};
             sc[2] = sc[3] = f16x2{g1, g1};
         }
+        if constexpr (!F8) {
 #pragma unroll
-        for (int pc = 0; pc < 4; ++pc)
-            if (pc >= valid) sc[pc] = f16x2{0, 0};
-        const uint32_t w[16] = {bc.q[0].x, bc.q[0].y, bc.q[0].z, bc.q[0].w, bc.q[1].x, bc.q[1].y,
-                                bc.q[1].z, bc.q[1].w, bc.q[2].x, bc.q[2].y, bc.q[2].z, bc.q[2].w,
-                                bc.q[3].x, bc.q[3].y, bc.q[3].z, bc.q[3].w};
+            for (int pc = 0; pc < 4; ++pc)
+                if (pc >= valid) sc[pc] = f16x2{0, 0};
+        }
+        uint32_t w[4 * NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+            w[4 * i] = bc.q[i].x;
+            w[4 * i + 1] = bc.q[i].y;
+            w[4 * i + 2] = bc.q[i].z;
+            w[4 * i + 3] = bc.q[i].w;
+        }
         const _Float16* arow_l = &As[lane & 31][0];
         f16x8 af[2];
         af[0] = *reinterpret_cast<const f16x8*>(arow_l + a_col(16 * x.hk));
@@ -271,8 +355,12 @@ __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0
                 // dword j: k 8j..8j+7 of the lane's half, block j / 2, piece j / 4
                 const f16x2 sp = sc[j / 4];
                 bfrag = fp4x8_f16(w[j], (j & 2) ? f16x2{sp.y, sp.y} : f16x2{sp.x, sp.x});
-            } else {
+            } else if constexpr (WF == FMT_INT4) {
                 bfrag = int4x8_f16(w[j], sc[j / 4]);
+            } else {
+                // dwords 2j, 2j + 1: k 8j..8j+7 of the lane's half, piece j / 2
+                bfrag = fp8x8_f16(w[2 * j], w[2 * j + 1]);
+                if (j / 2 >= valid) bfrag = f16x8{0, 0, 0, 0, 0, 0, 0, 0};
             }
             acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1], bfrag, acc, 0, 0, 0);
         }
@@ -298,7 +386,7 @@ __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0
                 a.out[(size_t)p * a.N + x.n] = u * u;
             }
         }
-    } else {
+    } else if constexpr (HILO) {
         // rows 2j (hi) and 2j + 1 (lo) of pair j sit in registers r and r + 1
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
@@ -307,6 +395,15 @@ __device__ __forceinline__ void a16_tile(const GemmA16Args& a, A16Ctx& x, int m0
                 const int p = a.perm[x.row0 + m0 + j];
                 const float z = acc[r] + acc[r + 1];
                 a.out[(size_t)p * a.N + x.n] = ldexpf(z, -(x.sigma + a.aexp[p])) * (a.gate[p] * x.g);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+            if (m < mv) {
+                const int p = a.perm[x.row0 + m0 + m];
+                a.out[(size_t)p * a.N + x.n] = ldexpf(acc[r], -(x.sigma + a.aexp[p])) * (a.gate[p] * x.g);
             }
         }
     }
@@ -333,10 +430,10 @@ __global__ __launch_bounds__(256, 2) void k_grouped_a16(GemmA16Args a) {
     x.n_e = ae.z;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     // this tile's block scales (contiguous rows), one dword per thread and pass
-    const int rb = WF == FMT_NVFP4 ? a.Kd / 16 : a.Kd / 32;  // scale bytes per weight row
+    const int rb = WF == FMT_NVFP4 ? a.Kd / 16 : WF == FMT_INT4 ? a.Kd / 32 : 0;  // scale bytes per weight row
     const int sc_ndw = min(kGemmBN, a.N - tile * kGemmBN) * rb / 4;
     uint32_t scv[32];
-    {
+    if constexpr (WF != FMT_FP8) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(a.wsc + ((uint32_t)e * a.N + tile * kGemmBN) * (uint32_t)rb);
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
@@ -347,19 +444,21 @@ __global__ __launch_bounds__(256, 2) void k_grouped_a16(GemmA16Args a) {
     x.hk = lane >> 5;
     x.nch = (a.Kd + kGemmBK - 1) / kGemmBK;
     x.n = tile * kGemmBN + 32 * wave + (lane & 31);
-    x.wc_off = ((uint32_t)e * a.N + min(x.n, a.N - 1)) * (uint32_t)(a.Kd / 2);
+    x.wc_off = ((uint32_t)e * a.N + min(x.n, a.N - 1)) * (uint32_t)(WF == FMT_FP8 ? a.Kd : a.Kd / 2);
     x.sc_row = (uint32_t)((32 * wave + (lane & 31)) * rb);
-    x.g = WF == FMT_NVFP4 ? a.wg[e] : 1.0f;
+    x.g = WF == FMT_NVFP4 ? a.wg[e] : WF == FMT_INT4 ? 1.0f : a.gs;
     x.sigma = 0;
     x.ap = threadIdx.x & 7;
     x.ar = threadIdx.x >> 3;
-    const int step = EPI == EPI_UP ? 32 : 16;
+    const int step = (EPI == EPI_DOWN && WF != FMT_FP8) ? 16 : 32;
     // the first M-tile's first loads leave before the scales are stored
     auto scales_in = [&] {
+        if constexpr (WF != FMT_FP8) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int d = (int)threadIdx.x + 256 * i;
-            if (d < sc_ndw) reinterpret_cast<uint32_t*>(g_gemm_sct)[d] = scv[i];
+            for (int i = 0; i < 32; ++i) {
+                const int d = (int)threadIdx.x + 256 * i;
+                if (d < sc_ndw) reinterpret_cast<uint32_t*>(g_gemm_sct)[d] = scv[i];
+            }
         }
         if constexpr (WF == FMT_INT4) {
             __syncthreads();

@@ -13,7 +13,7 @@
 
 namespace q4moe {
 
-enum : int { FMT_NVFP4 = 1, FMT_INT4 = 2 };
+enum : int { FMT_NVFP4 = 1, FMT_INT4 = 2, FMT_FP8 = 3 };
 
 // Control words at the start of every workspace.
 enum : int { CTRL_TICKET = 0, CTRL_FLAGS = 1, CTRL_WORDS = 1024 };

@@ -97,6 +97,9 @@ _SIGS = {
     "q4moe_w4a16_decode_shared_ws_bytes": (_sz, [_p, _p, _p, _i32]),
     "q4moe_w4a16_decode_shared": (_i32, [_p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_decode_shared_taps": (_i32, [_p, _p, _p, _i32, _p]),
+    "q4moe_w4a16_decode_shared_q4_ws_bytes": (_sz, [_p, _p, _p, _i32]),
+    "q4moe_w4a16_decode_shared_q4": (_i32, [_p, _p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
+    "q4moe_w4a16_decode_shared_q4_taps": (_i32, [_p, _p, _p, _i32, _p]),
     "q4moe_w4a4_grouped_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a4_grouped": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_grouped_taps": (_i32, [_p, _p, _i32, _p]),
@@ -348,6 +351,29 @@ def q4moe_w4a16_decode_shared(router, experts, shared, x, y, ids=None, w=None, w
     _check(lib().q4moe_w4a16_decode_shared(ctypes.byref(router.s), ctypes.byref(experts.s), ctypes.byref(shared.s),
                                            _ptr(x), n_tok, _ptr(y), _ptr(ids), _ptr(w), _ptr(ws), ws.numel(),
                                            _stream(stream)))
+    return ws
+
+
+def q4moe_w4a16_decode_shared_q4_ws_bytes(router, experts, shared, n_tok):
+    return lib().q4moe_w4a16_decode_shared_q4_ws_bytes(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                                       ctypes.byref(shared.s), n_tok)
+
+
+def q4moe_w4a16_decode_shared_q4_taps(router, experts, shared, n_tok):
+    t = SharedTaps()
+    _check(lib().q4moe_w4a16_decode_shared_q4_taps(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                                   ctypes.byref(shared.s), n_tok, ctypes.byref(t)))
+    return t
+
+
+def q4moe_w4a16_decode_shared_q4(router, experts, shared, x, y, ids=None, w=None, ws=None, stream=None):
+    """q4moe_w4a16_decode plus a 4-bit shared expert (an Experts bank of one expert)."""
+    n_tok = x.shape[0]
+    if ws is None:
+        ws = workspace(q4moe_w4a16_decode_shared_q4_ws_bytes(router, experts, shared, n_tok), x.device)
+    _check(lib().q4moe_w4a16_decode_shared_q4(ctypes.byref(router.s), ctypes.byref(experts.s),
+                                              ctypes.byref(shared.s), _ptr(x), n_tok, _ptr(y), _ptr(ids), _ptr(w),
+                                              _ptr(ws), ws.numel(), _stream(stream)))
     return ws
 
 

@@ -212,19 +212,40 @@ typedef struct {
     float up_wscale, up_iscale, down_wscale, down_iscale;
 } q4moe_shared_fp8;
 
-/* q4moe_w4a16_decode plus the shared expert: y = sum_i w_i z_i + z_shared,
- * rounded once to bf16.  NVFP4 routed experts and 1 <= n_tok <= 4, else
- * Q4MOE_EUNSUPPORTED.  One token: the same single launch, whose shared
- * weights are read while the router runs (EUNSUPPORTED where that launch
- * does not fit the device); 2-4 tokens: three launches for the shared expert
- * (each weight row read once for all tokens) before the small-batch routed
- * kernels, whose combine adds its output. */
+/* q4moe_w4a16_decode plus the FP8 shared expert: y = sum_i w_i z_i +
+ * z_shared, rounded once to bf16; 1 <= n_tok <= 65536, NVFP4 or int4-g64
+ * routed experts.  NVFP4 routed experts, one token: the same single launch,
+ * whose shared weights are read while the router runs; 2-4 tokens: three
+ * launches for the shared expert (each weight row read once for all tokens)
+ * before the small-batch routed kernels, whose combine adds its output.
+ * Otherwise (more tokens, or int4 routed experts): the shared expert through
+ * the grouped GEMMs as a one-expert dispatch of every token (E4M3FN weights
+ * and activation codes decode exactly to fp16 for the MFMA), beside the
+ * routed experts' grouped path (hidden and inter multiples of 64, else
+ * Q4MOE_EUNSUPPORTED). */
 size_t q4moe_w4a16_decode_shared_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
                                           const q4moe_shared_fp8* sh, int32_t n_tok);
 q4moe_status q4moe_w4a16_decode_shared(const q4moe_router* r, const q4moe_experts* ex,
                                        const q4moe_shared_fp8* sh, const uint16_t* x_bf16,
                                        int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w,
                                        void* ws, size_t ws_bytes, void* stream);
+
+/* The int4 checkpoint's form ([G] What was changed: the shared expert is
+ * int4 group 64, weight-only, like the routed experts; an NVFP4 W4A16
+ * checkpoint's shared expert is NVFP4): q4moe_w4a16_decode plus a 4-bit
+ * W4A16 shared expert, y = sum_i w_i z_i + z_shared rounded once; sh is a
+ * bank of one expert (n_experts = 1, hidden equal to the routed experts',
+ * inter a multiple of 64 up to 4096, NVFP4 or INT4_G64, its own format).
+ * The shared expert runs through the grouped GEMMs as a one-expert dispatch
+ * of every token (x staged exactly, h as fp16 hi + lo); the routed experts
+ * take the small-batch kernels (NVFP4, up to 4 tokens) or the grouped path
+ * (hidden and inter multiples of 64, else Q4MOE_EUNSUPPORTED).  Taps as in
+ * q4moe_shared_taps: y32, h and sh_h32 (xq and sh_hq are 0: no codes). */
+size_t q4moe_w4a16_decode_shared_q4_ws_bytes(const q4moe_router* r, const q4moe_experts* ex,
+                                             const q4moe_experts* sh, int32_t n_tok);
+q4moe_status q4moe_w4a16_decode_shared_q4(const q4moe_router* r, const q4moe_experts* ex, const q4moe_experts* sh,
+                                          const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16, int32_t* ids,
+                                          float* w, void* ws, size_t ws_bytes, void* stream);
 
 /* Byte offsets of the values q4moe_w4a16_decode_shared leaves in its
  * workspace: y32 and h as in q4moe_decode_taps; xq uint8 [n_tok][hidden] (x
@@ -234,6 +255,8 @@ typedef struct { size_t y32, h, xq, sh_h32, sh_hq; } q4moe_shared_taps;
 q4moe_status q4moe_w4a16_decode_shared_taps(const q4moe_router* r, const q4moe_experts* ex,
                                             const q4moe_shared_fp8* sh, int32_t n_tok,
                                             q4moe_shared_taps* out);
+q4moe_status q4moe_w4a16_decode_shared_q4_taps(const q4moe_router* r, const q4moe_experts* ex,
+                                               const q4moe_experts* sh, int32_t n_tok, q4moe_shared_taps* out);
 
 /* W4A4 routed-MoE decode of 1 <= n_tok <= 8 tokens ([W] Step 3: the
  * routed experts take 4-bit weights and activations; the MTP drafter's

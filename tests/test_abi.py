@@ -144,8 +144,13 @@ def test_decode_shared_validation(L):
     assert _decode_sh(L, r, ex, _shared(dn=A16 + 8)) == g.EALIGN
     assert _decode_sh(L, r, ex, _shared(sc=(1.0, 0.0, 1.0, 1.0))) == g.EINVAL
     assert _decode_sh(L, r, ex, _shared(sc=(1.0, 1.0, float("inf"), 1.0))) == g.EINVAL
-    assert _decode_sh(L, r, ex, _shared(), T=5) == g.EUNSUPPORTED
-    assert _decode_sh(L, r, _experts(fmt=2), _shared()) == g.EUNSUPPORTED
+    # more than 4 tokens (or int4 routed experts): the grouped GEMMs, hidden and inter multiples of 64
+    assert _decode_sh(L, r, _experts(I=1856 + 32), _shared(), T=5) == g.EUNSUPPORTED
+    need5 = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(_shared()), 5)
+    assert _decode_sh(L, r, ex, _shared(), T=5, wsb=need5 - 1) == g.EWORKSPACE
+    need_i4 = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(_experts(fmt=2)),
+                                                   ctypes.byref(_shared()), 1)
+    assert _decode_sh(L, r, _experts(fmt=2), _shared(), wsb=need_i4 - 1) == g.EWORKSPACE
     sh = _shared()
     need = L.q4moe_w4a16_decode_shared_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh), 1)
     plain = L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
@@ -236,3 +241,31 @@ def test_fp8_gemv_validation(L):
     off = ctypes.c_size_t(0)
     assert L.q4moe_fp8_gemv_taps(ctypes.byref(mat()), 4, ctypes.byref(off)) == g.OK
     assert 0 < off.value and off.value + 4 * 2688 <= need
+
+
+def test_decode_shared_q4_validation(L):
+    # the 4-bit shared expert is a bank of one expert; every call here fails
+    # validation, so nothing reaches a device
+    r, ex = _router(), _experts()
+
+    def sh4(fmt=2, E=1, H=2688, S=3712, gs=A16):
+        return g.ExpertsS(fmt, E, H, S, A16, A16, gs if fmt == 1 else None, A16, A16, gs if fmt == 1 else None)
+
+    def call(ex_, sh_, T=1, wsb=1 << 30):
+        shp = None if sh_ is None else ctypes.byref(sh_)
+        return L.q4moe_w4a16_decode_shared_q4(ctypes.byref(r), ctypes.byref(ex_), shp, A16, T, A16, None, None, A16,
+                                              wsb, None)
+
+    assert call(ex, None) == g.EINVAL
+    assert call(ex, sh4(E=2)) == g.EINVAL
+    assert call(ex, sh4(H=2560)) == g.EINVAL
+    assert call(ex, sh4(S=3700)) == g.EINVAL
+    assert call(ex, sh4(fmt=7)) == g.EINVAL
+    assert call(ex, g.ExpertsS(2, 1, 2688, 3712, A16, A16, A16, A16, A16, None)) == g.EINVAL  # int4 takes no gscale
+    need = L.q4moe_w4a16_decode_shared_q4_ws_bytes(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh4()), 1)
+    assert need > L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+    assert call(ex, sh4(), wsb=need - 1) == g.EWORKSPACE
+    t = g.SharedTaps()
+    assert L.q4moe_w4a16_decode_shared_q4_taps(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh4()), 4,
+                                               ctypes.byref(t)) == g.OK
+    assert t.xq == 0 and t.sh_hq == 0 and 0 < t.sh_h32 and 0 < t.y32

@@ -156,7 +156,7 @@ def check_shared_multi(L, sh, out):
     r = L["route"]
     assert np.array_equal(out["ids"], r["ids"])
     np.testing.assert_allclose(out["w"], r["w"], rtol=1e-5)
-    ob = oracle.Bank.from_dict(oracle.NVFP4, L["bank"])
+    ob = oracle.Bank.from_dict(oracle.NVFP4 if L.get("fmt", "nvfp4") == "nvfp4" else oracle.INT4_G64, L["bank"])
     yr, _ = oracle.moe_w4a16(ob, L["x"], r["ids"], r["w"])
     worst = 0.0
     for t in range(L["x"].shape[0]):
