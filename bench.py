@@ -31,7 +31,9 @@ S_SHARED = 3712  # shared expert intermediate size (2 x 1856; derived from the c
 SEED = 20261202
 PEAK_HBM_GBS = 8000.0
 PEAK_F16_TFLOPS = 2500.0   # dense fp16/bf16 MFMA
-TRAFFIC_PROFILE = "profiles/traffic_all_kernels_bench.md"
+TRAFFIC_PROFILE = "profiles/traffic_k_decode_fused_nvfp4_stack.md"
+PHASE_PROFILE = "profiles/k_decode_fused_phase_timeline_nvfp4_stack.md"
+MFMA_PROFILE = "profiles/k_grouped_gemm_mfma_counters_w4a4_1024.md"
 METRIC = "µs per routed-MoE layer at batch 1 + achieved HBM GB/s (% of MI355X peak)"
 
 
@@ -60,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the oracle CPU sample")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only-stack", action="store_true", help="time the NVFP4 decode stack only")
+    ap.add_argument("--only-w4a4-chunk", action="store_true",
+                    help="run the W4A4 1024-token chunk only (for counter passes); prints its dict")
     return ap.parse_args()
 
 
@@ -240,6 +244,10 @@ def bench_w4a4(torch, g, synth, steps):
     return {"us": round(ms * 1e3, 2), "hbm_gbps": round(byts / (ms * 1e-3) / 1e9, 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "mfma_frac_of_fp16_peak": round(flops / (ms * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
+            # MFMA pipe busy (counters, the committed profile of the grouped GEMMs)
+            "mfma_busy_frac_counters": read_profile_value(os.path.join(ROOT, MFMA_PROFILE), "mfma_busy_frac",
+                                                          ("csrc/q4moe_w4a4.hpp", "csrc/q4moe_device.hpp",
+                                                           "csrc/q4moe_kernels.hpp")),
             "us_spread": spread(per), "bytes": byts, "flop": flops, "tokens": T}
 
 
@@ -407,11 +415,27 @@ def bench_mid_batch(torch, g, synth, steps, fmt, layer=None):
     return out
 
 
-def cpu_baseline(seconds):
+def cpu_model():
+    """The host CPU's model name and the cores this process may use."""
+    name = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                name = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return name, len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(seconds, threads=None):
     """The oracle, as it stands, on layers of the NVFP4 stack until `seconds`
-    of CPU work have run; returns microseconds per layer."""
+    of CPU work have run (with `threads` OpenMP threads, default: all);
+    returns microseconds per layer, layers run and threads used."""
     import oracle
     import synth
+    if threads is not None:
+        oracle.set_threads(threads)
     done, t_total = 0, 0.0
     for li in range(LAYERS):
         wg, b = synth.router(SEED, synth.FAM_NVFP4, li, E, H)
@@ -430,6 +454,22 @@ def cpu_baseline(seconds):
     return 1e6 * t_total / done, done, oracle.threads()
 
 
+def read_profile_value(path, key, sources=None):
+    """A `key=value` line of a committed profile summary, with the kernel
+    source hash it was measured on (None once the sources have changed)."""
+    from gemm_router_fp32_amd.pmc_traffic import KERNEL_SOURCES, source_sha256
+    if not os.path.exists(path):
+        return None
+    val, sha = None, None
+    for line in open(path):
+        line = line.strip().strip("`")
+        if line.startswith(key + "="):
+            val = float(line.split("=", 1)[1])
+        if line.startswith("source_sha256="):
+            sha = line.split("=", 1)[1]
+    return val if (val is not None and sha == source_sha256(sources or KERNEL_SOURCES)) else None
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -442,6 +482,11 @@ def main():
 
     torch.cuda.set_device(0)
     g.lib()
+    if args.only_w4a4_chunk:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        torch.empty_like(src).copy_(src)  # the copy that calibrates the traffic counters
+        print(json.dumps(bench_w4a4(torch, g, synth, args.steps)), flush=True)
+        return
     # a plain copy of known size (256 MiB), to scale HBM traffic counters
     src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
     dst = torch.empty_like(src)
@@ -455,6 +500,10 @@ def main():
     gbs = bytes_layer / (us_layer * 1e-6) / 1e9
     log(f"nvfp4 stack: {ms_step:.4f} ms/step, {us_layer:.3f} us/layer, {gbs:.1f} GB/s; "
         f"single direct launch {ms_kernel * 1e3:.2f} us; flags {flags}")
+    # one layer alone, cold: 1 GiB read before each rep evicts the MALL and L2s
+    t_cold = Timer(torch).each(lambda: decode_call(g, layers[0]), max(10, args.steps // 2), Evictor(torch))
+    single_cold_us = float(np.median(t_cold)) * 1e3
+    log(f"single layer, evicted, direct launch: {single_cold_us:.2f} us")
 
     extra = {}
     if not args.only_stack:
@@ -524,9 +573,13 @@ def main():
 
     cpu = None
     if not args.skip_cpu:
+        model, avail = cpu_model()
         us_cpu, n, threads = cpu_baseline(args.cpu_seconds)
+        us_1, n_1, _ = cpu_baseline(args.cpu_seconds / 2, threads=1)
         cpu = {"value": round(us_cpu, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
-               "sample": f"{n} of the 23 layers, 1 token each (router + 6 experts), fp64 oracle"}
+               "sample": f"{n} of the 23 layers, 1 token each (router + 6 experts), fp64 oracle",
+               "cpu_model": model, "cores_available": avail,
+               "one_thread": {"value": round(us_1, 1), "unit": "us/layer", "layers": n_1}}
 
     from gemm_router_fp32_amd.pmc_traffic import read_traffic
     # HBM bytes per launch from the committed counter passes (None once the
@@ -555,6 +608,11 @@ def main():
         "us_per_layer_spread": spread(per_step / LAYERS),
         # the stack reads 806 MB per step, > the 256 MB MALL: every layer is cold
         "single_launch_us": round(ms_kernel * 1e3, 3),
+        # one layer alone with every cache evicted first (direct launch)
+        "single_layer_cold_us": round(single_cold_us, 3),
+        # the decode's expert phase (first up-load issue to the last down
+        # GEMV) from the committed phase timeline of the measurement build
+        "expert_phase_gbps": read_profile_value(os.path.join(ROOT, PHASE_PROFILE), "expert_phase_gbps"),
         # one k_decode_fused launch per layer: its average duration is the
         # timed region over the 23 * steps launches of the graph replays
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",

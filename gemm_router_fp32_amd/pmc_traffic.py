@@ -25,9 +25,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 KERNEL_SOURCES = ("csrc/q4moe_fused.hpp", "csrc/q4moe_device.hpp", "csrc/q4moe_kernels.hpp")
 
 
-def source_sha256():
+def source_sha256(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources:
         with open(os.path.join(HERE, rel), "rb") as f:
             h.update(rel.encode() + b"\0" + f.read())
     return h.hexdigest()

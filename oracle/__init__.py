@@ -58,6 +58,7 @@ def lib():
         L.q4o_bf16_from.restype = u32
         L.q4o_bf16_from.argtypes = [d]
         L.q4o_threads.restype = i32
+        L.q4o_set_threads.argtypes = [i32]
         L.q4o_dequant.argtypes = [i32, i32, i32, p, p, f, p]
         L.q4o_router.argtypes = [i32, i32, i32, i32, p, p, p, p, p, p, p, p]
         L.q4o_moe_w4a16.argtypes = [ctypes.POINTER(_Bank), i32, i32, p, p, p, p, p]
@@ -125,6 +126,10 @@ def bf16_round(a):
 
 def threads():
     return int(lib().q4o_threads())
+
+
+def set_threads(n):
+    lib().q4o_set_threads(int(n))
 
 
 # --- matrices ----------------------------------------------------------------

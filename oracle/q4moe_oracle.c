@@ -431,6 +431,14 @@ int32_t q4o_threads(void) {
 #endif
 }
 
+void q4o_set_threads(int32_t n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ---- Shared expert, FP8 per-tensor W8A8 -------------------------------
  * [W] Step 3 (shared experts go to FP8) and the precision table of [C]
  * (shared experts: FP8 per-tensor W8A8).  Readings: weights are E4M3FN

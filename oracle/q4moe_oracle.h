@@ -160,8 +160,10 @@ void q4o_wq_codes_excess_blocks(int64_t nblocks, const uint16_t* w, float g, con
 /* bf16 bit pattern nearest to v (RNE), for chaining an oracle output. */
 uint32_t q4o_bf16_from(double v);
 
-/* Threads the oracle's parallel loops use (1 without OpenMP). */
+/* Threads the oracle's parallel loops use (1 without OpenMP), and a way to
+ * set them (n > 0). */
 int32_t q4o_threads(void);
+void q4o_set_threads(int32_t n);
 
 #ifdef __cplusplus
 }
