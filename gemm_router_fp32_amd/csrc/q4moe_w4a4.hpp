@@ -240,12 +240,13 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
 // ---------------------------------------------------------------------------
 // Grouped GEMM on MFMA: for expert e and a 128-column output tile,
 // out[m][n] = sum_k A[m][k] * W_e[n][k] over the expert's rows m, with both
-// operands NVFP4 (codes + E4M3 scale per 16 along k), decoded exactly to fp16:
-// A into LDS, W in registers.  Workgroup: 4 waves; wave w owns output columns
-// 32w..32w+31 and up to three 32-row subtiles (96 rows) of M, one
-// v_mfma_f32_32x32x16_f16 accumulator each.  K advances 256 per chunk (128
-// bytes of every weight row); a 3-slot register ring keeps two chunks of
-// weight loads in flight while the current one computes.
+// operands NVFP4 (codes + E4M3 scale per 16 along k), decoded exactly to
+// fp16: A into LDS, W in registers.  Workgroup: 4 waves; wave w owns output
+// columns 32w..32w+31 (two 16-column blocks) and up to six 16-row subtiles
+// (96 rows) of M, one v_mfma_f32_16x16x32_f16 accumulator per (subtile,
+// block).  K advances 256 per chunk (128 bytes of every weight row); a
+// 3-slot register ring keeps two chunks of weight loads in flight while the
+// current one computes.
 // ---------------------------------------------------------------------------
 enum : int { EPI_UP = 0, EPI_DOWN = 1 };
 // Output columns (rows of W_e) per workgroup (4 waves x 32), A rows per
@@ -268,53 +269,64 @@ struct GemmArgs {
 };
 
 // Pieces of the grouped GEMM below (k_grouped_gemm describes the whole).
+// A chunk's weights of one lane: q[2 nb + h] = bytes 64 h + 16 kq .. +15 of
+// the chunk in the lane's row of block nb.
 struct BChunk {
     uint4 q[4];
 };
 
 // Block scales of the workgroup's 128 weight rows (row-major, Kd / 16 bytes a
-// row), staged once per workgroup: per chunk a lane then reads its 8 bytes
-// from LDS instead of two scattered 4-byte loads from 32 rows.
+// row), staged once per workgroup: per chunk a lane then reads its bytes
+// from LDS instead of scattered loads from its rows.
 extern __shared__ __attribute__((aligned(16))) uint8_t g_gemm_sct[];
 
-// Per-workgroup constants of the grouped GEMM.
+// Per-workgroup constants of the grouped GEMM.  Lane (n16 = lane % 16, kq =
+// lane / 16): n = column of its block-0 row (block 1: n + 16); wc_off[nb] /
+// sc_row[nb] = byte offsets of its rows' codes / staged scales.
 struct GemmCtx {
-    int e, row0, n, hk, nch, ap, ar, rb;
-    uint32_t wc_off, sc_row;
+    int e, row0, n, kq, nch, ap, ar, rb;
+    uint32_t wc_off[2], sc_row[2];
     float g;
 };
 
-// Valid 16-byte pieces (0..4) of this lane's half of chunk c.
-__device__ __forceinline__ int gemm_valid_pieces(const GemmArgs& a, const GemmCtx& x, int c) {
-    return min(4, max(0, (a.Kd - c * kGemmBK - 128 * x.hk) / 32));
+// Piece (h, kq) of chunk c (k 256 c + 128 h + 32 kq .. +31) lies inside K.
+__device__ __forceinline__ bool gemm_piece_ok(const GemmArgs& a, int c, int h, int kq) {
+    return c * kGemmBK + 128 * h + 32 * kq < a.Kd;
 }
 
-// Pieces past the end of the row read the row's last 16 code bytes and last
-// scale dword instead: those lines were fetched by the last full chunk and
-// are still in L2.
+// Pieces past the end of the row read the row's last 16 code bytes instead
+// (their scales are zeroed where they are used).  Each load instruction of a
+// wave reads 64 contiguous bytes of 16 rows: a wave load spread over 32 rows
+// streams about a third slower.
 __device__ __forceinline__ void gemm_load_b(const GemmArgs& a, const GemmCtx& x, int c, BChunk& b) {
-    const int kb = c * kGemmBK, valid = gemm_valid_pieces(a, x, c);
-    const uint32_t c_last = x.wc_off + a.Kd / 2 - 16;
-    const uint32_t base = x.wc_off + kb / 2 + 64 * x.hk;
+    const uint32_t kb = (uint32_t)c * kGemmBK / 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b.q[i] = ldg16(a.wc + (i < valid ? base + 16 * i : c_last));
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t c_last = x.wc_off[nb] + a.Kd / 2 - 16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            b.q[2 * nb + h] = ldg16(a.wc + (gemm_piece_ok(a, c, h, x.kq) ? x.wc_off[nb] + kb + 64 * h + 16 * x.kq
+                                                                           : c_last));
+    }
 }
 
 // A tile LDS column (fp16 elements) of 16-byte group g of a row: groups are
 // XOR-swizzled so that the 8 threads staging one row (group 4 ap + i for
 // piece ap, store i) write 8 different bank groups; the MFMA fragment reads
-// (one group per lane, 32 rows apart by the row pitch) stay conflict-free.
+// (16 rows at one group, rows 528 bytes apart) stay conflict-free.
 __device__ __forceinline__ int a_col(int g) { return 8 * (g ^ ((g >> 3) & 3)); }
 
-// One M-tile (rows m0 .. m0 + mv - 1 of expert e, MS = ceil(mv / 32)
-// subtiles) against the workgroup's 128 columns.
+// One M-tile (rows m0 .. m0 + mv - 1 of expert e, MS = ceil(mv / 16)
+// subtiles, staged in ceil(mv / 32) groups of 32 rows) against the
+// workgroup's 128 columns.
 template <int EPI, int MS>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, int m0, int mv,
                                           _Float16 (*As)[kApitch]) {
-    const int lane = threadIdx.x & 63;
-    uint32_t ac_off[MS], as_off[MS];
+    constexpr int MA = (MS + 1) / 2;  // staging groups of 32 rows
+    const int lane = threadIdx.x & 63, n16 = lane & 15;
+    uint32_t ac_off[MA], as_off[MA];
 #pragma unroll
-    for (int q = 0; q < MS; ++q) {
+    for (int q = 0; q < MA; ++q) {
         const int drow = x.row0 + m0 + min(x.ar + 32 * q, mv - 1);
         const uint32_t arow = a.a_by_token ? (uint32_t)(a.perm[drow] / a.K) : (uint32_t)drow;
         ac_off[q] = arow * (uint32_t)(a.Kd / 2);
@@ -322,13 +334,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
     }
     // A pieces in a three-slot register ring alongside B's: chunk c's A is
     // loaded two chunks ahead, into the slot chunk c - 1 staged from
-    uint4 qa3[3][MS];
-    uint32_t sa3[3][MS];
-    auto load_a = [&](int c, uint4 (&qa)[MS], uint32_t (&sa)[MS]) {
+    uint4 qa3[3][MA];
+    uint32_t sa3[3][MA];
+    auto load_a = [&](int c, uint4 (&qa)[MA], uint32_t (&sa)[MA]) {
         const int kb = c * kGemmBK;
         const bool ok = 32 * x.ap < a.Kd - kb;
 #pragma unroll
-        for (int q = 0; q < MS; ++q) {
+        for (int q = 0; q < MA; ++q) {
             // past the end: the row's last piece (just read), with scale 0
             qa[q] = ldg16(a.ac + (ok ? ac_off[q] + kb / 2 + 16 * x.ap : ac_off[q] + a.Kd / 2 - 16));
             // (the scale of a piece past the end is zeroed where it is used:
@@ -338,11 +350,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
         }
     };
 
-    f32x16 acc[MS];
+    f32x4g acc[MS][2];
 #pragma unroll
     for (int i = 0; i < MS; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+        for (int nb = 0; nb < 2; ++nb) acc[i][nb] = f32x4g{0.f, 0.f, 0.f, 0.f};
 
     // issue order = wait order: B0, A0, B1, A1 (the scheduler may not mix them)
     BChunk bb[3];
@@ -356,13 +368,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
     __builtin_amdgcn_sched_barrier(0);
     // chunk c stages its A from (qa, sa), computes on bc, and loads chunk
     // c + 2 into (qn, sn) and bn, the slots chunk c - 1 used
-    auto step = [&](const int c, const BChunk& bc, BChunk& bn, const uint4 (&qa)[MS], const uint32_t (&sa)[MS],
-                    uint4 (&qn)[MS], uint32_t (&sn)[MS]) {
+    auto step = [&](const int c, const BChunk& bc, BChunk& bn, const uint4 (&qa)[MA], const uint32_t (&sa)[MA],
+                    uint4 (&qn)[MA], uint32_t (&sn)[MA]) {
             // this chunk's A into LDS (after every wave is done with the last one)
             __syncthreads();
             const bool a_ok = 32 * x.ap < a.Kd - c * kGemmBK;
 #pragma unroll
-            for (int q = 0; q < MS; ++q) {
+            for (int q = 0; q < MA; ++q) {
                 const f16x2 sp = e4m3x2_f16<false>(a_ok ? sa[q] : 0u);
                 const f16x2 s_lo = {sp.x, sp.x}, s_hi = {sp.y, sp.y};
                 _Float16* dst = &As[x.ar + 32 * q][0];
@@ -378,42 +390,40 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             __builtin_amdgcn_sched_barrier(0);
             gemm_load_b(a, x, c + 2, bn);
             __builtin_amdgcn_sched_barrier(0);
-            // 16 MFMA steps on chunk c; block scales of the lane's 8 blocks,
-            // pieces past the end get 0
-            const int valid = gemm_valid_pieces(a, x, c);
-            // (a dword past the valid pieces reads the row's first bytes; its
-            // scales are zeroed below)
-            const int so = c * 16 + 8 * x.hk;
-            const uint32_t s0 = *reinterpret_cast<const uint32_t*>(g_gemm_sct + x.sc_row + (valid > 0 ? so : 0));
-            const uint32_t s1 = *reinterpret_cast<const uint32_t*>(g_gemm_sct + x.sc_row + (valid > 2 ? so + 4 : 0));
-            f16x2 sc[4] = {e4m3x2_f16<false>(s0), e4m3x2_f16<true>(s0), e4m3x2_f16<false>(s1), e4m3x2_f16<true>(s1)};
+            // 8 MFMA steps (h, d) on chunk c: lane (n16, kq) takes dword d of
+            // its piece h (k 128 h + 32 kq + 8 d .. +7 of the chunk) with
+            // block scale 8 h + 2 kq + d / 2; pieces past the end get scale 0
+            f16x2 sc[2][2];
 #pragma unroll
-            for (int pc = 0; pc < 4; ++pc)
-                if (pc >= valid) sc[pc] = f16x2{0, 0};
-            const uint32_t w[16] = {bc.q[0].x, bc.q[0].y, bc.q[0].z, bc.q[0].w, bc.q[1].x, bc.q[1].y,
-                                    bc.q[1].z, bc.q[1].w, bc.q[2].x, bc.q[2].y, bc.q[2].z, bc.q[2].w,
-                                    bc.q[3].x, bc.q[3].y, bc.q[3].z, bc.q[3].w};
-            // A fragments are read one step ahead of their MFMAs (step j reads
-            // group 16 hk + j of the lane's row)
-            const _Float16* arow = &As[lane & 31][0];
-            f16x8 af[2][MS];
+            for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-            for (int i = 0; i < MS; ++i)
-                af[0][i] = *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch + a_col(16 * x.hk));
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t sv = *reinterpret_cast<const uint16_t*>(g_gemm_sct + x.sc_row[nb] + c * 16 +
+                                                                           8 * h + 2 * x.kq);
+                    sc[nb][h] = e4m3x2_f16<false>(gemm_piece_ok(a, c, h, x.kq) ? sv : 0u);  // byte 0 is +0
+                }
+            // the A fragment of step (h, d): group 16 h + 4 kq + d of unit row 16 i + n16
+            const _Float16* arow = &As[n16][0];
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                if (j + 1 < 16) {
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    f16x8 af[MS];
 #pragma unroll
                     for (int i = 0; i < MS; ++i)
-                        af[(j + 1) & 1][i] =
-                            *reinterpret_cast<const f16x8*>(arow + 32 * i * kApitch + a_col(16 * x.hk + j + 1));
-                }
-                // dword j holds k 8j..8j+7 of the lane's half: block j / 2, piece j / 4
-                const f16x2 sp = sc[j / 4];
-                const f16x8 bfrag = fp4x8_f16(w[j], (j & 2) ? f16x2{sp.y, sp.y} : f16x2{sp.x, sp.x});
+                        af[i] = *reinterpret_cast<const f16x8*>(arow + 16 * i * kApitch +
+                                                                a_col(16 * h + 4 * x.kq + d));
 #pragma unroll
-                for (int i = 0; i < MS; ++i)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][i], bfrag, acc[i], 0, 0, 0);
+                    for (int nb = 0; nb < 2; ++nb) {
+                        const uint4 pc = bc.q[2 * nb + h];
+                        const uint32_t wd = d == 0 ? pc.x : d == 1 ? pc.y : d == 2 ? pc.z : pc.w;
+                        const f16x2 sp = sc[nb][h];
+                        const f16x8 bfrag = fp4x8_f16(wd, d < 2 ? f16x2{sp.x, sp.x} : f16x2{sp.y, sp.y});
+#pragma unroll
+                        for (int i = 0; i < MS; ++i)
+                            acc[i][nb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i], bfrag, acc[i][nb], 0, 0, 0);
+                    }
+                }
             }
     };
     // whole turns of the ring, then the one or two chunks left (no padding
@@ -426,49 +436,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
     }
     if (c < x.nch) step(c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
     if (c + 1 < x.nch) step(c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
-    // epilogue: lane holds column n and rows 32 i + 8 (r / 4) + 4 (lane / 32) + r % 4
+    // epilogue: lane (n16, kq) holds column n + 16 nb and rows 16 i + 4 kq + r
 #pragma unroll
-    for (int i = 0; i < MS; ++i) {
+    for (int nb = 0; nb < 2; ++nb) {
+        const int n = x.n + 16 * nb;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int m = 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-            if (m < mv && x.n < a.N) {
-                const int p = x.row0 + m0 + m;
-                float v = acc[i][r] * x.g;
-                if constexpr (EPI == EPI_UP) {
-                    v = fmaxf(v, 0.f);
-                    v = v * v;
+        for (int i = 0; i < MS; ++i) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = 16 * i + 4 * x.kq + r;
+                if (m < mv && n < a.N) {
+                    const int p = x.row0 + m0 + m;
+                    float v = acc[i][nb][r] * x.g;
+                    if constexpr (EPI == EPI_UP) {
+                        v = fmaxf(v, 0.f);
+                        v = v * v;
+                    }
+                    a.out[(size_t)p * a.N + n] = v;
                 }
-                a.out[(size_t)p * a.N + x.n] = v;
             }
         }
     }
 }
 
 // Grouped GEMM over the experts' dispatch rows: out[row][n] = epi(sum_k
-// A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_32x32x16_f16) with both
+// A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_16x16x32_f16) with both
 // operands decoded exactly from NVFP4.  A workgroup takes 128 columns of one
 // expert and all its rows in M-tiles of 96; wave w owns columns 32w..32w+31.
 //
 // The reduction runs in chunks of 256: every weight row contributes one whole
-// 128-byte line per chunk, loaded straight into registers (lane l: row l % 32,
-// bytes 64 (l / 32) .. +63, i.e. k 128 (l / 32) .. +127 of the chunk) two
-// chunks ahead in a three-slot ring (plain loads: the four load instructions
-// of a wave take 32 bytes of each line in turn, so the line must stay in L2
-// until the last one); the A pieces of the chunk, loaded two chunks ahead
-// in a ring of their own, are decoded into LDS once per workgroup.  MFMA step j (0..15) of a chunk sums k 8j..8j+7
-// (lanes 0..31) and 128+8j..128+8j+7 (lanes 32..63): the same k order on both
-// operands.  The block scales of the workgroup's 128 weight rows are copied
-// into LDS once, with coalesced loads issued beside the expert's offsets
-// (per chunk a wave would otherwise gather 4 bytes from each of 32 rows,
-// twice).  All loads are unconditional: pieces past the end of a row (in
-// the last chunk, and the prefetches issued by the last two chunks) read the
-// row's last bytes and get scale 0, so that every wait covers exactly the
-// loads it needs.  The chunk loop runs whole turns of the ring and then the
-// one or two chunks left, with no exit from inside a turn (an exit there makes
-// the compiler wait for every outstanding load).  Offsets are 32-bit from the
-// uniform bases: the argument limits (E <= 256, rows and columns <= 4096,
-// T * K <= 2^19) keep every matrix under 2^31 bytes.
+// 128-byte line per chunk, loaded straight into registers two chunks ahead in
+// a three-slot ring (lane (n16, kq) of block nb: row 32 w + 16 nb + n16,
+// bytes 64 h + 16 kq .. +15 for halves h = 0, 1: each load instruction
+// covers 64 bytes of 16 rows); the A pieces of the chunk, loaded two chunks
+// ahead in a ring of their own, are decoded into LDS once per workgroup.
+// MFMA step (h, d) of a chunk sums k 128 h + 32 kq + 8 d .. +7 on lanes
+// kq = 0..3: the same k order on both operands.  The block scales of the
+// workgroup's 128 weight rows are copied into LDS once, with coalesced loads
+// issued beside the expert's offsets.  All loads are unconditional: pieces
+// past the end of a row (in the last chunk, and the prefetches issued by the
+// last two chunks) read the row's last bytes and get scale 0, so that every
+// wait covers exactly the loads it needs.  The chunk loop runs whole turns
+// of the ring and then the one or two chunks left, with no exit from inside
+// a turn (an exit there makes the compiler wait for every outstanding load).
+// Offsets are 32-bit from the uniform bases: the argument limits (E <= 256,
+// rows and columns <= 4096, T * K <= 2^19) keep every matrix under 2^31
+// bytes.
 template <int EPI>
 __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 As[kGemmBM][kApitch];
@@ -505,13 +518,16 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     const int n_e = a.offsets[x.e + 1] - x.row0;
     if (n_e == 0) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    x.hk = lane >> 5;
+    x.kq = lane >> 4;
     x.nch = (a.Kd + kGemmBK - 1) / kGemmBK;
-    x.n = tile * kGemmBN + 32 * wave + (lane & 31);
-    const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n, a.N - 1);
-    x.wc_off = wrow * (uint32_t)(a.Kd / 2);
+    x.n = tile * kGemmBN + 32 * wave + (lane & 15);
     x.rb = sc_rb;
-    x.sc_row = (uint32_t)((32 * wave + (lane & 31)) * x.rb);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n + 16 * nb, a.N - 1);
+        x.wc_off[nb] = wrow * (uint32_t)(a.Kd / 2);
+        x.sc_row[nb] = (uint32_t)((32 * wave + 16 * nb + (lane & 15)) * x.rb);
+    }
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
         const int i = (int)threadIdx.x + 256 * j;
@@ -523,14 +539,15 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
     x.ar = threadIdx.x >> 3;
     for (int m0 = 0; m0 < n_e; m0 += kGemmBM) {
         const int mv = min(kGemmBM, n_e - m0);
-        const int ms = (mv + 31) / 32;
-        static_assert(kGemmBM == 96, "subtile dispatch below covers 1..3");
-        if (ms == 1)
-            gemm_tile<EPI, 1>(a, x, m0, mv, As);
-        else if (ms == 2)
-            gemm_tile<EPI, 2>(a, x, m0, mv, As);
-        else
-            gemm_tile<EPI, 3>(a, x, m0, mv, As);
+        static_assert(kGemmBM == 96, "subtile dispatch below covers 1..6");
+        switch ((mv + 15) / 16) {
+            case 1: gemm_tile<EPI, 1>(a, x, m0, mv, As); break;
+            case 2: gemm_tile<EPI, 2>(a, x, m0, mv, As); break;
+            case 3: gemm_tile<EPI, 3>(a, x, m0, mv, As); break;
+            case 4: gemm_tile<EPI, 4>(a, x, m0, mv, As); break;
+            case 5: gemm_tile<EPI, 5>(a, x, m0, mv, As); break;
+            default: gemm_tile<EPI, 6>(a, x, m0, mv, As); break;
+        }
     }
 }
 
