@@ -73,6 +73,18 @@ constexpr int kMaxWgUp = 512;        // up rows per workgroup (K * I / grid)
 constexpr int kRowBlock = 64;
 constexpr uint32_t kPollLimit = 200000;  // polls (each at least one memory round trip) before giving up
 
+// LDS layouts of x and h: one 16-byte pad after every 32-element chunk (x
+// and h as 16-bit values: 64 bytes, then 16 bytes of pad) or after every 32
+// fp32 values (128 bytes, then 16).  A GEMV lane reads its own chunk as
+// consecutive 16-byte pieces; unpadded, the chunks of all lanes start in the
+// same banks and every piece read serialises (8 ways for fp32, 4 for 16-bit),
+// while with the pad the chunks of any 8 consecutive lanes start 4 banks
+// apart (lane strides of 36 and 20 words) and one read pass serves them all.
+__device__ __forceinline__ int lds_pad_f32(int i) { return i + 4 * (i >> 5); }   // fp32 element i
+__device__ __forceinline__ int lds_pad_u16(int j) { return j + 8 * (j >> 5); }   // 16-bit element j
+__device__ __forceinline__ int lds_pad_u128(int t) { return t + (t >> 2); }      // 16-byte piece t of 16-bit values
+constexpr int kLdsH16Lo = 2 * 4096 + 2 * 4096 / 4;  // 16-bit h: the lo halves start here (past the padded hi halves)
+
 // Workspace control words of the fused decode.
 enum : int {
     FW_EPOCH = 256,  // [grid]: workgroup b's epoch of the last call (at most CTRL_WORDS - FW_EPOCH workgroups)
@@ -304,10 +316,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     __shared__ int s_sel_ids[8];
     __shared__ __attribute__((aligned(16))) float s_sel_sc[8];
     __shared__ float s_w_all[kWaves][8];  // each wave's copy of the gates
-    __shared__ float s_h[2 * 4096];     // h of the (at most two, adjacent) slots this workgroup's down rows use
-    uint16_t* const s_h16 = reinterpret_cast<uint16_t*>(s_h);  // int4: bf16 hi halves, then lo halves
+    // h of the (at most two, adjacent) slots this workgroup's down rows use,
+    // padded: fp32 (NVFP4), or 16-bit (int4: bf16 hi halves, then lo halves
+    // from kLdsH16Lo; W4A4: bf16)
+    __shared__ float s_h[kLdsH16Lo];
+    uint16_t* const s_h16 = reinterpret_cast<uint16_t*>(s_h);
     __shared__ float s_hrow[kMaxWgUp];  // this workgroup's up results, before they are published
-    __shared__ uint4 s_x[512];          // x (bf16, H <= 4096), read once per workgroup
+    __shared__ uint4 s_x[512 + 128];    // x (bf16, H <= 4096, padded), read once per workgroup
     // shared expert: x and h codes decoded to bf16 (natural order), and this
     // workgroup's (at most 16) h codes before they are published
     __shared__ uint32_t s_xb[SH ? 2048 : 1], s_shb[SH ? 2048 : 1], s_shq[SH ? 4 : 1];
@@ -355,7 +370,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     }
 
     // x into LDS once per workgroup (the up GEMV reads it from there)
-    if (!A4 && (int)threadIdx.x < a.H / 8) s_x[threadIdx.x] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+    if (!A4 && (int)threadIdx.x < a.H / 8)
+        s_x[lds_pad_u128(threadIdx.x)] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
     // x pieces the waves that will not poll the scores quantize during the
     // score hand-off (eight values each, at most two per thread: H / 8 <= 512
     // pieces over at least four such waves), loaded now with the router's
@@ -527,7 +543,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
-                s_x[t] = make_uint4(o[0], o[1], o[2], o[3]);
+                s_x[lds_pad_u128(t)] = make_uint4(o[0], o[1], o[2], o[3]);
                 if (blockIdx.x == 0) {
                     *reinterpret_cast<uint32_t*>(a.xq_codes + 4 * t) = b.code;
                     if ((t & 1) == 0) a.xq_scales[t / 2] = (uint8_t)b.sb;
@@ -661,7 +677,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         uint32_t nat[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const uint4 v = s_x[4 * ch + k];
+            const uint4 v = s_x[5 * ch + k];
             nat[4 * k + 0] = v.x;
             nat[4 * k + 1] = v.y;
             nat[4 * k + 2] = v.z;
@@ -678,9 +694,12 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
 
-    // ---- U: h = relu(W_up x)^2 for this wave's rows, into LDS
+    // ---- U: h = relu(W_up x)^2 for this wave's rows: unit u0 + 2 p + seg
+    // ends in lane 31 + 32 seg of hres[p] (for W4A4 also in LDS)
+    float hres[kMaxUp];
 #pragma unroll
     for (int p = 0; p < kMaxUp; ++p) {
+        hres[p] = 0.f;
         if (p < n_up_pass) {
             const int u = u0 + 2 * p + seg;
             const bool ok = u < u1;
@@ -700,26 +719,73 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
             acc = seg_sum_last<32>(acc);
             const float g = slot == us0 ? gu0 : gu1;
-            if (li == 31 && ok) {
-                const float rl = fmaxf(acc * g, 0.f);
-                s_hrow[u - wu0] = rl * rl;
-            }
+            const float rl = fmaxf(acc * g, 0.f);
+            hres[p] = rl * rl;
+            if constexpr (A4)
+                if (li == 31 && ok) s_hrow[u - wu0] = hres[p];
         }
     }
-    // Then the loads of a down wave's rows: issued only now, so that the up
-    // rows (which every workgroup needs first, for h) have the memory system
-    // to themselves, and the down weights stream during the h hand-off.  The
-    // rows past the slot's end (H % kDownRows != 0) read its last row and are
-    // dropped at the publish.  First every up load is retired (the ones of
-    // unused passes were issued before the used ones, so this costs nothing):
-    // otherwise the compiler counts them as pending past the branch and, where
-    // their registers are reused, waits for the down weights as well.
+    Q4MOE_PHASE(9);
+
+    // ---- P: publish h, then issue the down loads, then poll the h of the
+    // slots the workgroup's down rows use into LDS.  (A poll result counts
+    // only after every load the wave issued before it, so the first poll
+    // also waits for the down weights.)
+    if constexpr (!A4) {
+        // Every wave publishes its own (at most 2 kMaxUp) rows as soon as
+        // they are done, with no workgroup barrier: lane l stores copy
+        // l / (2 kMaxUp) of unit u0 + l % (2 kMaxUp), all copies in one store.
+        constexpr int NU = 2 * kMaxUp;
+        static_assert(NU * kReplicas <= 64, "one wave store holds every copy");
+        const int k = lane % NU, rp = lane / NU;
+        float v = 0.f;
+#pragma unroll
+        for (int p = 0; p < kMaxUp; ++p) {
+            const float h0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hres[p]), 31));
+            const float h1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hres[p]), 63));
+            v = k == 2 * p ? h0 : v;
+            v = k == 2 * p + 1 ? h1 : v;
+        }
+        if (rp < kReplicas && u0 + k < u1) put_tag(a.h_tag + (size_t)rp * RU + (u0 + k), v, ep);
+        if (lane < NU && u0 + lane < u1) a.h[u0 + lane] = v;
+    } else {
+        // W4A4: the workgroup's h blocks to NVFP4 (lane pairs: half a block
+        // each), published as one (8 codes, epoch) value per half block and
+        // one (scale, epoch) value per block, kReplicas copies each (per
+        // copy: K I / 8 code values, then K I / 16 scale values)
+        __syncthreads();
+        const int j = threadIdx.x;
+        if (j < wu1 - wu0) a.h[wu0 + j] = s_hrow[j];
+        if (j < (wu1 - wu0) / 8) {
+            float f[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) f[k] = s_hrow[8 * j + k];
+            const Nvfp4Half b = nvfp4_quant8_pair(f);
+            const int hb = wu0 / 8 + j;  // global half-block index (slot-major)
+            const size_t per = (size_t)(RU / 8 + RU / 16);
+#pragma unroll
+            for (int rp = 0; rp < kReplicas; ++rp) {
+                put_tag(a.h_tag + rp * per + hb, __uint_as_float(b.code), ep);
+                if ((j & 1) == 0) put_tag(a.h_tag + rp * per + RU / 8 + hb / 2, __uint_as_float(b.sb), ep);
+            }
+            *reinterpret_cast<uint32_t*>(a.hq_codes + (size_t)hb * 4) = b.code;
+            if ((j & 1) == 0) a.hq_scales[hb / 2] = (uint8_t)b.sb;
+        }
+    }
+
+    // Then the loads of a down wave's rows, once its h has left.  They leave
+    // only now: a load waits at issue while the CU's load queue is full, and
+    // the queue is full of up loads until about now, so issued earlier they
+    // would hold the wave (and its h) back.  The rows past the slot's end
+    // (H % kDownRows != 0) read its last row and are dropped at the publish.
+    // First every up load is retired (all were used by now): otherwise the
+    // compiler counts them as pending past the branch and, where their
+    // registers are reused, waits for the down weights as well.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     compiler_fence();
-    Q4MOE_PHASE(9);
     // Shared expert: one poll of the h-code quads (t and t + 512 for thread
     // t), issued before the down loads so that its results do not wait for
-    // them; its quads were published about a memory round trip earlier.
+    // them (the quads not yet published by then are polled again later).
     const unsigned long long* srcq = a.hq_tag + (size_t)rep * (a.S / 4);
     unsigned long long vq[2];
     if constexpr (SH) {
@@ -755,47 +821,11 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         if constexpr (FMT == FMT_NVFP4) gdn = a.dng[ids[dslot]];
     }
     compiler_fence();
+    // The polls leave once every wave's down loads have: they reach the
+    // memory system behind them, by when the h they read has been published.
     __syncthreads();
     Q4MOE_PHASE(4);
 
-    // ---- P: publish this workgroup's h rows (thread j takes row wu0 + j),
-    // then poll the h of the slots the workgroup's down rows use into LDS.
-    // (A poll result counts only after every load the wave issued before it,
-    // so the first poll also waits for the down weights.)
-    {
-        const int j = threadIdx.x;
-        if (j < wu1 - wu0) {
-            const int u = wu0 + j;
-            const int slot = u / a.I, r = u - slot * a.I;
-            const float v = s_hrow[j];
-            if constexpr (!A4) {
-#pragma unroll
-                for (int rp = 0; rp < kReplicas; ++rp) put_tag(a.h_tag + ((size_t)rp * a.K + slot) * a.I + r, v, ep);
-            }
-            a.h[(size_t)slot * a.I + r] = v;
-        }
-        if constexpr (A4) {
-            // the workgroup's h blocks to NVFP4 (lane pairs: half a block
-            // each), published as one (8 codes, epoch) value per half block
-            // and one (scale, epoch) value per block, kReplicas copies each
-            // (per copy: K I / 8 code values, then K I / 16 scale values)
-            if (j < (wu1 - wu0) / 8) {
-                float f[8];
-#pragma unroll
-                for (int k = 0; k < 8; ++k) f[k] = s_hrow[8 * j + k];
-                const Nvfp4Half b = nvfp4_quant8_pair(f);
-                const int hb = wu0 / 8 + j;  // global half-block index (slot-major)
-                const size_t per = (size_t)(RU / 8 + RU / 16);
-#pragma unroll
-                for (int rp = 0; rp < kReplicas; ++rp) {
-                    put_tag(a.h_tag + rp * per + hb, __uint_as_float(b.code), ep);
-                    if ((j & 1) == 0) put_tag(a.h_tag + rp * per + RU / 8 + hb / 2, __uint_as_float(b.sb), ep);
-                }
-                *reinterpret_cast<uint32_t*>(a.hq_codes + (size_t)hb * 4) = b.code;
-                if ((j & 1) == 0) a.hq_scales[hb / 2] = (uint8_t)b.sb;
-            }
-        }
-    }
     if constexpr (SH) {
         // The shared expert's h codes into LDS (from the early poll; quads
         // not yet there are polled again, which waits for the down
@@ -900,7 +930,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
-                reinterpret_cast<uint4*>(s_h)[t] = make_uint4(o[0], o[1], o[2], o[3]);
+                reinterpret_cast<uint4*>(s_h)[lds_pad_u128(t)] = make_uint4(o[0], o[1], o[2], o[3]);
             }
         }
     } else {
@@ -921,7 +951,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                 if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
                     const int i = threadIdx.x + 512 * m;
                     if constexpr (FMT == FMT_NVFP4) {
-                        s_h[i] = tag_value(v[m]);
+                        s_h[lds_pad_f32(i)] = tag_value(v[m]);
                     } else {
                         // int4: h as bf16 hi + lo halves (about 17 bits),
                         // each in the pair order of the nibble unpacking
@@ -929,8 +959,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
                         const uint32_t hi = f32_to_bf16_rne(hv);
                         const uint32_t lo = f32_to_bf16_rne(hv - bf16_bits_to_f32(hi));
                         const int pi = (i & ~7) | ((i & 3) << 1) | ((i >> 2) & 1);
-                        s_h16[pi] = (uint16_t)hi;
-                        s_h16[2 * 4096 + pi] = (uint16_t)lo;
+                        s_h16[lds_pad_u16(pi)] = (uint16_t)hi;
+                        s_h16[kLdsH16Lo + lds_pad_u16(pi)] = (uint16_t)lo;
                     }
                     pend &= ~(1u << m);
                 }
@@ -957,7 +987,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
                 const int ch = min(lane * C2 + c, nchI - 1);
-                const uint4* hp = reinterpret_cast<const uint4*>(s_h) + ((dslot - sl0) * a.I + ch * 32) / 8;
+                // (a slot's h starts on a chunk boundary: I % 32 == 0)
+                const uint4* hp = reinterpret_cast<const uint4*>(s_h) + 5 * ((dslot - sl0) * (a.I / 32) + ch);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const uint4 v = hp[k];
@@ -984,7 +1015,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
                 const int ch = min(lane * C2 + c, nchI - 1);
-                const float4* hp = reinterpret_cast<const float4*>(&s_h[(dslot - sl0) * a.I + ch * 32]);
+                const float4* hp = reinterpret_cast<const float4*>(&s_h[lds_pad_f32((dslot - sl0) * a.I + ch * 32)]);
 #pragma unroll
                 for (int k = 0; k < 8; ++k) {
                     const float4 v = hp[k];
@@ -1014,8 +1045,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
 #pragma unroll
             for (int c = 0; c < C2; ++c) {
                 const int ch = min(lane * C2 + c, nchI - 1);
-                const uint4* hp = reinterpret_cast<const uint4*>(&s_h16[(dslot - sl0) * a.I + ch * 32]);
-                const uint4* lp = reinterpret_cast<const uint4*>(&s_h16[2 * 4096 + (dslot - sl0) * a.I + ch * 32]);
+                const int e = lds_pad_u16((dslot - sl0) * a.I + ch * 32);
+                const uint4* hp = reinterpret_cast<const uint4*>(&s_h16[e]);
+                const uint4* lp = reinterpret_cast<const uint4*>(&s_h16[kLdsH16Lo + e]);
 #pragma unroll
                 for (int k = 0; k < 4; ++k) {
                     const uint4 v = hp[k], w = lp[k];

@@ -143,7 +143,7 @@ def phase(torch, fmt):
     names = {0: "start", 1: "router done", 2: "scores in", 3: "top-k done", 8: "up loads issued",
              9: "up GEMV done", 4: "down loads issued", 5: "h in", 6: "down done", 7: "combine done (wave 0)",
              10: "end (all waves)"}
-    order = [0, 1, 2, 3, 8, 9, 4, 5, 6, 7, 10]
+    order = [0, 1, 2, 3, 8, 4, 9, 5, 6, 7, 10]
     rel = []
     for s_ in slots:
         b = buf[s_].astype(np.float64)
