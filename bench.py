@@ -213,6 +213,47 @@ def time_stack(torch, g, layers, steps, warmup):
     return ms_step, float(np.mean(durs[LAYERS:])), flags, per
 
 
+def time_stack_launch(torch, g, layers, steps, warmup):
+    """The same 23 layers through q4moe_w4a16_decode_stack: one launch per
+    step, each layer starting its routing once the previous layer's y is
+    complete (the order of the per-layer graph, without its launch gaps)."""
+    routers = [L["r"] for L in layers]
+    banks = [L["ex"] for L in layers]
+    xs = [L["x"][0] for L in layers]
+    ys = [L["y"][0] for L in layers]
+    ws = g.workspace(g.q4moe_w4a16_decode_stack_ws_bytes(routers[0], banks[0]))
+
+    def step():
+        g.q4moe_w4a16_decode_stack(routers, banks, xs, ys, ws=ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(stream)
+    with torch.cuda.stream(s):
+        step()
+    stream.wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(steps):
+        graph.replay()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(steps)])
+    ms_step = evs[0].elapsed_time(evs[-1]) / steps
+    return ms_step, g.q4moe_ws_check(ws), per
+
+
 def bench_w4a4(torch, g, synth, steps):
     from gpu_util import dev
     T = 1024
@@ -500,12 +541,18 @@ def main():
     gbs = bytes_layer / (us_layer * 1e-6) / 1e9
     log(f"nvfp4 stack: {ms_step:.4f} ms/step, {us_layer:.3f} us/layer, {gbs:.1f} GB/s; "
         f"single direct launch {ms_kernel * 1e3:.2f} us; flags {flags}")
+    ms_one, f_one, per_one = time_stack_launch(torch, g, layers, args.steps, args.warmup)
+    stack_one = {"us_per_layer": round(1000.0 * ms_one / LAYERS, 3),
+                 "hbm_gbps": round(bytes_layer / (ms_one / LAYERS * 1e-3) / 1e9, 1),
+                 "tokens_per_s": round(1000.0 / ms_one, 1), "us_per_layer_spread": spread(per_one / LAYERS),
+                 "flags": f_one}
+    log(f"nvfp4 stack in one launch: {stack_one}")
     # one layer alone, cold: 1 GiB read before each rep evicts the MALL and L2s
     t_cold = Timer(torch).each(lambda: decode_call(g, layers[0]), max(10, args.steps // 2), Evictor(torch))
     single_cold_us = float(np.median(t_cold)) * 1e3
     log(f"single layer, evicted, direct launch: {single_cold_us:.2f} us")
 
-    extra = {}
+    extra = {"nvfp4_stack_one_launch": stack_one}
     if not args.only_stack:
         extra["verify_step"] = bench_verify(torch, g, synth, args.steps, layers[0])
         log(f"verify step: {extra['verify_step']}")
@@ -521,6 +568,12 @@ def main():
                                "us_per_layer_spread": spread(per4 / LAYERS),
                                "bytes_per_layer": b4, "flags": f4}
         log(f"int4 stack: {extra['int4_stack']}")
+        ms41, f41, per41 = time_stack_launch(torch, g, int4, args.steps, args.warmup)
+        extra["int4_stack_one_launch"] = {"us_per_layer": round(1000.0 * ms41 / LAYERS, 3),
+                                          "hbm_gbps": round(b4 / (ms41 / LAYERS * 1e-3) / 1e9, 1),
+                                          "tokens_per_s": round(1000.0 / ms41, 1),
+                                          "us_per_layer_spread": spread(per41 / LAYERS), "flags": f41}
+        log(f"int4 stack in one launch: {extra['int4_stack_one_launch']}")
         extra["mid_batch_int4"] = bench_mid_batch(torch, g, synth, args.steps, "int4", int4[0])
         del int4
         torch.cuda.empty_cache()

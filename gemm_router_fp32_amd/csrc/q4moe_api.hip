@@ -108,7 +108,8 @@ constexpr size_t kScTagOff = up_to(CTRL_WORDS * 4);
 constexpr size_t kHTagOff = kScTagOff + up_to((size_t)kReplicas * kMaxExperts * 8);
 constexpr size_t kZTagOff = kHTagOff + up_to((size_t)kReplicas * kMaxTopK * kMaxDim * 8);
 constexpr size_t kHqTagOff = kZTagOff + up_to((size_t)(kMaxTopK + 1) * kMaxDim * 8);
-constexpr size_t kPrefixBytes = kHqTagOff + up_to((size_t)kReplicas * (kMaxDim / 4) * 8);
+constexpr size_t kYTagOff = kHqTagOff + up_to((size_t)kReplicas * (kMaxDim / 4) * 8);
+constexpr size_t kPrefixBytes = kYTagOff + up_to((size_t)kReplicas * (kMaxDim / 2) * 8);
 
 struct RouterWs {
     size_t ctrl, logits, ids, w, total;
@@ -130,7 +131,7 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s;
+    size_t sc_tag, h_tag, z_tag, y_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s;
     // the grouped path (more than kSmallT tokens): dispatch, fp16 staging
     size_t counts, offsets, lists, perm, inv, act, n_act, x16, xexp, h16, hexp;
     // the shared expert through the grouped GEMMs (one-expert dispatch)
@@ -158,6 +159,7 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     l.h_tag = kHTagOff;    // (h, epoch) pairs [kReplicas][K][I] (W4A4: codes and scales)
     l.z_tag = kZTagOff;    // (w * g * z, epoch) pairs [K + 1][H]; slot K: the shared expert
     l.hq_tag = kHqTagOff;  // shared expert: (four h codes, epoch) [kReplicas][S / 4]
+    l.y_tag = kYTagOff;    // a stack's y for its next layer: (two bf16, epoch) [kReplicas][H / 2]
     size_t o = l.r.total;
     l.sh_xq = o;   // shared expert taps [T][H], [T][S], [T][S], and its z [T][H]
     o += up_to(S > 0 ? (size_t)T * H : 0);
@@ -245,33 +247,78 @@ int fused_grid(int dev, int variant) {
     return cached;
 }
 
+// Whether a one-launch decode of this shape runs on `grid` workgroups.  The
+// router needs one workgroup per expert; every wave's up rows must fit in
+// kMaxUp passes (all loads in flight at once), a workgroup stages at most
+// kMaxWgUp up rows, every down unit (kDownRows rows of one slot) needs a
+// wave, and a workgroup's kWaves units span at most two slots.  Otherwise
+// the caller uses separate launches.
+bool fused_fits(const FusedArgs& a, int grid, bool SH, bool A4) {
+    const long long RU = (long long)a.K * a.I;
+    const long long nw = (long long)grid * kWaves;
+    const long long dpu = (a.H + kDownRows - 1) / kDownRows;
+    if (grid < a.E || grid > CTRL_WORDS - FW_EPOCH || (RU + nw - 1) / nw > 2 * kMaxUp ||
+        (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw || dpu < kWaves - 1)
+        return false;
+    // shared expert: at most 4 h-code quads (16 up rows) per workgroup and
+    // two down rows per wave
+    if (SH && (a.S / 4 > 4LL * grid || a.H > 2 * nw)) return false;
+    // W4A4: a workgroup's up rows are whole 16-row blocks
+    if (A4) {
+        const long long wg_rows = 16 * ((RU / 16 + grid - 1) / grid);
+        if (RU % 16 != 0 || wg_rows > kMaxWgUp || (wg_rows + kWaves - 1) / kWaves > 2 * kMaxUp) return false;
+    }
+    return true;
+}
+
 template <int FMT, int C, int C2, bool SH, bool A4>
 q4moe_status launch_fused_v(const FusedArgs& a, hipStream_t s, int variant) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
     const int grid = fused_grid<FMT, C, C2, SH, A4>(dev, variant);
-    // The router needs one workgroup per expert; every wave's up rows must fit
-    // in kMaxUp passes (all loads in flight at once), a workgroup stages at
-    // most kMaxWgUp up rows, every down unit (kDownRows rows of one slot)
-    // needs a wave, and a workgroup's kWaves units span at most two slots.
-    // Otherwise the caller uses separate launches.
-    const long long RU = (long long)a.K * a.I;
-    const long long nw = (long long)grid * kWaves;
-    const long long dpu = (a.H + kDownRows - 1) / kDownRows;
-    if (grid < a.E || grid > CTRL_WORDS - FW_EPOCH || (RU + nw - 1) / nw > 2 * kMaxUp || (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw ||
-        dpu < kWaves - 1)
-        return Q4MOE_EUNSUPPORTED;
-    // shared expert: at most 4 h-code quads (16 up rows) per workgroup and
-    // two down rows per wave
-    if (SH && (a.S / 4 > 4LL * grid || a.H > 2 * nw)) return Q4MOE_EUNSUPPORTED;
-    // W4A4: a workgroup's up rows are whole 16-row blocks
-    if (A4) {
-        const long long wg_rows = 16 * ((RU / 16 + grid - 1) / grid);
-        if (RU % 16 != 0 || wg_rows > kMaxWgUp || (wg_rows + kWaves - 1) / kWaves > 2 * kMaxUp)
-            return Q4MOE_EUNSUPPORTED;
-    }
+    if (!fused_fits(a, grid, SH, A4)) return Q4MOE_EUNSUPPORTED;
     hipLaunchKernelGGL((k_decode_fused<FMT, C, C2, SH, A4>), dim3(grid), dim3(64 * kWaves), 0, s, a);
     return launched("fused decode");
+}
+
+// The stacked decode: the same grid rule (one workgroup per CU, all resident).
+int g_stack_grid[kMaxDevices][16];
+
+template <int FMT, int C, int C2>
+q4moe_status launch_stack_v(const StackArgs& sa, hipStream_t s, int variant) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(Q4MOE_EDEVICE, "hipGetDevice failed");
+    if (dev < 0 || dev >= kMaxDevices) return Q4MOE_EUNSUPPORTED;
+    int& grid = g_stack_grid[dev][variant];
+    if (grid == 0) {
+        int cus = 0, per_cu = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_decode_stack<FMT, C, C2>, 64 * kWaves, 0) !=
+                hipSuccess)
+            return Q4MOE_EUNSUPPORTED;
+        grid = per_cu < 1 ? -1 : cus;
+    }
+    if (grid < 0 || !fused_fits(sa.a, grid, false, false)) return Q4MOE_EUNSUPPORTED;
+    hipLaunchKernelGGL((k_decode_stack<FMT, C, C2>), dim3(grid), dim3(64 * kWaves), 0, s, sa);
+    return launched("stacked decode");
+}
+
+template <int FMT>
+q4moe_status launch_stack(const StackArgs& sa, hipStream_t s) {
+    const int C = (sa.a.H / 32 + 31) / 32, C2 = (sa.a.I / 32 + 63) / 64;
+    const int v = (C - 1) * 2 + (C2 - 1);
+    const int slot = v + (FMT == FMT_NVFP4 ? 0 : 8);
+    switch (v) {
+        case 0: return launch_stack_v<FMT, 1, 1>(sa, s, slot);
+        case 1: return launch_stack_v<FMT, 1, 2>(sa, s, slot);
+        case 2: return launch_stack_v<FMT, 2, 1>(sa, s, slot);
+        case 3: return launch_stack_v<FMT, 2, 2>(sa, s, slot);
+        case 4: return launch_stack_v<FMT, 3, 1>(sa, s, slot);
+        case 5: return launch_stack_v<FMT, 3, 2>(sa, s, slot);
+        case 6: return launch_stack_v<FMT, 4, 1>(sa, s, slot);
+        case 7: return launch_stack_v<FMT, 4, 2>(sa, s, slot);
+    }
+    return Q4MOE_EUNSUPPORTED;
 }
 
 template <int FMT, bool SH = false, bool A4 = false>
@@ -1088,6 +1135,96 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex, 
                                 int32_t n_tok, uint16_t* y_bf16, int32_t* ids, float* w, void* ws,
                                 size_t ws_bytes, void* stream) {
     return decode_impl(r, ex, nullptr, x_bf16, n_tok, y_bf16, ids, w, ws, ws_bytes, stream);
+}
+
+size_t q4moe_w4a16_decode_stack_ws_bytes(const q4moe_router* r, const q4moe_experts* ex) {
+    return q4moe_w4a16_decode_ws_bytes(r, ex, 1);
+}
+
+q4moe_status q4moe_w4a16_decode_stack(const q4moe_router* routers, const q4moe_experts* experts, int32_t n_layers,
+                                      const uint16_t* const* x_bf16, uint16_t* const* y_bf16, int32_t chain,
+                                      int32_t* const* ids, float* const* w, void* ws, size_t ws_bytes,
+                                      void* stream) {
+    if (!routers || !experts || !x_bf16 || !y_bf16) return fail(Q4MOE_EINVAL, "routers / experts / x / y is NULL");
+    if (n_layers < 1 || n_layers > 4096) return fail(Q4MOE_EINVAL, "n_layers %d outside [1, 4096]", n_layers);
+    const q4moe_router* r0 = &routers[0];
+    const q4moe_experts* e0 = &experts[0];
+    q4moe_status st;
+    for (int l = 0; l < n_layers; ++l) {
+        const q4moe_router* r = &routers[l];
+        const q4moe_experts* ex = &experts[l];
+        if ((st = check_router(r)) != Q4MOE_OK || (st = check_experts(ex, r)) != Q4MOE_OK) return st;
+        if (r->n_experts != r0->n_experts || r->hidden != r0->hidden || r->top_k != r0->top_k ||
+            ex->inter != e0->inter || ex->fmt != e0->fmt)
+            return fail(Q4MOE_EINVAL, "layer %d's shape or format differs from layer 0's", l);
+        const uint16_t* x = x_bf16[l];
+        if (!(chain && l > 0) && (!x || !aligned(x, 16)))
+            return fail(x ? Q4MOE_EALIGN : Q4MOE_EINVAL, "x of layer %d is NULL or not 16-byte aligned", l);
+        if (!y_bf16[l] || !aligned(y_bf16[l], 16))
+            return fail(y_bf16[l] ? Q4MOE_EALIGN : Q4MOE_EINVAL, "y of layer %d is NULL or not 16-byte aligned", l);
+        if ((ids && ids[l] && !aligned(ids[l], 4)) || (w && w[l] && !aligned(w[l], 4)))
+            return fail(Q4MOE_EALIGN, "ids / w of layer %d not 4-byte aligned", l);
+    }
+    const DecodeWs lay = decode_layout(r0, e0, nullptr, nullptr, 1);
+    if ((st = check_ws(ws, ws_bytes, lay.total)) != Q4MOE_OK) return st;
+    if ((st = device_ready()) != Q4MOE_OK) return st;
+    hipStream_t s = (hipStream_t)stream;
+    StackArgs sa{};
+    FusedArgs& f = sa.a;
+    f.E = r0->n_experts;
+    f.H = e0->hidden;
+    f.I = e0->inter;
+    f.K = r0->top_k;
+    f.ctrl = at<uint32_t>(ws, lay.r.ctrl);
+    f.sc_tag = at<unsigned long long>(ws, lay.sc_tag);
+    f.h_tag = at<unsigned long long>(ws, lay.h_tag);
+    f.z_tag = at<unsigned long long>(ws, lay.z_tag);
+    f.ids = at<int32_t>(ws, lay.r.ids);
+    f.w = at<float>(ws, lay.r.w);
+    f.h = at<float>(ws, lay.h);
+    f.y32 = at<float>(ws, lay.y32);
+    f.su_w = f.su_in = f.sd_w = f.sd_in = 1.0f;
+    sa.y_tag = at<unsigned long long>(ws, lay.y_tag);
+    sa.chain = chain ? 1 : 0;
+    // one launch per kStackMax layers; the first layer of a later launch
+    // reads the previous layer's y from memory (the launches are in order)
+    for (int l0 = 0; l0 < n_layers; l0 += kStackMax) {
+        const int n = std::min(kStackMax, n_layers - l0);
+        sa.n_layers = n;
+        for (int i = 0; i < n; ++i) {
+            const int l = l0 + i;
+            const q4moe_router* r = &routers[l];
+            const q4moe_experts* ex = &experts[l];
+            StackLayer& L = sa.layer[i];
+            L.wg = r->w_g;
+            L.bias = r->bias;
+            L.x = chain && l > 0 ? (i == 0 ? y_bf16[l - 1] : nullptr) : x_bf16[l];
+            L.upc = ex->up_codes;
+            L.ups = ex->up_scales;
+            L.upg = ex->up_gscale;
+            L.dnc = ex->down_codes;
+            L.dns = ex->down_scales;
+            L.dng = ex->down_gscale;
+            L.y = y_bf16[l];
+            L.ids_out = ids ? ids[l] : nullptr;
+            L.w_out = w ? w[l] : nullptr;
+        }
+        st = e0->fmt == Q4MOE_NVFP4 ? launch_stack<FMT_NVFP4>(sa, s) : launch_stack<FMT_INT4>(sa, s);
+        if (st == Q4MOE_EUNSUPPORTED) {
+            // a shape or device the one launch does not fit: one call per
+            // layer, in the same order and with the same results
+            for (int i = 0; i < n; ++i) {
+                const int l = l0 + i;
+                const uint16_t* x = chain && l > 0 ? y_bf16[l - 1] : x_bf16[l];
+                st = decode_impl(&routers[l], &experts[l], nullptr, x, 1, y_bf16[l], ids ? ids[l] : nullptr,
+                                 w ? w[l] : nullptr, ws, ws_bytes, stream);
+                if (st != Q4MOE_OK) return st;
+            }
+        } else if (st != Q4MOE_OK) {
+            return st;
+        }
+    }
+    return Q4MOE_OK;
 }
 
 size_t q4moe_w4a16_grouped_ws_bytes(const q4moe_router* r, const q4moe_experts* ex, int32_t n_tok) {

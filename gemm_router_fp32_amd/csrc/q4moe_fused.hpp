@@ -130,6 +130,38 @@ struct FusedArgs {
     uint8_t* hq_scales;           // [K][I/16]
 };
 
+// A stack of single-token layers of one shape in one launch: the per-layer
+// pointers (the rest of FusedArgs is common), at most kStackMax layers.
+constexpr int kStackMax = 24;
+struct StackLayer {
+    const float* wg;
+    const float* bias;
+    const uint16_t* x;
+    const uint8_t* upc;
+    const void* ups;
+    const float* upg;
+    const uint8_t* dnc;
+    const void* dns;
+    const float* dng;
+    uint16_t* y;
+    int32_t* ids_out;  // nullable
+    float* w_out;      // nullable
+};
+struct StackArgs {
+    FusedArgs a;
+    unsigned long long* y_tag;  // [kReplicas][H/2]: (two bf16 of y, epoch)
+    int n_layers;
+    int chain;  // layer l + 1 takes layer l's y as its x
+    StackLayer layer[kStackMax];
+};
+// Where a layer of the stack stands: its index, whether it takes the
+// previous layer's y as x, and the y tags (null outside a stack).
+struct StackCtl {
+    int layer;
+    int chain;
+    unsigned long long* y_tag;
+};
+
 __device__ __forceinline__ unsigned long long tagged(float v, uint32_t ep) {
     return ((unsigned long long)ep << 32) | __float_as_uint(v);
 }
@@ -307,8 +339,12 @@ __device__ __forceinline__ uint2 fp8x4_bf16(uint32_t v) {
 // the fly: x by the waves that do not poll the scores, h by every workgroup
 // for the slots it uses, once the h hand-off is in; both replaced in LDS by
 // their exact dequantized values, so the GEMVs themselves are unchanged.
-template <int FMT, int C, int C2, bool SH, bool A4>
-__global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
+// One single-token layer, run by every workgroup of the launch; ep is the
+// layer's epoch (one more than the last layer's, on this workspace).  STK:
+// the layer is one of a stack (k_decode_stack), and from the second layer on
+// it starts its routing only once the previous layer's y is complete.
+template <int FMT, int C, int C2, bool SH, bool A4, bool STK>
+__device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t ep, const StackCtl& sk) {
     __shared__ float s_part[kWaves];
     __shared__ __attribute__((aligned(16))) long long s_comp[256];  // selection composites (key, index)
     __shared__ float s_scores[256];
@@ -339,13 +375,6 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     Q4MOE_PHASE(0);
     // selection slots past E: composites below every key (never chosen)
     if ((int)threadIdx.x >= a.E && threadIdx.x < 256) s_comp[threadIdx.x] = topk_comp(__builtin_nanf(""), threadIdx.x);
-    // This call's epoch: one more than the last call's.  Each workgroup keeps
-    // its own copy in word FW_EPOCH + b, which only workgroup b of each call
-    // reads and writes; every call runs every workgroup once, so all copies
-    // advance together and stay equal.  Every wave loads it and first uses it
-    // after the router, so nothing waits for it here.
-    const uint32_t ep =
-        __hip_atomic_load(a.ctrl + FW_EPOCH + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     // Thread 128 + e polls the score of expert e: waves 2 and up store
     // nothing in the router phase, so their poll results do not wait for
     // the score stores to complete.
@@ -362,16 +391,62 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // (clamped; the extra one is masked)
     float4 wv[2];
     uint2 xb[2];
+    // In a chained stack, x of every layer but the first is the previous
+    // layer's y, which arrives with its tags (below).
+    const bool x_from_y = STK && sk.chain && sk.layer > 0;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int j = min(rlo + lane + 64 * i, rhi - 1);
         wv[i] = wr[j];
-        xb[i] = *reinterpret_cast<const uint2*>(a.x + 4 * j);
+        if (!x_from_y) xb[i] = *reinterpret_cast<const uint2*>(a.x + 4 * j);
     }
 
     // x into LDS once per workgroup (the up GEMV reads it from there)
-    if (!A4 && (int)threadIdx.x < a.H / 8)
+    if (!A4 && !x_from_y && (int)threadIdx.x < a.H / 8)
         s_x[lds_pad_u128(threadIdx.x)] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+    if constexpr (STK) {
+        if (sk.layer > 0) {
+            // The previous layer's y, complete: its (two bf16, epoch) values,
+            // one copy per workgroup, thread t polling pairs t + 512 m.  The
+            // routing waits for every one of them, as the next call would
+            // wait for the previous one's end; in a chain they are x.
+            const int np = a.H / 2;
+            const unsigned long long* src = sk.y_tag + (size_t)rep * np;
+            const uint32_t epy = ep - 1u;
+            uint32_t pend = 0;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                if ((int)threadIdx.x + 512 * m < np) pend |= 1u << m;
+            for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
+                unsigned long long v[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + threadIdx.x + 512 * m) : 0ull;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    if (((pend >> m) & 1u) && tag_is(v[m], epy)) {
+                        if (x_from_y) {
+                            const int t = threadIdx.x + 512 * m;  // elements 2t, 2t + 1
+                            reinterpret_cast<uint32_t*>(&s_x[lds_pad_u128(t >> 2)])[t & 3] = (uint32_t)v[m];
+                        }
+                        pend &= ~(1u << m);
+                    }
+                }
+                if (polls > kPollLimit) {
+                    if (lane == 0) atomicOr(flags, 1u);
+                    break;
+                }
+                if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        __syncthreads();
+        if (x_from_y) {
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int j = min(rlo + lane + 64 * i, rhi - 1);  // elements 4j .. 4j + 3
+                xb[i] = reinterpret_cast<const uint2*>(&s_x[lds_pad_u128(j >> 1)])[j & 1];
+            }
+        }
+    }
     // x pieces the waves that will not poll the scores quantize during the
     // score hand-off (eight values each, at most two per thread: H / 8 <= 512
     // pieces over at least four such waves), loaded now with the router's
@@ -561,21 +636,17 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // Shared expert down rows: after the score hand-off, for the same reason
     // (two smaller bursts delay the routing less than one).
     if constexpr (SH) issue_sh_dn();
-    Q4MOE_WAVE_MARK(0);
     if (a.E <= 64)
         topk_stage1<64>(a, s_comp, s_list);
     else if (a.E <= 128)
         topk_stage1<128>(a, s_comp, s_list);
     else
         topk_stage1<256>(a, s_comp, s_list);
-    Q4MOE_WAVE_MARK(1);
     __syncthreads();
     topk_stage2(a, s_list, s_scores, s_sel_ids, s_sel_sc);
-    Q4MOE_WAVE_MARK(2);
     __syncthreads();
     int* ids = s_sel_ids;
     float* wsel = s_w_all[wave];
-    Q4MOE_WAVE_MARK(3);
     // the workgroup's epoch copy advances now, long before the kernel ends,
     // so nothing is left for its last instructions
     if (threadIdx.x == 0) __hip_atomic_store(a.ctrl + FW_EPOCH + blockIdx.x, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -726,6 +797,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         }
     }
     Q4MOE_PHASE(9);
+    Q4MOE_WAVE_MARK(0);
 
     // ---- P: publish h, then issue the down loads, then poll the h of the
     // slots the workgroup's down rows use into LDS.  (A poll result counts
@@ -821,6 +893,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         if constexpr (FMT == FMT_NVFP4) gdn = a.dng[ids[dslot]];
     }
     compiler_fence();
+    Q4MOE_WAVE_MARK(1);
     // The polls leave once every wave's down loads have: they reach the
     // memory system behind them, by when the h they read has been published.
     __syncthreads();
@@ -972,6 +1045,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
         }
     }
+    Q4MOE_WAVE_MARK(2);
     __syncthreads();
     Q4MOE_PHASE(5);
 
@@ -1087,6 +1161,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
         const float wg = wsel[dslot] * gdn;
         if ((lane & 7) == 7 && drow0 + rl < a.H) put_tag(a.z_tag + (uint32_t)(dslot * a.H + drow0 + rl), wg * zs, ep);
     }
+    Q4MOE_WAVE_MARK(3);
     Q4MOE_PHASE(6);
 
     // ---- C: block b of 64 rows is combined by workgroup b * grid / nblocks
@@ -1121,18 +1196,72 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
             }
             __builtin_amdgcn_s_sleep(1);
         }
+        uint32_t yb = 0u;
         if (r < a.H) {
             float yv = 0.f;
 #pragma unroll
             for (int s2 = 0; s2 < NS; ++s2)
                 if (s2 < ns) yv += (pend >> s2) & 1u ? 0.f : part[s2];
+            yb = f32_to_bf16_rne(yv);
             a.y32[r] = yv;
-            a.y[r] = (uint16_t)f32_to_bf16_rne(yv);
+            a.y[r] = (uint16_t)yb;
+        }
+        if constexpr (STK) {
+            // y for the next layer of the stack: rows 2t, 2t + 1 as one
+            // (two bf16, epoch) value, kReplicas copies
+            const uint32_t yo = (uint32_t)__builtin_amdgcn_mov_dpp((int)yb, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+            if ((lane & 1) == 0 && r < a.H) {
+                const uint32_t pair = yb | (yo << 16);
+#pragma unroll
+                for (int rp = 0; rp < kReplicas; ++rp)
+                    put_tag(sk.y_tag + (size_t)rp * (a.H / 2) + r / 2, __uint_as_float(pair), ep);
+            }
         }
     }
     Q4MOE_PHASE(7);
 
     Q4MOE_PHASE(10);
+}
+
+// One layer for one token.
+template <int FMT, int C, int C2, bool SH, bool A4>
+__global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
+    // This call's epoch: one more than the last call's.  Each workgroup keeps
+    // its own copy in word FW_EPOCH + b, which only workgroup b of each call
+    // reads and writes; every call runs every workgroup once, so all copies
+    // advance together and stay equal.  Every wave loads it and first uses it
+    // after the router, so nothing waits for it here.
+    const uint32_t ep =
+        __hip_atomic_load(a.ctrl + FW_EPOCH + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
+    fused_layer<FMT, C, C2, SH, A4, false>(a, ep, StackCtl{0, 0, nullptr});
+}
+
+// A stack of single-token layers of one shape in one launch, in order: layer
+// l takes epoch e + 1 + l (e: the last epoch on this workspace), and from the
+// second layer on each starts its routing only once the previous layer's y
+// is complete on the device, the order of one launch per layer without the
+// device's gap between launches.
+template <int FMT, int C, int C2>
+__global__ __launch_bounds__(64 * kWaves, 1) void k_decode_stack(StackArgs s) {
+    const uint32_t ep0 = __hip_atomic_load(s.a.ctrl + FW_EPOCH + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll 1
+    for (int l = 0; l < s.n_layers; ++l) {
+        FusedArgs a = s.a;
+        const StackLayer& L = s.layer[l];
+        a.wg = L.wg;
+        a.bias = L.bias;
+        a.x = L.x;
+        a.upc = L.upc;
+        a.ups = L.ups;
+        a.upg = L.upg;
+        a.dnc = L.dnc;
+        a.dns = L.dns;
+        a.dng = L.dng;
+        a.y = L.y;
+        a.ids_out = L.ids_out;
+        a.w_out = L.w_out;
+        fused_layer<FMT, C, C2, false, false, true>(a, ep0 + 1u + (uint32_t)l, StackCtl{l, s.chain, s.y_tag});
+    }
 }
 
 }  // namespace q4moe

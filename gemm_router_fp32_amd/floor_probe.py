@@ -173,6 +173,26 @@ def phase(torch, fmt):
           f"{t_dn - t_up:.2f} us for {expert_bytes} expert bytes = "
           f"{expert_bytes / ((t_dn - t_up) * 1e-6) / 1e9:.1f} GB/s")
     print(f"expert_phase_gbps={expert_bytes / ((t_dn - t_up) * 1e-6) / 1e9:.1f}")
+    # per-wave marks: 0 up GEMV done, 1 h published and down loads issued,
+    # 2 h polled into LDS, 3 down GEMV done (every wave of every workgroup)
+    wm = []
+    for s_ in slots:
+        b = buf[s_].astype(np.float64)
+        w = b[:, 16:48].reshape(-1, 8, 4)
+        wm.append((w - b[:, 0].min()) * 0.01)
+    wm = np.stack(wm)  # [layers, wgs, waves, 4]
+    steps = [("up GEMV done", wm[..., 0]), ("h published, down loads issued", wm[..., 1]),
+             ("h polled into LDS", wm[..., 2]), ("down GEMV done", wm[..., 3])]
+    print("\n| per-wave mark | median (us) | p90 | max |\n|---|---|---|---|")
+    for name, v in steps:
+        print(f"| {name} | {np.median(v):.2f} | {np.median(np.percentile(v, 90, axis=(1, 2))):.2f} | "
+              f"{np.median(v.max(axis=(1, 2))):.2f} |")
+    durs = [("publish + down-load issue", wm[..., 1] - wm[..., 0]), ("barrier + h poll", wm[..., 2] - wm[..., 1]),
+            ("barrier + down GEMV", wm[..., 3] - wm[..., 2])]
+    print("\n| per-wave span | median (us) | p90 | max |\n|---|---|---|---|")
+    for name, v in durs:
+        print(f"| {name} | {np.median(v):.2f} | {np.median(np.percentile(v, 90, axis=(1, 2))):.2f} | "
+              f"{np.median(v.max(axis=(1, 2))):.2f} |")
 
 
 def main():

@@ -82,6 +82,8 @@ _SIGS = {
     "q4moe_w4a16_decode": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_decode_taps": (_i32, [_p, _p, _i32, _p]),
     "q4moe_w4a16_decode_noalloc": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p]),
+    "q4moe_w4a16_decode_stack_ws_bytes": (_sz, [_p, _p]),
+    "q4moe_w4a16_decode_stack": (_i32, [_p, _p, _i32, _p, _p, _i32, _p, _p, _p, _sz, _p]),
     "q4moe_w4a16_grouped_ws_bytes": (_sz, [_p, _p, _i32]),
     "q4moe_w4a16_grouped": (_i32, [_p, _p, _p, _i32, _p, _p, _p, _p, _sz, _p]),
     "q4moe_w4a4_decode_ws_bytes": (_sz, [_p, _p, _i32]),
@@ -238,6 +240,32 @@ def q4moe_w4a16_decode(router, experts, x, y, ids=None, w=None, ws=None, stream=
         ws = workspace(q4moe_w4a16_decode_ws_bytes(router, experts, n_tok), x.device)
     _check(lib().q4moe_w4a16_decode(ctypes.byref(router.s), ctypes.byref(experts.s), _ptr(x), n_tok, _ptr(y),
                                     _ptr(ids), _ptr(w), _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
+
+
+def q4moe_w4a16_decode_stack_ws_bytes(router, experts):
+    return lib().q4moe_w4a16_decode_stack_ws_bytes(ctypes.byref(router.s), ctypes.byref(experts.s))
+
+
+def _ptr_array(ts):
+    arr = (ctypes.c_void_p * len(ts))(*[None if t is None else t.data_ptr() for t in ts])
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def q4moe_w4a16_decode_stack(routers, experts, xs, ys, chain=False, ids=None, w=None, ws=None, stream=None):
+    """len(routers) single-token layers in order (x of layer l > 0 is layer l - 1's y when chain)."""
+    n = len(routers)
+    rs = (RouterS * n)(*[r.s for r in routers])
+    es = (ExpertsS * n)(*[e.s for e in experts])
+    xa, xp = _ptr_array(xs)
+    ya, yp = _ptr_array(ys)
+    ia, ip = _ptr_array(ids) if ids is not None else (None, None)
+    wa, wp = _ptr_array(w) if w is not None else (None, None)
+    if ws is None:
+        ws = workspace(q4moe_w4a16_decode_stack_ws_bytes(routers[0], experts[0]), ys[0].device)
+    _check(lib().q4moe_w4a16_decode_stack(ctypes.cast(rs, ctypes.c_void_p), ctypes.cast(es, ctypes.c_void_p), n,
+                                          xp, yp, 1 if chain else 0, ip, wp, _ptr(ws), ws.numel(),
+                                          _stream(stream)))
     return ws
 
 

@@ -161,6 +161,29 @@ q4moe_status q4moe_w4a16_decode(const q4moe_router* r, const q4moe_experts* ex,
                                 const uint16_t* x_bf16, int32_t n_tok, uint16_t* y_bf16,
                                 int32_t* ids, float* w, void* ws, size_t ws_bytes, void* stream);
 
+/* A stack of n_layers single-token W4A16 routed-MoE layers of one shape and
+ * format (routers[l], experts[l], 1 <= n_layers <= 4096) in as few launches
+ * as the device allows: one per 24 layers.  A decode step runs the model's
+ * layers back to back, and its floor is the GPU work alone ([W] Step 7: one
+ * graph for the drafter's passes leaves the step within ~5% of its GPU
+ * work); between two launches this device idles about 3 us, a fifth of a
+ * layer, so the stack runs in one persistent launch instead.  Order and
+ * results are those of n_layers q4moe_w4a16_decode calls in sequence: layer
+ * l + 1 starts its routing only once every row of layer l's y is written and
+ * visible on the device.  x_bf16[l], y_bf16[l]: bf16 [hidden], 16-byte
+ * aligned.  chain != 0: layer l + 1 takes layer l's y as its x (x_bf16[l]
+ * for l > 0 is not read and may be NULL).  ids / w: NULL, or arrays of
+ * n_layers (nullable) pointers receiving each layer's routing.  The
+ * workspace is that of a one-token q4moe_w4a16_decode (the taps hold the last
+ * layer's values).  Every workgroup of a launch must be resident at once,
+ * as for the one-token decode; a shape the single launch does not fit runs
+ * as one call per layer, with the same results. */
+size_t q4moe_w4a16_decode_stack_ws_bytes(const q4moe_router* r, const q4moe_experts* ex);
+q4moe_status q4moe_w4a16_decode_stack(const q4moe_router* routers, const q4moe_experts* experts,
+                                      int32_t n_layers, const uint16_t* const* x_bf16,
+                                      uint16_t* const* y_bf16, int32_t chain, int32_t* const* ids,
+                                      float* const* w, void* ws, size_t ws_bytes, void* stream);
+
 /* The grouped W4A16 path of q4moe_w4a16_decode for any token count
  * (1 <= n_tok <= 65536; hidden and inter multiples of 64, else
  * Q4MOE_EUNSUPPORTED): the same arguments, results and precision as
@@ -179,7 +202,7 @@ q4moe_status q4moe_w4a16_grouped(const q4moe_router* r, const q4moe_experts* ex,
  * (device memory held from load until the process ends) serves as the
  * workspace.  It allocates nothing.  Shapes whose workspace would exceed the
  * scratch return Q4MOE_EWORKSPACE (1-4 tokens of the 128 x 2688 x 1856
- * top-6 layer take at most 3.02 MiB).  Every call on a GPU shares that GPU's
+ * top-6 layer take at most 3.15 MiB).  Every call on a GPU shares that GPU's
  * scratch: calls that overlap in time on one GPU race and must not be
  * issued (calls in order on one stream are fine).  The expired-wait flag of
  * the one-launch decode is kept in the scratch and not reported. */

@@ -269,3 +269,27 @@ def test_decode_shared_q4_validation(L):
     assert L.q4moe_w4a16_decode_shared_q4_taps(ctypes.byref(r), ctypes.byref(ex), ctypes.byref(sh4()), 4,
                                                ctypes.byref(t)) == g.OK
     assert t.xq == 0 and t.sh_hq == 0 and 0 < t.sh_h32 and 0 < t.y32
+
+
+def test_decode_stack_validation(L):
+    r, ex = _router(), _experts()
+    rs = (g.RouterS * 2)(r, r)
+    es = (g.ExpertsS * 2)(ex, ex)
+    xs = (ctypes.c_void_p * 2)(A16, A16)
+    ys = (ctypes.c_void_p * 2)(A16, A16)
+    need = L.q4moe_w4a16_decode_stack_ws_bytes(ctypes.byref(r), ctypes.byref(ex))
+    assert need == L.q4moe_w4a16_decode_ws_bytes(ctypes.byref(r), ctypes.byref(ex), 1)
+
+    def call(rs=rs, es=es, n=2, xs=xs, ys=ys, chain=0, wsb=need):
+        cast = lambda a: None if a is None else ctypes.cast(a, ctypes.c_void_p)
+        return L.q4moe_w4a16_decode_stack(cast(rs), cast(es), n, cast(xs), cast(ys), chain, None, None, A16, wsb,
+                                          None)
+
+    assert call(n=0) == g.EINVAL
+    assert call(rs=None) == g.EINVAL
+    assert call(ys=None) == g.EINVAL
+    assert call(es=(g.ExpertsS * 2)(ex, _experts(I=1856 + 32))) == g.EINVAL  # shapes differ
+    assert b"differs" in L.q4moe_last_error()
+    assert call(xs=(ctypes.c_void_p * 2)(A16, None)) == g.EINVAL  # x of layer 1 outside a chain
+    assert call(xs=(ctypes.c_void_p * 2)(A16, A16 + 2)) == g.EALIGN
+    assert call(wsb=need - 16) == g.EWORKSPACE
