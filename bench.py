@@ -213,10 +213,8 @@ def time_stack(torch, g, layers, steps, warmup):
     return ms_step, float(np.mean(durs[LAYERS:])), flags, per
 
 
-def time_stack_launch(torch, g, layers, steps, warmup):
-    """The same 23 layers through q4moe_w4a16_decode_stack: one launch per
-    step, each layer starting its routing once the previous layer's y is
-    complete (the order of the per-layer graph, without its launch gaps)."""
+def stack_launch_step(g, layers):
+    """One call of q4moe_w4a16_decode_stack over the layers, and its workspace."""
     routers = [L["r"] for L in layers]
     banks = [L["ex"] for L in layers]
     xs = [L["x"][0] for L in layers]
@@ -225,6 +223,14 @@ def time_stack_launch(torch, g, layers, steps, warmup):
 
     def step():
         g.q4moe_w4a16_decode_stack(routers, banks, xs, ys, ws=ws)
+    return step, ws
+
+
+def time_stack_launch(torch, g, layers, steps, warmup):
+    """The same 23 layers through q4moe_w4a16_decode_stack: one launch per
+    step, each layer starting its routing once the previous layer's y is
+    complete (the order of the per-layer graph, without its launch gaps)."""
+    step, ws = stack_launch_step(g, layers)
 
     for _ in range(3):
         step()

@@ -260,6 +260,9 @@ bool fused_fits(const FusedArgs& a, int grid, bool SH, bool A4) {
     if (grid < a.E || grid > CTRL_WORDS - FW_EPOCH || (RU + nw - 1) / nw > 2 * kMaxUp ||
         (RU + grid - 1) / grid > kMaxWgUp || a.K * dpu > nw || dpu < kWaves - 1)
         return false;
+    // block scales are read as 8-byte pieces of a row's region (at least 8
+    // bytes: hidden >= 256) and 16-byte pieces of a down unit's whole rows
+    if (a.H < 256 || a.H % kDownRows != 0) return false;
     // shared expert: at most 4 h-code quads (16 up rows) per workgroup and
     // two down rows per wave
     if (SH && (a.S / 4 > 4LL * grid || a.H > 2 * nw)) return false;

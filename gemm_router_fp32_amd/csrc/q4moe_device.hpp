@@ -349,6 +349,12 @@ __device__ __forceinline__ uint4 ldg16(const uint8_t* p) { return *reinterpret_c
 // Streaming (read-once) 16-byte load: non-temporal, so weight streams do not
 // displace reused data (router weights, activations) from the caches.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// 8 and 16 bytes at an address that is only known to be 4-byte aligned
+typedef uint32_t u32x2_a4 __attribute__((ext_vector_type(2), aligned(4)));
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ u32x2 ldg8_a4(const uint8_t* p) { return *reinterpret_cast<const u32x2_a4*>(p); }
+__device__ __forceinline__ u32x4 ldg16_a4(const uint8_t* p) { return *reinterpret_cast<const u32x4_a4*>(p); }
 __device__ __forceinline__ uint4 ldg16_stream(const uint8_t* p) {
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);

@@ -85,6 +85,22 @@ __device__ __forceinline__ int lds_pad_u16(int j) { return j + 8 * (j >> 5); }  
 __device__ __forceinline__ int lds_pad_u128(int t) { return t + (t >> 2); }      // 16-byte piece t of 16-bit values
 constexpr int kLdsH16Lo = 2 * 4096 + 2 * 4096 / 4;  // 16-bit h: the lo halves start here (past the padded hi halves)
 
+// Block scales reach the GEMV lanes through LDS: a row's scales (or a down
+// unit's eight rows', which are adjacent) are read with one wide load per
+// lane, 8 or 16 bytes at 4-byte-aligned offsets clamped into the region, and
+// each wave stages them in its own kScaleStage bytes of LDS, from which a
+// lane takes the 2 bytes of each of its chunks.  One load instruction per
+// row pass (and one per down unit) replaces one 2-byte load per chunk and
+// row: the load path pays per instruction, not per byte.
+constexpr int kScaleStage = 2048;  // per wave: the 8 down rows' scales (I <= 2048), or 2 kMaxUp up rows of 256
+
+// The 4-byte-aligned region [b4, b4 + span4) holding bytes [s, s + n) of a
+// scale array (s even, n >= 8, array 4-byte aligned and a multiple of 4 long).
+__device__ __forceinline__ void scale_region(uint32_t s, uint32_t n, uint32_t& b4, uint32_t& span4) {
+    b4 = s & ~3u;
+    span4 = ((s + n + 3u) & ~3u) - b4;
+}
+
 // Workspace control words of the fused decode.
 enum : int {
     FW_EPOCH = 256,  // [grid]: workgroup b's epoch of the last call (at most CTRL_WORDS - FW_EPOCH workgroups)
@@ -344,7 +360,8 @@ __device__ __forceinline__ uint2 fp8x4_bf16(uint32_t v) {
 // the layer is one of a stack (k_decode_stack), and from the second layer on
 // it starts its routing only once the previous layer's y is complete.
 template <int FMT, int C, int C2, bool SH, bool A4, bool STK>
-__device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t ep, const StackCtl& sk) {
+__device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t ep, const StackCtl& sk, const uint32_t tid,
+                                            const uint32_t bid) {
     __shared__ float s_part[kWaves];
     __shared__ __attribute__((aligned(16))) long long s_comp[256];  // selection composites (key, index)
     __shared__ float s_scores[256];
@@ -359,26 +376,28 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     uint16_t* const s_h16 = reinterpret_cast<uint16_t*>(s_h);
     __shared__ float s_hrow[kMaxWgUp];  // this workgroup's up results, before they are published
     __shared__ uint4 s_x[512 + 128];    // x (bf16, H <= 4096, padded), read once per workgroup
+    __shared__ __attribute__((aligned(16))) uint8_t s_scst[kWaves][kScaleStage];  // each wave's block scales
+    uint8_t* const my_sc = s_scst[tid >> 6];
     // shared expert: x and h codes decoded to bf16 (natural order), and this
     // workgroup's (at most 16) h codes before they are published
     __shared__ uint32_t s_xb[SH ? 2048 : 1], s_shb[SH ? 2048 : 1], s_shq[SH ? 4 : 1];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     const int seg = lane >> 5, li = lane & 31;
-    const int NW = gridDim.x * kWaves, gw = blockIdx.x * kWaves + wave;
+    const int NW = gridDim.x * kWaves, gw = bid * kWaves + wave;
     const int nchH = a.H / 32, nchI = a.I / 32;
     // Up rows: lane li of a 32-lane segment takes chunks c * lpr + li
     // (c < C), so each load instruction reads one contiguous run of the row.
     const int lpr = (nchH + C - 1) / C;
     uint32_t* flags = a.ctrl + CTRL_FLAGS;
-    const int rep = blockIdx.x % kReplicas;
+    const int rep = bid % kReplicas;
 
     Q4MOE_PHASE(0);
     // selection slots past E: composites below every key (never chosen)
-    if ((int)threadIdx.x >= a.E && threadIdx.x < 256) s_comp[threadIdx.x] = topk_comp(__builtin_nanf(""), threadIdx.x);
+    if ((int)tid >= a.E && tid < 256) s_comp[tid] = topk_comp(__builtin_nanf(""), tid);
     // Thread 128 + e polls the score of expert e: waves 2 and up store
     // nothing in the router phase, so their poll results do not wait for
     // the score stores to complete.
-    const int pe = (int)threadIdx.x - 128;
+    const int pe = (int)tid - 128;
     const bool poller = pe >= 0 && pe < a.E;
     const float bias = a.bias[poller ? pe : 0];
     // Router row of workgroup e < E (its waves split it); every workgroup
@@ -386,7 +405,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     // of the kernel's first loads leave together, before anything waits.
     const int nf4 = a.H / 4;
     const int rlo = wave * nf4 / kWaves, rhi = (wave + 1) * nf4 / kWaves;
-    const float4* wr = reinterpret_cast<const float4*>(a.wg + (size_t)((int)blockIdx.x < a.E ? blockIdx.x : 0) * a.H);
+    const float4* wr = reinterpret_cast<const float4*>(a.wg + (size_t)((int)bid < a.E ? bid : 0) * a.H);
     // a wave's share is at most 128 pieces (H <= 4096): two per lane
     // (clamped; the extra one is masked)
     float4 wv[2];
@@ -402,8 +421,8 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     }
 
     // x into LDS once per workgroup (the up GEMV reads it from there)
-    if (!A4 && !x_from_y && (int)threadIdx.x < a.H / 8)
-        s_x[lds_pad_u128(threadIdx.x)] = *reinterpret_cast<const uint4*>(a.x + 8 * threadIdx.x);
+    if (!A4 && !x_from_y && (int)tid < a.H / 8)
+        s_x[lds_pad_u128(tid)] = *reinterpret_cast<const uint4*>(a.x + 8 * tid);
     if constexpr (STK) {
         if (sk.layer > 0) {
             // The previous layer's y, complete: its (two bf16, epoch) values,
@@ -416,16 +435,16 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
             uint32_t pend = 0;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
-                if ((int)threadIdx.x + 512 * m < np) pend |= 1u << m;
+                if ((int)tid + 512 * m < np) pend |= 1u << m;
             for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
                 unsigned long long v[4];
 #pragma unroll
-                for (int m = 0; m < 4; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + threadIdx.x + 512 * m) : 0ull;
+                for (int m = 0; m < 4; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + tid + 512 * m) : 0ull;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     if (((pend >> m) & 1u) && tag_is(v[m], epy)) {
                         if (x_from_y) {
-                            const int t = threadIdx.x + 512 * m;  // elements 2t, 2t + 1
+                            const int t = tid + 512 * m;  // elements 2t, 2t + 1
                             reinterpret_cast<uint32_t*>(&s_x[lds_pad_u128(t >> 2)])[t & 3] = (uint32_t)v[m];
                         }
                         pend &= ~(1u << m);
@@ -472,8 +491,8 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     int sq0 = 0, sq1 = 0, shr = 0, sd0 = 0, sd1 = 0;
     if constexpr (SH) {
         const int nq = a.S / 4;
-        sq0 = share_lo(nq, blockIdx.x, gridDim.x);
-        sq1 = share_lo(nq, blockIdx.x + 1, gridDim.x);
+        sq0 = share_lo(nq, bid, gridDim.x);
+        sq1 = share_lo(nq, bid + 1, gridDim.x);
         shr = 4 * sq0 + 2 * wave + seg;
         sd0 = share_lo(a.H, gw, NW);
         sd1 = share_lo(a.H, gw + 1, NW);
@@ -501,8 +520,8 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     compiler_fence();  // keep every load above in the entry block
 
     // ---- R: workgroup e computes router logit e; its waves split the row
-    if ((int)blockIdx.x < a.E) {
-        const int e = blockIdx.x;
+    if ((int)bid < a.E) {
+        const int e = bid;
         float acc = 0.f;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -516,12 +535,12 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         acc = seg_sum_last<64>(acc);
         if (lane == 63) s_part[wave] = acc;
         __syncthreads();
-        if (threadIdx.x < kReplicas) {  // thread t publishes copy t
+        if (tid < kReplicas) {  // thread t publishes copy t
             float l = 0.f;
 #pragma unroll
             for (int v = 0; v < kWaves; ++v) l += s_part[v];
             const float sc = 1.0f / (1.0f + expf(-l));
-            put_tag(a.sc_tag + threadIdx.x * a.E + e, sc, ep);
+            put_tag(a.sc_tag + tid * a.E + e, sc, ep);
         }
     }
     Q4MOE_PHASE(1);
@@ -540,15 +559,15 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         // W4A4: a workgroup owns whole 16-row blocks of h (the quantizer's
         // blocks), so that it can quantize them itself before publishing
         const int nbk = RU / 16;
-        wu0 = 16 * share_lo(nbk, blockIdx.x, gridDim.x);
-        wu1 = 16 * share_lo(nbk, blockIdx.x + 1, gridDim.x);
+        wu0 = 16 * share_lo(nbk, bid, gridDim.x);
+        wu1 = 16 * share_lo(nbk, bid + 1, gridDim.x);
         u0 = wu0 + share_lo(wu1 - wu0, wave, kWaves);
         u1 = wu0 + share_lo(wu1 - wu0, wave + 1, kWaves);
     } else {
         u0 = share_lo(RU, gw, NW);
         u1 = share_lo(RU, gw + 1, NW);
-        wu0 = share_lo(RU, blockIdx.x * kWaves, NW);
-        wu1 = share_lo(RU, (blockIdx.x + 1) * kWaves, NW);
+        wu0 = share_lo(RU, bid * kWaves, NW);
+        wu1 = share_lo(RU, (bid + 1) * kWaves, NW);
     }
     // A wave's up units span at most two slots: slot(u) = us0 + (u >= ubnd).
     const int us0 = (u1 > u0 ? u0 : 0) / a.I, ubnd = (us0 + 1) * a.I;
@@ -561,7 +580,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     const int dslot = dwave ? gw / dpu : 0, drow0 = dwave ? (gw - dslot * dpu) * kDownRows : 0;
     // the workgroup's down units span slots sl0 .. sl1 (at most two: dpu >=
     // kWaves - 1 is checked on the host)
-    const int wdu0 = blockIdx.x * kWaves, wdu1 = min(wdu0 + kWaves, n_du);
+    const int wdu0 = bid * kWaves, wdu1 = min(wdu0 + kWaves, n_du);
     const int sl0 = wdu1 > wdu0 ? wdu0 / dpu : 0, sl1 = wdu1 > wdu0 ? (wdu1 - 1) / dpu : -1;
 
     // ---- S: poll the scores (one copy per workgroup), form the keys.  One
@@ -609,7 +628,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
                 for (int j = 0; j < 8; ++j) cw[j >> 2] |= fp8_act_code(f[j], a.su_in) << (8 * (j & 3));
                 const uint2 b0 = fp8x4_bf16(cw[0]), b1 = fp8x4_bf16(cw[1]);
                 *reinterpret_cast<uint4*>(&s_xb[4 * t]) = make_uint4(b0.x, b0.y, b1.x, b1.y);
-                if (blockIdx.x == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
+                if (bid == 0) *reinterpret_cast<uint2*>(a.sh_xq + 8 * t) = make_uint2(cw[0], cw[1]);
             }
             if constexpr (A4) {
                 const Nvfp4Half b = nvfp4_quant8_pair(f);
@@ -619,7 +638,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
                 for (int j = 0; j < 4; ++j)
                     o[j] = (__float_as_uint(f[2 * j]) >> 16) | (__float_as_uint(f[2 * j + 1]) & 0xffff0000u);
                 s_x[lds_pad_u128(t)] = make_uint4(o[0], o[1], o[2], o[3]);
-                if (blockIdx.x == 0) {
+                if (bid == 0) {
                     *reinterpret_cast<uint32_t*>(a.xq_codes + 4 * t) = b.code;
                     if ((t & 1) == 0) a.xq_scales[t / 2] = (uint8_t)b.sb;
                 }
@@ -649,7 +668,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     float* wsel = s_w_all[wave];
     // the workgroup's epoch copy advances now, long before the kernel ends,
     // so nothing is left for its last instructions
-    if (threadIdx.x == 0) __hip_atomic_store(a.ctrl + FW_EPOCH + blockIdx.x, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) __hip_atomic_store(a.ctrl + FW_EPOCH + bid, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Q4MOE_PHASE(3);
 
     // ---- U: issue the loads of this wave's up rows.  Every lane issues every
@@ -674,6 +693,10 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     }
     uint4 qu[kMaxUp][C];
     uint32_t su[kMaxUp][C];
+    // up scales: the 8-byte piece at offset uso8[p] of pass p's row region
+    // (which starts at byte usk[p] of its 4-byte-aligned cover)
+    u32x2 usc[kMaxUp];
+    uint32_t uso8[kMaxUp], usk[kMaxUp];
     // per-tensor scales of the wave's two up slots
     const int idu0 = ids[us0], idu1 = ids[us1];
     float gu0 = 1.0f, gu1 = 1.0f;
@@ -682,18 +705,29 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         gu1 = a.upg[idu1];
     }
     const int uoff0 = idu0 * a.I - us0 * a.I, uoff1 = idu1 * a.I - (us0 + 1) * a.I;
-    compiler_fence();
+    uint32_t urow[kMaxUp];
 #pragma unroll
     for (int p = 0; p < kMaxUp; ++p) {
         int u = u0 + 2 * p + seg;
         if (u >= u1) u = u1 > u0 ? u0 : 0;
-        const uint32_t row = (uint32_t)(u + (u >= ubnd ? uoff1 : uoff0));
-        const uint32_t rc = __umul24(row, urb), rs = __umul24(row, usb);
+        urow[p] = (uint32_t)(u + (u >= ubnd ? uoff1 : uoff0));
+    }
+    compiler_fence();
+    // the scales first (one load per pass: each segment its row's region),
+    // so that they are in by the time the codes are
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            qu[p][c] = ldg16_stream(a.upc + (rc + uco[c]));
-            su[p][c] = *reinterpret_cast<const uint16_t*>(ups8 + (rs + uso[c]));
-        }
+    for (int p = 0; p < kMaxUp; ++p) {
+        uint32_t b4, span4;
+        scale_region(__umul24(urow[p], usb), usb, b4, span4);
+        usk[p] = __umul24(urow[p], usb) - b4;
+        uso8[p] = min(8u * (uint32_t)li, span4 - 8u);
+        usc[p] = ldg8_a4(ups8 + (b4 + uso8[p]));
+    }
+#pragma unroll
+    for (int p = 0; p < kMaxUp; ++p) {
+        const uint32_t rc = __umul24(urow[p], urb);
+#pragma unroll
+        for (int c = 0; c < C; ++c) qu[p][c] = ldg16_stream(a.upc + (rc + uco[c]));
     }
     compiler_fence();
     Q4MOE_PHASE(8);
@@ -731,7 +765,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
             a.sh_hq[shr] = (uint8_t)code;
         }
         __syncthreads();
-        const int j = threadIdx.x;
+        const int j = tid;
         if (j < sq1 - sq0) {
             const float v = __uint_as_float(s_shq[j]);
 #pragma unroll
@@ -764,6 +798,23 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
             xs[c] = pair_sum_bf16(nat);
         }
     }
+
+    // the up scales through LDS: pass p's row region at 256 (2 p + seg)
+    // (a row's scales are at most 256 bytes: H <= 4096)
+#pragma unroll
+    for (int p = 0; p < kMaxUp; ++p) {
+        uint32_t* d = reinterpret_cast<uint32_t*>(my_sc + 256 * (2 * p + seg) + uso8[p]);
+        d[0] = usc[p][0];
+        d[1] = usc[p][1];
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int p = 0; p < kMaxUp; ++p) {
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+            su[p][c] = *reinterpret_cast<const uint16_t*>(my_sc + 256 * (2 * p + seg) + usk[p] + uso[c]);
+    }
+    __builtin_amdgcn_wave_barrier();
 
     // ---- U: h = relu(W_up x)^2 for this wave's rows: unit u0 + 2 p + seg
     // ends in lane 31 + 32 seg of hres[p] (for W4A4 also in LDS)
@@ -826,7 +877,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         // one (scale, epoch) value per block, kReplicas copies each (per
         // copy: K I / 8 code values, then K I / 16 scale values)
         __syncthreads();
-        const int j = threadIdx.x;
+        const int j = tid;
         if (j < wu1 - wu0) a.h[wu0 + j] = s_hrow[j];
         if (j < (wu1 - wu0) / 8) {
             float f[8];
@@ -862,33 +913,43 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     unsigned long long vq[2];
     if constexpr (SH) {
 #pragma unroll
-        for (int m = 0; m < 2; ++m) vq[m] = get_tag(srcq + min((int)threadIdx.x + 512 * m, a.S / 4 - 1));
+        for (int m = 0; m < 2; ++m) vq[m] = get_tag(srcq + min((int)tid + 512 * m, a.S / 4 - 1));
     }
     compiler_fence();
     uint4 qd[kDownRows][C2];
     uint32_t sd[kDownRows][C2];
+    // down scales: the unit's kDownRows rows are adjacent (H % kDownRows ==
+    // 0), so their scales are one region, read as 16-byte pieces at dso16[k]
+    // of its 4-byte-aligned cover (the region starts at byte dsk of it)
+    u32x4 dsc[C2];
+    uint32_t dso16[C2], dso[C2], dsk = 0;
+#pragma unroll
+    for (int c = 0; c < C2; ++c) {
+        const int ch = min(lane * C2 + c, nchI - 1);
+        dso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
+    }
     float gdn = 1.0f;  // per-tensor scale of the down matrix (NVFP4)
     // (with the shared expert every wave issues them, the few without down
     // rows reading rows 0-7 of slot 0: loads under a branch would make the
     // compiler wait for all of them before the shared expert's h codes)
     if (SH || dwave) {
-        const int drow = ids[dslot] * a.H;
-        uint32_t dco[C2], dso[C2];
+        const int drow = ids[dslot] * a.H + drow0;
+        uint32_t b4, span4;
+        scale_region(__umul24((uint32_t)drow, dsb), kDownRows * dsb, b4, span4);
+        dsk = __umul24((uint32_t)drow, dsb) - b4;
 #pragma unroll
-        for (int c = 0; c < C2; ++c) {
-            const int ch = min(lane * C2 + c, nchI - 1);
-            dco[c] = ch * 16;
-            dso[c] = (FMT == FMT_NVFP4) ? ch * 2 : (ch >> 1) * 2;
+        for (int k = 0; k < C2; ++k) {
+            dso16[k] = min(16u * (uint32_t)(lane + 64 * k), span4 - 16u);
+            dsc[k] = ldg16_a4(dns8 + (b4 + dso16[k]));
         }
+        uint32_t dco[C2];
+#pragma unroll
+        for (int c = 0; c < C2; ++c) dco[c] = min(lane * C2 + c, nchI - 1) * 16;
 #pragma unroll
         for (int p = 0; p < kDownRows; ++p) {
-            const uint32_t row = (uint32_t)(drow + min(drow0 + p, a.H - 1));
-            const uint32_t rc = __umul24(row, drb), rs = __umul24(row, dsb);
+            const uint32_t rc = __umul24((uint32_t)(drow + p), drb);
 #pragma unroll
-            for (int c = 0; c < C2; ++c) {
-                qd[p][c] = ldg16_stream(a.dnc + (rc + dco[c]));
-                sd[p][c] = *reinterpret_cast<const uint16_t*>(dns8 + (rs + dso[c]));
-            }
+            for (int c = 0; c < C2; ++c) qd[p][c] = ldg16_stream(a.dnc + (rc + dco[c]));
         }
         if constexpr (FMT == FMT_NVFP4) gdn = a.dng[ids[dslot]];
     }
@@ -906,7 +967,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         uint32_t qp = 0;
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int q = threadIdx.x + 512 * m;
+            const int q = tid + 512 * m;
             if (q < a.S / 4) {
                 if (tag_is(vq[m], ep))
                     *reinterpret_cast<uint2*>(&s_shb[2 * q]) = fp8x4_bf16((uint32_t)vq[m]);
@@ -917,7 +978,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         for (uint32_t polls = 0; __any(qp != 0u); ++polls) {
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int q = threadIdx.x + 512 * m;
+                const int q = tid + 512 * m;
                 if ((qp >> m) & 1u) {
                     const unsigned long long v = get_tag(srcq + q);
                     if (tag_is(v, ep)) {
@@ -962,13 +1023,13 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         uint32_t pend = 0;
 #pragma unroll
         for (int m = 0; m < 2; ++m)
-            if ((int)threadIdx.x + 512 * m < nhb) pend |= 5u << m;  // bit m: codes, bit m + 2: scale
+            if ((int)tid + 512 * m < nhb) pend |= 5u << m;  // bit m: codes, bit m + 2: scale
         uint32_t cw[2] = {0u, 0u}, sw[2] = {0u, 0u};
         for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
             unsigned long long v[4];
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                const int hb = hb0 + (int)threadIdx.x + 512 * m;
+                const int hb = hb0 + (int)tid + 512 * m;
                 v[m] = (pend >> m) & 1u ? get_tag(src + hb) : 0ull;
                 v[m + 2] = (pend >> (m + 2)) & 1u ? get_tag(src + RU / 8 + hb / 2) : 0ull;
             }
@@ -991,7 +1052,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         }
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-            const int t = (int)threadIdx.x + 512 * m;
+            const int t = (int)tid + 512 * m;
             if (t < nhb) {
                 Nvfp4Half b;
                 b.code = cw[m];
@@ -1014,15 +1075,15 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         uint32_t pend = 0;
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            if ((int)threadIdx.x + 512 * m < nh) pend |= 1u << m;
+            if ((int)tid + 512 * m < nh) pend |= 1u << m;
         for (uint32_t polls = 0; __any(pend != 0u); ++polls) {
             unsigned long long v[16];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + threadIdx.x + 512 * m) : 0ull;
+            for (int m = 0; m < 16; ++m) v[m] = (pend >> m) & 1u ? get_tag(src + tid + 512 * m) : 0ull;
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
                 if (((pend >> m) & 1u) && tag_is(v[m], ep)) {
-                    const int i = threadIdx.x + 512 * m;
+                    const int i = tid + 512 * m;
                     if constexpr (FMT == FMT_NVFP4) {
                         s_h[lds_pad_f32(i)] = tag_value(v[m]);
                     } else {
@@ -1043,6 +1104,24 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
                 break;
             }
             if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
+        }
+    }
+    // the down scales through LDS (every load of the wave is in by now)
+    if (dwave) {
+#pragma unroll
+        for (int k = 0; k < C2; ++k) {
+            uint32_t* d = reinterpret_cast<uint32_t*>(my_sc + dso16[k]);
+            d[0] = dsc[k][0];
+            d[1] = dsc[k][1];
+            d[2] = dsc[k][2];
+            d[3] = dsc[k][3];
+        }
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int p = 0; p < kDownRows; ++p) {
+#pragma unroll
+            for (int c = 0; c < C2; ++c)
+                sd[p][c] = *reinterpret_cast<const uint16_t*>(my_sc + dsk + (uint32_t)p * dsb + dso[c]);
         }
     }
     Q4MOE_WAVE_MARK(2);
@@ -1167,7 +1246,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     // ---- C: block b of 64 rows is combined by workgroup b * grid / nblocks
     const int nb = (a.H + kRowBlock - 1) / kRowBlock;
     for (int b = wave; b < nb; b += kWaves) {
-        if ((int)((long long)b * gridDim.x / nb) != (int)blockIdx.x) continue;
+        if ((int)((long long)b * gridDim.x / nb) != (int)bid) continue;
         const int r = b * kRowBlock + lane;
         constexpr int NS = SH ? 9 : 8;       // routed slots, then the shared expert
         const int ns = a.K + (SH ? 1 : 0);
@@ -1233,7 +1312,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // after the router, so nothing waits for it here.
     const uint32_t ep =
         __hip_atomic_load(a.ctrl + FW_EPOCH + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    fused_layer<FMT, C, C2, SH, A4, false>(a, ep, StackCtl{0, 0, nullptr});
+    fused_layer<FMT, C, C2, SH, A4, false>(a, ep, StackCtl{0, 0, nullptr}, threadIdx.x, blockIdx.x);
 }
 
 // A stack of single-token layers of one shape in one launch, in order: layer
@@ -1260,7 +1339,13 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_stack(StackArgs s) {
         a.y = L.y;
         a.ids_out = L.ids_out;
         a.w_out = L.w_out;
-        fused_layer<FMT, C, C2, false, false, true>(a, ep0 + 1u + (uint32_t)l, StackCtl{l, s.chain, s.y_tag});
+        // the thread and workgroup indices pass through an empty asm each
+        // layer, so that nothing computed from them is hoisted out of the
+        // loop and held in registers across the layers
+        uint32_t tid = threadIdx.x, bid = blockIdx.x;
+        asm volatile("" : "+v"(tid), "+s"(bid));
+        fused_layer<FMT, C, C2, false, false, true>(a, ep0 + 1u + (uint32_t)l, StackCtl{l, s.chain, s.y_tag}, tid,
+                                                    bid);
     }
 }
 

@@ -6,16 +6,17 @@
 // Phase marks: at each Q4MOE_PHASE(i) of k_decode_fused thread 0 of every
 // workgroup records s_memrealtime (100 MHz) in LDS; at the end it writes the
 // workgroup's marks, its per-wave marks (Q4MOE_WAVE_MARK) and the shader
-// clock ticks (s_memtime) at the start and the end to slot (launch % 32) of
-// a device table.  The last workgroup to finish advances the launch count.
+// clock ticks (s_memtime) at the start and the end to slot (n % 32) of a
+// device table, n being the number of layers the workgroup has run before
+// (its own count, so that in a stacked launch, where workgroups pass from one
+// layer to the next at different times, every layer keeps its own slot).
 // The marks add a few instructions per phase and one 48-word store per
 // workgroup; they change no data path.
 #include <hip/hip_runtime.h>
 
 constexpr int kProbeSlots = 32, kProbeWgs = 256, kProbeWords = 48;
 __device__ unsigned long long q4p_buf[kProbeSlots][kProbeWgs][kProbeWords];
-__device__ unsigned int q4p_launch;
-__device__ unsigned int q4p_done;
+__device__ unsigned int q4p_count[kProbeWgs];  // layers run, per workgroup
 __shared__ unsigned long long q4p_wlds[8][4];
 
 __device__ __forceinline__ void q4p_wave(int i) {
@@ -28,7 +29,7 @@ __device__ __forceinline__ void q4p_mark(int i) {
     if (i == 10) __syncthreads();  // the end: every wave of the workgroup
     if (threadIdx.x == 0) {
         if (i == 0) {
-            q4p_slot = __hip_atomic_load(&q4p_launch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) % kProbeSlots;
+            q4p_slot = (blockIdx.x < kProbeWgs ? q4p_count[blockIdx.x] : 0u) % kProbeSlots;
             for (int j = 1; j < 11; ++j) q4p_lds[j] = 0ull;
         }
         q4p_lds[i] = __builtin_amdgcn_s_memrealtime();
@@ -38,11 +39,7 @@ __device__ __forceinline__ void q4p_mark(int i) {
             for (int j = 0; j < 16; ++j) q4p_buf[q4p_slot][blockIdx.x][j] = q4p_lds[j];
             for (int w = 0; w < 8; ++w)
                 for (int j = 0; j < 4; ++j) q4p_buf[q4p_slot][blockIdx.x][16 + 4 * w + j] = q4p_wlds[w][j];
-            const unsigned d = atomicAdd(&q4p_done, 1u);
-            if (d == gridDim.x - 1) {
-                atomicExch(&q4p_done, 0u);
-                atomicAdd(&q4p_launch, 1u);
-            }
+            q4p_count[blockIdx.x] += 1u;
         }
     }
 }
@@ -96,7 +93,7 @@ extern "C" {
 // The phase table and the launch count.
 int q4p_read(void* host, unsigned* nlaunch) {
     if (hipMemcpyFromSymbol(host, HIP_SYMBOL(q4p_buf), sizeof(q4p_buf)) != hipSuccess) return 1;
-    if (hipMemcpyFromSymbol(nlaunch, HIP_SYMBOL(q4p_launch), 4) != hipSuccess) return 2;
+    if (hipMemcpyFromSymbol(nlaunch, HIP_SYMBOL(q4p_count), 4) != hipSuccess) return 2;  // workgroup 0's
     return 0;
 }
 

@@ -103,13 +103,14 @@ def launch(torch):
     print("\n(200 empty 256 x 512 launches follow; their durations are in the kernel trace)")
 
 
-def phase(torch, fmt):
+def phase(torch, fmt, stack=False):
     """Phase timeline of the one-launch decode inside the 23-layer stack's
     graph replays (medians over the layers of the median, and of the
     maximum, over workgroups), the shader clock and the gaps between
     layers, and the expert phase's HBM rate: the selected experts' bytes
     over the time from the first up-load issue to the end of the down
-    GEMVs."""
+    GEMVs.  stack: the 23 layers in one stacked launch per replay (a layer's
+    start is then its workgroups' entry into the layer)."""
     import gemm_router_fp32_amd.q4moe as q
     sys.path.insert(0, ROOT)
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -123,12 +124,16 @@ def phase(torch, fmt):
     import synth
     import bench
     layers = bench.build_stack(torch, g, synth, fmt)
-    ms, _, flags, _ = bench.time_stack(torch, g, layers, 20, 5)
-    graph = torch.cuda.CUDAGraph()
+    if stack:
+        ms, flags, _ = bench.time_stack_launch(torch, g, layers, 20, 5)
+        step, _ws = bench.stack_launch_step(g, layers)
+    else:
+        ms, _, flags, _ = bench.time_stack(torch, g, layers, 20, 5)
 
-    def step():
-        for Ly in layers:
-            bench.decode_call(g, Ly)
+        def step():
+            for Ly in layers:
+                bench.decode_call(g, Ly)
+    graph = torch.cuda.CUDAGraph()
     step()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
@@ -150,7 +155,8 @@ def phase(torch, fmt):
         rel.append((b[:, :11] - b[:, 0].min()) * 0.01)  # us from the first workgroup's start
     med = np.median(np.stack([[np.median(r[:, p]) for p in order] for r in rel]), axis=0)
     mx = np.median(np.stack([[np.max(r[:, p]) for p in order] for r in rel]), axis=0)
-    print(f"{fmt} stack: {ms * 1000 / 23:.3f} us per layer (graph replay, measurement build), flags {flags}\n")
+    how = "one stacked launch per replay" if stack else "graph replay of one launch per layer"
+    print(f"{fmt} stack: {ms * 1000 / 23:.3f} us per layer ({how}, measurement build), flags {flags}\n")
     print("| phase | median over workgroups (us) | max over workgroups (us) |\n|---|---|---|")
     for i, p in enumerate(order):
         print(f"| {names[p]} | {med[i]:.2f} | {mx[i]:.2f} |")
@@ -204,7 +210,7 @@ def main():
     elif what == "launch":
         launch(torch)
     elif what == "phase":
-        phase(torch, sys.argv[2] if len(sys.argv) > 2 else "nvfp4")
+        phase(torch, sys.argv[2] if len(sys.argv) > 2 else "nvfp4", "--stack" in sys.argv)
     else:
         raise SystemExit(f"unknown measurement {what}")
 
