@@ -667,8 +667,10 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     int* ids = s_sel_ids;
     float* wsel = s_w_all[wave];
     // the workgroup's epoch copy advances now, long before the kernel ends,
-    // so nothing is left for its last instructions
-    if (tid == 0) __hip_atomic_store(a.ctrl + FW_EPOCH + bid, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // so nothing is left for its last instructions (a stack advances it once,
+    // after its last layer: inside the layer loop the compiler would wait for
+    // this store's completion before the next layer's up loads)
+    if (!STK && tid == 0) __hip_atomic_store(a.ctrl + FW_EPOCH + bid, ep, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     Q4MOE_PHASE(3);
 
     // ---- U: issue the loads of this wave's up rows.  Every lane issues every
@@ -1347,6 +1349,9 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_stack(StackArgs s) {
         fused_layer<FMT, C, C2, false, false, true>(a, ep0 + 1u + (uint32_t)l, StackCtl{l, s.chain, s.y_tag}, tid,
                                                     bid);
     }
+    if (threadIdx.x == 0)
+        __hip_atomic_store(s.a.ctrl + FW_EPOCH + blockIdx.x, ep0 + (uint32_t)s.n_layers, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace q4moe
