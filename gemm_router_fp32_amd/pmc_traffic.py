@@ -12,7 +12,7 @@ The summary also records a SHA-256 of the kernel sources, so that a reader
 (bench.py) can tell whether the counters still describe the current kernel.
 
     python -m gemm_router_fp32_amd.pmc_traffic FETCH.csv WRITE.csv [RDSZ.csv] \
-        --copy-bytes 268435456 --kernel k_decode_fused
+        --copy-bytes 268435456 --kernel k_decode_
 """
 import argparse
 import collections
@@ -112,7 +112,7 @@ if __name__ == "__main__":
     ap.add_argument("write")
     ap.add_argument("rdsz", nargs="?")
     ap.add_argument("--copy-bytes", type=int, default=256 << 20)
-    ap.add_argument("--kernel", default="k_decode_fused")
+    ap.add_argument("--kernel", default="k_decode_")
     ap.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
     print(summarize(a.fetch, a.write, a.rdsz, a.copy_bytes, a.kernel, a.command), end="")
