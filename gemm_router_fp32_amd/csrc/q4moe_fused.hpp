@@ -420,9 +420,13 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
         if (!x_from_y) xb[i] = *reinterpret_cast<const uint2*>(a.x + 4 * j);
     }
 
-    // x into LDS once per workgroup (the up GEMV reads it from there)
-    if (!A4 && !x_from_y && (int)tid < a.H / 8)
-        s_x[lds_pad_u128(tid)] = *reinterpret_cast<const uint4*>(a.x + 8 * tid);
+    // x into LDS once per workgroup (the up GEMV reads it from there); the
+    // store waits for the load, so in a stack it follows the y poll, whose
+    // loads then leave without waiting for it
+    const bool x_lds = !A4 && !x_from_y && (int)tid < a.H / 8;
+    uint4 xl = make_uint4(0u, 0u, 0u, 0u);
+    if (x_lds) xl = *reinterpret_cast<const uint4*>(a.x + 8 * tid);
+    if (!STK && x_lds) s_x[lds_pad_u128(tid)] = xl;
     if constexpr (STK) {
         if (sk.layer > 0) {
             // The previous layer's y, complete: its (two bf16, epoch) values,
@@ -457,6 +461,7 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
                 if (__any(pend != 0u)) __builtin_amdgcn_s_sleep(1);
             }
         }
+        if (x_lds) s_x[lds_pad_u128(tid)] = xl;
         __syncthreads();
         if (x_from_y) {
 #pragma unroll

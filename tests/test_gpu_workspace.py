@@ -1,5 +1,5 @@
-"""One workspace shared by every entry point, and the one-launch decode's
-bounded waits.
+"""One workspace shared by every entry point (the stacked decode among
+them), and the one-launch decode's bounded waits.
 
 Every workspace starts with the same prefix (control words and the
 one-launch decode's epoch-tagged hand-off values) at fixed offsets, written
@@ -85,6 +85,17 @@ def test_workspace_reuse_across_paths(full_layer):
     torch.cuda.synchronize()
     assert _same(_decode(g.q4moe_w4a16_decode, router, ex, x1, ws), ref_a16)
     assert _same(_decode(g.q4moe_w4a4_decode, router, ex, x1, ws), ref_a4)
+    # the stacked decode (three layers sharing the bank, inputs rows 0-2),
+    # each layer equal to its one-token call on a fresh workspace, then one
+    # token again
+    xs = [dev(L["x"][i]) for i in range(3)]
+    ys = [torch.empty(H, dtype=torch.int16, device=DEV) for _ in range(3)]
+    g.q4moe_w4a16_decode_stack([router] * 3, [ex] * 3, xs, ys, ws=ws)
+    torch.cuda.synchronize()
+    for i in range(3):
+        one = _decode(g.q4moe_w4a16_decode, router, ex, L["x"][i:i + 1], None)
+        assert np.array_equal(host(ys[i], np.uint16), one[0][0]), f"stacked layer {i}"
+    assert _same(_decode(g.q4moe_w4a16_decode, router, ex, x1, ws), ref_a16)
     assert g.q4moe_ws_check(ws) == 0
 
 
