@@ -109,7 +109,8 @@ constexpr size_t kHTagOff = kScTagOff + up_to((size_t)kReplicas * kMaxExperts * 
 constexpr size_t kZTagOff = kHTagOff + up_to((size_t)kReplicas * kMaxTopK * kMaxDim * 8);
 constexpr size_t kHqTagOff = kZTagOff + up_to((size_t)(kMaxTopK + 1) * kMaxDim * 8);
 constexpr size_t kYTagOff = kHqTagOff + up_to((size_t)kReplicas * (kMaxDim / 4) * 8);
-constexpr size_t kPrefixBytes = kYTagOff + up_to((size_t)kReplicas * (kMaxDim / 2) * 8);
+constexpr size_t kDoneTagOff = kYTagOff + up_to((size_t)kReplicas * (kMaxDim / 2) * 8);
+constexpr size_t kPrefixBytes = kDoneTagOff + up_to((size_t)kReplicas * 64 * 8);
 
 struct RouterWs {
     size_t ctrl, logits, ids, w, total;
@@ -131,7 +132,7 @@ RouterWs router_ws(int E, int K, int T) {
 
 struct DecodeWs {
     RouterWs r;
-    size_t sc_tag, h_tag, z_tag, y_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s;
+    size_t sc_tag, h_tag, z_tag, y_tag, done_tag, h, y32, zw, hq_tag, sh_xq, sh_h, sh_hq, sh_z, xq_c, xq_s, hq_c, hq_s;
     // the grouped path (more than kSmallT tokens): dispatch, fp16 staging
     size_t counts, offsets, lists, perm, inv, act, n_act, x16, xexp, h16, hexp;
     // the shared expert through the grouped GEMMs (one-expert dispatch)
@@ -159,7 +160,8 @@ DecodeWs decode_ws(int E, int H, int I, int K, int T, int S = 0, bool a4 = false
     l.h_tag = kHTagOff;    // (h, epoch) pairs [kReplicas][K][I] (W4A4: codes and scales)
     l.z_tag = kZTagOff;    // (w * g * z, epoch) pairs [K + 1][H]; slot K: the shared expert
     l.hq_tag = kHqTagOff;  // shared expert: (four h codes, epoch) [kReplicas][S / 4]
-    l.y_tag = kYTagOff;    // a stack's y for its next layer: (two bf16, epoch) [kReplicas][H / 2]
+    l.y_tag = kYTagOff;    // a chained stack's y for its next layer: (two bf16, epoch) [kReplicas][H / 2]
+    l.done_tag = kDoneTagOff;  // a stack's combined blocks of y: (0, epoch) [kReplicas][64]
     size_t o = l.r.total;
     l.sh_xq = o;   // shared expert taps [T][H], [T][S], [T][S], and its z [T][H]
     o += up_to(S > 0 ? (size_t)T * H : 0);
@@ -1188,6 +1190,7 @@ q4moe_status q4moe_w4a16_decode_stack(const q4moe_router* routers, const q4moe_e
     f.y32 = at<float>(ws, lay.y32);
     f.su_w = f.su_in = f.sd_w = f.sd_in = 1.0f;
     sa.y_tag = at<unsigned long long>(ws, lay.y_tag);
+    sa.done_tag = at<unsigned long long>(ws, lay.done_tag);
     sa.chain = chain ? 1 : 0;
     // one launch per kStackMax layers; the first layer of a later launch
     // reads the previous layer's y from memory (the launches are in order)

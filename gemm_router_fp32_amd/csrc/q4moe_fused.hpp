@@ -165,7 +165,8 @@ struct StackLayer {
 };
 struct StackArgs {
     FusedArgs a;
-    unsigned long long* y_tag;  // [kReplicas][H/2]: (two bf16 of y, epoch)
+    unsigned long long* y_tag;     // [kReplicas][H/2]: (two bf16 of y, epoch), chained stacks
+    unsigned long long* done_tag;  // [kReplicas][64]: (0, epoch) per combined block of 64 rows of y
     int n_layers;
     int chain;  // layer l + 1 takes layer l's y as its x
     StackLayer layer[kStackMax];
@@ -176,6 +177,7 @@ struct StackCtl {
     int layer;
     int chain;
     unsigned long long* y_tag;
+    unsigned long long* done_tag;
 };
 
 __device__ __forceinline__ unsigned long long tagged(float v, uint32_t ep) {
@@ -428,11 +430,32 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
     if (x_lds) xl = *reinterpret_cast<const uint4*>(a.x + 8 * tid);
     if (!STK && x_lds) s_x[lds_pad_u128(tid)] = xl;
     if constexpr (STK) {
-        if (sk.layer > 0) {
-            // The previous layer's y, complete: its (two bf16, epoch) values,
-            // one copy per workgroup, thread t polling pairs t + 512 m.  The
-            // routing waits for every one of them, as the next call would
-            // wait for the previous one's end; in a chain they are x.
+        if (sk.layer > 0 && !sk.chain) {
+            // Independent layers: the routing waits until every block of the
+            // previous layer's y has been combined (its done tags), as the
+            // next call would wait for the previous one's end.  One wave
+            // polls the 42 (H / 64) tags of this workgroup's copy: a poll of
+            // every y value by every workgroup would put megabytes of poll
+            // traffic beside the previous layer's last hand-offs.
+            if (wave == 0) {
+                const int nbk = (a.H + kRowBlock - 1) / kRowBlock;
+                const unsigned long long* src = sk.done_tag + (size_t)rep * 64 + min(lane, nbk - 1);
+                bool have = lane >= nbk;
+                for (uint32_t polls = 0; !__all(have); ++polls) {
+                    const unsigned long long v = get_tag(src);
+                    have = have || tag_is(v, ep - 1u);
+                    if (polls > kPollLimit) {
+                        if (lane == 0) atomicOr(flags, 1u);
+                        break;
+                    }
+                    if (!__all(have)) __builtin_amdgcn_s_sleep(1);
+                }
+            }
+        }
+        if (sk.layer > 0 && sk.chain) {
+            // A chain: the previous layer's y is this layer's x, its (two
+            // bf16, epoch) values, one copy per workgroup, thread t polling
+            // pairs t + 512 m.
             const int np = a.H / 2;
             const unsigned long long* src = sk.y_tag + (size_t)rep * np;
             const uint32_t epy = ep - 1u;
@@ -1293,14 +1316,19 @@ __device__ __forceinline__ void fused_layer(const FusedArgs& a, const uint32_t e
             a.y[r] = (uint16_t)yb;
         }
         if constexpr (STK) {
-            // y for the next layer of the stack: rows 2t, 2t + 1 as one
-            // (two bf16, epoch) value, kReplicas copies
-            const uint32_t yo = (uint32_t)__builtin_amdgcn_mov_dpp((int)yb, 0xB1, 0xF, 0xF, true);  // lane ^ 1
-            if ((lane & 1) == 0 && r < a.H) {
-                const uint32_t pair = yb | (yo << 16);
+            if (sk.chain) {
+                // y for the next layer of the chain: rows 2t, 2t + 1 as one
+                // (two bf16, epoch) value, kReplicas copies
+                const uint32_t yo = (uint32_t)__builtin_amdgcn_mov_dpp((int)yb, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+                if ((lane & 1) == 0 && r < a.H) {
+                    const uint32_t pair = yb | (yo << 16);
 #pragma unroll
-                for (int rp = 0; rp < kReplicas; ++rp)
-                    put_tag(sk.y_tag + (size_t)rp * (a.H / 2) + r / 2, __uint_as_float(pair), ep);
+                    for (int rp = 0; rp < kReplicas; ++rp)
+                        put_tag(sk.y_tag + (size_t)rp * (a.H / 2) + r / 2, __uint_as_float(pair), ep);
+                }
+            } else if (lane < kReplicas) {
+                // this block is combined (after its y stores)
+                put_tag(sk.done_tag + (size_t)lane * 64 + b, 0.f, ep);
             }
         }
     }
@@ -1319,7 +1347,7 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_fused(FusedArgs a) {
     // after the router, so nothing waits for it here.
     const uint32_t ep =
         __hip_atomic_load(a.ctrl + FW_EPOCH + blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-    fused_layer<FMT, C, C2, SH, A4, false>(a, ep, StackCtl{0, 0, nullptr}, threadIdx.x, blockIdx.x);
+    fused_layer<FMT, C, C2, SH, A4, false>(a, ep, StackCtl{0, 0, nullptr, nullptr}, threadIdx.x, blockIdx.x);
 }
 
 // A stack of single-token layers of one shape in one launch, in order: layer
@@ -1351,8 +1379,8 @@ __global__ __launch_bounds__(64 * kWaves, 1) void k_decode_stack(StackArgs s) {
         // loop and held in registers across the layers
         uint32_t tid = threadIdx.x, bid = blockIdx.x;
         asm volatile("" : "+v"(tid), "+s"(bid));
-        fused_layer<FMT, C, C2, false, false, true>(a, ep0 + 1u + (uint32_t)l, StackCtl{l, s.chain, s.y_tag}, tid,
-                                                    bid);
+        fused_layer<FMT, C, C2, false, false, true>(a, ep0 + 1u + (uint32_t)l,
+                                                    StackCtl{l, s.chain, s.y_tag, s.done_tag}, tid, bid);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(s.a.ctrl + FW_EPOCH + blockIdx.x, ep0 + (uint32_t)s.n_layers, __ATOMIC_RELAXED,
