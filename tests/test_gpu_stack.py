@@ -140,3 +140,23 @@ def test_stack_validation():
     # in a chain the later x are not read
     g.q4moe_w4a16_decode_stack([r, r], [ex, ex], [x, None], [y, y], chain=True)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("chain", [False, True])
+def test_stack_fallback_shape(chain):
+    """hidden 128: below what the single launch takes, so the stack runs one
+    call per layer; the results equal the one-layer decode's bit for bit
+    (chained: on the previous layer's y)."""
+    E, H, I, K = 16, 128, 64, 4
+    routers, banks, xs = [], [], []
+    for li in range(3):
+        L = layer(SEED + 11, synth.FAM_NVFP4, li, E, H, I, 1, K, "nvfp4")
+        routers.append(upload_router(L["wg"], L["b"], K))
+        banks.append(upload_bank(L["bank"], "nvfp4"))
+        xs.append(L["x"][0])
+    ys, ids, w = _run_stack(routers, banks, [xs[0]] + ([None] * 2 if chain else xs[1:]), H, K, chain=chain)
+    for li in range(3):
+        xin = xs[li] if not chain or li == 0 else ys[li - 1]
+        one = run_decode(routers[li], banks[li], xin[None])
+        assert np.array_equal(one["y"][0], ys[li]), f"layer {li}"
+        assert np.array_equal(one["ids"][0], ids[li]), f"layer {li}"
