@@ -242,8 +242,8 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
 // out[m][n] = sum_k A[m][k] * W_e[n][k] over the expert's rows m, with both
 // operands NVFP4 (codes + E4M3 scale per 16 along k), decoded exactly to
 // fp16: A into LDS, W in registers.  Workgroup: 4 waves; wave w owns output
-// columns 32w..32w+31 (two 16-column blocks) and up to six 16-row subtiles
-// (96 rows) of M, one v_mfma_f32_16x16x32_f16 accumulator per (subtile,
+// columns 32w..32w+31 (two 16-column blocks) and up to four 16-row subtiles
+// (64 rows) of M, one v_mfma_f32_16x16x32_f16 accumulator per (subtile,
 // block).  K advances 256 per chunk (128 bytes of every weight row); a
 // 3-slot register ring keeps two chunks of weight loads in flight while the
 // current one computes.
@@ -251,8 +251,13 @@ __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
 enum : int { EPI_UP = 0, EPI_DOWN = 1 };
 // Output columns (rows of W_e) per workgroup (4 waves x 32), A rows per
 // M-tile (an expert's rows beyond it take further M-tiles), k per chunk (128
-// bytes of every weight row), LDS pitch of A (fp16).
-constexpr int kGemmBN = 128, kGemmBM = 96, kGemmBK = 256, kApitch = kGemmBK + 8;
+// bytes of every weight row), LDS pitch of A (fp16).  BM = 64 (four
+// subtiles) keeps the kernel within the 256 registers of two workgroups per
+// CU.  At 96 rows the six-subtile path pushed it over that limit: values
+// spilled and reloaded ahead of each ring loop, and the first use of such
+// a reload waits for every load issued before it.  That emptied the ring
+// once per turn.
+constexpr int kGemmBN = 128, kGemmBM = 64, kGemmBK = 256, kApitch = kGemmBK + 8;
 
 struct GemmArgs {
     int N, Kd;                 // output columns (rows of W_e), reduction length
@@ -316,19 +321,33 @@ __device__ __forceinline__ void gemm_load_b(const GemmArgs& a, const GemmCtx& x,
 // (16 rows at one group, rows 528 bytes apart) stay conflict-free.
 __device__ __forceinline__ int a_col(int g) { return 8 * (g ^ ((g >> 3) & 3)); }
 
+// A compile-time switch for the chunk step: whether it loads chunk c + 2.
+template <bool B> struct ChunkPrefetch {
+    static constexpr bool value = B;
+};
+
 // One M-tile (rows m0 .. m0 + mv - 1 of expert e, MS = ceil(mv / 16)
 // subtiles, staged in ceil(mv / 32) groups of 32 rows) against the
-// workgroup's 128 columns.
-template <int EPI, int MS>
+// workgroup's 128 columns.  FIRST: the workgroup's first M-tile, whose
+// weight chunks 0 and 1 (bb[0], bb[1]) and A rows (arow) the kernel's
+// prologue has already loaded; later M-tiles load their own.
+template <int EPI, int MS, bool FIRST>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, int m0, int mv,
-                                          _Float16 (*As)[kApitch]) {
+                                          _Float16 (*As)[kApitch], BChunk (&bb)[3],
+                                          const uint32_t (&arow_first)[2]) {
     constexpr int MA = (MS + 1) / 2;  // staging groups of 32 rows
+    static_assert(MA <= 2, "arow_first holds two staging groups");
     const int lane = threadIdx.x & 63, n16 = lane & 15;
     uint32_t ac_off[MA], as_off[MA];
 #pragma unroll
     for (int q = 0; q < MA; ++q) {
-        const int drow = x.row0 + m0 + min(x.ar + 32 * q, mv - 1);
-        const uint32_t arow = a.a_by_token ? (uint32_t)(a.perm[drow] / a.K) : (uint32_t)drow;
+        uint32_t arow;
+        if constexpr (FIRST) {
+            arow = arow_first[q];
+        } else {
+            const int drow = x.row0 + m0 + min(x.ar + 32 * q, mv - 1);
+            arow = a.a_by_token ? (uint32_t)(a.perm[drow] / a.K) : (uint32_t)drow;
+        }
         ac_off[q] = arow * (uint32_t)(a.Kd / 2);
         as_off[q] = arow * (uint32_t)(a.Kd / 16);
     }
@@ -356,20 +375,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) acc[i][nb] = f32x4g{0.f, 0.f, 0.f, 0.f};
 
-    // issue order = wait order: B0, A0, B1, A1 (the scheduler may not mix them)
-    BChunk bb[3];
-    gemm_load_b(a, x, 0, bb[0]);
+    // issue order = wait order (the scheduler may not mix the groups):
+    // FIRST: (B0, B1 from the prologue) A0, A1; otherwise B0, A0, B1, A1
+    if constexpr (!FIRST) gemm_load_b(a, x, 0, bb[0]);
     __builtin_amdgcn_sched_barrier(0);
     load_a(0, qa3[0], sa3[0]);
     __builtin_amdgcn_sched_barrier(0);
-    gemm_load_b(a, x, 1, bb[1]);
+    if constexpr (!FIRST) gemm_load_b(a, x, 1, bb[1]);
     __builtin_amdgcn_sched_barrier(0);
     load_a(1, qa3[1], sa3[1]);
     __builtin_amdgcn_sched_barrier(0);
-    // chunk c stages its A from (qa, sa), computes on bc, and loads chunk
-    // c + 2 into (qn, sn) and bn, the slots chunk c - 1 used
-    auto step = [&](const int c, const BChunk& bc, BChunk& bn, const uint4 (&qa)[MA], const uint32_t (&sa)[MA],
-                    uint4 (&qn)[MA], uint32_t (&sn)[MA]) {
+    // chunk c stages its A from (qa, sa), computes on bc, and (PF) loads
+    // chunk c + 2 into (qn, sn) and bn, the slots chunk c - 1 used
+    auto step = [&](auto pf, const int c, const BChunk& bc, BChunk& bn, const uint4 (&qa)[MA],
+                    const uint32_t (&sa)[MA], uint4 (&qn)[MA], uint32_t (&sn)[MA]) {
             // this chunk's A into LDS (after every wave is done with the last one)
             __syncthreads();
             const bool a_ok = 32 * x.ap < a.Kd - c * kGemmBK;
@@ -385,11 +404,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
             }
             __syncthreads();
             // next loads: A and B of chunk c+2 into the free slots
-            __builtin_amdgcn_sched_barrier(0);
-            load_a(c + 2, qn, sn);
-            __builtin_amdgcn_sched_barrier(0);
-            gemm_load_b(a, x, c + 2, bn);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (decltype(pf)::value) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_a(c + 2, qn, sn);
+                __builtin_amdgcn_sched_barrier(0);
+                gemm_load_b(a, x, c + 2, bn);
+                __builtin_amdgcn_sched_barrier(0);
+            }
             // 8 MFMA steps (h, d) on chunk c: lane (n16, kq) takes dword d of
             // its piece h (k 128 h + 32 kq + 8 d .. +7 of the chunk) with
             // block scale 8 h + 2 kq + d / 2; pieces past the end get scale 0
@@ -426,16 +447,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
                 }
             }
     };
-    // whole turns of the ring, then the one or two chunks left (no padding
-    // chunks, and no exit from inside a turn)
+    // Whole turns of the ring, then the one or two chunks left, which load
+    // nothing (no exit from inside a turn).  A turn's loads past the end of
+    // K read the rows' last bytes.  They come only when nch % 3 != 2, and
+    // then they stay in flight into the epilogue, whose registers wait for
+    // them.  The hidden and inter sizes here (11 and 8 chunks) have none.
+    constexpr ChunkPrefetch<true> PF{};
+    constexpr ChunkPrefetch<false> NP{};
     int c = 0;
     for (; c + 3 <= x.nch; c += 3) {
-        step(c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
-        step(c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
-        step(c + 2, bb[2], bb[1], qa3[2], sa3[2], qa3[1], sa3[1]);
+        step(PF, c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
+        step(PF, c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
+        step(PF, c + 2, bb[2], bb[1], qa3[2], sa3[2], qa3[1], sa3[1]);
     }
-    if (c < x.nch) step(c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
-    if (c + 1 < x.nch) step(c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
+    if (c < x.nch) step(NP, c, bb[0], bb[2], qa3[0], sa3[0], qa3[2], sa3[2]);
+    if (c + 1 < x.nch) step(NP, c + 1, bb[1], bb[0], qa3[1], sa3[1], qa3[0], sa3[0]);
     // epilogue: lane (n16, kq) holds column n + 16 nb and rows 16 i + 4 kq + r
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -462,7 +488,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 // Grouped GEMM over the experts' dispatch rows: out[row][n] = epi(sum_k
 // A[row][k] W_e[n][k]) on fp16 MFMA (v_mfma_f32_16x16x32_f16) with both
 // operands decoded exactly from NVFP4.  A workgroup takes 128 columns of one
-// expert and all its rows in M-tiles of 96; wave w owns columns 32w..32w+31.
+// expert and all its rows in M-tiles of 64; wave w owns columns 32w..32w+31.
 //
 // The reduction runs in chunks of 256: every weight row contributes one whole
 // 128-byte line per chunk, loaded straight into registers two chunks ahead in
@@ -472,13 +498,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
 // ahead in a ring of their own, are decoded into LDS once per workgroup.
 // MFMA step (h, d) of a chunk sums k 128 h + 32 kq + 8 d .. +7 on lanes
 // kq = 0..3: the same k order on both operands.  The block scales of the
-// workgroup's 128 weight rows are copied into LDS once, with coalesced loads
-// issued beside the expert's offsets.  All loads are unconditional: pieces
-// past the end of a row (in the last chunk, and the prefetches issued by the
-// last two chunks) read the row's last bytes and get scale 0, so that every
-// wait covers exactly the loads it needs.  The chunk loop runs whole turns
-// of the ring and then the one or two chunks left, with no exit from inside
-// a turn (an exit there makes the compiler wait for every outstanding load).
+// workgroup's 128 weight rows are copied into LDS once.  The prologue
+// issues every load that does not wait on another before its first wait:
+// weight chunks 0 and 1, the scale rows and the first M-tile's dispatch
+// entries (the A rows of the up GEMM), so that the workgroup's start costs
+// one memory round trip, then one more for the A pieces of chunks 0 and 1.
+// The chunk loads are unconditional: pieces past the end of a row (in the
+// last chunk, and a turn's loads of chunks past K) read the row's last
+// bytes and get scale 0, so that every wait covers exactly the loads it
+// needs.
 // Offsets are 32-bit from the uniform bases: the argument limits (E <= 256,
 // rows and columns <= 4096, T * K <= 2^19) keep every matrix under 2^31
 // bytes.
@@ -499,10 +527,30 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
         x.e = b % 8 + 8 * (j / ntiles);
         tile = j % ntiles;
     }
-    // The scale rows of this tile (contiguous: rows e N + 128 tile ..), one
-    // dword per thread and pass, loaded together with the expert's offsets
-    // and stored to LDS once they are in.
+    x.row0 = a.offsets[x.e];
+    const int n_e = a.offsets[x.e + 1] - x.row0;
+    if (n_e == 0) return;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    x.kq = lane >> 4;
+    x.nch = (a.Kd + kGemmBK - 1) / kGemmBK;
+    x.n = tile * kGemmBN + 32 * wave + (lane & 15);
     const int sc_rb = a.Kd / 16;
+    x.rb = sc_rb;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+        const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n + 16 * nb, a.N - 1);
+        x.wc_off[nb] = wrow * (uint32_t)(a.Kd / 2);
+        x.sc_row[nb] = (uint32_t)((32 * wave + 16 * nb + (lane & 15)) * x.rb);
+    }
+    // A staging role: piece ap (k 32ap..32ap+31 of the chunk) of rows ar + 32q
+    x.ap = threadIdx.x & 7;
+    x.ar = threadIdx.x >> 3;
+    // The prologue's loads, in wait order: weight chunks 0 and 1, the scale
+    // rows of this tile (contiguous: rows e N + 128 tile .., one dword per
+    // thread and pass), the dispatch entries of the first M-tile's rows.
+    BChunk bb[3];
+    gemm_load_b(a, x, 0, bb[0]);
+    gemm_load_b(a, x, 1, bb[1]);
     const int sc_ndw = min(kGemmBN, a.N - tile * kGemmBN) * sc_rb / 4;
     uint32_t scv[32];
     {
@@ -514,19 +562,12 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
             scv[j] = i < sc_ndw ? src[i] : 0u;
         }
     }
-    x.row0 = a.offsets[x.e];
-    const int n_e = a.offsets[x.e + 1] - x.row0;
-    if (n_e == 0) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    x.kq = lane >> 4;
-    x.nch = (a.Kd + kGemmBK - 1) / kGemmBK;
-    x.n = tile * kGemmBN + 32 * wave + (lane & 15);
-    x.rb = sc_rb;
+    const int mv0 = min(kGemmBM, n_e);
+    uint32_t arow[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t wrow = (uint32_t)x.e * a.N + min(x.n + 16 * nb, a.N - 1);
-        x.wc_off[nb] = wrow * (uint32_t)(a.Kd / 2);
-        x.sc_row[nb] = (uint32_t)((32 * wave + 16 * nb + (lane & 15)) * x.rb);
+    for (int q = 0; q < 2; ++q) {
+        const int drow = x.row0 + min(x.ar + 32 * q, mv0 - 1);
+        arow[q] = a.a_by_token ? (uint32_t)(a.perm[drow] / a.K) : (uint32_t)drow;
     }
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
@@ -534,21 +575,16 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
         if (i < sc_ndw) reinterpret_cast<uint32_t*>(g_gemm_sct)[i] = scv[j];
     }
     x.g = a.wg[x.e];
-    // A staging role: piece ap (k 32ap..32ap+31 of the chunk) of rows ar + 32q
-    x.ap = threadIdx.x & 7;
-    x.ar = threadIdx.x >> 3;
-    for (int m0 = 0; m0 < n_e; m0 += kGemmBM) {
-        const int mv = min(kGemmBM, n_e - m0);
-        static_assert(kGemmBM == 96, "subtile dispatch below covers 1..6");
-        switch ((mv + 15) / 16) {
-            case 1: gemm_tile<EPI, 1>(a, x, m0, mv, As); break;
-            case 2: gemm_tile<EPI, 2>(a, x, m0, mv, As); break;
-            case 3: gemm_tile<EPI, 3>(a, x, m0, mv, As); break;
-            case 4: gemm_tile<EPI, 4>(a, x, m0, mv, As); break;
-            case 5: gemm_tile<EPI, 5>(a, x, m0, mv, As); break;
-            default: gemm_tile<EPI, 6>(a, x, m0, mv, As); break;
-        }
+    static_assert(kGemmBM == 64, "subtile dispatch below covers 1..4");
+    switch ((mv0 + 15) / 16) {
+        case 1: gemm_tile<EPI, 1, true>(a, x, 0, mv0, As, bb, arow); break;
+        case 2: gemm_tile<EPI, 2, true>(a, x, 0, mv0, As, bb, arow); break;
+        case 3: gemm_tile<EPI, 3, true>(a, x, 0, mv0, As, bb, arow); break;
+        default: gemm_tile<EPI, 4, true>(a, x, 0, mv0, As, bb, arow); break;
     }
+    // an expert's rows beyond the first 64 (rare at a few thousand tokens)
+    for (int m0 = kGemmBM; m0 < n_e; m0 += kGemmBM)
+        gemm_tile<EPI, 4, false>(a, x, m0, min(kGemmBM, n_e - m0), As, bb, arow);
 }
 
 // y32[t][n] = sum over slots s (in order) of w[t*K + s] * z[inv[t*K + s]][n]
