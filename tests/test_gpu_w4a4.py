@@ -111,6 +111,29 @@ def test_w4a4_full_chunk():
           f"max {counts.max()} mean {counts.mean():.1f} std {counts.std():.1f}; h {wh:.3f}, y {wy:.3f}")
 
 
+@pytest.mark.parametrize("shape", [(16, 2688, 1856), (16, 256, 192)], ids=["full-hidden", "one-chunk"])
+def test_w4a4_skewed_routing(shape):
+    # every token picks experts 0..5 (bias far above any score): 200 rows per
+    # expert, so each GEMM runs M-tiles 64 + 64 + 64 + 8 for those experts
+    # (the later M-tiles load their own weight chunks and dispatch rows) and
+    # skips the idle ones; full-hidden streams 11 (up) and 8 (down) chunks,
+    # one-chunk a single chunk each
+    E, H, I = shape
+    T, K = 200, 6
+    bank = synth.expert_bank(SEED, synth.FAM_W4A4, 7, E, H, I, "nvfp4")
+    wg, b = synth.router(SEED, synth.FAM_W4A4, 7, E, H, 0.5 / np.sqrt(H))
+    b = b.copy()
+    b[:K] += 10.0
+    x, r, _ = x_with_clear_routing(SEED, synth.FAM_W4A4, 7, wg, b, T, K)
+    assert set(np.unique(r["ids"])) == set(range(K))
+    print(f"W4A4 skewed routing T={T} E={E} H={H} I={I}", flush=True)
+    out = _run(upload_router(wg, b, K), upload_bank(bank, "nvfp4"), x, K)
+    counts = np.diff(out["offsets"])
+    assert np.array_equal(counts, np.array([T] * K + [0] * (E - K)))
+    wh, wy = _check(bank, wg, b, x, r, out, K)
+    print(f"skewed {H}x{I}: h {wh:.3f}, y {wy:.3f}")
+
+
 @pytest.mark.parametrize("T", [1, 2, 8, 37, 200])
 def test_w4a4_mid_batch(T):
     # the token counts between one-token decode and a prefill chunk: few rows
