@@ -445,10 +445,22 @@ RouterArgs router_args(const q4moe_router* r, const uint16_t* x, int T, void* ws
     return a;
 }
 
+// The MFMA router GEMM: two token blocks per workgroup (the router matrix
+// read half as often) when that still leaves 256 workgroups, else one.  The
+// logits are the same either way.
+void launch_router_gemm(const RouterArgs& a, hipStream_t s) {
+    const unsigned ge = (unsigned)((a.E + kRouterTile - 1) / kRouterTile);
+    const unsigned gt2 = (unsigned)((a.T + 2 * kRouterTile - 1) / (2 * kRouterTile));
+    if (gt2 * ge >= 256)
+        hipLaunchKernelGGL(k_router_gemm<2>, dim3(gt2, ge), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL(k_router_gemm<1>, dim3((unsigned)((a.T + kRouterTile - 1) / kRouterTile), ge), dim3(512),
+                           0, s, a);
+}
+
 q4moe_status launch_router(const RouterArgs& a, hipStream_t s) {
     if (a.T >= 16) {  // many tokens: the MFMA router GEMM
-        hipLaunchKernelGGL(k_router_gemm, dim3((a.T + kRouterTile - 1) / kRouterTile, (a.E + kRouterTile - 1) / kRouterTile),
-                           dim3(512), 0, s, a);
+        launch_router_gemm(a, s);
     } else {
         dim3 g1(a.E, (a.T + 3) / 4);
         hipLaunchKernelGGL(k_router_logits, g1, dim3(256), 0, s, a);
@@ -1513,8 +1525,7 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
 
     // router
     RouterArgs ra = router_args(r, x_bf16, T, ws, l.r, ids, w, nullptr);
-    hipLaunchKernelGGL(k_router_gemm, dim3((T + kRouterTile - 1) / kRouterTile, (E + kRouterTile - 1) / kRouterTile),
-                       dim3(512), 0, s, ra);
+    launch_router_gemm(ra, s);
     if ((st = launched("router gemm")) != Q4MOE_OK) return st;
     hipLaunchKernelGGL(k_topk, dim3((T + 3) / 4), dim3(256), 0, s, ra);
     if ((st = launched("router top-k")) != Q4MOE_OK) return st;

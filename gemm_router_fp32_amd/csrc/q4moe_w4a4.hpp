@@ -28,55 +28,71 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // Router logits for many tokens on fp32 MFMA (v_mfma_f32_16x16x4_f32): a
-// workgroup computes a 16-token x 16-expert tile (512 tiles for 1024 tokens
-// and 128 experts, so every CU gets work); its 8 waves split the hidden
-// dimension and their partial tiles are summed in LDS in wave order.  Lane l
-// feeds token/expert row l % 16 and, for each block of 16 k-values, k-values
-// 4 (l / 16) .. +3 (one per MFMA; A and B use the same k order).  The grid is
-// (token tiles, expert tiles): workgroup b runs on XCD b % 8, so all expert
-// tiles of a token tile share one XCD and read its x rows from HBM once.
+// workgroup computes a (16 TB)-token x 16-expert tile; its 8 waves split the
+// hidden dimension, and their partial tiles are summed in LDS in wave order.
+// Each wave runs the TB token blocks of its part of the hidden dimension
+// side by side: one router-weight fragment feeds TB MFMAs.  A wider token
+// tile cuts the re-reads of the fp32 router matrix, which dominate the
+// kernel's L2 traffic (every token tile reads all of it).  Each (token
+// block, expert block, wave) runs the same MFMA sequence at any TB, so the
+// logits do not depend on TB.  Lane l feeds token/expert row l % 16 and,
+// for each block of 16 k-values, k-values 4 (l / 16) .. +3 (one per MFMA; A
+// and B use the same k order).  The grid is (token tiles, expert tiles):
+// workgroup b runs on XCD b % 8, so all expert tiles of a token tile share
+// one XCD and read its x rows from HBM once.
 // ---------------------------------------------------------------------------
 constexpr int kRouterTile = 16;
 
+template <int TB>
 __global__ __launch_bounds__(512) void k_router_gemm(RouterArgs a) {
-    __shared__ float part[8][16][17];
+    __shared__ float part[8][16 * TB][17];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int t0 = blockIdx.x * kRouterTile, e0 = blockIdx.y * kRouterTile;
+    const int t0 = blockIdx.x * kRouterTile * TB, e0 = blockIdx.y * kRouterTile;
     const int row = lane & 15, kq = lane >> 4;
-    const int t = min(t0 + row, a.T - 1), e = min(e0 + row, a.E - 1);
-    const uint16_t* xr = a.x + (size_t)t * a.H + 4 * kq;
+    const int e = min(e0 + row, a.E - 1);
+    const uint16_t* xr[TB];
+#pragma unroll
+    for (int j = 0; j < TB; ++j) xr[j] = a.x + (size_t)min(t0 + 16 * j + row, a.T - 1) * a.H + 4 * kq;
     const float* wr = a.wg + (size_t)e * a.H + 4 * kq;
     const int nblk = a.H / 16;
     const int b0 = wave * nblk / 8, b1 = (wave + 1) * nblk / 8;
-    f32x4g acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4g acc[TB];
+#pragma unroll
+    for (int j = 0; j < TB; ++j) acc[j] = f32x4g{0.f, 0.f, 0.f, 0.f};
     // kRouterBatch blocks' loads leave before their MFMAs (blocks past b1 are
     // clamped to b1 - 1 and skipped)
     constexpr int kRouterBatch = 7;
     for (int bb = b0; bb < b1; bb += kRouterBatch) {
-        uint2 xv[kRouterBatch];
+        uint2 xv[kRouterBatch][TB];
         float4 wv[kRouterBatch];
 #pragma unroll
         for (int i = 0; i < kRouterBatch; ++i) {
             const int b = min(bb + i, b1 - 1);
-            xv[i] = *reinterpret_cast<const uint2*>(xr + 16 * b);
             wv[i] = *reinterpret_cast<const float4*>(wr + 16 * b);
+#pragma unroll
+            for (int j = 0; j < TB; ++j) xv[i][j] = *reinterpret_cast<const uint2*>(xr[j] + 16 * b);
         }
 #pragma unroll
         for (int i = 0; i < kRouterBatch; ++i) {
             if (bb + i < b1) {
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].x & 0xffffu), wv[i].x, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].x >> 16), wv[i].y, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].y & 0xffffu), wv[i].z, acc, 0, 0, 0);
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i].y >> 16), wv[i].w, acc, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < TB; ++j) {
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i][j].x & 0xffffu), wv[i].x, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i][j].x >> 16), wv[i].y, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i][j].y & 0xffffu), wv[i].z, acc[j], 0, 0, 0);
+                    acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(bf16_bits_to_f32(xv[i][j].y >> 16), wv[i].w, acc[j], 0, 0, 0);
+                }
             }
         }
     }
-    // lane holds column j = lane % 16 (expert) and rows 4 (lane / 16) + i (tokens)
+    // lane holds column lane % 16 (expert) and rows 4 (lane / 16) + i (tokens)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][4 * kq + i][row] = acc[i];
+    for (int j = 0; j < TB; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][16 * j + 4 * kq + i][row] = acc[j][i];
     __syncthreads();
-    if (threadIdx.x < kRouterTile * kRouterTile) {
-        const int i = threadIdx.x >> 4, j = threadIdx.x & 15;
+    for (int u = threadIdx.x; u < 16 * TB * kRouterTile; u += 512) {
+        const int i = u >> 4, j = u & 15;
         float v = 0.f;
 #pragma unroll
         for (int w = 0; w < 8; ++w) v += part[w][i][j];
