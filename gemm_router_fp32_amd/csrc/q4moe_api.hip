@@ -1555,8 +1555,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     qx.v = x_bf16;
     qx.codes = at<uint8_t>(ws, l.xq_codes);
     qx.scales = at<uint8_t>(ws, l.xq_scales);
-    const size_t npx = (size_t)T * H / 8;  // 8 bf16 values per lane
-    hipLaunchKernelGGL((k_quant_nvfp4<true>), dim3((unsigned)((npx + 255) / 256)), dim3(256), 0, s, qx);
+    const size_t nbx = (size_t)T * H / 16;  // one 16-block per lane
+    hipLaunchKernelGGL((k_quant_nvfp4<true>), dim3((unsigned)((nbx + 255) / 256)), dim3(256), 0, s, qx);
     if ((st = launched("x quantization")) != Q4MOE_OK) return st;
 
     // up: h = relu(g u)^2
@@ -1584,8 +1584,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     qh.v = gu.out;
     qh.codes = at<uint8_t>(ws, l.hq_codes);
     qh.scales = at<uint8_t>(ws, l.hq_scales);
-    const size_t nph = rows * I / 4;  // 4 fp32 values per lane
-    hipLaunchKernelGGL((k_quant_nvfp4<false>), dim3((unsigned)((nph + 255) / 256)), dim3(256), 0, s, qh);
+    const size_t nbh = rows * I / 16;  // one 16-block per lane
+    hipLaunchKernelGGL((k_quant_nvfp4<false>), dim3((unsigned)((nbh + 255) / 256)), dim3(256), 0, s, qh);
     if ((st = launched("h quantization")) != Q4MOE_OK) return st;
 
     // down: g z per (token, slot) row (the gate is applied in the combine)

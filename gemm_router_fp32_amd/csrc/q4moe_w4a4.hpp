@@ -202,54 +202,51 @@ struct QuantArgs {
     uint8_t* scales;    // [rows][cols/16]
 };
 
-// One lane per 16 input bytes (4 fp32 or 8 bf16 values: a quarter or a half
-// of a block), so every load instruction reads 1 KB in one run; the block
-// maximum is taken across the block's 2 or 4 neighbouring lanes (quad
-// permutes), each lane stores its own code bytes and the block's first lane
-// the scale byte.  Lanes past the end work on the last piece and store
-// nothing (a block's lanes are always all live or all past the end).
+// One lane per 16-value block: it loads the block's 32 (bf16) or 64 (fp32)
+// bytes as 16-byte pieces (all in flight at once), takes the block maximum
+// in registers, and stores the block's 8 code bytes in one store and its
+// scale byte.  Lanes past the end work on the last block and store nothing.
 template <bool BF16_IN>
 __global__ __launch_bounds__(256) void k_quant_nvfp4(QuantArgs a) {
-    constexpr int VPL = BF16_IN ? 8 : 4;  // values per lane
-    constexpr int LPB = 16 / VPL;         // lanes per block
-    const size_t n_pieces = (size_t)a.rows * (size_t)a.cols / VPL;
-    const size_t gp = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const bool live = gp < n_pieces;
-    const size_t pc = live ? gp : n_pieces - 1;
-    float v[VPL];
+    const size_t n_blocks = (size_t)a.rows * (size_t)a.cols / 16;
+    const size_t gb = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = gb < n_blocks;
+    const size_t bk = live ? gb : n_blocks - 1;
+    float v[16];
     if constexpr (BF16_IN) {
-        const uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + pc * VPL);
-        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        const uint4* src = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.v) + bk * 16);
+        const uint4 q0 = src[0], q1 = src[1];
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
             v[2 * k] = bf16_bits_to_f32(w[k] & 0xffffu);
             v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
         }
     } else {
-        const float4 q = *reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + pc * VPL);
-        v[0] = q.x;
-        v[1] = q.y;
-        v[2] = q.z;
-        v[3] = q.w;
+        const float4* src = reinterpret_cast<const float4*>(static_cast<const float*>(a.v) + bk * 16);
+        float4 q[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = src[k];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[4 * k + 0] = q[k].x;
+            v[4 * k + 1] = q[k].y;
+            v[4 * k + 2] = q[k].z;
+            v[4 * k + 3] = q[k].w;
+        }
     }
     float amax = 0.f;
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) amax = fmaxf(amax, fabsf(v[k]));
-    // across the block's lanes: quad_perm [1,0,3,2], then [2,3,0,1]
-    amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0xB1, 0xF, 0xF, true)));
-    if constexpr (LPB == 4)
-        amax = fmaxf(amax, __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, amax), 0x4E, 0xF, 0xF, true)));
+    for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(v[k]));
     const uint32_t sb = e4m3fn_rne_sat(__fdiv_rn(amax, 6.0f));
     const E2m1Thresholds th = e2m1_thresholds(e4m3fn_to_f32(sb));
-    uint32_t word = 0;
+    uint32_t word[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) word |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * k);
+    for (int k = 0; k < 16; ++k)
+        word[k >> 3] |= (e2m1_code(fabsf(v[k]), th) | ((__float_as_uint(v[k]) >> 31) << 3)) << (4 * (k & 7));
     if (live) {
-        if constexpr (BF16_IN)
-            *reinterpret_cast<uint32_t*>(a.codes + pc * (VPL / 2)) = word;
-        else
-            *reinterpret_cast<uint16_t*>(a.codes + pc * (VPL / 2)) = (uint16_t)word;
-        if (pc % LPB == 0) a.scales[pc / LPB] = (uint8_t)sb;
+        *reinterpret_cast<uint2*>(a.codes + bk * 8) = make_uint2(word[0], word[1]);
+        a.scales[bk] = (uint8_t)sb;
     }
 }
 
