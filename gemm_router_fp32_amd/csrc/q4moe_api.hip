@@ -1604,8 +1604,8 @@ q4moe_status q4moe_w4a4_grouped(const q4moe_router* r, const q4moe_experts* ex, 
     if ((st = launched("grouped down gemm")) != Q4MOE_OK) return st;
 
     // combine
-    const size_t nq = (size_t)T * H / 4;  // 4 columns per thread (H % 64 == 0)
-    hipLaunchKernelGGL(k_combine, dim3((unsigned)((nq + 255) / 256)), dim3(256), 0, s, T, K, H, da.inv, ra.w,
+    // one workgroup per token, 4 columns per lane (H % 64 == 0, H <= 4096)
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)T), dim3((unsigned)((H / 4 + 63) / 64 * 64)), 0, s, T, K, H, da.inv, ra.w,
                        gd.out, at<float>(ws, l.y32), y_bf16);
     return launched("combine");
 }

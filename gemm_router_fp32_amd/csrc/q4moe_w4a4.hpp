@@ -601,20 +601,22 @@ __global__ __launch_bounds__(256, 2) void k_grouped_gemm(GemmArgs a) {
 }
 
 // y32[t][n] = sum over slots s (in order) of w[t*K + s] * z[inv[t*K + s]][n]
-// (the product rounded to fp32, then added); y = bf16.  A thread takes 4
-// columns (H % 4 == 0) and issues its K row loads before summing them.
-__global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const int32_t* inv, const float* w,
-                                                 const float* z, float* y32, uint16_t* y) {
-    const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
-    if (i >= (size_t)T * H) return;
-    const size_t t = i / H, n = i % H;
+// (the product rounded to fp32, then added); y = bf16.  One workgroup per
+// token (H / 4 lanes rounded up to whole waves): the token's K rows and
+// weights are uniform, read once through the scalar cache, and each lane
+// takes 4 columns (H % 4 == 0), issuing its K row loads before summing them.
+__global__ __launch_bounds__(1024) void k_combine(int T, int K, int H, const int32_t* inv, const float* w,
+                                                  const float* z, float* y32, uint16_t* y) {
+    const int t = blockIdx.x;
+    const int n = 4 * (int)threadIdx.x;
+    if (t >= T || n >= H) return;
     float4 v[8];
     float g[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
         if (s < K) {
-            v[s] = *reinterpret_cast<const float4*>(z + (size_t)inv[t * K + s] * H + n);
-            g[s] = w[t * K + s];
+            v[s] = *reinterpret_cast<const float4*>(z + (size_t)inv[(size_t)t * K + s] * H + n);
+            g[s] = w[(size_t)t * K + s];
         }
     }
     float4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -627,6 +629,7 @@ __global__ __launch_bounds__(256) void k_combine(int T, int K, int H, const int3
             acc.w += __fmul_rn(g[s], v[s].w);
         }
     }
+    const size_t i = (size_t)t * H + n;
     *reinterpret_cast<float4*>(y32 + i) = acc;
     uint2 b;
     b.x = f32_to_bf16_rne(acc.x) | (f32_to_bf16_rne(acc.y) << 16);
