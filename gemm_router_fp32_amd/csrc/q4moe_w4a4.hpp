@@ -126,16 +126,23 @@ struct DispatchArgs {
 __global__ __launch_bounds__(64) void k_dispatch(DispatchArgs a) {
     const int e = blockIdx.x, lane = threadIdx.x;
     int base = 0;
-    // four chunks of 64 tokens per round: all their id loads (token index
-    // clamped, K <= 8) leave before any is compared
+    // four chunks of 64 tokens per round: all their id loads leave before
+    // any is compared.  Token and slot indices are clamped (K <= 8), so the
+    // loads need no branch; slots past K are masked afterwards.  (A branch
+    // around each load made every load wait for the one before it.)
     for (int t0 = 0; t0 < a.T; t0 += 256) {
         int idv[4][8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int tc = min(t0 + 64 * c + lane, a.T - 1);
 #pragma unroll
-            for (int s = 0; s < 8; ++s) idv[c][s] = s < a.K ? a.ids[(size_t)tc * a.K + s] : -1;
+            for (int s = 0; s < 8; ++s) idv[c][s] = a.ids[(size_t)tc * a.K + min(s, a.K - 1)];
         }
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s >= a.K) idv[c][s] = -1;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int t = t0 + 64 * c + lane;
@@ -156,28 +163,46 @@ __global__ __launch_bounds__(64) void k_dispatch(DispatchArgs a) {
 
 // Offsets (exclusive scan of the counts), the dispatch permutation and its
 // inverse, and (when asked) the list of experts that have rows.  Workgroup e
-// (grid E) loads all counts, scans them in LDS and writes expert e's part of
-// the permutation and its entry of the list.
+// (grid E <= 256) loads all counts, one per lane, scans them (and the
+// has-rows flags) across its 256 lanes and writes expert e's part of the
+// permutation and its entry of the list.
 __global__ __launch_bounds__(256) void k_dispatch_scan(DispatchArgs a) {
-    __shared__ int s_cnt[256], s_off[257], s_rank;
+    __shared__ int s_cnt[256], s_off[257], s_rank, s_nact, s_wc[4], s_wf[4];
     const int e = blockIdx.x;
-    for (int i = threadIdx.x; i < a.E; i += 256) s_cnt[i] = a.counts[i];
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int o = 0, nact = 0;
-        for (int i = 0; i < a.E; ++i) {
-            s_off[i] = o;
-            o += s_cnt[i];
-            if (i == e) s_rank = nact;
-            nact += s_cnt[i] > 0;
-        }
-        s_off[a.E] = o;
-        if (a.act) {
-            if (s_cnt[e] > 0) a.act[s_rank] = make_int4(e, s_off[e], s_cnt[e], 0);
-            if (e == 0) a.n_act[0] = nact;
+    const int i = threadIdx.x, lane = i & 63, wave = i >> 6;
+    const int c = i < a.E ? a.counts[i] : 0;
+    const int f = c > 0 ? 1 : 0;
+    s_cnt[i] = c;
+    // inclusive scans of c and f: within the wave, then over the waves
+    int sc = c, sf = f;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int tc = __shfl_up(sc, d, 64), tf = __shfl_up(sf, d, 64);
+        if (lane >= d) {
+            sc += tc;
+            sf += tf;
         }
     }
+    if (lane == 63) {
+        s_wc[wave] = sc;
+        s_wf[wave] = sf;
+    }
     __syncthreads();
+    for (int w = 0; w < wave; ++w) {
+        sc += s_wc[w];
+        sf += s_wf[w];
+    }
+    if (i < a.E) s_off[i] = sc - c;
+    if (i == a.E - 1) {
+        s_off[a.E] = sc;
+        s_nact = sf;
+    }
+    if (i == e) s_rank = sf - f;
+    __syncthreads();
+    if (threadIdx.x == 0 && a.act) {
+        if (s_cnt[e] > 0) a.act[s_rank] = make_int4(e, s_off[e], s_cnt[e], 0);
+        if (e == 0) a.n_act[0] = s_nact;
+    }
     if (e == 0)
         for (int i = threadIdx.x; i <= a.E; i += 256) a.offsets[i] = s_off[i];
     const int n = s_cnt[e];
