@@ -489,7 +489,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, const GemmCtx& x, i
     // nothing (no exit from inside a turn).  A turn's loads past the end of
     // K read the rows' last bytes.  They come only when nch % 3 != 2, and
     // then they stay in flight into the epilogue, whose registers wait for
-    // them.  The hidden and inter sizes here (11 and 8 chunks) have none.
+    // them.  Hidden 2688 and inter 1856 (11 and 8 chunks) have none.
     constexpr ChunkPrefetch<true> PF{};
     constexpr ChunkPrefetch<false> NP{};
     int c = 0;
