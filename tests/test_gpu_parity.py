@@ -63,8 +63,11 @@ def test_dequant_full_expert_matrix(fmt):
 
 # --- router: ids exact, gates within 1e-5 ------------------------------------
 
-@pytest.mark.parametrize("T", [1, 4, 37])
+@pytest.mark.parametrize("T", [1, 4, 37, 200, 1000])
 def test_router_topk(T):
+    # 1: fused-decode form; 4: the small-batch logits kernel; 37, 200: the
+    # MFMA router GEMM one token block per wave; 1000: two blocks per wave,
+    # with a ragged last 32-token tile
     wg, b = synth.router(SEED, 0, 3, E, H)
     x, r, _ = x_with_clear_routing(SEED, 0, 3, wg, b, T, K)
     router = upload_router(wg, b, K)
