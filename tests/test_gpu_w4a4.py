@@ -84,8 +84,13 @@ def _check(bank, wg, b, x, r, out, K, sample=None):
     return worst_h, worst_y
 
 
-def test_w4a4_small_ragged():
-    T, E, H, I, K = 64, 16, 256, 192, 6
+@pytest.mark.parametrize("T,H,I", [(64, 256, 192), (40, 320, 128)], ids=["h256", "h320"])
+def test_w4a4_small_ragged(T, H, I):
+    # h320: hidden 320 and inter 128 leave ragged ends everywhere: a last
+    # down-GEMM column tile of 64, an up-GEMM chunk of 64 k, router
+    # partitions of 2 or 3 blocks of 16, 20 quantizer blocks per row and a
+    # combine workgroup with idle lanes
+    E, K = 16, 6
     bank = synth.expert_bank(SEED, synth.FAM_W4A4, 0, E, H, I, "nvfp4")
     wg, b = synth.router(SEED, synth.FAM_W4A4, 0, E, H, 0.5 / np.sqrt(H))
     x, r, _ = x_with_clear_routing(SEED, synth.FAM_W4A4, 0, wg, b, T, K)
