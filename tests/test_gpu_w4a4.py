@@ -103,6 +103,19 @@ def test_w4a4_small_ragged(T, H, I):
     print(f"small: h {wh:.3f}, y {wy:.3f}; end-to-end ratio {worst_e2e:.3f}, h code bytes differing {flips}")
 
 
+@pytest.mark.parametrize("K", [1, 8])
+def test_w4a4_top_k_range(K):
+    # the smallest and the largest top-k: the dispatch reads every slot of a
+    # token's ids with the slot index clamped to K - 1 and masks slots >= K
+    T, E, H, I = 48, 16, 256, 192
+    bank = synth.expert_bank(SEED, synth.FAM_W4A4, 2, E, H, I, "nvfp4")
+    wg, b = synth.router(SEED, synth.FAM_W4A4, 2, E, H, 0.5 / np.sqrt(H))
+    x, r, _ = x_with_clear_routing(SEED, synth.FAM_W4A4, 2, wg, b, T, K)
+    out = _run(upload_router(wg, b, K), upload_bank(bank, "nvfp4"), x, K)
+    wh, wy = _check(bank, wg, b, x, r, out, K)
+    print(f"K={K}: h {wh:.3f}, y {wy:.3f}")
+
+
 def test_w4a4_full_chunk():
     # every one of the 1024 tokens, every stage
     T, E, H, I, K = 1024, 128, 2688, 1856, 6
